@@ -1,0 +1,350 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test checks the oracle against something the pages print (tests/golden),
+a closed form, an invariant of the method, a library routine, or exact integer
+arithmetic, chosen so that a plausible slip (a dropped term, swapped primes or
+axes, the wrong scale, + instead of XOR, overwrite instead of accumulate)
+fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy.interpolate import RegularGridInterpolator
+
+from multiresolution_hash_grid_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+
+
+@pytest.fixture(scope="module")
+def page():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def exact_floor_resolution(L, n_min, n_max, l):
+    """floor(N_min * (N_max/N_min)^(l/(L-1))) in exact integer arithmetic: the
+    largest m with m^(L-1) <= N_min^(L-1-l) * N_max^l."""
+    if L == 1:
+        return n_min
+    rhs = n_min ** (L - 1 - l) * n_max ** l
+    m = int(round(n_min * (n_max / n_min) ** (l / (L - 1)))) + 2
+    while m ** (L - 1) > rhs:
+        m -= 1
+    while (m + 1) ** (L - 1) <= rhs:
+        m += 1
+    return m
+
+
+# ----------------------------------------------------------------------------- resolutions
+
+def test_resolution_table_endpoints_from_page(oracle, page):
+    d = page["defaults"]
+    res = oracle.resolutions(d["n_levels"], d["base_resolution"], d["finest_resolution"])
+    rt = page["resolution_table"]
+    assert len(res) == rt["n_levels"]
+    assert res[0] == rt["first_level"] and res[-1] == rt["last_level"]
+    # The page table's second row (32^3) disagrees with the formula on the same page
+    # (it gives 20): that row is read as garbled.
+    assert res[1] != page["resolution_table_level2_printed"]["value"]
+
+
+@pytest.mark.parametrize("name", ["tiny", "standard", "large_f16"])
+def test_resolutions_match_exact_integer_roots(oracle, name):
+    w = I.WORKLOADS[name]
+    res = oracle.resolutions(w.n_levels, w.base_resolution, w.finest_resolution)
+    exact = [exact_floor_resolution(w.n_levels, w.base_resolution, w.finest_resolution, l)
+             for l in range(w.n_levels)]
+    assert list(res) == exact
+
+
+def test_resolutions_power_of_two_progression(oracle):
+    # Where the float64 growth factor comes out exactly 2, every level is N_min * 2^l.
+    import math
+    hits = 0
+    for L in range(2, 12):
+        for n_min in (1, 2, 3, 4, 5, 16):
+            n_max = n_min << (L - 1)
+            b = math.exp((math.log(n_max) - math.log(n_min)) / (L - 1))
+            if b != 2.0:
+                continue
+            hits += 1
+            assert list(oracle.resolutions(L, n_min, n_max)) == [n_min << l for l in range(L)]
+    assert hits >= 20
+
+
+def test_resolutions_follow_float64_page_expression(oracle):
+    # Reading: the page's Python float64 expression is the definition, also where it
+    # lands below an exact integer (b = exp(ln 6 - ln 3) = 1.9999999999999998 -> 5).
+    import math
+    for L, n_min, n_max in ((2, 3, 6), (2, 1, 64), (5, 7, 700), (16, 16, 512), (32, 16, 4096)):
+        b = math.exp((math.log(n_max) - math.log(n_min)) / (L - 1))
+        page = [int(math.floor(n_min * (b ** l))) for l in range(L)]
+        assert list(oracle.resolutions(L, n_min, n_max)) == page
+    assert list(oracle.resolutions(2, 3, 6)) == [3, 5]
+
+
+def test_resolutions_single_level_and_errors(oracle):
+    assert list(oracle.resolutions(1, 7, 9)) == [7]
+    with pytest.raises(ValueError):
+        oracle.resolutions(4, 16, 8)
+
+
+def test_parameter_count_from_page(page):
+    d = page["defaults"]
+    assert d["n_levels"] * (1 << d["log2_table_size"]) * d["n_features"] == page["parameter_count"]["value"]
+
+
+# ----------------------------------------------------------------------------- spatial hash
+
+def _vertex_hash(oracle, verts, log2T, N=8):
+    """Hash of integer vertices through the oracle's corner export, using a one-level
+    grid of power-of-two resolution N so that x = v / N lands exactly on v."""
+    g = oracle.grid(1, 2, log2T, N, N)
+    x = (np.asarray(verts, dtype=np.float64) / N).astype(np.float32)
+    idx, _ = oracle.corners(g, x)
+    return idx[:, 0, 0].astype(np.int64)
+
+
+@pytest.mark.parametrize("log2T", [10, 19, 21])
+def test_hash_axis_primes_from_page(oracle, page, log2T):
+    T = 1 << log2T
+    primes = page["primes_xyz"]["values"]
+    h = _vertex_hash(oracle, [[1, 0, 0], [0, 1, 0], [0, 0, 1], [0, 0, 0]], log2T)
+    assert list(h) == [primes[0] % T, primes[1] % T, primes[2] % T, 0]
+
+
+@pytest.mark.parametrize("log2T", [10, 19])
+def test_hash_is_xor_of_per_axis_products(oracle, log2T):
+    rng = np.random.default_rng(1)
+    v = rng.integers(0, 4000, size=(200, 3))
+    z = np.zeros_like(v)
+    hx = _vertex_hash(oracle, np.stack([v[:, 0], z[:, 1], z[:, 2]], 1), log2T)
+    hy = _vertex_hash(oracle, np.stack([z[:, 0], v[:, 1], z[:, 2]], 1), log2T)
+    hz = _vertex_hash(oracle, np.stack([z[:, 0], z[:, 1], v[:, 2]], 1), log2T)
+    h = _vertex_hash(oracle, v, log2T)
+    assert np.array_equal(h, hx ^ hy ^ hz)          # XOR, not +
+    assert np.array_equal(hx, v[:, 0] % (1 << log2T))  # prime 1 on x
+
+
+@pytest.mark.parametrize("axis", [1, 2])
+def test_hash_axis_term_is_a_product(oracle, axis):
+    # (a + b) * p = a * p + b * p (mod T): the per-axis term is multiplicative.
+    T = 1 << 19
+    rng = np.random.default_rng(2)
+    a = rng.integers(0, 2000, size=100)
+    b = rng.integers(0, 2000, size=100)
+
+    def along(c):
+        v = np.zeros((len(c), 3), dtype=np.int64)
+        v[:, axis] = c
+        return _vertex_hash(oracle, v, 19)
+
+    assert np.array_equal((along(a) + along(b)) % T, along(a + b))
+
+
+def test_hash_negative_coordinate_wraps(oracle):
+    # Python's % on the int64 product (page code) and two's-complement low bits agree.
+    T = 1 << 10
+    h = _vertex_hash(oracle, [[-1, 0, 0], [0, -1, 0], [-3, -5, -7]], 10)
+    assert h[0] == T - 1
+    assert h[1] == (-2654435761) % T
+    assert h[2] == ((-3) ^ (-5 * 2654435761) ^ (-7 * 805459861)) % T
+
+
+def test_corner_order_dx_outer_dz_inner(oracle):
+    # Corner k = 4 dx + 2 dy + dz is the hash of v0 + (dx, dy, dz) (page loop nesting).
+    g = oracle.grid(1, 2, 19, 16, 16)
+    rng = np.random.default_rng(3)
+    v0 = rng.integers(0, 15, size=(50, 3))
+    x = ((v0 + 0.25) / 16).astype(np.float32)
+    idx, _ = oracle.corners(g, x)
+    for k in range(8):
+        d = np.array([(k >> 2) & 1, (k >> 1) & 1, k & 1])
+        assert np.array_equal(idx[:, 0, k], _vertex_hash(oracle, v0 + d, 19, N=16))
+
+
+def test_collision_free_levels_census(oracle):
+    # Derived census: level 0 of the tiny and standard grids hashes injectively,
+    # the next level does not.
+    for name in ("tiny", "standard"):
+        w = I.WORKLOADS[name]
+        res = oracle.resolutions(w.n_levels, w.base_resolution, w.finest_resolution)
+        for l, expect in ((0, True), (1, False)):
+            N = int(res[l])
+            v = np.stack(np.meshgrid(*[np.arange(N + 1)] * 3, indexing="ij"), -1).reshape(-1, 3)
+            h = _vertex_hash(oracle, v, w.log2_table_size, N=8 if N % 8 else N)
+            assert (len(np.unique(h)) == len(v)) == expect
+
+
+# ----------------------------------------------------------------------------- interpolation
+
+@pytest.mark.parametrize("name", ["tiny", "standard"])
+def test_weights_partition_of_unity(oracle, name):
+    w = I.WORKLOADS[name]
+    x = I.points_uniform(7, 2000)
+    _, wt = oracle.corners(oracle.grid_of(w), x)
+    assert np.all(wt >= 0.0)
+    assert np.max(np.abs(wt.sum(-1) - 1.0)) < 1e-14
+
+
+def test_vertex_points_return_the_vertex_feature(oracle):
+    # x = v / N_l at power-of-two N_l: fl32(x * N_l) = v, all weight on corner 0.
+    w = I.WORKLOADS["tiny"]
+    g = oracle.grid_of(w)
+    t = I.make_table(w)
+    res = oracle.resolutions(w.n_levels, w.base_resolution, w.finest_resolution)
+    rng = np.random.default_rng(4)
+    for l, N in enumerate(res):
+        v = rng.integers(0, N + 1, size=(300, 3))
+        x = (v / N).astype(np.float32)
+        out = oracle.forward(g, x, t)
+        idx, _ = oracle.corners(g, x)
+        expect = t[l][idx[:, l, 0]].astype(np.float64)
+        assert np.array_equal(out[:, 2 * l:2 * l + 2], expect)
+
+
+def test_matches_library_trilinear_interpolation(oracle):
+    # Dense vertex grid G_l[v] = table[h(v)] read back at vertex points, then scipy's
+    # RegularGridInterpolator (linear) evaluated at the float32 scaled position.
+    w = I.WORKLOADS["tiny"]
+    g = oracle.grid_of(w)
+    t = I.make_table(w)
+    res = oracle.resolutions(w.n_levels, w.base_resolution, w.finest_resolution)
+    x = I.points_uniform(11, 3000)
+    out = oracle.forward(g, x, t)
+    for l, N in enumerate(res):
+        ax = np.arange(N + 1)
+        v = np.stack(np.meshgrid(ax, ax, ax, indexing="ij"), -1).reshape(-1, 3)
+        G = oracle.forward(g, (v / N).astype(np.float32), t)[:, 2 * l:2 * l + 2]
+        G = G.reshape(N + 1, N + 1, N + 1, 2)
+        pos = (x * np.float32(N)).astype(np.float64)  # one float32 multiply per coordinate
+        ref = RegularGridInterpolator((ax, ax, ax), G, method="linear")(pos)
+        assert np.max(np.abs(out[:, 2 * l:2 * l + 2] - ref)) <= 1e-15
+
+
+@pytest.mark.parametrize("name", ["tiny", "standard"])
+def test_linear_table_reproduced_at_collision_free_level(oracle, name):
+    # table[h(v)] = a . v + c on level 0 (injective) => encoding = a . (x * N_0) + c.
+    w = I.WORKLOADS[name]
+    g = oracle.grid_of(w)
+    N = int(oracle.resolutions(w.n_levels, w.base_resolution, w.finest_resolution)[0])
+    ax = np.arange(N + 1)
+    v = np.stack(np.meshgrid(ax, ax, ax, indexing="ij"), -1).reshape(-1, 3)
+    h = _vertex_hash(oracle, v, w.log2_table_size, N=N)
+    assert len(np.unique(h)) == len(v)
+    a = np.array([[0.5, -0.25, 0.125], [-0.0625, 0.75, 0.375]])
+    c = np.array([0.25, -1.0])
+    t = np.zeros((w.n_levels, w.table_size, 2), dtype=np.float32)
+    t[0][h] = (v @ a.T + c).astype(np.float32)   # dyadic values: exact in float32
+    x = I.points_uniform(5, 4000)
+    out = oracle.forward(g, x, t)
+    pos = (x * np.float32(N)).astype(np.float64)
+    assert np.max(np.abs(out[:, 0:2] - (pos @ a.T + c))) < 1e-12
+
+
+def test_constant_table_gives_constant_encoding(oracle):
+    w = I.WORKLOADS["standard"]
+    g = oracle.grid_of(w)
+    t = np.full((w.n_levels, w.table_size, 2), 0.375, dtype=np.float32)
+    out = oracle.forward(g, I.points_uniform(9, 1000), t)
+    assert np.max(np.abs(out - 0.375)) < 1e-15
+
+
+def test_half_table_decoding_matches_numpy(oracle):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(b) for b in bits[::7]])
+    r = ref[::7]
+    ok = np.isnan(r)
+    assert np.array_equal(np.isnan(got), ok)
+    assert np.array_equal(got[~ok], r[~ok])
+    for b in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0x8001):
+        assert oracle.half_to_double(b) == float(np.uint16(b).view(np.float16))
+
+
+def test_half_table_forward_equals_widened_float_table(oracle):
+    w = I.resized(I.WORKLOADS["large_f16"], 500)
+    t16 = I.make_table(w)
+    x = I.make_points(w)
+    a = oracle.forward(oracle.grid_of(w), x, t16)
+    g32 = oracle.grid(w.n_levels, w.n_features, w.log2_table_size, w.base_resolution, w.finest_resolution)
+    b = oracle.forward(g32, x, t16.astype(np.float32))
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("name", ["tiny", "ray"])
+def test_backward_is_adjoint_of_forward(oracle, name):
+    w = I.resized(I.WORKLOADS[name], 4096)
+    g = oracle.grid_of(w)
+    x = I.make_points(w)
+    t = I.make_table(w)
+    d = I.make_dout(w)
+    lhs = float(np.sum(d.astype(np.float64) * oracle.forward(g, x, t)))
+    rhs = float(np.sum(oracle.backward(g, x, d) * t.astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_backward_level_sums_equal_upstream_sums(oracle):
+    w = I.resized(I.WORKLOADS["standard"], 3000)
+    g = oracle.grid_of(w)
+    x = I.make_points(w)
+    d = I.make_dout(w)
+    grad = oracle.backward(g, x, d)
+    got = grad.sum(axis=1)                                   # [L, F]
+    want = d.astype(np.float64).reshape(-1, w.n_levels, 2).sum(axis=0)
+    assert np.max(np.abs(got - want)) < 1e-9
+
+
+def test_backward_equals_central_difference(oracle):
+    # The encoding is linear in the table, so a central difference is exact up to rounding.
+    w = I.resized(I.WORKLOADS["tiny"], 64)
+    g = oracle.grid_of(w)
+    x = I.make_points(w)
+    d = I.make_dout(w)
+    t = np.zeros((w.n_levels, w.table_size, 2), dtype=np.float32)
+    grad = oracle.backward(g, x, d)
+    idx, _ = oracle.corners(g, x)
+    rng = np.random.default_rng(6)
+    for _ in range(12):
+        l = int(rng.integers(0, w.n_levels))
+        e = int(idx[int(rng.integers(0, 64)), l, int(rng.integers(0, 8))])
+        j = int(rng.integers(0, 2))
+        tp, tm = t.copy(), t.copy()
+        tp[l, e, j] += 0.5
+        tm[l, e, j] -= 0.5
+        fd = np.sum(d * (oracle.forward(g, x, tp) - oracle.forward(g, x, tm)))
+        assert abs(fd - grad[l, e, j]) < 1e-12
+
+
+def test_backward_accumulates_into_buffer(oracle):
+    w = I.resized(I.WORKLOADS["tiny"], 500)
+    g = oracle.grid_of(w)
+    x = I.make_points(w)
+    d = I.make_dout(w)
+    base = np.random.default_rng(8).standard_normal((w.n_levels, w.table_size, 2))
+    got = oracle.backward(g, x, d, base.copy())
+    assert np.allclose(got, base + oracle.backward(g, x, d), rtol=0, atol=1e-12)
+
+
+def test_backward_reads_strided_upstream_rows(oracle):
+    w = I.resized(I.WORKLOADS["tiny"], 300)
+    g = oracle.grid_of(w)
+    x = I.make_points(w)
+    d = I.make_dout(w)
+    wide = np.concatenate([d, np.full((300, 5), 1e9, dtype=np.float32)], axis=1)
+    assert np.array_equal(oracle.backward(g, x, wide), oracle.backward(g, x, d))
+
+
+def test_out_of_domain_points_follow_the_same_formula(oracle):
+    # Coordinates below 0 or above 1 are scaled, floored and hashed like any other
+    # (negative vertices wrap as in the page's Python %).
+    g = oracle.grid(1, 2, 10, 8, 8)
+    x = np.array([[-0.125, 0.0, 0.0], [1.125, 0.0, 0.0]], dtype=np.float32)
+    idx, wt = oracle.corners(g, x)
+    assert idx[0, 0, 0] == (1 << 10) - 1 and idx[1, 0, 0] == 9
+    assert np.all(wt[:, 0, 0] == 1.0)
