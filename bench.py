@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Throughput of the hash-grid encoder on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one forward encoding plus one backward table-gradient scatter of the
+standard Instant-NGP grid (L=16, F=2, T=2^19, N_min=16, N_max=512, fp32
+tables) over 2^18 uniform points in [0,1)^3, all inputs resident in HBM.
+Prints one JSON line with points/s for fwd+bwd, the roofline of the dominant
+kernel (HIP events on the launch stream) and the CPU oracle's throughput on
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_standard.json")
+KERNEL_SOURCE = os.path.join(ROOT, "multiresolution_hash_grid_amd", "csrc", "encode_kernels.hip")
+
+
+def algorithmic_bytes_per_point(w, table_esize: int) -> dict:
+    """Bytes the method itself moves per point: the point once, 2^D corners x L
+    levels x F features of table, the L*F outputs (forward); the point, the L*F
+    upstream values and 2^D x L x F fp32 atomic adds (backward)."""
+    D, L, F = 3, w.n_levels, w.n_features
+    corners = (1 << D) * L * F
+    return {"fwd": 4 * D + corners * table_esize + 4 * L * F,
+            "bwd": 4 * D + 4 * L * F + corners * 4}
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on other kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, t, d, budget_s: float) -> dict:
+    """The CPU oracle, as it stands, on the same workload: forward + backward of
+    all points, repeated until about `budget_s` seconds of work."""
+    from oracle import hashgrid_oracle as oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    oracle.set_threads(threads)
+    g = oracle.grid_of(w)
+    reps, spent = 0, 0.0
+    while spent < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        oracle.forward(g, x, t)
+        oracle.backward(g, x, d)
+        spent += time.perf_counter() - t0
+        reps += 1
+    return {"value": w.n_points * reps / spent, "unit": "points/s", "cores": min(threads, w.n_levels),
+            "kind": "oracle",
+            "sample": f"full workload ({w.n_points} points) forward+backward x{reps}, {spent:.1f} s, "
+                      f"OpenMP over levels"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="standard")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the encoder shards by points; see the design notes)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import multiresolution_hash_grid_amd as hg
+    from multiresolution_hash_grid_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    if w.mlp:
+        raise SystemExit("the fused encode+MLP workload is measured by its own entry point")
+    cfg = hg.HashGridConfig.of(w)
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
+    x_h, t_h, d_h = inputs.make_points(w), inputs.make_table(w), inputs.make_dout(w)
+    x = torch.from_numpy(x_h).to(dev)
+    t = torch.from_numpy(t_h).to(dev)
+    d = torch.from_numpy(d_h).to(dev)
+    out = torch.empty((w.n_points, cfg.out_features), device=dev)
+    grad = torch.zeros(cfg.table_shape, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        hg.hashgrid_forward(cfg, x, t, out=out)
+        hg.hashgrid_backward(cfg, x, d, grad)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        hg.hashgrid_forward(cfg, x, t, out=out)
+        ev[k][1].record()
+        hg.hashgrid_backward(cfg, x, d, grad)
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+
+    esize = 2 if w.table_dtype == "f16" else 4
+    bpp = algorithmic_bytes_per_point(w, esize)
+    if bwd_ms >= fwd_ms:
+        dom, dom_ms, dom_bytes, kname = "backward", bwd_ms, bpp["bwd"], "bwd_f2_kernel"
+    else:
+        dom, dom_ms, dom_bytes, kname = "forward", fwd_ms, bpp["fwd"], "fwd_f2_kernel"
+    achieved = dom_bytes * w.n_points / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(kname)
+
+    result = {
+        "metric": "points/sec hash-grid encode fwd & fwd+bwd (L16,T2^19,F2); % HBM roofline",
+        "value": w.n_points * K / elapsed,
+        "unit": "points/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: L={w.n_levels} F={w.n_features} T=2^{w.log2_table_size} "
+                        f"N_min={w.base_resolution} N_max={w.finest_resolution} {w.table_dtype} tables, "
+                        f"N={w.n_points} {w.structure} points, forward+backward per step",
+            "points_per_step": w.n_points,
+        },
+        "fwd_points_per_s": w.n_points / (fwd_ms * 1e-3),
+        "bwd_points_per_s": w.n_points / (bwd_ms * 1e-3),
+        "fwd_kernel_ms": fwd_ms,
+        "bwd_kernel_ms": bwd_ms,
+        "algorithmic_bytes_per_point": bpp,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+        },
+        "roofline_fwd_frac": bpp["fwd"] * w.n_points / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline_fwd_bwd_frac": (bpp["fwd"] + bpp["bwd"]) * w.n_points * K / elapsed / 1e9 / HBM_PEAK_GBS,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, x_h, t_h, d_h, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

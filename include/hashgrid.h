@@ -1,0 +1,134 @@
+/*
+ * hashgrid.h -- C ABI of the MI355X (gfx950) multiresolution hash-grid encoder.
+ *
+ * The method (Instant-NGP style multiresolution hash encoding) is described on
+ * the page "Speeding up NeRFace with Instant-NGP hash encoding" (ipipp.com),
+ * section 2 and its HashGridEncoder listing, and on the Instant-NGP overview
+ * (ijyty.com) section 2.2:
+ *   - L levels with resolutions N_l = floor(N_min * b^l),
+ *     b = exp((ln N_max - ln N_min) / (L - 1)), evaluated in IEEE float64;
+ *   - one table of T = 2^log2_table_size entries of F features per level;
+ *   - a point x is scaled by N_l, the 2^D corners of its voxel are hashed with
+ *     h(c) = (c_0 * 1) XOR (c_1 * 2654435761) XOR (c_2 * 805459861) mod T,
+ *     the corner features are gathered and blended with multilinear weights;
+ *   - the per-level F-vectors are concatenated level-major into L*F outputs.
+ *
+ * Conventions for every entry point:
+ *   - All array arguments are DEVICE pointers (memory of the current HIP device)
+ *     unless the comment says "host".  The caller owns every buffer; the library
+ *     allocates nothing and keeps no per-call state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     only enqueue work on it; they never synchronise.  Results are ready when
+ *     the stream's work has completed.
+ *   - Return value: HG_OK (0) on success, a negative HG_E* code otherwise; the
+ *     thread-local text of the last failure is returned by hashgrid_last_error().
+ *     Argument checks happen on the host before anything is enqueued, so a
+ *     rejected call has no effect.
+ *   - n == 0 is valid and does nothing (pointers are then not inspected).
+ *   - Points outside [0,1)^D are processed by the same formula (the voxel index
+ *     is floor(x * N_l) as a signed 32-bit integer and the hash wraps in uint32),
+ *     and every table access is masked into [0, T): no input can make the
+ *     library read or write out of bounds.  Inputs with |x * N_l| >= 2^31, NaN
+ *     or Inf give unspecified (but in-bounds) results.
+ */
+#ifndef HASHGRID_H
+#define HASHGRID_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HASHGRID_ABI_VERSION 1
+
+/* Return codes. */
+#define HG_OK 0
+#define HG_EINVAL (-1)       /* bad config, pointer, alignment, size or stride */
+#define HG_EUNSUPPORTED (-2) /* valid but not built: F, D or dtype combination */
+#define HG_EHIP (-3)         /* the HIP runtime reported an error on launch     */
+
+/* Element types. */
+#define HG_F32 0 /* IEEE binary32                                        */
+#define HG_F16 1 /* IEEE binary16 (storage only; all arithmetic is fp32) */
+
+/* Grid description.  Field names follow the pages' constructor arguments
+ * (n_levels, n_features_per_level, log2_hashmap_size, base_resolution,
+ * finest_resolution). */
+typedef struct hg_config {
+    int32_t n_dims;            /* D, coordinates per point: 3                                   */
+    int32_t n_levels;          /* L, 1..64                                                      */
+    int32_t n_features;        /* F, features per table entry: 2                                */
+    int32_t log2_table_size;   /* T = 2^log2_table_size entries per level, 1..28                */
+    int32_t base_resolution;   /* N_min >= 1                                                    */
+    int32_t finest_resolution; /* N_max, N_min <= N_max < 2^24                                  */
+    int32_t table_dtype;       /* HG_F32 or HG_F16                                              */
+    int32_t grad_dtype;        /* HG_F32 (the gradient buffer is always accumulated in fp32)    */
+} hg_config;
+
+/* Version of this ABI (HASHGRID_ABI_VERSION of the built library). */
+int hashgrid_abi_version(void);
+
+/* Text of the last failure on the calling thread ("" if none).  Valid until
+ * the next call on the same thread. */
+const char *hashgrid_last_error(void);
+
+/* Level resolutions N_0..N_{L-1} (ipipp.com HashGridEncoder.__init__: the
+ * float64 expression floor(N_min * b^l); with L == 1 the only level is N_min).
+ * res_out: HOST int32[L].  Errors: HG_EINVAL on a bad config or NULL. */
+int hashgrid_resolutions(const hg_config *cfg, int32_t *res_out);
+
+/* Forward encoding (ipipp.com section 2 and HashGridEncoder.forward).
+ *   x     : float32 [n][D], row-major (AoS), 4-byte aligned.
+ *   table : [L][T][F] of cfg->table_dtype, contiguous, level-major; aligned to
+ *           F * sizeof(element) (8 bytes for fp32 F=2, 4 bytes for fp16 F=2).
+ *   out   : float32, row p holds the L*F encoded features of point p at
+ *           out[p * out_row_stride + l * F + j]; columns beyond L*F are not
+ *           touched, so the encoding can be written into a wider buffer.
+ *           4-byte aligned; out_row_stride >= L*F (elements).
+ *   The blend of level l is sum_k w_k * table[l][h(corner_k)][j] computed in
+ *   fp32, with w_k the trilinear weight of corner k.
+ * Errors: HG_EINVAL (config, NULL, alignment, n < 0, stride), HG_EUNSUPPORTED,
+ *         HG_EHIP. */
+int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void *table,
+                     float *out, int64_t out_row_stride, void *stream);
+
+/* Backward: gradient of the encoding with respect to the tables (ipipp.com
+ * section 2 -- only the corners a point sampled receive gradient -- i.e. the
+ * adjoint of the forward gather).
+ *   x      : float32 [n][D], the points of the forward call.
+ *   dout   : float32, dL/dout with row stride dout_row_stride >= L*F elements;
+ *            element (p, l*F + j) is read, other columns are ignored.
+ *   dtable : float32 [L][T][F], 4-byte aligned.  ACCUMULATED INTO:
+ *            dtable[l][h(corner_k)][j] += w_k * dout[p][l*F + j] for every point,
+ *            level and corner (fp32 atomic adds; their order is unspecified, so
+ *            results can differ from run to run in the last bits).  The caller
+ *            zeroes the buffer when it wants the gradient of one batch alone.
+ * Errors: as hashgrid_forward. */
+int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const float *dout,
+                      int64_t dout_row_stride, float *dtable, void *stream);
+
+/* Debug export of the corner table indices and interpolation weights.
+ *   idx : uint32 [n][L][2^D]  -- hashed index in [0, T) of corner k of level l,
+ *   w   : float32 [n][L][2^D] -- its fp32 weight,
+ * with corners ordered k = 4*dx + 2*dy + dz (the pages' loop nesting, x outer).
+ * Either pointer may be NULL to skip that output.  Errors: as hashgrid_forward. */
+int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint32_t *idx,
+                           float *w, void *stream);
+
+/* Performance knobs (launch shapes).  They never change results beyond the
+ * unspecified order of the backward's atomic adds.  Process-wide; not
+ * thread-safe against concurrent launches.  Returns HG_EINVAL for an unknown
+ * key or an out-of-range value. */
+#define HG_TUNE_FWD_LANES 0    /* lanes per (point, level) in the forward: 1 or 2        */
+#define HG_TUNE_BWD_LANES 1    /* lanes per (point, level) in the backward: 1, 2 or 4    */
+#define HG_TUNE_CHUNK_POINTS 2 /* points per workgroup work item: 64..65536, power of 2  */
+#define HG_TUNE_XCD_MAP 3      /* 1: give each XCD its own levels, 0: plain linear order */
+int hashgrid_tune(int key, int value);
+int hashgrid_tune_get(int key);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HASHGRID_H */

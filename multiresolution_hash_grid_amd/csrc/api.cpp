@@ -1,0 +1,208 @@
+// Host side of libhashgrid: the C ABI declared in include/hashgrid.h --
+// argument checks, level resolutions, work decomposition and kernel launch.
+// No device memory is allocated here and nothing synchronises the stream.
+#include "hashgrid.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "hashgrid_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return HG_OK;
+}
+
+struct Tuning {
+    int fwd_lanes = 2;
+    int bwd_lanes = 4;
+    int chunk_points = 1024;
+    int xcd_map = 1;
+};
+Tuning g_tune;
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Level resolutions: ipipp.com HashGridEncoder.__init__, the float64
+// expression floor(N_min * b^l) with b = exp((ln N_max - ln N_min) / (L - 1)).
+void resolutions(const hg_config &c, int32_t *res) {
+    if (c.n_levels == 1) {
+        res[0] = c.base_resolution;
+        return;
+    }
+    const double b = exp((log((double)c.finest_resolution) - log((double)c.base_resolution)) /
+                         (double)(c.n_levels - 1));
+    for (int l = 0; l < c.n_levels; ++l) res[l] = (int32_t)floor((double)c.base_resolution * pow(b, (double)l));
+}
+
+int check_config(const hg_config *c) {
+    if (!c) return fail(HG_EINVAL, "config is NULL");
+    if (c->n_levels < 1 || c->n_levels > hg::kMaxLevels)
+        return fail(HG_EINVAL, "n_levels %d outside 1..%d", c->n_levels, hg::kMaxLevels);
+    if (c->log2_table_size < 1 || c->log2_table_size > 28)
+        return fail(HG_EINVAL, "log2_table_size %d outside 1..28", c->log2_table_size);
+    if (c->base_resolution < 1) return fail(HG_EINVAL, "base_resolution %d < 1", c->base_resolution);
+    if (c->finest_resolution < c->base_resolution || c->finest_resolution >= (1 << 24))
+        return fail(HG_EINVAL, "finest_resolution %d outside [base_resolution, 2^24)", c->finest_resolution);
+    if (c->n_dims < 1 || c->n_features < 1) return fail(HG_EINVAL, "n_dims and n_features must be >= 1");
+    if (c->table_dtype != HG_F32 && c->table_dtype != HG_F16)
+        return fail(HG_EINVAL, "table_dtype %d is neither HG_F32 nor HG_F16", c->table_dtype);
+    if (c->grad_dtype != HG_F32 && c->grad_dtype != HG_F16)
+        return fail(HG_EINVAL, "grad_dtype %d is neither HG_F32 nor HG_F16", c->grad_dtype);
+    if (c->n_dims != 3) return fail(HG_EUNSUPPORTED, "n_dims %d: only 3 is built", c->n_dims);
+    if (c->n_features != 2) return fail(HG_EUNSUPPORTED, "n_features %d: only 2 is built", c->n_features);
+    if (c->grad_dtype != HG_F32) return fail(HG_EUNSUPPORTED, "grad_dtype must be HG_F32");
+    return HG_OK;
+}
+
+int plan(const hg_config &c, int64_t n, hg::LaunchParams &lp) {
+    lp.n_levels = c.n_levels;
+    lp.log2_table_size = c.log2_table_size;
+    lp.mask = (uint32_t)((1ull << c.log2_table_size) - 1);
+    lp.chunk_pts = g_tune.chunk_points;
+    const int64_t chunks = (n + lp.chunk_pts - 1) / lp.chunk_pts;
+    if (chunks * c.n_levels > ((int64_t)1 << 30))
+        return fail(HG_EINVAL, "n = %lld: too many points for one call", (long long)n);
+    lp.chunks = (int32_t)chunks;
+    lp.items = lp.chunks * c.n_levels;
+    lp.per_xcd = (lp.items + hg::kNumXcd - 1) / hg::kNumXcd;
+    lp.xcd_map = g_tune.xcd_map;
+    resolutions(c, lp.res);
+    // Levels ordered by (l mod 8, l): the contiguous run of work items an XCD
+    // receives then mixes coarse and fine levels (L = 16: levels x and x + 8).
+    int pos = 0;
+    for (int r = 0; r < hg::kNumXcd; ++r)
+        for (int l = r; l < c.n_levels; l += hg::kNumXcd) lp.level_order[pos++] = (int8_t)l;
+    return HG_OK;
+}
+
+int check_points(int64_t n, const float *x) {
+    if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
+    if (!x) return fail(HG_EINVAL, "x is NULL");
+    if (!aligned(x, 4)) return fail(HG_EINVAL, "x is not 4-byte aligned");
+    return HG_OK;
+}
+
+int launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(HG_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int hashgrid_abi_version(void) { return HASHGRID_ABI_VERSION; }
+
+const char *hashgrid_last_error(void) { return g_last_error.c_str(); }
+
+int hashgrid_resolutions(const hg_config *cfg, int32_t *res_out) {
+    int rc = check_config(cfg);
+    if (rc == HG_EINVAL) return rc;
+    if (!res_out) return fail(HG_EINVAL, "res_out is NULL");
+    resolutions(*cfg, res_out);
+    return ok();
+}
+
+int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void *table, float *out,
+                     int64_t out_row_stride, void *stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n == 0) return ok();
+    if ((rc = check_points(n, x))) return rc;
+    const size_t esize = cfg->table_dtype == HG_F32 ? 4 : 2;
+    if (!table || !aligned(table, esize * cfg->n_features))
+        return fail(HG_EINVAL, "table is NULL or not %zu-byte aligned", esize * cfg->n_features);
+    if (!out || !aligned(out, 4)) return fail(HG_EINVAL, "out is NULL or not 4-byte aligned");
+    if (out_row_stride < (int64_t)cfg->n_levels * cfg->n_features)
+        return fail(HG_EINVAL, "out_row_stride %lld < L*F", (long long)out_row_stride);
+    hg::LaunchParams lp;
+    if ((rc = plan(*cfg, n, lp))) return rc;
+    return launch_status(hg::launch_forward(lp, x, n, table, cfg->table_dtype, out, out_row_stride,
+                                            g_tune.fwd_lanes, (hipStream_t)stream),
+                         "forward");
+}
+
+int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const float *dout,
+                      int64_t dout_row_stride, float *dtable, void *stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n == 0) return ok();
+    if ((rc = check_points(n, x))) return rc;
+    if (!dout || !aligned(dout, 4)) return fail(HG_EINVAL, "dout is NULL or not 4-byte aligned");
+    if (!dtable || !aligned(dtable, 4)) return fail(HG_EINVAL, "dtable is NULL or not 4-byte aligned");
+    if (dout_row_stride < (int64_t)cfg->n_levels * cfg->n_features)
+        return fail(HG_EINVAL, "dout_row_stride %lld < L*F", (long long)dout_row_stride);
+    hg::LaunchParams lp;
+    if ((rc = plan(*cfg, n, lp))) return rc;
+    return launch_status(hg::launch_backward(lp, x, n, dout, dout_row_stride, dtable, g_tune.bwd_lanes,
+                                             (hipStream_t)stream),
+                         "backward");
+}
+
+int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint32_t *idx, float *w,
+                           void *stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n == 0) return ok();
+    if ((rc = check_points(n, x))) return rc;
+    if (idx && !aligned(idx, 4)) return fail(HG_EINVAL, "idx is not 4-byte aligned");
+    if (w && !aligned(w, 4)) return fail(HG_EINVAL, "w is not 4-byte aligned");
+    if (n > ((int64_t)1 << 31) - 256) return fail(HG_EINVAL, "n too large for the debug export");
+    hg::LaunchParams lp;
+    if ((rc = plan(*cfg, n, lp))) return rc;
+    return launch_status(hg::launch_debug_corners(lp, x, n, idx, w, (hipStream_t)stream), "debug_corners");
+}
+
+int hashgrid_tune(int key, int value) {
+    switch (key) {
+    case HG_TUNE_FWD_LANES:
+        if (value != 1 && value != 2) break;
+        g_tune.fwd_lanes = value;
+        return ok();
+    case HG_TUNE_BWD_LANES:
+        if (value != 1 && value != 2 && value != 4) break;
+        g_tune.bwd_lanes = value;
+        return ok();
+    case HG_TUNE_CHUNK_POINTS:
+        if (value < 64 || value > 65536 || (value & (value - 1))) break;
+        g_tune.chunk_points = value;
+        return ok();
+    case HG_TUNE_XCD_MAP:
+        if (value != 0 && value != 1) break;
+        g_tune.xcd_map = value;
+        return ok();
+    default:
+        return fail(HG_EINVAL, "unknown tuning key %d", key);
+    }
+    return fail(HG_EINVAL, "value %d out of range for tuning key %d", value, key);
+}
+
+int hashgrid_tune_get(int key) {
+    switch (key) {
+    case HG_TUNE_FWD_LANES: return g_tune.fwd_lanes;
+    case HG_TUNE_BWD_LANES: return g_tune.bwd_lanes;
+    case HG_TUNE_CHUNK_POINTS: return g_tune.chunk_points;
+    case HG_TUNE_XCD_MAP: return g_tune.xcd_map;
+    default: return fail(HG_EINVAL, "unknown tuning key %d", key);
+    }
+}
+
+}  // extern "C"

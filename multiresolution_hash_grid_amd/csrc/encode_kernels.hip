@@ -1,0 +1,272 @@
+// HIP kernels of the hash-grid encoder for gfx950 (CDNA4, wave64).
+//
+// Method: ipipp.com "Speeding up NeRFace with Instant-NGP hash encoding",
+// section 2 and its HashGridEncoder listing; hash formula of the ijyty.com
+// Instant-NGP overview, section 2.2.  Per (point, level):
+//   pos_d = x_d * N_l (one fp32 multiply, round to nearest), v_d = floor(pos_d),
+//   f_d = pos_d - v_d (exact), corner c = v + (dx, dy, dz),
+//   h(c) = (c_x ^ c_y * 2654435761 ^ c_z * 805459861) mod 2^log2T in uint32,
+//   out[l*F + j] = sum over the 8 corners of w_c * table[l][h(c)][j],
+//   w_c = prod_d (d-th offset ? f_d : 1 - f_d).
+// The backward scatters dL/dout * w_c back into every table entry a corner
+// hashed to (the adjoint of the gather) with fp32 atomic adds.
+//
+// Memory behaviour on MI355X.  The corner gathers are the traffic: 8 random
+// F-vectors per point and level.  Because the x prime is 1, the corners
+// (v_x, y, z) and (v_x + 1, y, z) differ only in the low bits of their index
+// (they are 2^(t+1) - 1 apart at most, t = trailing ones of v_x), so they share
+// a 128-byte line 15 times out of 16.  The "lane pair" layout below gives the
+// two x-corners of one point to two adjacent lanes of the same load or atomic
+// instruction, so the memory pipeline sees about 4 distinct lines per
+// (point, level) instead of 8.
+#include "hashgrid_internal.h"
+
+namespace hg {
+namespace {
+
+// ---------------------------------------------------------------- helpers
+
+struct Item {
+    int level;
+    int64_t p0;
+};
+
+__device__ __forceinline__ bool decode_item(const LaunchParams &lp, Item &it) {
+    int g = blockIdx.x;
+    int item = lp.xcd_map ? (g % kNumXcd) * lp.per_xcd + g / kNumXcd : g;
+    if (item >= lp.items) return false;
+    int pos = item / lp.chunks;
+    it.level = lp.level_order[pos];
+    it.p0 = (int64_t)(item - pos * lp.chunks) * lp.chunk_pts;
+    return true;
+}
+
+// Voxel of one coordinate: scaled position (fp32 multiply without
+// contraction), its floor as a signed integer and the exact fraction.
+__device__ __forceinline__ void locate1(float xd, float N, int32_t &v, float &f) {
+    float s = __fmul_rn(xd, N);
+    float fl = floorf(s);
+    v = (int32_t)fl;
+    f = s - fl;
+}
+
+// Exchange a value with the other lane of an aligned lane pair (DPP
+// quad_perm [1,0,3,2]); the pair never leaves its quad.
+__device__ __forceinline__ float swap_pair(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// Table element pairs (F = 2).  fp16 entries are widened exactly (subnormals
+// included) and all arithmetic is fp32.
+template <int DT>
+struct Table2;
+
+template <>
+struct Table2<0> {
+    static __device__ __forceinline__ float2 load(const void *base, uint64_t e) {
+        return reinterpret_cast<const float2 *>(base)[e];
+    }
+};
+
+template <>
+struct Table2<1> {
+    static __device__ __forceinline__ float2 load(const void *base, uint64_t e) {
+        uint32_t r = reinterpret_cast<const uint32_t *>(base)[e];
+        _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(r & 0xFFFFu));
+        _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(r >> 16));
+        return make_float2((float)lo, (float)hi);
+    }
+};
+
+__device__ __forceinline__ void fadd(float *p, float v) { unsafeAtomicAdd(p, v); }
+
+// ---------------------------------------------------------------- forward
+
+// LANES = 2: lane `sub` of a pair takes the corners with dx = sub, blends
+// its four (dy, dz) corners with weight w_x(sub) * w_y * w_z, and the pair
+// adds its two halves; lane sub then writes feature sub.
+// LANES = 1: one lane takes all eight corners.
+template <int DT, int LANES>
+__global__ __launch_bounds__(kBlock) void fwd_f2_kernel(const float *__restrict__ x, int64_t n,
+                                                        const void *__restrict__ table,
+                                                        float *__restrict__ out, int64_t ostride,
+                                                        LaunchParams lp) {
+    Item it;
+    if (!decode_item(lp, it)) return;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint32_t mask = lp.mask;
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    const int sub = threadIdx.x % LANES;
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    for (int64_t p = it.p0 + threadIdx.x / LANES; p < end; p += kBlock / LANES) {
+        int32_t v0, v1, v2;
+        float a0, a1, a2;
+        locate1(x[3 * p + 0], N, v0, a0);
+        locate1(x[3 * p + 1], N, v1, a1);
+        locate1(x[3 * p + 2], N, v2, a2);
+        const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hy1 = hy0 + kPrimeY;
+        const uint32_t hz0 = (uint32_t)v2 * kPrimeZ, hz1 = hz0 + kPrimeZ;
+        const float wy0 = 1.f - a1, wz0 = 1.f - a2;
+        float* orow = out + p * ostride + (int64_t)l * 2;
+        if (LANES == 2) {
+            const uint32_t cx = (uint32_t)v0 + (uint32_t)sub;
+            const float2 e00 = Table2<DT>::load(table, lbase + ((cx ^ hy0 ^ hz0) & mask));
+            const float2 e01 = Table2<DT>::load(table, lbase + ((cx ^ hy0 ^ hz1) & mask));
+            const float2 e10 = Table2<DT>::load(table, lbase + ((cx ^ hy1 ^ hz0) & mask));
+            const float2 e11 = Table2<DT>::load(table, lbase + ((cx ^ hy1 ^ hz1) & mask));
+            const float wx = sub ? a0 : 1.f - a0;
+            const float rx = wx * (wy0 * (wz0 * e00.x + a2 * e01.x) + a1 * (wz0 * e10.x + a2 * e11.x));
+            const float ry = wx * (wy0 * (wz0 * e00.y + a2 * e01.y) + a1 * (wz0 * e10.y + a2 * e11.y));
+            // lane 0 keeps feature 0 and needs lane 1's x-half; lane 1 the reverse.
+            const float recv = swap_pair(sub ? rx : ry);
+            orow[sub] = (sub ? ry : rx) + recv;
+        } else {
+            const uint32_t c0 = (uint32_t)v0, c1 = c0 + 1u;
+            float2 e[8];
+            e[0] = Table2<DT>::load(table, lbase + ((c0 ^ hy0 ^ hz0) & mask));
+            e[1] = Table2<DT>::load(table, lbase + ((c0 ^ hy0 ^ hz1) & mask));
+            e[2] = Table2<DT>::load(table, lbase + ((c0 ^ hy1 ^ hz0) & mask));
+            e[3] = Table2<DT>::load(table, lbase + ((c0 ^ hy1 ^ hz1) & mask));
+            e[4] = Table2<DT>::load(table, lbase + ((c1 ^ hy0 ^ hz0) & mask));
+            e[5] = Table2<DT>::load(table, lbase + ((c1 ^ hy0 ^ hz1) & mask));
+            e[6] = Table2<DT>::load(table, lbase + ((c1 ^ hy1 ^ hz0) & mask));
+            e[7] = Table2<DT>::load(table, lbase + ((c1 ^ hy1 ^ hz1) & mask));
+            const float wx0 = 1.f - a0;
+            float r[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float ej[8] = {j ? e[0].y : e[0].x, j ? e[1].y : e[1].x, j ? e[2].y : e[2].x,
+                                     j ? e[3].y : e[3].x, j ? e[4].y : e[4].x, j ? e[5].y : e[5].x,
+                                     j ? e[6].y : e[6].x, j ? e[7].y : e[7].x};
+                const float lo = wy0 * (wz0 * ej[0] + a2 * ej[1]) + a1 * (wz0 * ej[2] + a2 * ej[3]);
+                const float hi = wy0 * (wz0 * ej[4] + a2 * ej[5]) + a1 * (wz0 * ej[6] + a2 * ej[7]);
+                r[j] = wx0 * lo + a0 * hi;
+            }
+            orow[0] = r[0];
+            orow[1] = r[1];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- backward
+
+// LANES = 4: lane (dx, j) = (sub >> 1, sub & 1) adds feature j of the four
+// corners with that dx; the four lanes of a point hit one or two lines.
+// LANES = 2: lane dx adds both features of its four corners.
+// LANES = 1: one lane adds all sixteen values.
+template <int LANES>
+__global__ __launch_bounds__(kBlock) void bwd_f2_kernel(const float *__restrict__ x, int64_t n,
+                                                        const float *__restrict__ dout,
+                                                        int64_t dstride, float *__restrict__ grad,
+                                                        LaunchParams lp) {
+    Item it;
+    if (!decode_item(lp, it)) return;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint32_t mask = lp.mask;
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    float *__restrict__ g = grad + 2 * lbase;
+    const int sub = threadIdx.x % LANES;
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    for (int64_t p = it.p0 + threadIdx.x / LANES; p < end; p += kBlock / LANES) {
+        int32_t v0, v1, v2;
+        float a0, a1, a2;
+        locate1(x[3 * p + 0], N, v0, a0);
+        locate1(x[3 * p + 1], N, v1, a1);
+        locate1(x[3 * p + 2], N, v2, a2);
+        const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hy1 = hy0 + kPrimeY;
+        const uint32_t hz0 = (uint32_t)v2 * kPrimeZ, hz1 = hz0 + kPrimeZ;
+        const float wy0 = 1.f - a1, wz0 = 1.f - a2;
+        const float w00 = wy0 * wz0, w01 = wy0 * a2, w10 = a1 * wz0, w11 = a1 * a2;
+        const float *drow = dout + p * dstride + (int64_t)l * 2;
+        if (LANES == 4) {
+            const int dx = sub >> 1, j = sub & 1;
+            const uint32_t cx = (uint32_t)v0 + (uint32_t)dx;
+            const float gw = drow[j] * (dx ? a0 : 1.f - a0);
+            fadd(g + 2 * ((cx ^ hy0 ^ hz0) & mask) + j, gw * w00);
+            fadd(g + 2 * ((cx ^ hy0 ^ hz1) & mask) + j, gw * w01);
+            fadd(g + 2 * ((cx ^ hy1 ^ hz0) & mask) + j, gw * w10);
+            fadd(g + 2 * ((cx ^ hy1 ^ hz1) & mask) + j, gw * w11);
+        } else {
+            const float d0 = drow[0], d1 = drow[1];
+#pragma unroll
+            for (int dx = 0; dx < 2; ++dx) {
+                if (LANES == 2 && dx != sub) continue;
+                const uint32_t cx = (uint32_t)v0 + (uint32_t)dx;
+                const float wx = dx ? a0 : 1.f - a0;
+                const float g0 = d0 * wx, g1 = d1 * wx;
+                const uint32_t i00 = (cx ^ hy0 ^ hz0) & mask, i01 = (cx ^ hy0 ^ hz1) & mask;
+                const uint32_t i10 = (cx ^ hy1 ^ hz0) & mask, i11 = (cx ^ hy1 ^ hz1) & mask;
+                fadd(g + 2 * i00, g0 * w00);
+                fadd(g + 2 * i00 + 1, g1 * w00);
+                fadd(g + 2 * i01, g0 * w01);
+                fadd(g + 2 * i01 + 1, g1 * w01);
+                fadd(g + 2 * i10, g0 * w10);
+                fadd(g + 2 * i10 + 1, g1 * w10);
+                fadd(g + 2 * i11, g0 * w11);
+                fadd(g + 2 * i11 + 1, g1 * w11);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- debug export
+
+__global__ __launch_bounds__(kBlock) void corners_kernel(const float *__restrict__ x, int64_t n,
+                                                         uint32_t *__restrict__ idx,
+                                                         float *__restrict__ w, LaunchParams lp) {
+    const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int l = blockIdx.y;
+    if (p >= n) return;
+    const float N = (float)lp.res[l];
+    int32_t v[3];
+    float a[3];
+    for (int d = 0; d < 3; ++d) locate1(x[3 * p + d], N, v[d], a[d]);
+    const int64_t o = (p * lp.n_levels + l) * 8;
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t dx = (k >> 2) & 1, dy = (k >> 1) & 1, dz = k & 1;
+        const uint32_t h = ((uint32_t)v[0] + dx) ^ (((uint32_t)v[1] + dy) * kPrimeY) ^
+                           (((uint32_t)v[2] + dz) * kPrimeZ);
+        if (idx) idx[o + k] = h & lp.mask;
+        if (w) w[o + k] = ((dx ? a[0] : 1.f - a[0]) * (dy ? a[1] : 1.f - a[1])) * (dz ? a[2] : 1.f - a[2]);
+    }
+}
+
+int grid_blocks(const LaunchParams &lp) {
+    return lp.xcd_map ? kNumXcd * lp.per_xcd : lp.items;
+}
+
+}  // namespace
+
+hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, const void *table,
+                          int table_dtype, float *out, int64_t out_stride, int lanes,
+                          hipStream_t stream) {
+    dim3 grid(grid_blocks(lp)), block(kBlock);
+    if (table_dtype == 0) {
+        if (lanes == 2) fwd_f2_kernel<0, 2><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+        else fwd_f2_kernel<0, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+    } else {
+        if (lanes == 2) fwd_f2_kernel<1, 2><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+        else fwd_f2_kernel<1, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, const float *dout,
+                           int64_t dout_stride, float *dtable, int lanes, hipStream_t stream) {
+    dim3 grid(grid_blocks(lp)), block(kBlock);
+    if (lanes == 4) bwd_f2_kernel<4><<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
+    else if (lanes == 2) bwd_f2_kernel<2><<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
+    else bwd_f2_kernel<1><<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_corners(const LaunchParams &lp, const float *x, int64_t n, uint32_t *idx,
+                                float *w, hipStream_t stream) {
+    dim3 grid((unsigned)((n + kBlock - 1) / kBlock), lp.n_levels), block(kBlock);
+    corners_kernel<<<grid, block, 0, stream>>>(x, n, idx, w, lp);
+    return hipGetLastError();
+}
+
+}  // namespace hg

@@ -1,0 +1,250 @@
+"""Thin Python binding of libhashgrid (include/hashgrid.h).
+
+Argument marshalling only: every step of the encoding runs in the HIP kernels
+of the library.  PyTorch provides device memory and the current stream.  The
+functions carry the C names and raise ``HashGridError`` with the library's
+message when a call returns a negative code.  There is no fallback: if the
+library is not built, loading it fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG, "libhashgrid.so")
+
+HG_OK, HG_EINVAL, HG_EUNSUPPORTED, HG_EHIP = 0, -1, -2, -3
+HG_F32, HG_F16 = 0, 1
+HG_TUNE_FWD_LANES, HG_TUNE_BWD_LANES, HG_TUNE_CHUNK_POINTS, HG_TUNE_XCD_MAP = 0, 1, 2, 3
+_DTYPES = {"f32": HG_F32, "f16": HG_F16}
+_TORCH_DTYPES = {HG_F32: torch.float32, HG_F16: torch.float16}
+
+
+class HashGridError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"hashgrid error {code}: {message}")
+        self.code = code
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n_dims", "n_levels", "n_features", "log2_table_size", "base_resolution",
+        "finest_resolution", "table_dtype", "grad_dtype")]
+
+
+@dataclass(frozen=True)
+class HashGridConfig:
+    """Grid description; defaults are the pages' standard grid (L=16, F=2,
+    T=2^19, N_min=16, N_max=512)."""
+    n_levels: int = 16
+    n_features: int = 2
+    log2_table_size: int = 19
+    base_resolution: int = 16
+    finest_resolution: int = 512
+    table_dtype: str = "f32"
+    grad_dtype: str = "f32"
+    n_dims: int = 3
+
+    @property
+    def table_size(self) -> int:
+        return 1 << self.log2_table_size
+
+    @property
+    def out_features(self) -> int:
+        return self.n_levels * self.n_features
+
+    @property
+    def table_shape(self) -> tuple:
+        return (self.n_levels, self.table_size, self.n_features)
+
+    @property
+    def torch_table_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPES[_DTYPES[self.table_dtype]]
+
+    def c(self) -> _Config:
+        return _Config(self.n_dims, self.n_levels, self.n_features, self.log2_table_size,
+                       self.base_resolution, self.finest_resolution,
+                       _DTYPES.get(self.table_dtype, -1), _DTYPES.get(self.grad_dtype, -1))
+
+    @staticmethod
+    def of(w) -> "HashGridConfig":
+        """Config of a workload from ``multiresolution_hash_grid_amd.inputs``."""
+        return HashGridConfig(w.n_levels, w.n_features, w.log2_table_size, w.base_resolution,
+                              w.finest_resolution, w.table_dtype)
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
+    """Load the built library; raises if it is missing (build it with
+    ``python -m multiresolution_hash_grid_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(f"{path} is not built; run python -m multiresolution_hash_grid_amd.build")
+            lib = ctypes.CDLL(path)
+            P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+            C = ctypes.POINTER(_Config)
+            sigs = {
+                "hashgrid_abi_version": ([], ctypes.c_int),
+                "hashgrid_last_error": ([], ctypes.c_char_p),
+                "hashgrid_resolutions": ([C, P], ctypes.c_int),
+                "hashgrid_forward": ([C, P, I64, P, P, I64, P], ctypes.c_int),
+                "hashgrid_backward": ([C, P, I64, P, I64, P, P], ctypes.c_int),
+                "hashgrid_debug_corners": ([C, P, I64, P, P, P], ctypes.c_int),
+                "hashgrid_tune": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),
+                "hashgrid_tune_get": ([ctypes.c_int], ctypes.c_int),
+            }
+            for name, (args, res) in sigs.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = res
+            del I32
+            _lib = lib
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != HG_OK:
+        raise HashGridError(rc, load_library().hashgrid_last_error().decode())
+
+
+def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _points(cfg: HashGridConfig, x: torch.Tensor) -> torch.Tensor:
+    _dev(x, "x", torch.float32)
+    if x.dim() != 2 or x.shape[1] != cfg.n_dims or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous [n, {cfg.n_dims}] tensor")
+    return x
+
+
+def abi_version() -> int:
+    return load_library().hashgrid_abi_version()
+
+
+def hashgrid_resolutions(cfg: HashGridConfig) -> list:
+    out = (ctypes.c_int32 * max(cfg.n_levels, 1))()
+    c = cfg.c()
+    _check(load_library().hashgrid_resolutions(ctypes.byref(c), out))
+    return list(out)
+
+
+def hashgrid_forward(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tensor,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Encode points ``x`` [n, D] into ``out`` [n, >= L*F] (allocated when None;
+    only the first L*F columns of each row are written)."""
+    _points(cfg, x)
+    _dev(table, "table", cfg.torch_table_dtype)
+    if tuple(table.shape) != cfg.table_shape or not table.is_contiguous():
+        raise ValueError(f"table must be a contiguous {cfg.table_shape} tensor")
+    n = x.shape[0]
+    if out is None:
+        out = torch.empty((n, cfg.out_features), device=x.device, dtype=torch.float32)
+    _dev(out, "out", torch.float32)
+    if out.dim() != 2 or out.shape[0] != n or out.stride(1) != 1 or out.shape[1] < cfg.out_features:
+        raise ValueError("out must be [n, >= L*F] with unit column stride")
+    c = cfg.c()
+    _check(load_library().hashgrid_forward(ctypes.byref(c), x.data_ptr(), n, table.data_ptr(),
+                                           out.data_ptr(), out.stride(0), _stream(x, stream)))
+    return out
+
+
+def hashgrid_backward(cfg: HashGridConfig, x: torch.Tensor, dout: torch.Tensor,
+                      dtable: torch.Tensor, stream=None) -> torch.Tensor:
+    """Accumulate the table gradient of ``dout`` [n, >= L*F] into ``dtable``
+    (float32, table shape)."""
+    _points(cfg, x)
+    n = x.shape[0]
+    _dev(dout, "dout", torch.float32)
+    if dout.dim() != 2 or dout.shape[0] != n or dout.stride(1) != 1 or dout.shape[1] < cfg.out_features:
+        raise ValueError("dout must be [n, >= L*F] with unit column stride")
+    _dev(dtable, "dtable", torch.float32)
+    if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
+        raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
+    c = cfg.c()
+    _check(load_library().hashgrid_backward(ctypes.byref(c), x.data_ptr(), n, dout.data_ptr(),
+                                            dout.stride(0), dtable.data_ptr(), _stream(x, stream)))
+    return dtable
+
+
+def hashgrid_debug_corners(cfg: HashGridConfig, x: torch.Tensor, stream=None):
+    """(idx int32 [n, L, 2^D] holding the uint32 indices, w float32 [n, L, 2^D])."""
+    _points(cfg, x)
+    n = x.shape[0]
+    K = 1 << cfg.n_dims
+    idx = torch.empty((n, cfg.n_levels, K), device=x.device, dtype=torch.int32)
+    w = torch.empty((n, cfg.n_levels, K), device=x.device, dtype=torch.float32)
+    c = cfg.c()
+    _check(load_library().hashgrid_debug_corners(ctypes.byref(c), x.data_ptr(), n, idx.data_ptr(),
+                                                 w.data_ptr(), _stream(x, stream)))
+    return idx, w
+
+
+def hashgrid_tune(key: int, value: int) -> None:
+    _check(load_library().hashgrid_tune(key, value))
+
+
+def hashgrid_tune_get(key: int) -> int:
+    v = load_library().hashgrid_tune_get(key)
+    if v < 0:
+        _check(v)
+    return v
+
+
+class HashGridFunction(torch.autograd.Function):
+    """Autograd wrapper: forward through hashgrid_forward, table gradient through
+    hashgrid_backward into a zeroed fp32 buffer.  No gradient flows to x."""
+
+    @staticmethod
+    def forward(ctx, x, table, cfg):
+        ctx.cfg = cfg
+        ctx.save_for_backward(x)
+        return hashgrid_forward(cfg, x.contiguous(), table.contiguous())
+
+    @staticmethod
+    def backward(ctx, dout):
+        (x,) = ctx.saved_tensors
+        cfg = ctx.cfg
+        grad = torch.zeros(cfg.table_shape, device=x.device, dtype=torch.float32)
+        hashgrid_backward(cfg, x, dout.contiguous(), grad)
+        if cfg.table_dtype == "f16":
+            grad = grad.to(torch.float16)
+        return None, grad, None
+
+
+class HashGridEncoder(torch.nn.Module):
+    """Multiresolution hash-grid encoder with the pages' constructor arguments
+    (ipipp.com HashGridEncoder): ``forward(x [N, 3]) -> [N, L*F]``.  The L
+    tables live in one [L, T, F] parameter initialised uniform(-1e-4, 1e-4)."""
+
+    def __init__(self, n_levels=16, n_features_per_level=2, log2_hashmap_size=19,
+                 base_resolution=16, finest_resolution=512, table_dtype="f32", device="cuda"):
+        super().__init__()
+        self.cfg = HashGridConfig(n_levels, n_features_per_level, log2_hashmap_size,
+                                  base_resolution, finest_resolution, table_dtype)
+        self.resolutions = hashgrid_resolutions(self.cfg)
+        t = torch.empty(self.cfg.table_shape, dtype=torch.float32, device=device).uniform_(-1e-4, 1e-4)
+        self.embeddings = torch.nn.Parameter(t.to(self.cfg.torch_table_dtype))
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return HashGridFunction.apply(x, self.embeddings, self.cfg)

@@ -24,6 +24,8 @@ encoder; page 1 "HashGridEncoder" constructor defaults give the standard grid):
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 
 import numpy as np
@@ -50,18 +52,34 @@ def _mix64(z: np.ndarray) -> np.ndarray:
 def _key(seed: int, stream: int) -> np.uint64:
     base = np.array([(seed * 0x100000001B3 + stream * 0x9E3779B97F4A7C15) & 0xFFFFFFFFFFFFFFFF],
                     dtype=np.uint64)
-    return _mix64(base)[0]
+    with np.errstate(over="ignore"):
+        return _mix64(base)[0]
+
+
+_BLOCK = 1 << 18
+_STEPS = np.arange(1, _BLOCK + 1, dtype=np.uint64) * GAMMA  # wraps mod 2^64
 
 
 def splitmix64(seed: int, stream: int, count: int, offset: int = 0) -> np.ndarray:
-    """Raw 64-bit draws ``offset .. offset+count-1`` of one stream."""
+    """Raw 64-bit draws ``offset .. offset+count-1`` of one stream
+    (state_i = key + (i + 1) * GAMMA, output = the SplitMix64 finaliser)."""
     key = _key(seed, stream)
     out = np.empty(count, dtype=np.uint64)
+    tmp = np.empty(_BLOCK, dtype=np.uint64)
+    s30, s27, s31 = np.uint64(30), np.uint64(27), np.uint64(31)
     with np.errstate(over="ignore"):
-        for s in range(0, count, _CHUNK):
-            e = min(count, s + _CHUNK)
-            ctr = np.arange(offset + s + 1, offset + e + 1, dtype=np.uint64)
-            out[s:e] = _mix64(key + ctr * GAMMA)
+        for s in range(0, count, _BLOCK):
+            e = min(count, s + _BLOCK)
+            z, t = out[s:e], tmp[:e - s]
+            np.add(_STEPS[:e - s], key + np.uint64(offset + s) * GAMMA, out=z)
+            np.right_shift(z, s30, out=t)
+            np.bitwise_xor(z, t, out=z)
+            np.multiply(z, _M1, out=z)
+            np.right_shift(z, s27, out=t)
+            np.bitwise_xor(z, t, out=z)
+            np.multiply(z, _M2, out=z)
+            np.right_shift(z, s31, out=t)
+            np.bitwise_xor(z, t, out=z)
     return out
 
 
@@ -77,14 +95,29 @@ def uniform_f64(seed: int, stream: int, count: int, offset: int = 0) -> np.ndarr
     return (bits >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
 
 
+def _parallel_chunks(count: int, fill) -> None:
+    """Run fill(start, end) over CHUNK-sized pieces on a few threads (numpy
+    releases the GIL inside its loops); each piece depends only on its range."""
+    spans = [(s, min(count, s + _CHUNK)) for s in range(0, count, _CHUNK)]
+    if len(spans) <= 1:
+        for s, e in spans:
+            fill(s, e)
+        return
+    workers = max(1, min(8, os.cpu_count() or 1, len(spans)))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda se: fill(*se), spans))
+
+
 def normal_f32(seed: int, stream: int, count: int) -> np.ndarray:
     """N(0,1) by the Box-Muller transform, one normal per pair of uniforms."""
     out = np.empty(count, dtype=np.float32)
-    for s in range(0, count, _CHUNK):
-        e = min(count, s + _CHUNK)
+
+    def fill(s, e):
         u = uniform_f64(seed, stream, 2 * (e - s), offset=2 * s)
         r = np.sqrt(-2.0 * np.log1p(-u[0::2]))  # 1 - u1 lies in (0, 1]
         out[s:e] = (r * np.cos(2.0 * math.pi * u[1::2])).astype(np.float32)
+
+    _parallel_chunks(count, fill)
     return out
 
 
@@ -101,13 +134,21 @@ def table_uniform(seed: int, n_levels: int, table_size: int, n_features: int,
     subnormals kept)."""
     count = n_levels * table_size * n_features
     out = np.empty(count, dtype=np.float32)
-    for s in range(0, count, _CHUNK):
-        e = min(count, s + _CHUNK)
+
+    def fill(s, e):
         u = uniform_f64(seed, STREAM_TABLE, e - s, offset=s)
         out[s:e] = ((2.0 * u - 1.0) * scale).astype(np.float32)
-    out = out.reshape(n_levels, table_size, n_features)
+
+    _parallel_chunks(count, fill)
     if dtype == "f16":
-        return out.astype(np.float16)
+        half = np.empty(count, dtype=np.float16)
+
+        def narrow(s, e):
+            half[s:e] = out[s:e].astype(np.float16)
+
+        _parallel_chunks(count, narrow)
+        return half.reshape(n_levels, table_size, n_features)
+    out = out.reshape(n_levels, table_size, n_features)
     if dtype != "f32":
         raise ValueError(f"unknown table dtype {dtype!r}")
     return out

@@ -1,0 +1,154 @@
+"""Host-side checks of libhashgrid that need no GPU: the library loads, exports
+every entry point include/hashgrid.h declares, and rejects bad arguments on the
+host before anything is enqueued (so no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import multiresolution_hash_grid_amd as hg
+from multiresolution_hash_grid_amd import hashgrid as B
+from multiresolution_hash_grid_amd import inputs as I
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(hashgrid_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hg.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "hashgrid_forward" in names and "hashgrid_backward" in names
+    assert "hashgrid_debug_corners" in names
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+
+
+def test_abi_version(lib):
+    hdr = open(os.path.join(ROOT, "include", "hashgrid.h")).read()
+    want = int(re.search(r"#define HASHGRID_ABI_VERSION (\d+)", hdr).group(1))
+    assert hg.abi_version() == want
+
+
+@pytest.mark.parametrize("name", ["tiny", "standard", "large_f16"])
+def test_resolutions_agree_with_oracle(oracle, name):
+    w = I.WORKLOADS[name]
+    got = hg.hashgrid_resolutions(hg.HashGridConfig.of(w))
+    assert got == list(oracle.resolutions(w.n_levels, w.base_resolution, w.finest_resolution))
+
+
+def test_resolutions_many_configs_agree_with_oracle(oracle):
+    for L in (1, 2, 3, 5, 8, 16, 24, 32, 64):
+        for nmin, nmax in ((1, 1), (3, 6), (16, 512), (16, 4096), (7, 1000), (2, 1 << 20)):
+            cfg = hg.HashGridConfig(L, 2, 19, nmin, nmax)
+            assert hg.hashgrid_resolutions(cfg) == list(oracle.resolutions(L, nmin, nmax))
+
+
+def _call_forward(lib, cfg, x=0x1000, n=16, table=0x2000, out=0x3000, stride=None):
+    c = cfg.c()
+    stride = cfg.out_features if stride is None else stride
+    return lib.hashgrid_forward(ctypes.byref(c), x, n, table, out, stride, None)
+
+
+def _call_backward(lib, cfg, x=0x1000, n=16, dout=0x2000, stride=None, dtable=0x3000):
+    c = cfg.c()
+    stride = cfg.out_features if stride is None else stride
+    return lib.hashgrid_backward(ctypes.byref(c), x, n, dout, stride, dtable, None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n_levels=0), B.HG_EINVAL),
+    (dict(n_levels=65), B.HG_EINVAL),
+    (dict(log2_table_size=0), B.HG_EINVAL),
+    (dict(log2_table_size=29), B.HG_EINVAL),
+    (dict(base_resolution=0), B.HG_EINVAL),
+    (dict(base_resolution=64, finest_resolution=32), B.HG_EINVAL),
+    (dict(finest_resolution=1 << 24), B.HG_EINVAL),
+    (dict(table_dtype="bf16"), B.HG_EINVAL),
+    (dict(n_features=3), B.HG_EUNSUPPORTED),
+    (dict(n_dims=5), B.HG_EUNSUPPORTED),
+    (dict(grad_dtype="f16"), B.HG_EUNSUPPORTED),
+])
+def test_bad_config_is_rejected(lib, bad, code):
+    cfg = hg.HashGridConfig(**bad)
+    assert _call_forward(lib, cfg) == code
+    assert _call_backward(lib, cfg) == code
+    assert lib.hashgrid_last_error().decode() != ""
+
+
+def test_bad_arguments_are_rejected(lib):
+    cfg = hg.HashGridConfig()
+    assert lib.hashgrid_forward(None, 0x1000, 16, 0x2000, 0x3000, 32, None) == B.HG_EINVAL
+    assert _call_forward(lib, cfg, n=-1) == B.HG_EINVAL
+    assert _call_forward(lib, cfg, x=None) == B.HG_EINVAL
+    assert _call_forward(lib, cfg, x=0x1002) == B.HG_EINVAL          # misaligned x
+    assert _call_forward(lib, cfg, table=None) == B.HG_EINVAL
+    assert _call_forward(lib, cfg, table=0x2004) == B.HG_EINVAL      # fp32 F=2 needs 8 bytes
+    assert _call_forward(lib, cfg, out=None) == B.HG_EINVAL
+    assert _call_forward(lib, cfg, stride=31) == B.HG_EINVAL
+    assert _call_backward(lib, cfg, dout=None) == B.HG_EINVAL
+    assert _call_backward(lib, cfg, dtable=0x3002) == B.HG_EINVAL
+    assert _call_backward(lib, cfg, stride=7) == B.HG_EINVAL
+    assert "stride" in lib.hashgrid_last_error().decode()
+    big = hg.HashGridConfig(n_levels=64)
+    assert _call_forward(lib, big, n=1 << 40) == B.HG_EINVAL
+
+
+def test_half_table_alignment_is_four_bytes(lib):
+    cfg = hg.HashGridConfig(table_dtype="f16")
+    assert _call_forward(lib, cfg, table=0x2002) == B.HG_EINVAL
+
+
+def test_zero_points_is_a_no_op(lib):
+    cfg = hg.HashGridConfig()
+    # n == 0 succeeds without looking at the pointers (NULL is fine).
+    c = cfg.c()
+    assert lib.hashgrid_forward(ctypes.byref(c), None, 0, None, None, 32, None) == B.HG_OK
+    assert lib.hashgrid_backward(ctypes.byref(c), None, 0, None, 32, None, None) == B.HG_OK
+    assert lib.hashgrid_debug_corners(ctypes.byref(c), None, 0, None, None, None) == B.HG_OK
+    assert lib.hashgrid_last_error().decode() == ""
+
+
+def test_tuning_knobs(lib):
+    for key, good, bad in ((B.HG_TUNE_FWD_LANES, 1, 3), (B.HG_TUNE_BWD_LANES, 2, 8),
+                           (B.HG_TUNE_CHUNK_POINTS, 512, 100), (B.HG_TUNE_XCD_MAP, 0, 2)):
+        old = hg.hashgrid_tune_get(key)
+        hg.hashgrid_tune(key, good)
+        assert hg.hashgrid_tune_get(key) == good
+        with pytest.raises(hg.HashGridError):
+            hg.hashgrid_tune(key, bad)
+        hg.hashgrid_tune(key, old)
+    with pytest.raises(hg.HashGridError):
+        hg.hashgrid_tune(99, 1)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    cfg = hg.HashGridConfig.of(I.WORKLOADS["tiny"])
+    x = torch.zeros((4, 3))
+    t = torch.zeros(cfg.table_shape)
+    with pytest.raises(ValueError):
+        hg.hashgrid_forward(cfg, x, t)
+
+
+def test_inputs_are_deterministic():
+    a = I.make_points(I.resized(I.WORKLOADS["standard"], 1000))
+    b = I.make_points(I.resized(I.WORKLOADS["standard"], 1000))
+    assert np.array_equal(a, b)
+    assert a.min() >= 0.0 and a.max() < 1.0
+    r = I.make_points(I.resized(I.WORKLOADS["ray"], 4 * 256))
+    assert r.shape == (1024, 3) and r.min() >= 0.0 and r.max() < 1.0

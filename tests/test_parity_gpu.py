@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: corner indices bit-exact; forward fp32 max abs error <= 1e-6 * max|table|;
+backward max abs error <= 1e-5 * max|oracle gradient| per level (fp32 atomics in
+unspecified order); fp16-table grids <= 1e-3 relative (and, as expected from
+fp32 arithmetic on exactly widened halves, within the fp32 bound as well).
+"""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import multiresolution_hash_grid_amd as hg  # noqa: E402
+from multiresolution_hash_grid_amd import hashgrid as B  # noqa: E402
+from multiresolution_hash_grid_amd import inputs as I  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+FWD_TOL = 1e-6
+BWD_TOL = 1e-5
+F16_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _threads(oracle):
+    oracle.set_threads(min(16, os.cpu_count() or 1))
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def fwd_err(out, ref, table):
+    return float(np.max(np.abs(out - ref))) / float(np.max(np.abs(table.astype(np.float64))))
+
+
+def bwd_check(grad, ref, L):
+    for l in range(L):
+        scale = float(np.max(np.abs(ref[l])))
+        err = float(np.max(np.abs(grad[l].astype(np.float64) - ref[l])))
+        assert err <= BWD_TOL * scale, f"level {l}: backward err {err:.3g} > {BWD_TOL} * {scale:.3g}"
+
+
+def run_forward(cfg, x, t, stride=None):
+    n = x.shape[0]
+    if stride is None:
+        return hg.hashgrid_forward(cfg, dev(x), dev(t)).cpu().numpy()
+    buf = torch.full((n, stride), 7.0, device=DEV)
+    hg.hashgrid_forward(cfg, dev(x), dev(t), out=buf)
+    return buf.cpu().numpy()
+
+
+def run_backward(cfg, x, d, init=None):
+    g = torch.zeros(cfg.table_shape, device=DEV) if init is None else dev(init)
+    hg.hashgrid_backward(cfg, dev(x), dev(d), g)
+    return g.cpu().numpy()
+
+
+# ----------------------------------------------------------------------------- corners
+
+@pytest.mark.parametrize("name,n", [("tiny", 4096), ("standard", 3 * 1024 + 37), ("ray", 2 * 256),
+                                    ("large_f16", 2000)])
+def test_corner_indices_bit_exact(oracle, name, n):
+    w = I.resized(I.WORKLOADS[name], n)
+    cfg = hg.HashGridConfig.of(w)
+    x = I.make_points(w)
+    idx, wt = hg.hashgrid_debug_corners(cfg, dev(x))
+    ridx, rw = oracle.corners(oracle.grid_of(w), x)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ridx)
+    assert np.max(np.abs(wt.cpu().numpy() - rw)) <= 2.5e-7
+
+
+def test_corner_indices_out_of_domain_points(oracle):
+    w = I.WORKLOADS["standard"]
+    cfg = hg.HashGridConfig.of(w)
+    rng = np.random.default_rng(12)
+    x = rng.uniform(-3.0, 4.0, size=(3000, 3)).astype(np.float32)
+    x[:3] = [[1.0, 1.0, 1.0], [0.0, 0.0, 0.0], [-0.0, 1.0, 0.5]]
+    idx, _ = hg.hashgrid_debug_corners(cfg, dev(x))
+    ridx, _ = oracle.corners(oracle.grid_of(w), x)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ridx)
+
+
+# ----------------------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("name,n", [("tiny", None), ("standard", 3 * 1024 + 37), ("standard", None),
+                                    ("ray", None)])
+def test_forward_matches_oracle(oracle, name, n):
+    w = I.WORKLOADS[name] if n is None else I.resized(I.WORKLOADS[name], n)
+    print(f"forward parity {name} n={w.n_points}", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    x, t = I.make_points(w), I.make_table(w)
+    out = run_forward(cfg, x, t)
+    ref = oracle.forward(oracle.grid_of(w), x, t)
+    assert out.shape == ref.shape
+    assert fwd_err(out, ref, t) <= FWD_TOL
+
+
+def test_forward_half_tables_full_size_sampled(oracle):
+    w = I.WORKLOADS["large_f16"]
+    print(f"forward parity large_f16 n={w.n_points} (sampled)", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    x, t = I.make_points(w), I.make_table(w)
+    out = run_forward(cfg, x, t)
+    rows = np.random.default_rng(13).choice(w.n_points, size=20000, replace=False)
+    rows[:2] = [0, w.n_points - 1]
+    ref = oracle.forward(oracle.grid_of(w), x[rows], t)
+    err = np.max(np.abs(out[rows] - ref))
+    assert err <= F16_TOL * np.max(np.abs(ref))
+    assert fwd_err(out[rows], ref, t) <= FWD_TOL
+
+
+def test_forward_writes_only_its_columns_of_a_wider_row(oracle):
+    w = I.resized(I.WORKLOADS["standard"], 1000)
+    cfg = hg.HashGridConfig.of(w)
+    x, t = I.make_points(w), I.make_table(w)
+    buf = run_forward(cfg, x, t, stride=cfg.out_features + 64)
+    ref = oracle.forward(oracle.grid_of(w), x, t)
+    assert fwd_err(buf[:, :cfg.out_features], ref, t) <= FWD_TOL
+    assert np.all(buf[:, cfg.out_features:] == 7.0)
+
+
+def test_forward_vertex_points_exact(oracle):
+    # Points on vertices of power-of-two levels return the table entry exactly.
+    w = I.WORKLOADS["tiny"]
+    cfg = hg.HashGridConfig.of(w)
+    t = I.make_table(w)
+    v = np.random.default_rng(14).integers(0, 33, size=(2000, 3))
+    x = (v / 32.0).astype(np.float32)
+    out = run_forward(cfg, x, t)
+    ref = oracle.forward(oracle.grid_of(w), x, t)
+    assert np.array_equal(out[:, 6:8].astype(np.float64), ref[:, 6:8])
+
+
+def test_forward_out_of_domain_points(oracle):
+    w = I.WORKLOADS["standard"]
+    cfg = hg.HashGridConfig.of(w)
+    t = I.make_table(w)
+    x = np.random.default_rng(15).uniform(-2.0, 3.0, size=(5000, 3)).astype(np.float32)
+    assert fwd_err(run_forward(cfg, x, t), oracle.forward(oracle.grid_of(w), x, t), t) <= FWD_TOL
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 1023, 1025])
+def test_forward_ragged_sizes(oracle, n):
+    w = I.resized(I.WORKLOADS["standard"], n)
+    cfg = hg.HashGridConfig.of(w)
+    x, t = I.make_points(w), I.make_table(w)
+    assert fwd_err(run_forward(cfg, x, t), oracle.forward(oracle.grid_of(w), x, t), t) <= FWD_TOL
+
+
+# ----------------------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("name,n", [("tiny", None), ("standard", 3 * 1024 + 37), ("standard", None),
+                                    ("ray", None), ("large_f16", 1 << 16)])
+def test_backward_matches_oracle(oracle, name, n):
+    w = I.WORKLOADS[name] if n is None else I.resized(I.WORKLOADS[name], n)
+    print(f"backward parity {name} n={w.n_points}", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    x, d = I.make_points(w), I.make_dout(w)
+    grad = run_backward(cfg, x, d)
+    ref = oracle.backward(oracle.grid_of(w), x, d)
+    bwd_check(grad, ref, w.n_levels)
+
+
+def test_backward_half_grid_full_size_properties():
+    # At full size (2^21 points, 32 levels): per-level gradient sums equal the
+    # upstream column sums (the weights of a point sum to one).
+    w = I.WORKLOADS["large_f16"]
+    print(f"backward properties large_f16 n={w.n_points}", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    x, d = dev(I.make_points(w)), dev(I.make_dout(w))
+    g = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_backward(cfg, x, d, g)
+    got = g.double().sum(dim=1)
+    want = d.double().reshape(-1, w.n_levels, 2).sum(dim=0)
+    scale = d.double().abs().reshape(-1, w.n_levels, 2).sum(dim=0)
+    assert float(((got - want).abs() / scale).max()) < 1e-6
+
+
+def test_backward_exact_dyadic_case(oracle):
+    # Dyadic points on power-of-two levels and dout in {-1, 0, 1}: every partial
+    # sum is exact in fp32, so the atomic order cannot matter and the result is
+    # bit-exact.
+    w = I.WORKLOADS["tiny"]
+    cfg = hg.HashGridConfig.of(w)
+    rng = np.random.default_rng(16)
+    x = (rng.integers(0, 128, size=(4096, 3)) / 128.0).astype(np.float32)
+    d = rng.integers(-1, 2, size=(4096, 8)).astype(np.float32)
+    grad = run_backward(cfg, x, d)
+    ref = oracle.backward(oracle.grid_of(w), x, d)
+    assert np.array_equal(grad.astype(np.float64), ref)
+
+
+def test_backward_accumulates_and_reads_strided_rows(oracle):
+    w = I.resized(I.WORKLOADS["standard"], 2000)
+    cfg = hg.HashGridConfig.of(w)
+    x, d = I.make_points(w), I.make_dout(w)
+    wide = np.concatenate([d, np.full((2000, 3), 1e30, dtype=np.float32)], axis=1)
+    base = np.random.default_rng(17).standard_normal(cfg.table_shape).astype(np.float32)
+    grad = run_backward(cfg, x, wide, init=base)
+    ref = oracle.backward(oracle.grid_of(w), x, d, base.astype(np.float64))
+    delta = oracle.backward(oracle.grid_of(w), x, d)
+    for l in range(w.n_levels):
+        err = np.max(np.abs(grad[l] - ref[l]))
+        assert err <= BWD_TOL * np.max(np.abs(delta[l])) + 4e-7 * np.max(np.abs(base[l]))
+
+
+# ----------------------------------------------------------------------------- launch shapes
+
+@pytest.mark.parametrize("key,value", [(B.HG_TUNE_FWD_LANES, 1), (B.HG_TUNE_BWD_LANES, 1),
+                                       (B.HG_TUNE_BWD_LANES, 2), (B.HG_TUNE_XCD_MAP, 0),
+                                       (B.HG_TUNE_CHUNK_POINTS, 64), (B.HG_TUNE_CHUNK_POINTS, 8192)])
+def test_launch_variants_match_oracle(oracle, key, value):
+    w = I.resized(I.WORKLOADS["standard"], 5 * 1024 + 77)
+    cfg = hg.HashGridConfig.of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    old = hg.hashgrid_tune_get(key)
+    try:
+        hg.hashgrid_tune(key, value)
+        out = run_forward(cfg, x, t)
+        grad = run_backward(cfg, x, d)
+    finally:
+        hg.hashgrid_tune(key, old)
+    g = oracle.grid_of(w)
+    assert fwd_err(out, oracle.forward(g, x, t), t) <= FWD_TOL
+    bwd_check(grad, oracle.backward(g, x, d), w.n_levels)
+
+
+# ----------------------------------------------------------------------------- module
+
+def test_encoder_module_autograd(oracle):
+    w = I.resized(I.WORKLOADS["standard"], 3000)
+    enc = hg.HashGridEncoder(device=DEV)
+    t = I.make_table(w)
+    with torch.no_grad():
+        enc.embeddings.copy_(dev(t))
+    x = I.make_points(w)
+    d = I.make_dout(w)
+    out = enc(dev(x))
+    out.backward(dev(d))
+    g = oracle.grid_of(w)
+    assert fwd_err(out.detach().cpu().numpy(), oracle.forward(g, x, t), t) <= FWD_TOL
+    bwd_check(enc.embeddings.grad.cpu().numpy(), oracle.backward(g, x, d), w.n_levels)
