@@ -110,11 +110,13 @@ def main() -> int:
     d = torch.from_numpy(d_h).to(dev)
     out = torch.empty((w.n_points, cfg.out_features), device=dev)
     grad = torch.zeros(cfg.table_shape, device=dev)
+    ws = hg.backward_workspace(cfg, w.n_points, dev)
+    fws = hg.forward_workspace(cfg, w.n_points, dev)
     torch.cuda.synchronize()
 
     def step():
-        hg.hashgrid_forward(cfg, x, t, out=out)
-        hg.hashgrid_backward(cfg, x, d, grad)
+        hg.hashgrid_forward(cfg, x, t, out=out, workspace=fws)
+        hg.hashgrid_backward(cfg, x, d, grad, workspace=ws)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -128,9 +130,9 @@ def main() -> int:
     t0 = time.perf_counter()
     for k in range(K):
         ev[k][0].record()
-        hg.hashgrid_forward(cfg, x, t, out=out)
+        hg.hashgrid_forward(cfg, x, t, out=out, workspace=fws)
         ev[k][1].record()
-        hg.hashgrid_backward(cfg, x, d, grad)
+        hg.hashgrid_backward(cfg, x, d, grad, workspace=ws)
         ev[k][2].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0

@@ -34,6 +34,7 @@
 #ifndef HASHGRID_H
 #define HASHGRID_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -78,6 +79,12 @@ const char *hashgrid_last_error(void);
  * res_out: HOST int32[L].  Errors: HG_EINVAL on a bad config or NULL. */
 int hashgrid_resolutions(const hg_config *cfg, int32_t *res_out);
 
+/* Bytes of device workspace with which hashgrid_forward stages the encoding
+ * level-major before writing the rows: L * n * F * 4 rounded up to 256
+ * (32 MiB for L = 16, F = 2, n = 2^18).  *bytes_out is a HOST size_t.
+ * Errors: HG_EINVAL, HG_EUNSUPPORTED. */
+int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out);
+
 /* Forward encoding (ipipp.com section 2 and HashGridEncoder.forward).
  *   x     : float32 [n][D], row-major (AoS), 4-byte aligned.
  *   table : [L][T][F] of cfg->table_dtype, contiguous, level-major; aligned to
@@ -86,12 +93,31 @@ int hashgrid_resolutions(const hg_config *cfg, int32_t *res_out);
  *           out[p * out_row_stride + l * F + j]; columns beyond L*F are not
  *           touched, so the encoding can be written into a wider buffer.
  *           4-byte aligned; out_row_stride >= L*F (elements).
+ *   workspace, workspace_bytes : caller-owned device scratch, 256-byte
+ *           aligned, contents clobbered; may be NULL.  With at least
+ *           hashgrid_forward_workspace_size bytes each level's encodings are
+ *           first written level-major (whole cache lines, so the level's table
+ *           stays in L2) and then transposed into the rows; without it every
+ *           level writes its F values straight into the rows.  Results are
+ *           identical either way.  Concurrent calls must not share a workspace.
  *   The blend of level l is sum_k w_k * table[l][h(corner_k)][j] computed in
  *   fp32, with w_k the trilinear weight of corner k.
  * Errors: HG_EINVAL (config, NULL, alignment, n < 0, stride), HG_EUNSUPPORTED,
  *         HG_EHIP. */
 int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void *table,
-                     float *out, int64_t out_row_stride, void *stream);
+                     float *out, int64_t out_row_stride, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace that let hashgrid_backward route the whole
+ * gradient of n points through its binned (atomic-free) path in one pass:
+ * 64 * L * ceil(n / 512) * 512 bytes of records plus small counters
+ * (about 268 MB for L = 16, n = 2^18).  *bytes_out is a HOST size_t.
+ * A workspace of at least *min_bytes_out (one level's share; may be NULL)
+ * also works -- the levels are then processed in groups.  Returns 0 bytes
+ * when the configuration has no binned path (T > 2^24, n >= 2^29).
+ * Errors: HG_EINVAL, HG_EUNSUPPORTED. */
+int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out,
+                                     size_t *min_bytes_out);
 
 /* Backward: gradient of the encoding with respect to the tables (ipipp.com
  * section 2 -- only the corners a point sampled receive gradient -- i.e. the
@@ -101,12 +127,21 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
  *            element (p, l*F + j) is read, other columns are ignored.
  *   dtable : float32 [L][T][F], 4-byte aligned.  ACCUMULATED INTO:
  *            dtable[l][h(corner_k)][j] += w_k * dout[p][l*F + j] for every point,
- *            level and corner (fp32 atomic adds; their order is unspecified, so
- *            results can differ from run to run in the last bits).  The caller
+ *            level and corner.  Additions happen in an unspecified order, so
+ *            results can differ from run to run in the last bits.  The caller
  *            zeroes the buffer when it wants the gradient of one batch alone.
+ *   workspace, workspace_bytes : caller-owned device scratch (contents need
+ *            not be initialised and are clobbered).  With at least the minimum
+ *            of hashgrid_backward_workspace_size and a 16-byte aligned dtable
+ *            the gradient is binned by table partition and accumulated in
+ *            on-chip memory with no global atomics; with NULL or too little
+ *            workspace it is scattered with fp32 global atomics (correct, but
+ *            an order of magnitude slower on MI355X).  Concurrent calls must
+ *            not share a workspace.
  * Errors: as hashgrid_forward. */
 int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const float *dout,
-                      int64_t dout_row_stride, float *dtable, void *stream);
+                      int64_t dout_row_stride, float *dtable, void *workspace,
+                      size_t workspace_bytes, void *stream);
 
 /* Debug export of the corner table indices and interpolation weights.
  *   idx : uint32 [n][L][2^D]  -- hashed index in [0, T) of corner k of level l,
@@ -124,6 +159,10 @@ int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint
 #define HG_TUNE_BWD_LANES 1    /* lanes per (point, level) in the backward: 1, 2 or 4    */
 #define HG_TUNE_CHUNK_POINTS 2 /* points per workgroup work item: 64..65536, power of 2  */
 #define HG_TUNE_XCD_MAP 3      /* 1: give each XCD its own levels, 0: plain linear order */
+#define HG_TUNE_BWD_BINNED 4   /* 1: binned backward when the workspace allows, 0: atomics */
+#define HG_TUNE_FWD_UNROLL 5   /* points per lane pair in flight in the forward: 1, 2 or 4 */
+#define HG_TUNE_FWD_NT 6       /* 1: non-temporal point reads and output writes         */
+#define HG_TUNE_FWD_STAGED 7   /* 1: stage the forward level-major when given workspace */
 int hashgrid_tune(int key, int value);
 int hashgrid_tune_get(int key);
 

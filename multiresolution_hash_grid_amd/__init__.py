@@ -10,9 +10,13 @@ from .hashgrid import (  # noqa: F401
     HashGridError,
     HashGridFunction,
     abi_version,
+    backward_workspace,
     hashgrid_backward,
+    hashgrid_backward_workspace_size,
     hashgrid_debug_corners,
+    forward_workspace,
     hashgrid_forward,
+    hashgrid_forward_workspace_size,
     hashgrid_resolutions,
     hashgrid_tune,
     hashgrid_tune_get,

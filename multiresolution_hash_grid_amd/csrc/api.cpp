@@ -35,6 +35,10 @@ struct Tuning {
     int bwd_lanes = 4;
     int chunk_points = 1024;
     int xcd_map = 1;
+    int bwd_binned = 1;
+    int fwd_unroll = 4;
+    int fwd_nt = 0;
+    int fwd_staged = 1;
 };
 Tuning g_tune;
 
@@ -93,6 +97,29 @@ int plan(const hg_config &c, int64_t n, hg::LaunchParams &lp) {
     return HG_OK;
 }
 
+// Binned backward layout; returns false when the configuration has no binned
+// path (partition count or record count beyond the kernels' index widths).
+bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
+    if (c.n_dims != 3 || c.n_features != 2) return false;
+    const int s_log2 = c.log2_table_size < hg::kMaxSLog2 ? c.log2_table_size : hg::kMaxSLog2;
+    const int64_t parts = (int64_t)1 << (c.log2_table_size - s_log2);
+    const int64_t tiles = (n + hg::kBinTile - 1) / hg::kBinTile;
+    if (parts > hg::kMaxParts || n >= ((int64_t)1 << 29)) return false;
+    bp.level0 = 0;
+    bp.group = c.n_levels;
+    bp.tiles = (int32_t)tiles;
+    bp.parts = (int32_t)parts;
+    bp.s_log2 = s_log2;
+    bp.log2_table_size = c.log2_table_size;
+    bp.mask = (uint32_t)((1ull << c.log2_table_size) - 1);
+    bp.pad_ = 0;
+    bp.n = n;
+    resolutions(c, bp.res);
+    return true;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
 int check_points(int64_t n, const float *x) {
     if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
     if (!x) return fail(HG_EINVAL, "x is NULL");
@@ -121,8 +148,17 @@ int hashgrid_resolutions(const hg_config *cfg, int32_t *res_out) {
     return ok();
 }
 
+int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
+    if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
+    *bytes_out = round_up((size_t)n * cfg->n_levels * cfg->n_features * sizeof(float), 256);
+    return ok();
+}
+
 int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void *table, float *out,
-                     int64_t out_row_stride, void *stream) {
+                     int64_t out_row_stride, void *workspace, size_t workspace_bytes, void *stream) {
     int rc = check_config(cfg);
     if (rc) return rc;
     if (n == 0) return ok();
@@ -133,15 +169,34 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
     if (!out || !aligned(out, 4)) return fail(HG_EINVAL, "out is NULL or not 4-byte aligned");
     if (out_row_stride < (int64_t)cfg->n_levels * cfg->n_features)
         return fail(HG_EINVAL, "out_row_stride %lld < L*F", (long long)out_row_stride);
+    if (workspace && !aligned(workspace, 256)) return fail(HG_EINVAL, "workspace is not 256-byte aligned");
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
-    return launch_status(hg::launch_forward(lp, x, n, table, cfg->table_dtype, out, out_row_stride,
-                                            g_tune.fwd_lanes, (hipStream_t)stream),
+    const size_t stage_bytes = (size_t)n * cfg->n_levels * cfg->n_features * sizeof(float);
+    float *stage = (g_tune.fwd_staged && workspace && workspace_bytes >= stage_bytes) ? (float *)workspace : nullptr;
+    const hg::FwdTune ft{g_tune.fwd_lanes, g_tune.fwd_unroll, g_tune.fwd_nt};
+    return launch_status(hg::launch_forward(lp, x, n, table, cfg->table_dtype, out, out_row_stride, ft, stage,
+                                            (hipStream_t)stream),
                          "forward");
 }
 
+int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out,
+                                     size_t *min_bytes_out) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
+    if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
+    hg::BinParams bp;
+    size_t per_level = 0;
+    if (n > 0 && plan_binned(*cfg, n, bp)) per_level = round_up(hg::binned_level_bytes(bp), 256);
+    *bytes_out = per_level * (size_t)cfg->n_levels;
+    if (min_bytes_out) *min_bytes_out = per_level;
+    return ok();
+}
+
 int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const float *dout,
-                      int64_t dout_row_stride, float *dtable, void *stream) {
+                      int64_t dout_row_stride, float *dtable, void *workspace, size_t workspace_bytes,
+                      void *stream) {
     int rc = check_config(cfg);
     if (rc) return rc;
     if (n == 0) return ok();
@@ -150,6 +205,18 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
     if (!dtable || !aligned(dtable, 4)) return fail(HG_EINVAL, "dtable is NULL or not 4-byte aligned");
     if (dout_row_stride < (int64_t)cfg->n_levels * cfg->n_features)
         return fail(HG_EINVAL, "dout_row_stride %lld < L*F", (long long)dout_row_stride);
+    if (workspace && !aligned(workspace, 256)) return fail(HG_EINVAL, "workspace is not 256-byte aligned");
+    hg::BinParams bp;
+    if (g_tune.bwd_binned && workspace && aligned(dtable, 16) && plan_binned(*cfg, n, bp)) {
+        const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
+        if (workspace_bytes >= per_level) {
+            // Whole levels per group; the launcher splits the workspace itself.
+            const size_t usable = workspace_bytes / per_level * hg::binned_level_bytes(bp);
+            return launch_status(hg::launch_binned_backward(bp, cfg->n_levels, x, n, dout, dout_row_stride,
+                                                            dtable, workspace, usable, (hipStream_t)stream),
+                                 "binned backward");
+        }
+    }
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
     return launch_status(hg::launch_backward(lp, x, n, dout, dout_row_stride, dtable, g_tune.bwd_lanes,
@@ -189,6 +256,22 @@ int hashgrid_tune(int key, int value) {
         if (value != 0 && value != 1) break;
         g_tune.xcd_map = value;
         return ok();
+    case HG_TUNE_BWD_BINNED:
+        if (value != 0 && value != 1) break;
+        g_tune.bwd_binned = value;
+        return ok();
+    case HG_TUNE_FWD_UNROLL:
+        if (value != 1 && value != 2 && value != 4) break;
+        g_tune.fwd_unroll = value;
+        return ok();
+    case HG_TUNE_FWD_NT:
+        if (value != 0 && value != 1) break;
+        g_tune.fwd_nt = value;
+        return ok();
+    case HG_TUNE_FWD_STAGED:
+        if (value != 0 && value != 1) break;
+        g_tune.fwd_staged = value;
+        return ok();
     default:
         return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
@@ -201,6 +284,10 @@ int hashgrid_tune_get(int key) {
     case HG_TUNE_BWD_LANES: return g_tune.bwd_lanes;
     case HG_TUNE_CHUNK_POINTS: return g_tune.chunk_points;
     case HG_TUNE_XCD_MAP: return g_tune.xcd_map;
+    case HG_TUNE_BWD_BINNED: return g_tune.bwd_binned;
+    case HG_TUNE_FWD_UNROLL: return g_tune.fwd_unroll;
+    case HG_TUNE_FWD_NT: return g_tune.fwd_nt;
+    case HG_TUNE_FWD_STAGED: return g_tune.fwd_staged;
     default: return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
 }

@@ -41,10 +41,14 @@ __device__ __forceinline__ bool decode_item(const LaunchParams &lp, Item &it) {
     return true;
 }
 
-// Voxel of one coordinate: scaled position (fp32 multiply without
-// contraction), its floor as a signed integer and the exact fraction.
+// Voxel of one coordinate: scaled position rounded to fp32, its floor as a
+// signed integer and the fraction s - floor(s), which is exact.  Contraction
+// is off here: fusing the multiply into the subtraction would compute the
+// fraction of the unrounded product and move the weights off the voxel that
+// floor(s) picked.
 __device__ __forceinline__ void locate1(float xd, float N, int32_t &v, float &f) {
-    float s = __fmul_rn(xd, N);
+#pragma clang fp contract(off)
+    float s = xd * N;
     float fl = floorf(s);
     v = (int32_t)fl;
     f = s - fl;
@@ -149,6 +153,70 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_kernel(const float *__restrict_
     }
 }
 
+// Lane-pair forward with U points per pair in flight: all 4*U corner loads
+// of a lane are issued before the first blend, so each wave keeps U times as
+// many table requests outstanding.  NT marks the streamed x reads and output
+// writes non-temporal so that they do not displace the level's table from L2.
+// Output element (p, l, j) is out[p * ostride + l * lstride + j]: lstride = 2
+// writes the [n][L*F] rows directly, ostride = 2 with lstride = 2 n writes a
+// level-major [L][n][F] staging array whose stores are fully coalesced.
+template <int DT, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__restrict__ x, int64_t n,
+                                                             const void *__restrict__ table,
+                                                             float *__restrict__ out, int64_t ostride,
+                                                             int64_t lstride, LaunchParams lp) {
+    Item it;
+    if (!decode_item(lp, it)) return;
+    constexpr int kPairs = kBlock / 2;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint32_t mask = lp.mask;
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    const uint32_t sub = threadIdx.x & 1;
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    for (int64_t p0 = it.p0 + (threadIdx.x >> 1); p0 < end; p0 += (int64_t)kPairs * U) {
+        float2 e[U][4];
+        float a0[U], a1[U], a2[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t p = p0 + (int64_t)u * kPairs;
+            ok[u] = p < end;
+            const int64_t q = ok[u] ? p : p0;  // p0 < end: always a valid point
+            const float x0 = NT ? __builtin_nontemporal_load(x + 3 * q + 0) : x[3 * q + 0];
+            const float x1 = NT ? __builtin_nontemporal_load(x + 3 * q + 1) : x[3 * q + 1];
+            const float x2 = NT ? __builtin_nontemporal_load(x + 3 * q + 2) : x[3 * q + 2];
+            int32_t v0, v1, v2;
+            locate1(x0, N, v0, a0[u]);
+            locate1(x1, N, v1, a1[u]);
+            locate1(x2, N, v2, a2[u]);
+            const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hy1 = hy0 + kPrimeY;
+            const uint32_t hz0 = (uint32_t)v2 * kPrimeZ, hz1 = hz0 + kPrimeZ;
+            const uint32_t cx = (uint32_t)v0 + sub;
+            e[u][0] = Table2<DT>::load(table, lbase + ((cx ^ hy0 ^ hz0) & mask));
+            e[u][1] = Table2<DT>::load(table, lbase + ((cx ^ hy0 ^ hz1) & mask));
+            e[u][2] = Table2<DT>::load(table, lbase + ((cx ^ hy1 ^ hz0) & mask));
+            e[u][3] = Table2<DT>::load(table, lbase + ((cx ^ hy1 ^ hz1) & mask));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float wy0 = 1.f - a1[u], wz0 = 1.f - a2[u];
+            const float wx = sub ? a0[u] : 1.f - a0[u];
+            const float rx = wx * (wy0 * (wz0 * e[u][0].x + a2[u] * e[u][1].x) +
+                                   a1[u] * (wz0 * e[u][2].x + a2[u] * e[u][3].x));
+            const float ry = wx * (wy0 * (wz0 * e[u][0].y + a2[u] * e[u][1].y) +
+                                   a1[u] * (wz0 * e[u][2].y + a2[u] * e[u][3].y));
+            // lane 0 keeps feature 0 and needs lane 1's x-half; lane 1 the reverse.
+            const float v = (sub ? ry : rx) + swap_pair(sub ? rx : ry);
+            if (ok[u]) {
+                float *dst = out + (p0 + (int64_t)u * kPairs) * ostride + (int64_t)l * lstride + sub;
+                if (NT) __builtin_nontemporal_store(v, dst);
+                else *dst = v;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- backward
 
 // LANES = 4: lane (dx, j) = (sub >> 1, sub & 1) adds feature j of the four
@@ -237,19 +305,63 @@ int grid_blocks(const LaunchParams &lp) {
     return lp.xcd_map ? kNumXcd * lp.per_xcd : lp.items;
 }
 
+// Level-major staging [L][n][2] -> rows out[p * ostride + l * 2 + j], 64
+// points per workgroup through LDS so that both sides move whole lines.
+constexpr int kTransposePts = 64;
+
+__global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restrict__ stage, int64_t n, int L,
+                                                           float *__restrict__ out, int64_t ostride) {
+    extern __shared__ float tile[];  // [kTransposePts][2L + 1]
+    const int row = 2 * L + 1;
+    const int64_t p0 = (int64_t)blockIdx.x * kTransposePts;
+    const int np = (int)min((int64_t)kTransposePts, n - p0);
+    const int total = kTransposePts * 2 * L;
+    for (int e = threadIdx.x; e < total; e += kBlock) {
+        const int l = e / (2 * kTransposePts), r = e - l * 2 * kTransposePts;
+        const int i = r >> 1, j = r & 1;
+        if (i < np) tile[i * row + 2 * l + j] = stage[((int64_t)l * n + p0 + i) * 2 + j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < total; e += kBlock) {
+        const int i = e / (2 * L), c = e - i * 2 * L;
+        if (i < np) out[(p0 + i) * ostride + c] = tile[i * row + c];
+    }
+}
+
+template <int DT>
+hipError_t launch_gather_dt(const LaunchParams &lp, const float *x, int64_t n, const void *table, float *out,
+                            int64_t ostride, int64_t lstride, const FwdTune &ft, hipStream_t stream) {
+    dim3 grid(grid_blocks(lp)), block(kBlock);
+    if (lstride == 2 && ft.lanes == 1) {
+        fwd_f2_kernel<DT, 1><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lp);
+    } else if (ft.nt) {
+        if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
+        else if (ft.unroll == 2) fwd_f2_pair_kernel<DT, 2, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
+        else fwd_f2_pair_kernel<DT, 4, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
+    } else {
+        if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
+        else if (ft.unroll == 2) fwd_f2_pair_kernel<DT, 2, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
+        else fwd_f2_pair_kernel<DT, 4, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, const void *table,
-                          int table_dtype, float *out, int64_t out_stride, int lanes,
-                          hipStream_t stream) {
-    dim3 grid(grid_blocks(lp)), block(kBlock);
-    if (table_dtype == 0) {
-        if (lanes == 2) fwd_f2_kernel<0, 2><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
-        else fwd_f2_kernel<0, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
-    } else {
-        if (lanes == 2) fwd_f2_kernel<1, 2><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
-        else fwd_f2_kernel<1, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+                          int table_dtype, float *out, int64_t out_stride, const FwdTune &ft,
+                          float *stage, hipStream_t stream) {
+    hipError_t e;
+    if (!stage) {
+        return table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, out, out_stride, 2, ft, stream)
+                                : launch_gather_dt<1>(lp, x, n, table, out, out_stride, 2, ft, stream);
     }
+    e = table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, stage, 2, 2 * n, ft, stream)
+                         : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream);
+    if (e != hipSuccess) return e;
+    const unsigned blocks = (unsigned)((n + kTransposePts - 1) / kTransposePts);
+    const size_t lds = (size_t)kTransposePts * (2 * lp.n_levels + 1) * sizeof(float);
+    transpose_kernel<<<blocks, kBlock, lds, stream>>>(stage, n, lp.n_levels, out, out_stride);
     return hipGetLastError();
 }
 

@@ -36,10 +36,44 @@ struct LaunchParams {
     int8_t level_order[kMaxLevels];
 };
 
+// Binned backward (binned_backward.hip): the table gradient routed to
+// per-partition owners instead of global atomics.
+constexpr int kBinTile = 512;     // points per binning tile
+constexpr int kMaxParts = 2048;   // partitions per level
+constexpr int kMaxSLog2 = 12;     // partition = 2^12 entries = 64 KB of 2 x int64 accumulators
+
+struct BinParams {
+    int32_t level0;          // first level of this launch group
+    int32_t group;           // levels in this launch group
+    int32_t tiles;           // ceil(n / kBinTile)
+    int32_t parts;           // partitions per level = T >> s_log2
+    int32_t s_log2;          // log2 entries per partition
+    int32_t log2_table_size;
+    uint32_t mask;           // T - 1
+    int32_t pad_;
+    int64_t n;
+    int32_t res[kMaxLevels];
+};
+
+size_t binned_level_bytes(const BinParams &bp);
+hipError_t launch_binned_backward(BinParams bp, int n_levels, const float *x, int64_t n,
+                                  const float *dout, int64_t dout_stride, float *dtable,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+// Forward launch shape: lanes per (point, level), points per lane pair in
+// flight, non-temporal x reads / output writes.
+struct FwdTune {
+    int lanes;
+    int unroll;
+    int nt;
+};
+
 // Kernel launchers (encode_kernels.hip).  They return the launch status.
+// stage == NULL: write rows directly; otherwise stage is an fp32 [L][n][2]
+// scratch array and the rows are assembled by a transpose pass.
 hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, const void *table,
-                          int table_dtype, float *out, int64_t out_stride, int lanes,
-                          hipStream_t stream);
+                          int table_dtype, float *out, int64_t out_stride, const FwdTune &ft,
+                          float *stage, hipStream_t stream);
 hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, const float *dout,
                            int64_t dout_stride, float *dtable, int lanes, hipStream_t stream);
 hipError_t launch_debug_corners(const LaunchParams &lp, const float *x, int64_t n, uint32_t *idx,

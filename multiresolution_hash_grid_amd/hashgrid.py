@@ -20,7 +20,8 @@ LIBRARY_PATH = os.path.join(_PKG, "libhashgrid.so")
 
 HG_OK, HG_EINVAL, HG_EUNSUPPORTED, HG_EHIP = 0, -1, -2, -3
 HG_F32, HG_F16 = 0, 1
-HG_TUNE_FWD_LANES, HG_TUNE_BWD_LANES, HG_TUNE_CHUNK_POINTS, HG_TUNE_XCD_MAP = 0, 1, 2, 3
+(HG_TUNE_FWD_LANES, HG_TUNE_BWD_LANES, HG_TUNE_CHUNK_POINTS, HG_TUNE_XCD_MAP, HG_TUNE_BWD_BINNED,
+ HG_TUNE_FWD_UNROLL, HG_TUNE_FWD_NT, HG_TUNE_FWD_STAGED) = range(8)
 _DTYPES = {"f32": HG_F32, "f16": HG_F16}
 _TORCH_DTYPES = {HG_F32: torch.float32, HG_F16: torch.float16}
 
@@ -97,8 +98,10 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
                 "hashgrid_abi_version": ([], ctypes.c_int),
                 "hashgrid_last_error": ([], ctypes.c_char_p),
                 "hashgrid_resolutions": ([C, P], ctypes.c_int),
-                "hashgrid_forward": ([C, P, I64, P, P, I64, P], ctypes.c_int),
-                "hashgrid_backward": ([C, P, I64, P, I64, P, P], ctypes.c_int),
+                "hashgrid_forward": ([C, P, I64, P, P, I64, P, ctypes.c_size_t, P], ctypes.c_int),
+                "hashgrid_forward_workspace_size": ([C, I64, P], ctypes.c_int),
+                "hashgrid_backward": ([C, P, I64, P, I64, P, P, ctypes.c_size_t, P], ctypes.c_int),
+                "hashgrid_backward_workspace_size": ([C, I64, P, P], ctypes.c_int),
                 "hashgrid_debug_corners": ([C, P, I64, P, P, P], ctypes.c_int),
                 "hashgrid_tune": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),
                 "hashgrid_tune_get": ([ctypes.c_int], ctypes.c_int),
@@ -149,10 +152,36 @@ def hashgrid_resolutions(cfg: HashGridConfig) -> list:
     return list(out)
 
 
+def _workspace(workspace, sizer, name):
+    """(pointer, bytes) of a workspace argument: a uint8 GPU tensor, "auto"
+    (allocated here through torch's caching allocator) or None."""
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"{name} must be a tensor, 'auto' or None")
+        workspace = sizer()
+    if workspace is None:
+        return None, 0, None
+    _dev(workspace, name, torch.uint8)
+    return workspace.data_ptr(), workspace.numel(), workspace
+
+
+def hashgrid_forward_workspace_size(cfg: HashGridConfig, n: int) -> int:
+    """Bytes of the level-major staging buffer of a forward over n points."""
+    out = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().hashgrid_forward_workspace_size(ctypes.byref(c), n, ctypes.byref(out)))
+    return out.value
+
+
+def forward_workspace(cfg: HashGridConfig, n: int, device) -> torch.Tensor:
+    return torch.empty(max(1, hashgrid_forward_workspace_size(cfg, n)), dtype=torch.uint8, device=device)
+
+
 def hashgrid_forward(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tensor,
-                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                     out: torch.Tensor | None = None, workspace="auto", stream=None) -> torch.Tensor:
     """Encode points ``x`` [n, D] into ``out`` [n, >= L*F] (allocated when None;
-    only the first L*F columns of each row are written)."""
+    only the first L*F columns of each row are written).  ``workspace``: a
+    uint8 GPU tensor, "auto" or None (write the rows directly)."""
     _points(cfg, x)
     _dev(table, "table", cfg.torch_table_dtype)
     if tuple(table.shape) != cfg.table_shape or not table.is_contiguous():
@@ -163,16 +192,39 @@ def hashgrid_forward(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tensor,
     _dev(out, "out", torch.float32)
     if out.dim() != 2 or out.shape[0] != n or out.stride(1) != 1 or out.shape[1] < cfg.out_features:
         raise ValueError("out must be [n, >= L*F] with unit column stride")
+    ws_ptr, ws_bytes, _keep = _workspace(workspace, lambda: forward_workspace(cfg, n, x.device) if n else None,
+                                         "workspace")
     c = cfg.c()
     _check(load_library().hashgrid_forward(ctypes.byref(c), x.data_ptr(), n, table.data_ptr(),
-                                           out.data_ptr(), out.stride(0), _stream(x, stream)))
+                                           out.data_ptr(), out.stride(0), ws_ptr, ws_bytes,
+                                           _stream(x, stream)))
     return out
 
 
+def hashgrid_backward_workspace_size(cfg: HashGridConfig, n: int) -> tuple:
+    """(bytes for a one-pass binned backward of n points, minimum bytes)."""
+    full, least = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().hashgrid_backward_workspace_size(ctypes.byref(c), n, ctypes.byref(full),
+                                                           ctypes.byref(least)))
+    return full.value, least.value
+
+
+def backward_workspace(cfg: HashGridConfig, n: int, device) -> torch.Tensor | None:
+    """A device buffer sized for the one-pass binned backward (None if the
+    configuration has no binned path)."""
+    full, _ = hashgrid_backward_workspace_size(cfg, n)
+    if full == 0:
+        return None
+    return torch.empty(full, dtype=torch.uint8, device=device)
+
+
 def hashgrid_backward(cfg: HashGridConfig, x: torch.Tensor, dout: torch.Tensor,
-                      dtable: torch.Tensor, stream=None) -> torch.Tensor:
+                      dtable: torch.Tensor, workspace="auto", stream=None) -> torch.Tensor:
     """Accumulate the table gradient of ``dout`` [n, >= L*F] into ``dtable``
-    (float32, table shape)."""
+    (float32, table shape).  ``workspace``: a uint8 GPU tensor, "auto" (sized
+    by hashgrid_backward_workspace_size and allocated here) or None (the
+    atomic scatter)."""
     _points(cfg, x)
     n = x.shape[0]
     _dev(dout, "dout", torch.float32)
@@ -181,9 +233,12 @@ def hashgrid_backward(cfg: HashGridConfig, x: torch.Tensor, dout: torch.Tensor,
     _dev(dtable, "dtable", torch.float32)
     if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
         raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
+    ws_ptr, ws_bytes, _keep = _workspace(workspace, lambda: backward_workspace(cfg, n, x.device) if n else None,
+                                         "workspace")
     c = cfg.c()
     _check(load_library().hashgrid_backward(ctypes.byref(c), x.data_ptr(), n, dout.data_ptr(),
-                                            dout.stride(0), dtable.data_ptr(), _stream(x, stream)))
+                                            dout.stride(0), dtable.data_ptr(), ws_ptr, ws_bytes,
+                                            _stream(x, stream)))
     return dtable
 
 

@@ -61,13 +61,13 @@ def test_resolutions_many_configs_agree_with_oracle(oracle):
 def _call_forward(lib, cfg, x=0x1000, n=16, table=0x2000, out=0x3000, stride=None):
     c = cfg.c()
     stride = cfg.out_features if stride is None else stride
-    return lib.hashgrid_forward(ctypes.byref(c), x, n, table, out, stride, None)
+    return lib.hashgrid_forward(ctypes.byref(c), x, n, table, out, stride, None, 0, None)
 
 
 def _call_backward(lib, cfg, x=0x1000, n=16, dout=0x2000, stride=None, dtable=0x3000):
     c = cfg.c()
     stride = cfg.out_features if stride is None else stride
-    return lib.hashgrid_backward(ctypes.byref(c), x, n, dout, stride, dtable, None)
+    return lib.hashgrid_backward(ctypes.byref(c), x, n, dout, stride, dtable, None, 0, None)
 
 
 @pytest.mark.parametrize("bad,code", [
@@ -92,7 +92,7 @@ def test_bad_config_is_rejected(lib, bad, code):
 
 def test_bad_arguments_are_rejected(lib):
     cfg = hg.HashGridConfig()
-    assert lib.hashgrid_forward(None, 0x1000, 16, 0x2000, 0x3000, 32, None) == B.HG_EINVAL
+    assert lib.hashgrid_forward(None, 0x1000, 16, 0x2000, 0x3000, 32, None, 0, None) == B.HG_EINVAL
     assert _call_forward(lib, cfg, n=-1) == B.HG_EINVAL
     assert _call_forward(lib, cfg, x=None) == B.HG_EINVAL
     assert _call_forward(lib, cfg, x=0x1002) == B.HG_EINVAL          # misaligned x
@@ -104,6 +104,9 @@ def test_bad_arguments_are_rejected(lib):
     assert _call_backward(lib, cfg, dtable=0x3002) == B.HG_EINVAL
     assert _call_backward(lib, cfg, stride=7) == B.HG_EINVAL
     assert "stride" in lib.hashgrid_last_error().decode()
+    c = cfg.c()
+    assert lib.hashgrid_backward(ctypes.byref(c), 0x1000, 16, 0x2000, 32, 0x3000, 0x4010, 1 << 20,
+                                 None) == B.HG_EINVAL                 # workspace not 256-aligned
     big = hg.HashGridConfig(n_levels=64)
     assert _call_forward(lib, big, n=1 << 40) == B.HG_EINVAL
 
@@ -117,15 +120,38 @@ def test_zero_points_is_a_no_op(lib):
     cfg = hg.HashGridConfig()
     # n == 0 succeeds without looking at the pointers (NULL is fine).
     c = cfg.c()
-    assert lib.hashgrid_forward(ctypes.byref(c), None, 0, None, None, 32, None) == B.HG_OK
-    assert lib.hashgrid_backward(ctypes.byref(c), None, 0, None, 32, None, None) == B.HG_OK
+    assert lib.hashgrid_forward(ctypes.byref(c), None, 0, None, None, 32, None, 0, None) == B.HG_OK
+    assert lib.hashgrid_backward(ctypes.byref(c), None, 0, None, 32, None, None, 0, None) == B.HG_OK
     assert lib.hashgrid_debug_corners(ctypes.byref(c), None, 0, None, None, None) == B.HG_OK
     assert lib.hashgrid_last_error().decode() == ""
 
 
+def test_backward_workspace_size():
+    # 64 bytes per point, level and corner pair slot (tiles of 512 points) plus counters.
+    cfg = hg.HashGridConfig()
+    full, least = hg.hashgrid_backward_workspace_size(cfg, 1 << 18)
+    assert least * 16 == full
+    assert least >= 64 * (1 << 18) and least < 64 * (1 << 18) + (1 << 20)
+    assert hg.hashgrid_backward_workspace_size(cfg, 0) == (0, 0)
+    assert hg.hashgrid_backward_workspace_size(cfg, 1)[1] >= 64 * 512
+    big = hg.HashGridConfig(log2_table_size=25)   # beyond 1024 partitions: atomic path only
+    assert hg.hashgrid_backward_workspace_size(big, 1000) == (0, 0)
+    with pytest.raises(hg.HashGridError):
+        hg.hashgrid_backward_workspace_size(cfg, -1)
+
+
+def test_forward_workspace_size():
+    cfg = hg.HashGridConfig()
+    assert hg.hashgrid_forward_workspace_size(cfg, 1 << 18) == 32 << 20
+    assert hg.hashgrid_forward_workspace_size(cfg, 3) == 512      # 3 * 16 * 2 * 4 = 384, rounded to 256
+    assert hg.hashgrid_forward_workspace_size(cfg, 0) == 0
+
+
 def test_tuning_knobs(lib):
     for key, good, bad in ((B.HG_TUNE_FWD_LANES, 1, 3), (B.HG_TUNE_BWD_LANES, 2, 8),
-                           (B.HG_TUNE_CHUNK_POINTS, 512, 100), (B.HG_TUNE_XCD_MAP, 0, 2)):
+                           (B.HG_TUNE_CHUNK_POINTS, 512, 100), (B.HG_TUNE_XCD_MAP, 0, 2),
+                           (B.HG_TUNE_BWD_BINNED, 0, 3), (B.HG_TUNE_FWD_UNROLL, 2, 3),
+                           (B.HG_TUNE_FWD_NT, 1, 2), (B.HG_TUNE_FWD_STAGED, 0, 2)):
         old = hg.hashgrid_tune_get(key)
         hg.hashgrid_tune(key, good)
         assert hg.hashgrid_tune_get(key) == good

@@ -45,18 +45,18 @@ def bwd_check(grad, ref, L):
         assert err <= BWD_TOL * scale, f"level {l}: backward err {err:.3g} > {BWD_TOL} * {scale:.3g}"
 
 
-def run_forward(cfg, x, t, stride=None):
+def run_forward(cfg, x, t, stride=None, workspace="auto"):
     n = x.shape[0]
     if stride is None:
-        return hg.hashgrid_forward(cfg, dev(x), dev(t)).cpu().numpy()
+        return hg.hashgrid_forward(cfg, dev(x), dev(t), workspace=workspace).cpu().numpy()
     buf = torch.full((n, stride), 7.0, device=DEV)
-    hg.hashgrid_forward(cfg, dev(x), dev(t), out=buf)
+    hg.hashgrid_forward(cfg, dev(x), dev(t), out=buf, workspace=workspace)
     return buf.cpu().numpy()
 
 
-def run_backward(cfg, x, d, init=None):
+def run_backward(cfg, x, d, init=None, workspace="auto"):
     g = torch.zeros(cfg.table_shape, device=DEV) if init is None else dev(init)
-    hg.hashgrid_backward(cfg, dev(x), dev(d), g)
+    hg.hashgrid_backward(cfg, dev(x), dev(d), g, workspace=workspace)
     return g.cpu().numpy()
 
 
@@ -114,11 +114,12 @@ def test_forward_half_tables_full_size_sampled(oracle):
     assert fwd_err(out[rows], ref, t) <= FWD_TOL
 
 
-def test_forward_writes_only_its_columns_of_a_wider_row(oracle):
+@pytest.mark.parametrize("workspace", ["auto", None])
+def test_forward_writes_only_its_columns_of_a_wider_row(oracle, workspace):
     w = I.resized(I.WORKLOADS["standard"], 1000)
     cfg = hg.HashGridConfig.of(w)
     x, t = I.make_points(w), I.make_table(w)
-    buf = run_forward(cfg, x, t, stride=cfg.out_features + 64)
+    buf = run_forward(cfg, x, t, stride=cfg.out_features + 64, workspace=workspace)
     ref = oracle.forward(oracle.grid_of(w), x, t)
     assert fwd_err(buf[:, :cfg.out_features], ref, t) <= FWD_TOL
     assert np.all(buf[:, cfg.out_features:] == 7.0)
@@ -145,11 +146,21 @@ def test_forward_out_of_domain_points(oracle):
 
 
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 1023, 1025])
-def test_forward_ragged_sizes(oracle, n):
+@pytest.mark.parametrize("workspace", ["auto", None])
+def test_forward_ragged_sizes(oracle, n, workspace):
     w = I.resized(I.WORKLOADS["standard"], n)
     cfg = hg.HashGridConfig.of(w)
     x, t = I.make_points(w), I.make_table(w)
-    assert fwd_err(run_forward(cfg, x, t), oracle.forward(oracle.grid_of(w), x, t), t) <= FWD_TOL
+    out = run_forward(cfg, x, t, workspace=workspace)
+    assert fwd_err(out, oracle.forward(oracle.grid_of(w), x, t), t) <= FWD_TOL
+
+
+def test_forward_staged_and_direct_are_identical():
+    # Both output paths compute every value with the same instructions.
+    w = I.resized(I.WORKLOADS["standard"], 7777)
+    cfg = hg.HashGridConfig.of(w)
+    x, t = I.make_points(w), I.make_table(w)
+    assert np.array_equal(run_forward(cfg, x, t, workspace="auto"), run_forward(cfg, x, t, workspace=None))
 
 
 # ----------------------------------------------------------------------------- backward
@@ -209,11 +220,61 @@ def test_backward_accumulates_and_reads_strided_rows(oracle):
         assert err <= BWD_TOL * np.max(np.abs(delta[l])) + 4e-7 * np.max(np.abs(base[l]))
 
 
+@pytest.mark.parametrize("name,n", [("standard", 3 * 1024 + 37), ("tiny", None)])
+def test_backward_atomic_path_matches_oracle(oracle, name, n):
+    # No workspace: the fp32 global-atomic scatter.
+    w = I.WORKLOADS[name] if n is None else I.resized(I.WORKLOADS[name], n)
+    cfg = hg.HashGridConfig.of(w)
+    x, d = I.make_points(w), I.make_dout(w)
+    bwd_check(run_backward(cfg, x, d, workspace=None), oracle.backward(oracle.grid_of(w), x, d), w.n_levels)
+
+
+@pytest.mark.parametrize("levels_per_pass", [1, 3, 16])
+def test_backward_binned_in_level_groups(oracle, levels_per_pass):
+    # A workspace for fewer levels than L: the library processes level groups.
+    w = I.resized(I.WORKLOADS["standard"], 4 * 512 + 300)
+    cfg = hg.HashGridConfig.of(w)
+    x, d = I.make_points(w), I.make_dout(w)
+    full, least = hg.hashgrid_backward_workspace_size(cfg, w.n_points)
+    ws = torch.empty(least * levels_per_pass + 100, dtype=torch.uint8, device=DEV)
+    grad = run_backward(cfg, x, d, workspace=ws)
+    bwd_check(grad, oracle.backward(oracle.grid_of(w), x, d), w.n_levels)
+
+
+def test_backward_binned_split_corner_pairs(oracle):
+    # Negative coordinates make x = -1 corners whose x+1 neighbour lies in another
+    # table partition: those pairs take the split path.
+    w = I.WORKLOADS["standard"]
+    cfg = hg.HashGridConfig.of(w)
+    rng = np.random.default_rng(18)
+    x = rng.uniform(-0.02, 0.02, size=(6000, 3)).astype(np.float32)
+    d = rng.standard_normal((6000, 32)).astype(np.float32)
+    bwd_check(run_backward(cfg, x, d), oracle.backward(oracle.grid_of(w), x, d), w.n_levels)
+
+
+def test_backward_binned_reused_workspace_and_dirty_contents(oracle):
+    w = I.resized(I.WORKLOADS["standard"], 5000)
+    cfg = hg.HashGridConfig.of(w)
+    x, d = I.make_points(w), I.make_dout(w)
+    full, _ = hg.hashgrid_backward_workspace_size(cfg, w.n_points)
+    ws = torch.full((full,), 0xA5, dtype=torch.uint8, device=DEV)
+    g1 = run_backward(cfg, x, d, workspace=ws)
+    x2 = x[:3001].copy()
+    d2 = d[:3001].copy()
+    g2 = run_backward(cfg, x2, d2, workspace=ws)
+    ref1 = oracle.backward(oracle.grid_of(w), x, d)
+    ref2 = oracle.backward(oracle.grid_of(w), x2, d2)
+    bwd_check(g1, ref1, w.n_levels)
+    bwd_check(g2, ref2, w.n_levels)
+
+
 # ----------------------------------------------------------------------------- launch shapes
 
 @pytest.mark.parametrize("key,value", [(B.HG_TUNE_FWD_LANES, 1), (B.HG_TUNE_BWD_LANES, 1),
                                        (B.HG_TUNE_BWD_LANES, 2), (B.HG_TUNE_XCD_MAP, 0),
-                                       (B.HG_TUNE_CHUNK_POINTS, 64), (B.HG_TUNE_CHUNK_POINTS, 8192)])
+                                       (B.HG_TUNE_CHUNK_POINTS, 64), (B.HG_TUNE_CHUNK_POINTS, 8192),
+                                       (B.HG_TUNE_BWD_BINNED, 0), (B.HG_TUNE_FWD_UNROLL, 2),
+                                       (B.HG_TUNE_FWD_UNROLL, 4), (B.HG_TUNE_FWD_NT, 1)])
 def test_launch_variants_match_oracle(oracle, key, value):
     w = I.resized(I.WORKLOADS["standard"], 5 * 1024 + 77)
     cfg = hg.HashGridConfig.of(w)
