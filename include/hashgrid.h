@@ -114,7 +114,8 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
  * (about 268 MB for L = 16, n = 2^18).  *bytes_out is a HOST size_t.
  * A workspace of at least *min_bytes_out (one level's share; may be NULL)
  * also works -- the levels are then processed in groups.  Returns 0 bytes
- * when the configuration has no binned path (T > 2^24, n >= 2^29).
+ * when the configuration has no binned path (more than 4096 partitions of
+ * 2^13 entries, i.e. T > 2^25, or n >= 2^29).
  * Errors: HG_EINVAL, HG_EUNSUPPORTED. */
 int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out,
                                      size_t *min_bytes_out);
@@ -163,6 +164,7 @@ int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint
 #define HG_TUNE_FWD_UNROLL 5   /* points per lane pair in flight in the forward: 1, 2 or 4 */
 #define HG_TUNE_FWD_NT 6       /* 1: non-temporal point reads and output writes         */
 #define HG_TUNE_FWD_STAGED 7   /* 1: stage the forward level-major when given workspace */
+#define HG_TUNE_BWD_PART_LOG2 8 /* log2 entries per binned-backward partition: 11..13, 0 = by T */
 int hashgrid_tune(int key, int value);
 int hashgrid_tune_get(int key);
 

@@ -39,6 +39,7 @@ struct Tuning {
     int fwd_unroll = 4;
     int fwd_nt = 0;
     int fwd_staged = 1;
+    int bwd_part_log2 = 0;  // 0: by table size
 };
 Tuning g_tune;
 
@@ -101,7 +102,11 @@ int plan(const hg_config &c, int64_t n, hg::LaunchParams &lp) {
 // path (partition count or record count beyond the kernels' index widths).
 bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
     if (c.n_dims != 3 || c.n_features != 2) return false;
-    const int s_log2 = c.log2_table_size < hg::kMaxSLog2 ? c.log2_table_size : hg::kMaxSLog2;
+    // Partition of 2^12 entries (32 KB of accumulators, 512-thread owners) for
+    // tables up to 2^20 entries; 2^13 (1024 threads) for larger tables, whose
+    // runs per tile would otherwise get short.
+    const int want = g_tune.bwd_part_log2 ? g_tune.bwd_part_log2 : (c.log2_table_size <= 20 ? 12 : 13);
+    const int s_log2 = c.log2_table_size < want ? c.log2_table_size : want;
     const int64_t parts = (int64_t)1 << (c.log2_table_size - s_log2);
     const int64_t tiles = (n + hg::kBinTile - 1) / hg::kBinTile;
     if (parts > hg::kMaxParts || n >= ((int64_t)1 << 29)) return false;
@@ -114,6 +119,7 @@ bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
     bp.mask = (uint32_t)((1ull << c.log2_table_size) - 1);
     bp.pad_ = 0;
     bp.n = n;
+    bp.level_records = tiles * hg::kBinTile * 4;
     resolutions(c, bp.res);
     return true;
 }
@@ -272,6 +278,10 @@ int hashgrid_tune(int key, int value) {
         if (value != 0 && value != 1) break;
         g_tune.fwd_staged = value;
         return ok();
+    case HG_TUNE_BWD_PART_LOG2:
+        if (value != 0 && (value < 11 || value > hg::kMaxSLog2)) break;
+        g_tune.bwd_part_log2 = value;
+        return ok();
     default:
         return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
@@ -288,6 +298,7 @@ int hashgrid_tune_get(int key) {
     case HG_TUNE_FWD_UNROLL: return g_tune.fwd_unroll;
     case HG_TUNE_FWD_NT: return g_tune.fwd_nt;
     case HG_TUNE_FWD_STAGED: return g_tune.fwd_staged;
+    case HG_TUNE_BWD_PART_LOG2: return g_tune.bwd_part_log2;
     default: return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
 }

@@ -46,20 +46,23 @@ constexpr int kBinThreads = 256;
 constexpr int kPtsPerThread = kBinTile / kBinThreads;  // 2
 constexpr int kRecPerTile = kBinTile * 4;              // 4 corner pairs per point
 constexpr int kLevelsPerBlock = 4;                     // levels per bin workgroup
-constexpr int kAccThreads = 1024;
+// Tiles fold their max |dL/dout| into one of kMaxSlots words per level (tile
+// mod kMaxSlots): global atomics on one address serialise at the memory-side
+// atomic unit, so the many tiles of a level must not all hit the same word.
+constexpr int kMaxSlots = 64;
 
 // Workspace of one launch group.
 struct Space {
-    uint4 *records;     // [group][tiles][kRecPerTile], each tile sorted by partition
+    uint4 *records;     // [group][tiles][kRecPerTile], each tile's records sorted by partition
     uint32_t *runs;     // [group][tiles][parts + 1], start of every partition's run in the tile
-    uint32_t *dmax;     // [group], bits of max |dL/dout| (non-negative floats order as uints)
+    uint32_t *dmax;     // [group][kMaxSlots], bits of max |dL/dout| (non-negative floats order as uints)
 };
 
 Space carve(void *ws, const BinParams &bp) {
     Space s;
     char *p = reinterpret_cast<char *>(ws);
     s.records = reinterpret_cast<uint4 *>(p);
-    p += (size_t)bp.group * bp.tiles * kRecPerTile * sizeof(uint4);
+    p += (size_t)bp.group * bp.level_records * sizeof(uint4);
     s.runs = reinterpret_cast<uint32_t *>(p);
     p += (size_t)bp.group * bp.tiles * (bp.parts + 1) * sizeof(uint32_t);
     s.dmax = reinterpret_cast<uint32_t *>(p);
@@ -83,20 +86,17 @@ struct Pairs {
     float dabs;             // max(|g_0|, |g_1|)
 };
 
-__device__ __forceinline__ void make_pairs(const float *__restrict__ x, const float *__restrict__ dout,
-                                           int64_t dstride, int64_t p, int l, const BinParams &bp,
+__device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1, int l, const BinParams &bp,
                                            Pairs &out) {
     const float N = (float)bp.res[l];
     int32_t v0, v1, v2;
     float a0, a1, a2;
-    locate1b(x[3 * p + 0], N, v0, a0);
-    locate1b(x[3 * p + 1], N, v1, a1);
-    locate1b(x[3 * p + 2], N, v2, a2);
+    locate1b(xp[0], N, v0, a0);
+    locate1b(xp[1], N, v1, a1);
+    locate1b(xp[2], N, v2, a2);
     const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hz0 = (uint32_t)v2 * kPrimeZ;
     const uint32_t cx0 = (uint32_t)v0, cx1 = cx0 + 1u;
     const uint32_t smask = (1u << bp.s_log2) - 1u;
-    const float d0 = dout[p * dstride + 2 * l];
-    const float d1 = dout[p * dstride + 2 * l + 1];
     out.dabs = fmaxf(fabsf(d0), fabsf(d1));
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -132,43 +132,109 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
     return v;
 }
 
+// Exclusive prefix of cnt[0..count) into base[0..count] (base[count] = total)
+// by all kBinThreads threads: each thread sums a contiguous slice, the wave
+// sums are combined through wsum, and every thread writes its slice.
+__device__ __forceinline__ void block_exclusive_scan(const uint32_t *cnt, int count, uint32_t *base,
+                                                     uint32_t *wsum) {
+    const int per = (count + kBinThreads - 1) / kBinThreads;
+    const int b = per * threadIdx.x, e = min(count, b + per);
+    uint32_t s = 0;
+    for (int i = b; i < e; ++i) s += cnt[i];
+    const uint32_t incl = wave_inclusive_scan(s);
+    if ((threadIdx.x & 63) == 63) wsum[threadIdx.x >> 6] = incl;
+    __syncthreads();
+    uint32_t run = incl - s;
+    for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) run += wsum[w];
+    for (int i = b; i < e; ++i) {
+        base[i] = run;
+        run += cnt[i];
+    }
+    if (threadIdx.x == kBinThreads - 1) base[count] = run;
+}
+
 // ---------------------------------------------------------------- init
 
 __global__ void init_kernel(uint32_t *dmax, int group) {
-    if ((int)threadIdx.x < group) dmax[threadIdx.x] = 0u;
+    for (int i = threadIdx.x; i < group * kMaxSlots; i += blockDim.x) dmax[i] = 0u;
+}
+
+// ---------------------------------------------------------------- loads
+
+// The coordinates and the block's dL/dout of one thread's points, loaded once
+// per workgroup (one 32-byte row segment per point when aligned).
+struct TilePoints {
+    float xs[kPtsPerThread][3];
+    float dv[kPtsPerThread][kLevelsPerBlock][2];
+    bool valid[kPtsPerThread];
+};
+
+template <bool kDout>
+__device__ __forceinline__ void load_points(const float *__restrict__ x, int64_t n, const float *__restrict__ dout,
+                                            int64_t dstride, int tile, int lfirst, int nlev, TilePoints &tp) {
+    const bool vec = nlev == kLevelsPerBlock && (dstride & 3) == 0 &&
+                     (((uintptr_t)(dout + 2 * lfirst)) & 15) == 0;
+#pragma unroll
+    for (int k = 0; k < kPtsPerThread; ++k) {
+        const int64_t p = (int64_t)tile * kBinTile + k * kBinThreads + threadIdx.x;
+        tp.valid[k] = p < n;
+        // Points past n recompute the last point (always initialised) and emit nothing.
+        const int64_t q = tp.valid[k] ? p : n - 1;
+        tp.xs[k][0] = x[3 * q + 0];
+        tp.xs[k][1] = x[3 * q + 1];
+        tp.xs[k][2] = x[3 * q + 2];
+        if (!kDout) continue;
+        const float *drow = dout + q * dstride + 2 * lfirst;
+        if (vec) {
+            const float4 a = *reinterpret_cast<const float4 *>(drow);
+            const float4 b = *reinterpret_cast<const float4 *>(drow + 4);
+            tp.dv[k][0][0] = a.x; tp.dv[k][0][1] = a.y; tp.dv[k][1][0] = a.z; tp.dv[k][1][1] = a.w;
+            tp.dv[k][2][0] = b.x; tp.dv[k][2][1] = b.y; tp.dv[k][3][0] = b.z; tp.dv[k][3][1] = b.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kLevelsPerBlock; ++j) {
+                tp.dv[k][j][0] = j < nlev ? drow[2 * j] : 0.f;
+                tp.dv[k][j][1] = j < nlev ? drow[2 * j + 1] : 0.f;
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- bin
 
+// Workgroup (tile, block of kLevelsPerBlock consecutive levels).
 __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restrict__ x, int64_t n,
                                                           const float *__restrict__ dout, int64_t dstride,
                                                           BinParams bp, Space sp, float *__restrict__ grad) {
     __shared__ uint4 stage[kRecPerTile];
     __shared__ uint32_t wmax[kBinThreads / 64];
+    __shared__ uint32_t wsum[kBinThreads / 64];
     extern __shared__ uint32_t dyn[];  // cnt[parts], base[parts + 1]
     uint32_t *cnt = dyn;
     uint32_t *base = dyn + bp.parts;
     const int tile = blockIdx.x;
-    const int g_end = min(bp.group, (int)(blockIdx.y + 1) * kLevelsPerBlock);
-    for (int g = blockIdx.y * kLevelsPerBlock; g < g_end; ++g) {
+    const int gb = blockIdx.y * kLevelsPerBlock;
+    const int nlev = min(bp.group - gb, kLevelsPerBlock);
+    TilePoints tp;
+    load_points<true>(x, n, dout, dstride, tile, bp.level0 + gb, nlev, tp);
+#pragma unroll
+    for (int j = 0; j < kLevelsPerBlock; ++j) {
+        if (j >= nlev) break;
+        const int g = gb + j;
         const int l = bp.level0 + g;
         for (int i = threadIdx.x; i < bp.parts; i += kBinThreads) cnt[i] = 0;
         __syncthreads();
         Pairs pr[kPtsPerThread];
         uint32_t rank[kPtsPerThread][4];
-        bool valid[kPtsPerThread];
         float dm = 0.f;
 #pragma unroll
         for (int k = 0; k < kPtsPerThread; ++k) {
-            const int64_t p = (int64_t)tile * kBinTile + k * kBinThreads + threadIdx.x;
-            valid[k] = p < n;
-            // Points past n recompute the last point (always initialised) and emit nothing.
-            make_pairs(x, dout, dstride, valid[k] ? p : n - 1, l, bp, pr[k]);
-            dm = fmaxf(dm, pr[k].dabs);
+            make_pairs(tp.xs[k], tp.dv[k][j][0], tp.dv[k][j][1], l, bp, pr[k]);
+            if (tp.valid[k]) dm = fmaxf(dm, pr[k].dabs);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                rank[k][c] = valid[k] ? atomicAdd(&cnt[pr[k].part[c]], 1u) : 0u;
-                if (valid[k] && pr[k].split_idx[c] != ~0u) {
+                rank[k][c] = tp.valid[k] ? atomicAdd(&cnt[pr[k].part[c]], 1u) : 0u;
+                if (tp.valid[k] && pr[k].split_idx[c] != ~0u) {
                     float *e = grad + (((uint64_t)l << bp.log2_table_size) + pr[k].split_idx[c]) * 2;
                     unsafeAtomicAdd(e, pr[k].split_val[c].x);
                     unsafeAtomicAdd(e + 1, pr[k].split_val[c].y);
@@ -178,41 +244,25 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
         for (int off = 32; off > 0; off >>= 1) dm = fmaxf(dm, __shfl_xor(dm, off, 64));
         if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = __float_as_uint(dm);
         __syncthreads();
-        // Run starts of the tile's partitions (wave 0), published for the owners.
-        uint32_t *runs = sp.runs + ((int64_t)g * bp.tiles + tile) * (bp.parts + 1);
-        if (threadIdx.x < 64) {
-            const int per = (bp.parts + 63) / 64;
-            const int b = per * threadIdx.x, e = min(bp.parts, b + per);
-            uint32_t s = 0;
-            for (int i = b; i < e; ++i) s += cnt[i];
-            const uint32_t incl = wave_inclusive_scan(s);
-            uint32_t run = incl - s;
-            for (int i = b; i < e; ++i) {
-                base[i] = run;
-                runs[i] = run;
-                run += cnt[i];
-            }
-            if (threadIdx.x == 63) {
-                base[bp.parts] = incl;
-                runs[bp.parts] = incl;
-            }
-            if (threadIdx.x == 0) {
-                uint32_t m = wmax[0];
-                for (int w = 1; w < kBinThreads / 64; ++w) m = max(m, wmax[w]);
-                atomicMax(sp.dmax + g, m);
-            }
+        // Run starts of the tile's partitions, published for the owners.
+        block_exclusive_scan(cnt, bp.parts, base, wsum);
+        if (threadIdx.x == 0) {
+            uint32_t m = wmax[0];
+            for (int w = 1; w < kBinThreads / 64; ++w) m = max(m, wmax[w]);
+            atomicMax(sp.dmax + g * kMaxSlots + (tile % kMaxSlots), m);
         }
         __syncthreads();
+        uint32_t *runs = sp.runs + ((int64_t)g * bp.tiles + tile) * (bp.parts + 1);
+        for (int i = threadIdx.x; i <= bp.parts; i += kBinThreads) runs[i] = base[i];
 #pragma unroll
         for (int k = 0; k < kPtsPerThread; ++k) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (valid[k]) stage[base[pr[k].part[c]] + rank[k][c]] = pr[k].rec[c];
-            }
+            for (int c = 0; c < 4; ++c)
+                if (tp.valid[k]) stage[base[pr[k].part[c]] + rank[k][c]] = pr[k].rec[c];
         }
         __syncthreads();
         const uint32_t total = base[bp.parts];
-        uint4 *trec = sp.records + ((int64_t)g * bp.tiles + tile) * kRecPerTile;
+        uint4 *trec = sp.records + (int64_t)g * bp.level_records + (int64_t)tile * kRecPerTile;
         for (uint32_t i = threadIdx.x; i < total; i += kBinThreads) trec[i] = stage[i];
         __syncthreads();
     }
@@ -246,34 +296,38 @@ __device__ __forceinline__ int fixed_exponent(uint32_t dmax_bits) {
     return 30 - e;
 }
 
-// Workgroup (level, partition).  The tiles are walked in chunks of 1024:
-// wave w takes tiles chunk + w + 16 i (lane i), scans its lanes' run lengths
-// and then works through the concatenation of those runs, 64 records per
-// step and kAccBatch steps in flight, finding each record's tile by a binary
-// search over the wave's 64 run offsets.
+// Workgroup (level, partition) of THREADS threads.  The tiles are walked in
+// chunks of THREADS: wave w takes tiles chunk + 64 w + i (lane i), scans its
+// lanes' run lengths and works through the concatenation of those runs, 64
+// records per step, finding each record's tile by a binary search over the
+// wave's 64 run offsets.  Two batches of kAccBatch steps are in flight: the
+// next batch is requested before the current one is added.
 constexpr int kAccBatch = 4;
-constexpr int kAccWaves = kAccThreads / 64;
 
-__global__ __launch_bounds__(kAccThreads) void accumulate_kernel(BinParams bp, Space sp,
-                                                                 float *__restrict__ grad) {
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space sp, float *__restrict__ grad) {
+    constexpr int kWaves = THREADS / 64;
     extern __shared__ unsigned long long slice[];    // [2^s][2] fixed-point accumulators
-    __shared__ uint32_t pre[kAccWaves][65];         // per wave: run offsets in the concatenation
-    __shared__ uint32_t start[kAccWaves][64];       // per wave: run start inside each tile
+    __shared__ uint32_t pre[kWaves][65];            // per wave: run offsets in the concatenation
+    __shared__ uint32_t start[kWaves][64];          // per wave: run start inside each tile
     __shared__ uint32_t touched;
     const int g = blockIdx.x / bp.parts;
     const int part = blockIdx.x - g * bp.parts;
     const int l = bp.level0 + g;
     const int S = 1 << bp.s_log2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < 2 * S; i += kAccThreads) slice[i] = 0ull;
+    for (int i = threadIdx.x; i < 2 * S; i += THREADS) slice[i] = 0ull;
     if (threadIdx.x == 0) touched = 0;
-    const int k = fixed_exponent(sp.dmax[g]);
-    const uint4 *grec = sp.records + (int64_t)g * bp.tiles * kRecPerTile;
-    for (int chunk = 0; chunk < bp.tiles; chunk += kAccThreads) {
-        const int t = chunk + wave + kAccWaves * lane;
+    uint32_t dm = sp.dmax[g * kMaxSlots + lane];
+    for (int off = 32; off > 0; off >>= 1) dm = max(dm, __shfl_xor(dm, off, 64));
+    const int k = fixed_exponent(dm);
+    const uint4 *grec = sp.records + (int64_t)g * bp.level_records;
+    const uint32_t *truns = sp.runs + (int64_t)g * bp.tiles * (bp.parts + 1) + part;
+    for (int chunk = 0; chunk < bp.tiles; chunk += THREADS) {
+        const int t = chunk + 64 * wave + lane;
         uint32_t s = 0, len = 0;
         if (t < bp.tiles) {
-            const uint32_t *r = sp.runs + ((int64_t)g * bp.tiles + t) * (bp.parts + 1) + part;
+            const uint32_t *r = truns + (int64_t)t * (bp.parts + 1);
             s = r[0];
             len = r[1] - s;
         }
@@ -285,26 +339,34 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(BinParams bp, S
         const uint32_t total = pre[wave][64];
         if (total && lane == 0) touched = 1;
         const uint32_t *wp = pre[wave];
-        for (uint32_t base = 0; base < total; base += 64 * kAccBatch) {
-            uint4 q[kAccBatch];
-            bool ok[kAccBatch];
+        const uint32_t *ws = start[wave];
+        const uint4 *trec = grec + (int64_t)(chunk + 64 * wave) * kRecPerTile;
+        // Record i of the wave's concatenated runs (i < total).
+        auto fetch = [&](uint32_t i) -> uint4 {
+            int lo = 0;  // last run j with pre[j] <= i
+#pragma unroll
+            for (int step = 32; step > 0; step >>= 1)
+                if (wp[lo + step] <= i) lo += step;
+            return trec[(int64_t)lo * kRecPerTile + ws[lo] + (i - wp[lo])];
+        };
+        uint4 cur[kAccBatch], nxt[kAccBatch];
+#pragma unroll
+        for (int u = 0; u < kAccBatch; ++u) {
+            const uint32_t i = u * 64 + lane;
+            if (i < total) cur[u] = fetch(i);
+        }
+        for (uint32_t b0 = 0; b0 < total; b0 += 64 * kAccBatch) {
+            const uint32_t b1 = b0 + 64 * kAccBatch;
 #pragma unroll
             for (int u = 0; u < kAccBatch; ++u) {
-                const uint32_t i = base + u * 64 + lane;
-                ok[u] = i < total;
-                int lo = 0;
-                if (ok[u]) {
-                    // last run j with pre[j] <= i
-#pragma unroll
-                    for (int step = 32; step > 0; step >>= 1)
-                        if (wp[lo + step] <= i) lo += step;
-                    const int64_t tile = chunk + wave + kAccWaves * lo;
-                    q[u] = grec[tile * kRecPerTile + start[wave][lo] + (i - wp[lo])];
-                }
+                const uint32_t i = b1 + u * 64 + lane;
+                if (i < total) nxt[u] = fetch(i);
             }
 #pragma unroll
             for (int u = 0; u < kAccBatch; ++u)
-                if (ok[u]) apply_record(slice, q[u], k);
+                if (b0 + u * 64 + lane < total) apply_record(slice, cur[u], k);
+#pragma unroll
+            for (int u = 0; u < kAccBatch; ++u) cur[u] = nxt[u];
         }
         __syncthreads();
     }
@@ -312,7 +374,7 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(BinParams bp, S
     // The partition's entries are [part * S, (part + 1) * S) of level l.
     float4 *gl = reinterpret_cast<float4 *>(grad + ((((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * 2));
     const long long *sl = reinterpret_cast<const long long *>(slice);
-    for (int j = threadIdx.x; j < S / 2; j += kAccThreads) {
+    for (int j = threadIdx.x; j < S / 2; j += THREADS) {
         float4 a = gl[j];
         a.x += (float)ldexp((double)sl[4 * j + 0], -k);
         a.y += (float)ldexp((double)sl[4 * j + 1], -k);
@@ -322,11 +384,22 @@ __global__ __launch_bounds__(kAccThreads) void accumulate_kernel(BinParams bp, S
     }
 }
 
+template <int THREADS>
+hipError_t launch_accumulate(const BinParams &bp, const Space &sp, float *dtable, hipStream_t stream) {
+    const size_t lds = ((size_t)2 << bp.s_log2) * sizeof(unsigned long long);
+    // The partition slice can exceed the default 64 KB of dynamic LDS.
+    hipError_t e = hipFuncSetAttribute((const void *)accumulate_kernel<THREADS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    accumulate_kernel<THREADS><<<bp.group * bp.parts, THREADS, lds, stream>>>(bp, sp, dtable);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t binned_level_bytes(const BinParams &bp) {
-    const size_t recs = (size_t)bp.tiles * kRecPerTile * sizeof(uint4);
-    const size_t words = (size_t)bp.tiles * (bp.parts + 1) + 1;
+    const size_t recs = (size_t)bp.level_records * sizeof(uint4);
+    const size_t words = (size_t)bp.tiles * (bp.parts + 1) + kMaxSlots;
     return recs + words * sizeof(uint32_t);
 }
 
@@ -337,21 +410,20 @@ hipError_t launch_binned_backward(BinParams bp, int n_levels, const float *x, in
     int group = (int)(workspace_bytes / per_level);
     if (group > n_levels) group = n_levels;
     if (group < 1) return hipErrorInvalidValue;
-    const size_t acc_lds = ((size_t)2 << bp.s_log2) * sizeof(unsigned long long);
-    // The partition slice can exceed the default 64 KB of dynamic LDS.
-    hipError_t e = hipFuncSetAttribute((const void *)accumulate_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)acc_lds);
-    if (e != hipSuccess) return e;
     for (int l0 = 0; l0 < n_levels; l0 += group) {
         bp.level0 = l0;
         bp.group = min(group, n_levels - l0);
         const Space sp = carve(workspace, bp);
-        init_kernel<<<1, 64, 0, stream>>>(sp.dmax, bp.group);
         const dim3 tgrid(bp.tiles, (bp.group + kLevelsPerBlock - 1) / kLevelsPerBlock);
+        init_kernel<<<1, 256, 0, stream>>>(sp.dmax, bp.group);
         bin_kernel<<<tgrid, kBinThreads, (2 * bp.parts + 1) * sizeof(uint32_t), stream>>>(x, n, dout, dout_stride,
                                                                                          bp, sp, dtable);
-        accumulate_kernel<<<bp.group * bp.parts, kAccThreads, acc_lds, stream>>>(bp, sp, dtable);
-        e = hipGetLastError();
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // Larger partitions (longer runs per tile) take more LDS and more threads.
+        if (bp.s_log2 >= 13) e = launch_accumulate<1024>(bp, sp, dtable, stream);
+        else if (bp.s_log2 == 12) e = launch_accumulate<512>(bp, sp, dtable, stream);
+        else e = launch_accumulate<256>(bp, sp, dtable, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

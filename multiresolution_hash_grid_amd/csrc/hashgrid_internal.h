@@ -39,8 +39,8 @@ struct LaunchParams {
 // Binned backward (binned_backward.hip): the table gradient routed to
 // per-partition owners instead of global atomics.
 constexpr int kBinTile = 512;     // points per binning tile
-constexpr int kMaxParts = 2048;   // partitions per level
-constexpr int kMaxSLog2 = 12;     // partition = 2^12 entries = 64 KB of 2 x int64 accumulators
+constexpr int kMaxParts = 4096;   // partitions per level
+constexpr int kMaxSLog2 = 13;     // largest partition: 2^13 entries = 128 KB of 2 x int64 accumulators
 
 struct BinParams {
     int32_t level0;          // first level of this launch group
@@ -52,6 +52,7 @@ struct BinParams {
     uint32_t mask;           // T - 1
     int32_t pad_;
     int64_t n;
+    int64_t level_records;   // record slots per level = tiles * kBinTile * 4
     int32_t res[kMaxLevels];
 };
 

@@ -134,7 +134,7 @@ def test_backward_workspace_size():
     assert least >= 64 * (1 << 18) and least < 64 * (1 << 18) + (1 << 20)
     assert hg.hashgrid_backward_workspace_size(cfg, 0) == (0, 0)
     assert hg.hashgrid_backward_workspace_size(cfg, 1)[1] >= 64 * 512
-    big = hg.HashGridConfig(log2_table_size=25)   # beyond 1024 partitions: atomic path only
+    big = hg.HashGridConfig(log2_table_size=28)   # beyond 4096 partitions: atomic path only
     assert hg.hashgrid_backward_workspace_size(big, 1000) == (0, 0)
     with pytest.raises(hg.HashGridError):
         hg.hashgrid_backward_workspace_size(cfg, -1)
@@ -151,7 +151,8 @@ def test_tuning_knobs(lib):
     for key, good, bad in ((B.HG_TUNE_FWD_LANES, 1, 3), (B.HG_TUNE_BWD_LANES, 2, 8),
                            (B.HG_TUNE_CHUNK_POINTS, 512, 100), (B.HG_TUNE_XCD_MAP, 0, 2),
                            (B.HG_TUNE_BWD_BINNED, 0, 3), (B.HG_TUNE_FWD_UNROLL, 2, 3),
-                           (B.HG_TUNE_FWD_NT, 1, 2), (B.HG_TUNE_FWD_STAGED, 0, 2)):
+                           (B.HG_TUNE_FWD_NT, 1, 2), (B.HG_TUNE_FWD_STAGED, 0, 2),
+                           (B.HG_TUNE_BWD_PART_LOG2, 12, 14)):
         old = hg.hashgrid_tune_get(key)
         hg.hashgrid_tune(key, good)
         assert hg.hashgrid_tune_get(key) == good
