@@ -1,0 +1,175 @@
+"""Summaries of rocprofv3 output for the encoder's passes.
+
+    # kernel durations of a --kernel-trace --stats -f csv run
+    python -m multiresolution_hash_grid_amd.profile_summary stats DIR --command "..." --out FILE.md
+
+    # HBM traffic per pass from --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of the
+    # benchmark and of a plain device copy (the calibration)
+    python -m multiresolution_hash_grid_amd.profile_summary traffic --fetch D1 --write D2 \\
+        --copy-fetch D3 --copy-write D4 --copy-bytes B --out FILE.json
+
+    # the calibration workload itself: a device-to-device copy of B bytes
+    python -m multiresolution_hash_grid_amd.profile_summary copy --bytes B
+
+A pass is the group of kernels one library call launches: the forward is the
+gather plus the level-major transpose, the backward the binned path's init,
+bin and accumulate kernels (or the atomic scatter).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+PASSES = {
+    "forward": ("fwd_f2_kernel", "fwd_f2_pair_kernel", "transpose_kernel"),
+    "backward": ("init_kernel", "bin_kernel", "accumulate_kernel", "bwd_f2_kernel"),
+}
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCES = ("encode_kernels.hip", "binned_backward.hip")
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources (the traffic figures are only valid for them)."""
+    h = hashlib.sha256()
+    for f in SOURCES:
+        with open(os.path.join(ROOT, "multiresolution_hash_grid_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    name = name.replace("hg::(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", name)
+
+
+def pass_of(name: str):
+    base = re.sub(r"<.*", "", short_name(name))
+    for p, kernels in PASSES.items():
+        if base in kernels:
+            return p
+    return None
+
+
+def _find(d: str, suffix: str) -> str:
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def stats(args) -> None:
+    rows = list(csv.DictReader(open(_find(args.dir, "kernel_stats.csv"))))
+    lines = [f"# Kernel durations: {args.title}", "", "Command:", "", "```", args.command, "```", "",
+             "| kernel | pass | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|---|"]
+    per_pass = collections.defaultdict(float)
+    for r in rows:
+        p = pass_of(r["Name"])
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{short_name(r['Name'])}` | {p or '-'} | {r['Calls']} | {avg:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
+        if p:
+            per_pass[p] += avg
+    lines += ["", "Sum of kernel averages per pass (us): " +
+              ", ".join(f"{p} {v:.1f}" for p, v in sorted(per_pass.items())), ""]
+    text = "\n".join(lines)
+    with open(args.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def _counter_per_dispatch(d: str, counter: str):
+    """{kernel short name: [per-dispatch value summed over dimensions]}"""
+    per = collections.defaultdict(float)
+    names = {}
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    out = collections.defaultdict(list)
+    for did in sorted(per, key=int):
+        out[names[did]].append(per[did])
+    return out
+
+
+def _avg(vals):
+    vals = vals[2:] if len(vals) > 4 else vals   # drop the first (cold) dispatches
+    return sum(vals) / len(vals)
+
+
+def traffic(args) -> None:
+    fetch = _counter_per_dispatch(args.fetch, "FETCH_SIZE")
+    write = _counter_per_dispatch(args.write, "WRITE_SIZE")
+    cf = _counter_per_dispatch(args.copy_fetch, "FETCH_SIZE")
+    cw = _counter_per_dispatch(args.copy_write, "WRITE_SIZE")
+    # The copy moves copy_bytes in and copy_bytes out; counters are in KiB.
+    copy_read_kib = max(max(v) for v in cf.values())
+    copy_write_kib = max(max(v) for v in cw.values())
+    f_scale = args.copy_bytes / (copy_read_kib * 1024.0)
+    w_scale = args.copy_bytes / (copy_write_kib * 1024.0)
+    kernels = {}
+    passes = collections.defaultdict(lambda: {"fetch_bytes": 0.0, "write_bytes": 0.0})
+    for name in set(fetch) | set(write):
+        p = pass_of(name)
+        fb = _avg(fetch.get(name, [0.0])) * 1024.0 * f_scale
+        wb = _avg(write.get(name, [0.0])) * 1024.0 * w_scale
+        kernels[short_name(name)] = {"pass": p, "fetch_bytes": fb, "write_bytes": wb}
+        if p:
+            passes[p]["fetch_bytes"] += fb
+            passes[p]["write_bytes"] += wb
+    for p in passes.values():
+        p["hbm_bytes_per_launch"] = p["fetch_bytes"] + p["write_bytes"]
+    rec = {
+        "about": "HBM bytes per launch of each pass from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                 "dispatch), each scaled by the factor that makes the same counter read the known size "
+                 "of a plain device copy.",
+        "command_fetch": args.command_fetch, "command_write": args.command_write,
+        "copy_bytes": args.copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+        "source_sha256": source_digest(), "passes": dict(passes), "kernels": kernels,
+    }
+    with open(args.out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def copy(args) -> None:
+    import torch
+    n = args.bytes // 4
+    a = torch.ones(n, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied", args.bytes, "bytes x5", flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--out", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", default="rocprofv3 --kernel-trace --stats")
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write", "out"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--command-fetch", default="")
+    t.add_argument("--command-write", default="")
+    c = sub.add_parser("copy")
+    c.add_argument("--bytes", type=int, default=256 << 20)
+    args = ap.parse_args()
+    {"stats": stats, "traffic": traffic, "copy": copy}[args.cmd](args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
