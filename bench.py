@@ -25,7 +25,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_standard.json")
 PASS_KERNELS = {"forward": "fwd_f2_pair_kernel + transpose_kernel",
-                "backward": "init_kernel + bin_kernel + accumulate_kernel"}
+                "backward": "bin_kernel + accumulate_kernel per level group"}
 
 
 def algorithmic_bytes_per_point(w, table_esize: int) -> dict:

@@ -109,13 +109,16 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
                      size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace that let hashgrid_backward route the whole
- * gradient of n points through its binned (atomic-free) path in one pass:
- * 64 * L * ceil(n / 512) * 512 bytes of records plus small counters
- * (about 268 MB for L = 16, n = 2^18).  *bytes_out is a HOST size_t.
- * A workspace of at least *min_bytes_out (one level's share; may be NULL)
- * also works -- the levels are then processed in groups.  Returns 0 bytes
- * when the configuration has no binned path (more than 4096 partitions of
- * 2^13 entries, i.e. T > 2^25, or n >= 2^29).
+ * gradient of n points through its binned (atomic-free) path at full speed:
+ * per level, 64 * ceil(n / 512) * 512 bytes of records plus small counters
+ * (about 17 MB for n = 2^18), times the number of levels binned together.
+ * That group is sized so its records fit the MI355X last-level cache (the
+ * HG_TUNE_BWD_GROUP_MIB budget, 160 MiB by default: 8 levels for n = 2^18,
+ * about 136 MB).  *bytes_out is a HOST size_t.  A workspace of at least
+ * *min_bytes_out (one level's share; may be NULL) also works -- the levels
+ * are then processed in smaller groups.  Returns 0 bytes when the
+ * configuration has no binned path (more than 4096 partitions of 2^13
+ * entries, i.e. T > 2^25, or n >= 2^29).
  * Errors: HG_EINVAL, HG_EUNSUPPORTED. */
 int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out,
                                      size_t *min_bytes_out);
@@ -165,6 +168,8 @@ int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint
 #define HG_TUNE_FWD_NT 6       /* 1: non-temporal point reads and output writes         */
 #define HG_TUNE_FWD_STAGED 7   /* 1: stage the forward level-major when given workspace */
 #define HG_TUNE_BWD_PART_LOG2 8 /* log2 entries per binned-backward partition: 11..13, 0 = by T */
+#define HG_TUNE_BWD_GROUP_MIB 9 /* record MiB per binned level group (levels binned and
+                                   accumulated together), 0 = all levels in one group   */
 int hashgrid_tune(int key, int value);
 int hashgrid_tune_get(int key);
 

@@ -4,6 +4,7 @@
 #include "hashgrid.h"
 
 #include <math.h>
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -40,6 +41,7 @@ struct Tuning {
     int fwd_nt = 0;
     int fwd_staged = 1;
     int bwd_part_log2 = 0;  // 0: by table size
+    int bwd_group_mib = 160;  // record bytes per binned level group, 0: all levels at once
 };
 Tuning g_tune;
 
@@ -126,6 +128,19 @@ bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Levels per binned group: as many as keep one group's records (written by
+// the bin kernel, read back by the accumulate kernel right after) within the
+// budget, so that they can stay in the 256 MB last-level cache of the
+// MI355X; groups are then made equal.
+int binned_group(const hg::BinParams &bp, int n_levels) {
+    if (g_tune.bwd_group_mib <= 0) return n_levels;
+    const size_t rec_bytes = (size_t)bp.level_records * 16;
+    const size_t budget = (size_t)g_tune.bwd_group_mib << 20;
+    const int cap = (int)std::max<size_t>(1, std::min<size_t>(n_levels, budget / std::max<size_t>(rec_bytes, 1)));
+    const int ngroups = (n_levels + cap - 1) / cap;
+    return (n_levels + ngroups - 1) / ngroups;
+}
+
 int check_points(int64_t n, const float *x) {
     if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
     if (!x) return fail(HG_EINVAL, "x is NULL");
@@ -194,8 +209,12 @@ int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *by
     if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
     hg::BinParams bp;
     size_t per_level = 0;
-    if (n > 0 && plan_binned(*cfg, n, bp)) per_level = round_up(hg::binned_level_bytes(bp), 256);
-    *bytes_out = per_level * (size_t)cfg->n_levels;
+    int group = 0;
+    if (n > 0 && plan_binned(*cfg, n, bp)) {
+        per_level = round_up(hg::binned_level_bytes(bp), 256);
+        group = binned_group(bp, cfg->n_levels);
+    }
+    *bytes_out = per_level * (size_t)group;
     if (min_bytes_out) *min_bytes_out = per_level;
     return ok();
 }
@@ -218,7 +237,8 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
         if (workspace_bytes >= per_level) {
             // Whole levels per group; the launcher splits the workspace itself.
             const size_t usable = workspace_bytes / per_level * hg::binned_level_bytes(bp);
-            return launch_status(hg::launch_binned_backward(bp, cfg->n_levels, x, n, dout, dout_row_stride,
+            return launch_status(hg::launch_binned_backward(bp, cfg->n_levels, binned_group(bp, cfg->n_levels), x,
+                                                            n, dout, dout_row_stride,
                                                             dtable, workspace, usable, (hipStream_t)stream),
                                  "binned backward");
         }
@@ -278,6 +298,10 @@ int hashgrid_tune(int key, int value) {
         if (value != 0 && value != 1) break;
         g_tune.fwd_staged = value;
         return ok();
+    case HG_TUNE_BWD_GROUP_MIB:
+        if (value < 0 || value > (1 << 20)) return fail(HG_EINVAL, "BWD_GROUP_MIB %d outside 0..2^20", value);
+        g_tune.bwd_group_mib = value;
+        return ok();
     case HG_TUNE_BWD_PART_LOG2:
         if (value != 0 && (value < 11 || value > hg::kMaxSLog2)) break;
         g_tune.bwd_part_log2 = value;
@@ -299,6 +323,7 @@ int hashgrid_tune_get(int key) {
     case HG_TUNE_FWD_NT: return g_tune.fwd_nt;
     case HG_TUNE_FWD_STAGED: return g_tune.fwd_staged;
     case HG_TUNE_BWD_PART_LOG2: return g_tune.bwd_part_log2;
+    case HG_TUNE_BWD_GROUP_MIB: return g_tune.bwd_group_mib;
     default: return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
 }

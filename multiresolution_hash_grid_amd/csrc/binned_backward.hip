@@ -37,6 +37,8 @@
 // A corner pair whose x+1 corner lands in another partition (only when the
 // low s bits of the x coordinate are all ones, e.g. x = -1) keeps the x
 // corner in its record and adds the x+1 corner with a global fp32 atomic.
+#include <algorithm>
+
 #include "hashgrid_internal.h"
 
 namespace hg {
@@ -46,16 +48,12 @@ constexpr int kBinThreads = 256;
 constexpr int kPtsPerThread = kBinTile / kBinThreads;  // 2
 constexpr int kRecPerTile = kBinTile * 4;              // 4 corner pairs per point
 constexpr int kLevelsPerBlock = 4;                     // levels per bin workgroup
-// Tiles fold their max |dL/dout| into one of kMaxSlots words per level (tile
-// mod kMaxSlots): global atomics on one address serialise at the memory-side
-// atomic unit, so the many tiles of a level must not all hit the same word.
-constexpr int kMaxSlots = 64;
 
 // Workspace of one launch group.
 struct Space {
     uint4 *records;     // [group][tiles][kRecPerTile], each tile's records sorted by partition
     uint32_t *runs;     // [group][tiles][parts + 1], start of every partition's run in the tile
-    uint32_t *dmax;     // [group][kMaxSlots], bits of max |dL/dout| (non-negative floats order as uints)
+    uint32_t *dmax;     // [group][tiles], bits of each tile's max |dL/dout| (non-negative floats order as uints)
 };
 
 Space carve(void *ws, const BinParams &bp) {
@@ -153,12 +151,6 @@ __device__ __forceinline__ void block_exclusive_scan(const uint32_t *cnt, int co
     if (threadIdx.x == kBinThreads - 1) base[count] = run;
 }
 
-// ---------------------------------------------------------------- init
-
-__global__ void init_kernel(uint32_t *dmax, int group) {
-    for (int i = threadIdx.x; i < group * kMaxSlots; i += blockDim.x) dmax[i] = 0u;
-}
-
 // ---------------------------------------------------------------- loads
 
 // The coordinates and the block's dL/dout of one thread's points, loaded once
@@ -249,7 +241,7 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
         if (threadIdx.x == 0) {
             uint32_t m = wmax[0];
             for (int w = 1; w < kBinThreads / 64; ++w) m = max(m, wmax[w]);
-            atomicMax(sp.dmax + g * kMaxSlots + (tile % kMaxSlots), m);
+            sp.dmax[(int64_t)g * bp.tiles + tile] = m;
         }
         __syncthreads();
         uint32_t *runs = sp.runs + ((int64_t)g * bp.tiles + tile) * (bp.parts + 1);
@@ -297,20 +289,67 @@ __device__ __forceinline__ int fixed_exponent(uint32_t dmax_bits) {
 }
 
 // Workgroup (level, partition) of THREADS threads.  The tiles are walked in
-// chunks of THREADS: wave w takes tiles chunk + 64 w + i (lane i), scans its
-// lanes' run lengths and works through the concatenation of those runs, 64
-// records per step, finding each record's tile by a binary search over the
-// wave's 64 run offsets.  Two batches of kAccBatch steps are in flight: the
-// next batch is requested before the current one is added.
-constexpr int kAccBatch = 4;
+// chunks of THREADS: lane i of wave w takes tile chunk + i * waves + w (the
+// waves share out a short chunk evenly) and the wave works through the
+// concatenation of its tiles' runs, 64 records per step.  The
+// run that holds concatenation position i comes from a byte map built per
+// window of kMapWindow positions: every run that starts inside the window
+// marks its start with its lane index + 1, and a max-scan along the window
+// spreads each mark to the positions up to the next start (0 stays where the
+// run in progress when the window opened continues).  A record address is
+// then two LDS reads away (map entry, run offset) instead of a search.  Two
+// batches of kAccBatch steps are in flight: the next batch is requested
+// before the current one is added.
+constexpr int kAccBatch = 2;
+constexpr int kMapWindow = 1024;  // positions per map window, a multiple of 64 * kAccBatch
+static_assert(kMapWindow % (64 * kAccBatch) == 0, "map windows must hold whole batches");
+
+// LDS order between lanes of one wave (the wave's LDS operations complete in
+// issue order; this keeps the compiler from moving them across).
+__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// Byte map of window [w0, w0 + kMapWindow) of a wave's run concatenation.
+// pre / len: this lane's run offset and length.
+__device__ __forceinline__ void build_run_map(uint4 *map, uint32_t w0, uint32_t pre, uint32_t len) {
+    const int lane = threadIdx.x & 63;
+    map[lane] = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_fence();
+    if (len > 0 && pre > w0 && pre < w0 + kMapWindow) reinterpret_cast<uint8_t *>(map)[pre - w0] = (uint8_t)(lane + 1);
+    wave_lds_fence();
+    const uint4 q = map[lane];
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t run = 0;
+    uint32_t loc[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        run = max(run, (w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+        loc[b] = run;
+    }
+    // Largest mark in the lanes below (the window positions before this lane's 16).
+    uint32_t incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl = max(incl, t);
+    }
+    uint32_t below = __shfl_up(incl, 1, 64);
+    if (lane == 0) below = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        w[m] = max(loc[4 * m], below) | (max(loc[4 * m + 1], below) << 8) | (max(loc[4 * m + 2], below) << 16) |
+               (max(loc[4 * m + 3], below) << 24);
+    map[lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    wave_lds_fence();
+}
 
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space sp, float *__restrict__ grad) {
     constexpr int kWaves = THREADS / 64;
-    extern __shared__ unsigned long long slice[];    // [2^s][2] fixed-point accumulators
-    __shared__ uint32_t pre[kWaves][65];            // per wave: run offsets in the concatenation
-    __shared__ uint32_t start[kWaves][64];          // per wave: run start inside each tile
+    extern __shared__ unsigned long long slice[];       // [2^s][2] fixed-point accumulators
+    __shared__ int32_t offs[kWaves][64];                // per run: record index minus concatenation position
+    __shared__ uint4 maps[kWaves][kMapWindow / 16];     // per wave: byte map of the current window
     __shared__ uint32_t touched;
+    __shared__ uint32_t wmax[kWaves];
     const int g = blockIdx.x / bp.parts;
     const int part = blockIdx.x - g * bp.parts;
     const int l = bp.level0 + g;
@@ -318,13 +357,22 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int i = threadIdx.x; i < 2 * S; i += THREADS) slice[i] = 0ull;
     if (threadIdx.x == 0) touched = 0;
-    uint32_t dm = sp.dmax[g * kMaxSlots + lane];
+    // The level's max |dL/dout| over the tiles' maxima.
+    uint32_t dm = 0;
+    for (int t = threadIdx.x; t < bp.tiles; t += THREADS) dm = max(dm, sp.dmax[(int64_t)g * bp.tiles + t]);
     for (int off = 32; off > 0; off >>= 1) dm = max(dm, __shfl_xor(dm, off, 64));
-    const int k = fixed_exponent(dm);
+    if (lane == 0) wmax[wave] = dm;
     const uint4 *grec = sp.records + (int64_t)g * bp.level_records;
     const uint32_t *truns = sp.runs + (int64_t)g * bp.tiles * (bp.parts + 1) + part;
+    uint4 *map = maps[wave];
+    const uint8_t *mapb = reinterpret_cast<const uint8_t *>(map);
+    __syncthreads();
+    dm = wmax[0];
+    for (int w = 1; w < kWaves; ++w) dm = max(dm, wmax[w]);
+    const int k = fixed_exponent(dm);
     for (int chunk = 0; chunk < bp.tiles; chunk += THREADS) {
-        const int t = chunk + 64 * wave + lane;
+        const int tl = lane * kWaves + wave;  // tile within the chunk
+        const int t = chunk + tl;
         uint32_t s = 0, len = 0;
         if (t < bp.tiles) {
             const uint32_t *r = truns + (int64_t)t * (bp.parts + 1);
@@ -332,23 +380,25 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
             len = r[1] - s;
         }
         const uint32_t incl = wave_inclusive_scan(len);
-        pre[wave][lane] = incl - len;
-        start[wave][lane] = s;
-        if (lane == 63) pre[wave][64] = incl;
-        __syncthreads();
-        const uint32_t total = pre[wave][64];
+        const uint32_t pre = incl - len;
+        const uint32_t total = __shfl(incl, 63, 64);
+        // Records of the chunk's tiles, relative to the first of them.
+        const uint4 *trec = grec + (int64_t)chunk * kRecPerTile;
+        offs[wave][lane] = tl * kRecPerTile + (int32_t)s - (int32_t)pre;
         if (total && lane == 0) touched = 1;
-        const uint32_t *wp = pre[wave];
-        const uint32_t *ws = start[wave];
-        const uint4 *trec = grec + (int64_t)(chunk + 64 * wave) * kRecPerTile;
-        // Record i of the wave's concatenated runs (i < total).
+        // Run holding position i (the window that holds i is in the map).
+        uint32_t carry = 0;
         auto fetch = [&](uint32_t i) -> uint4 {
-            int lo = 0;  // last run j with pre[j] <= i
-#pragma unroll
-            for (int step = 32; step > 0; step >>= 1)
-                if (wp[lo + step] <= i) lo += step;
-            return trec[(int64_t)lo * kRecPerTile + ws[lo] + (i - wp[lo])];
+            const uint32_t m = mapb[i % kMapWindow];
+            const int j = m ? (int)m - 1 : (int)carry;
+            return trec[offs[wave][j] + (int32_t)i];
         };
+        auto open_window = [&](uint32_t w0) {
+            // The run in progress at w0: the last run starting at or before it.
+            carry = (uint32_t)__popcll(__ballot(pre <= w0)) - 1u;
+            build_run_map(map, w0, pre, len);
+        };
+        if (total) open_window(0);
         uint4 cur[kAccBatch], nxt[kAccBatch];
 #pragma unroll
         for (int u = 0; u < kAccBatch; ++u) {
@@ -357,6 +407,8 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
         }
         for (uint32_t b0 = 0; b0 < total; b0 += 64 * kAccBatch) {
             const uint32_t b1 = b0 + 64 * kAccBatch;
+            // The batch in flight already has its addresses: the map may move on.
+            if (b1 < total && b1 % kMapWindow == 0) open_window(b1);
 #pragma unroll
             for (int u = 0; u < kAccBatch; ++u) {
                 const uint32_t i = b1 + u * 64 + lane;
@@ -368,8 +420,9 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
 #pragma unroll
             for (int u = 0; u < kAccBatch; ++u) cur[u] = nxt[u];
         }
-        __syncthreads();
+        wave_lds_fence();
     }
+    __syncthreads();
     if (!touched) return;  // no corner of this batch fell in the partition: nothing to add
     // The partition's entries are [part * S, (part + 1) * S) of level l.
     float4 *gl = reinterpret_cast<float4 *>(grad + ((((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * 2));
@@ -399,23 +452,24 @@ hipError_t launch_accumulate(const BinParams &bp, const Space &sp, float *dtable
 
 size_t binned_level_bytes(const BinParams &bp) {
     const size_t recs = (size_t)bp.level_records * sizeof(uint4);
-    const size_t words = (size_t)bp.tiles * (bp.parts + 1) + kMaxSlots;
+    const size_t words = (size_t)bp.tiles * (bp.parts + 2);
     return recs + words * sizeof(uint32_t);
 }
 
-hipError_t launch_binned_backward(BinParams bp, int n_levels, const float *x, int64_t n,
+hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, const float *x, int64_t n,
                                   const float *dout, int64_t dout_stride, float *dtable,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
     const size_t per_level = binned_level_bytes(bp);
-    int group = (int)(workspace_bytes / per_level);
-    if (group > n_levels) group = n_levels;
+    int group = (int)std::min<size_t>(workspace_bytes / per_level, (size_t)std::min(max_group, n_levels));
     if (group < 1) return hipErrorInvalidValue;
+    // Equal groups: 16 levels in groups of at most 6 run as 6 + 5 + 5.
+    const int ngroups = (n_levels + group - 1) / group;
+    group = (n_levels + ngroups - 1) / ngroups;
     for (int l0 = 0; l0 < n_levels; l0 += group) {
         bp.level0 = l0;
         bp.group = min(group, n_levels - l0);
         const Space sp = carve(workspace, bp);
         const dim3 tgrid(bp.tiles, (bp.group + kLevelsPerBlock - 1) / kLevelsPerBlock);
-        init_kernel<<<1, 256, 0, stream>>>(sp.dmax, bp.group);
         bin_kernel<<<tgrid, kBinThreads, (2 * bp.parts + 1) * sizeof(uint32_t), stream>>>(x, n, dout, dout_stride,
                                                                                          bp, sp, dtable);
         hipError_t e = hipGetLastError();

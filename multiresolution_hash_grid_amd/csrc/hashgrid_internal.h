@@ -56,8 +56,11 @@ struct BinParams {
     int32_t res[kMaxLevels];
 };
 
+// Workspace bytes of one level (records, run starts, tile maxima).
 size_t binned_level_bytes(const BinParams &bp);
-hipError_t launch_binned_backward(BinParams bp, int n_levels, const float *x, int64_t n,
+// Levels are binned and accumulated in equal groups of at most max_group
+// levels (and no more than the workspace holds).
+hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, const float *x, int64_t n,
                                   const float *dout, int64_t dout_stride, float *dtable,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -1,19 +1,21 @@
 """Summaries of rocprofv3 output for the encoder's passes.
 
-    # kernel durations of a --kernel-trace --stats -f csv run
-    python -m multiresolution_hash_grid_amd.profile_summary stats DIR --command "..." --out FILE.md
+    # kernel durations of a --kernel-trace --stats -f csv run that made PASSES
+    # calls of each library entry point
+    python -m multiresolution_hash_grid_amd.profile_summary stats DIR --passes P --command "..." --out FILE.md
 
     # HBM traffic per pass from --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of the
     # benchmark and of a plain device copy (the calibration)
     python -m multiresolution_hash_grid_amd.profile_summary traffic --fetch D1 --write D2 \\
-        --copy-fetch D3 --copy-write D4 --copy-bytes B --out FILE.json
+        --copy-fetch D3 --copy-write D4 --copy-bytes B --passes P --out FILE.json
 
     # the calibration workload itself: a device-to-device copy of B bytes
     python -m multiresolution_hash_grid_amd.profile_summary copy --bytes B
 
 A pass is the group of kernels one library call launches: the forward is the
-gather plus the level-major transpose, the backward the binned path's init,
-bin and accumulate kernels (or the atomic scatter).
+gather plus the level-major transpose, the backward the binned path's bin and
+accumulate kernels, once per level group (or the atomic scatter).  Per-pass
+figures weight each kernel by its launches per call.
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ import sys
 
 PASSES = {
     "forward": ("fwd_f2_kernel", "fwd_f2_pair_kernel", "transpose_kernel"),
-    "backward": ("init_kernel", "bin_kernel", "accumulate_kernel", "bwd_f2_kernel"),
+    "backward": ("bin_kernel", "accumulate_kernel", "bwd_f2_kernel"),
 }
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = ("encode_kernels.hip", "binned_backward.hip")
@@ -75,8 +77,8 @@ def stats(args) -> None:
         lines.append(f"| `{short_name(r['Name'])}` | {p or '-'} | {r['Calls']} | {avg:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
         if p:
-            per_pass[p] += avg
-    lines += ["", "Sum of kernel averages per pass (us): " +
+            per_pass[p] += avg * int(r["Calls"]) / args.passes
+    lines += ["", f"Kernel time per call of each entry point ({args.passes} calls each, us): " +
               ", ".join(f"{p} {v:.1f}" for p, v in sorted(per_pass.items())), ""]
     text = "\n".join(lines)
     with open(args.out, "w") as f:
@@ -118,18 +120,22 @@ def traffic(args) -> None:
     passes = collections.defaultdict(lambda: {"fetch_bytes": 0.0, "write_bytes": 0.0})
     for name in set(fetch) | set(write):
         p = pass_of(name)
-        fb = _avg(fetch.get(name, [0.0])) * 1024.0 * f_scale
-        wb = _avg(write.get(name, [0.0])) * 1024.0 * w_scale
-        kernels[short_name(name)] = {"pass": p, "fetch_bytes": fb, "write_bytes": wb}
+        fv, wv = fetch.get(name, [0.0]), write.get(name, [0.0])
+        fb = _avg(fv) * 1024.0 * f_scale
+        wb = _avg(wv) * 1024.0 * w_scale
+        per_call = len(fv) / args.passes  # launches of this kernel per library call
+        kernels[short_name(name)] = {"pass": p, "fetch_bytes": fb, "write_bytes": wb,
+                                     "launches_per_call": per_call}
         if p:
-            passes[p]["fetch_bytes"] += fb
-            passes[p]["write_bytes"] += wb
+            passes[p]["fetch_bytes"] += fb * per_call
+            passes[p]["write_bytes"] += wb * per_call
     for p in passes.values():
         p["hbm_bytes_per_launch"] = p["fetch_bytes"] + p["write_bytes"]
     rec = {
-        "about": "HBM bytes per launch of each pass from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
-                 "dispatch), each scaled by the factor that makes the same counter read the known size "
-                 "of a plain device copy.",
+        "about": "HBM bytes per call of each entry point from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB "
+                 "per dispatch, times dispatches per call), each scaled by the factor that makes the same "
+                 "counter read the known size of a plain device copy.",
+        "calls_per_run": args.passes,
         "command_fetch": args.command_fetch, "command_write": args.command_write,
         "copy_bytes": args.copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
         "source_sha256": source_digest(), "passes": dict(passes), "kernels": kernels,
@@ -158,10 +164,12 @@ def main() -> int:
     s.add_argument("--out", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--title", default="rocprofv3 --kernel-trace --stats")
+    s.add_argument("--passes", type=int, required=True, help="calls of each entry point in the run")
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write", "out"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--passes", type=int, required=True, help="calls of each entry point in the run")
     t.add_argument("--command-fetch", default="")
     t.add_argument("--command-write", default="")
     c = sub.add_parser("copy")

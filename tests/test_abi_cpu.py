@@ -130,7 +130,17 @@ def test_backward_workspace_size():
     # 64 bytes per point, level and corner pair slot (tiles of 512 points) plus counters.
     cfg = hg.HashGridConfig()
     full, least = hg.hashgrid_backward_workspace_size(cfg, 1 << 18)
-    assert least * 16 == full
+    # 16 MiB of records per level: the 160 MiB group budget takes 10 levels,
+    # so the 16 levels run as two equal groups of 8.
+    assert least * 8 == full
+    old = hg.hashgrid_tune_get(B.HG_TUNE_BWD_GROUP_MIB)
+    try:
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 0)      # one group of all levels
+        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 16, least)
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 48)     # 3 levels per group -> 6 groups of 3 (16 = 3*5 + 1)
+        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 3, least)
+    finally:
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, old)
     assert least >= 64 * (1 << 18) and least < 64 * (1 << 18) + (1 << 20)
     assert hg.hashgrid_backward_workspace_size(cfg, 0) == (0, 0)
     assert hg.hashgrid_backward_workspace_size(cfg, 1)[1] >= 64 * 512
@@ -152,7 +162,7 @@ def test_tuning_knobs(lib):
                            (B.HG_TUNE_CHUNK_POINTS, 512, 100), (B.HG_TUNE_XCD_MAP, 0, 2),
                            (B.HG_TUNE_BWD_BINNED, 0, 3), (B.HG_TUNE_FWD_UNROLL, 2, 3),
                            (B.HG_TUNE_FWD_NT, 1, 2), (B.HG_TUNE_FWD_STAGED, 0, 2),
-                           (B.HG_TUNE_BWD_PART_LOG2, 12, 14)):
+                           (B.HG_TUNE_BWD_PART_LOG2, 12, 14), (B.HG_TUNE_BWD_GROUP_MIB, 64, -1)):
         old = hg.hashgrid_tune_get(key)
         hg.hashgrid_tune(key, good)
         assert hg.hashgrid_tune_get(key) == good

@@ -275,7 +275,8 @@ def test_backward_binned_reused_workspace_and_dirty_contents(oracle):
                                        (B.HG_TUNE_CHUNK_POINTS, 64), (B.HG_TUNE_CHUNK_POINTS, 8192),
                                        (B.HG_TUNE_BWD_BINNED, 0), (B.HG_TUNE_FWD_UNROLL, 2),
                                        (B.HG_TUNE_FWD_UNROLL, 4), (B.HG_TUNE_FWD_NT, 1),
-                                       (B.HG_TUNE_BWD_PART_LOG2, 11), (B.HG_TUNE_BWD_PART_LOG2, 12)])
+                                       (B.HG_TUNE_BWD_PART_LOG2, 11), (B.HG_TUNE_BWD_PART_LOG2, 12),
+                                       (B.HG_TUNE_BWD_GROUP_MIB, 0), (B.HG_TUNE_BWD_GROUP_MIB, 1)])
 def test_launch_variants_match_oracle(oracle, key, value):
     w = I.resized(I.WORKLOADS["standard"], 5 * 1024 + 77)
     cfg = hg.HashGridConfig.of(w)
