@@ -53,6 +53,43 @@ def load_traffic(pass_name: str):
     return None if p is None else p.get("hbm_bytes_per_launch")
 
 
+def time_calls(fn, iters: int) -> float:
+    """Mean milliseconds of fn() over iters calls, HIP events on the current stream."""
+    import torch
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def measure_adam(cfg, dev, iters: int) -> dict:
+    """Adam update of the standard tables (L*T*F fp32 entries): reads param, m,
+    v, grad and writes param, m, v -- 28 algorithmic bytes per entry."""
+    import torch
+    import multiresolution_hash_grid_amd as hg
+    count = cfg.n_levels * cfg.table_size * cfg.n_features
+    g = torch.Generator(device=dev).manual_seed(5)
+    p = torch.empty(count, device=dev).uniform_(-1e-4, 1e-4, generator=g)
+    m, v = torch.zeros_like(p), torch.zeros_like(p)
+    grad = torch.randn(count, device=dev, generator=g)
+    step = [0]
+
+    def call():
+        step[0] += 1
+        hg.hashgrid_adam_step(p, m, v, grad, lr=1e-2, step=step[0], beta1=0.9, beta2=0.99, eps=1e-15)
+
+    ms = time_calls(call, iters)
+    gbs = 28 * count / (ms * 1e-3) / 1e9
+    return {"entries": count, "us_per_call": ms * 1e3, "algorithmic_bytes_per_entry": 28,
+            "achieved_GBps": gbs, "frac": gbs / HBM_PEAK_GBS}
+
+
 def cpu_baseline(w, x, t, d, budget_s: float) -> dict:
     """The CPU oracle, as it stands, on the same workload: forward + backward of
     all points, repeated until about `budget_s` seconds of work."""
@@ -179,6 +216,8 @@ def main() -> int:
         "roofline_fwd_frac": bpp["fwd"] * w.n_points / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline_fwd_bwd_frac": (bpp["fwd"] + bpp["bwd"]) * w.n_points * K / elapsed / 1e9 / HBM_PEAK_GBS,
     }
+    # The table optimizer step that follows the backward (Adam over the tables).
+    result["next"] = {"adam": measure_adam(cfg, dev, 50)}
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x_h, t_h, d_h, args.cpu_seconds)

@@ -155,6 +155,38 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
 int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint32_t *idx,
                            float *w, void *stream);
 
+/* Adam update of the tables (ipipp.com section 4: Adam, no weight decay on
+ * the hash tables, whose learning rate is 5-10x the MLP's per section 3;
+ * ijyty.com overview section 4: torch.optim.Adam).  The algorithm is Adam as
+ * published (Kingma and Ba 2015): m = b1 m + (1-b1) g, v = b2 v + (1-b2) g^2,
+ * param -= lr * (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps), in fp32, for
+ * every one of the count entries (entries with a zero gradient still move,
+ * as in torch.optim.Adam).
+ *   opt       : host struct; step is the 1-based index t of this update.  The
+ *               hyperparameters are the fp32 values given (1 - beta and the
+ *               bias corrections are formed from them in double).
+ *   param, m, v, grad : fp32 device arrays of count elements (the [L][T][F]
+ *               tables, their two moments -- zero before step 1 -- and the
+ *               gradient hashgrid_backward accumulated), 4-byte aligned;
+ *               16-byte alignment and count % 4 == 0 take the vector path.
+ *   param_f16 : optional device array of count binary16 values that receives
+ *               the updated tables rounded to nearest-even (the fp16 tables a
+ *               fp16-table forward reads), or NULL.
+ *   flags     : HG_ADAM_ZERO_GRAD writes 0 into grad after reading it, ready
+ *               for the next backward, which accumulates.
+ * Errors: HG_EINVAL (NULL pointer, count < 0, step < 1, lr/eps not finite,
+ * betas outside [0, 1)), HG_EHIP. */
+typedef struct {
+    float lr;      /* step size (alpha)                                      */
+    float beta1;   /* decay of the first moment, in [0, 1)                   */
+    float beta2;   /* decay of the second moment, in [0, 1)                  */
+    float eps;     /* added to the root of the corrected second moment, >= 0 */
+    int32_t step;  /* t >= 1                                                 */
+} hg_adam;
+#define HG_ADAM_ZERO_GRAD 1
+int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m, float *v,
+                       float *grad, void *param_f16, int32_t flags, void *stream);
+
 /* Performance knobs (launch shapes).  They never change results beyond the
  * unspecified order of the backward's atomic adds.  Process-wide; not
  * thread-safe against concurrent launches.  Returns HG_EINVAL for an unknown

@@ -5,12 +5,14 @@ ABI of ``include/hashgrid.h``); ``hashgrid`` is its Python binding and
 ``inputs`` the seeded synthetic workload generator.
 """
 from .hashgrid import (  # noqa: F401
+    HashGridAdam,
     HashGridConfig,
     HashGridEncoder,
     HashGridError,
     HashGridFunction,
     abi_version,
     backward_workspace,
+    hashgrid_adam_step,
     hashgrid_backward,
     hashgrid_backward_workspace_size,
     hashgrid_debug_corners,

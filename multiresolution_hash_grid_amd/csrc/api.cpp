@@ -4,6 +4,7 @@
 #include "hashgrid.h"
 
 #include <math.h>
+#include <cmath>
 #include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
@@ -248,6 +249,27 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
     return launch_status(hg::launch_backward(lp, x, n, dout, dout_row_stride, dtable, g_tune.bwd_lanes,
                                              (hipStream_t)stream),
                          "backward");
+}
+
+int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m, float *v, float *grad,
+                       void *param_f16, int32_t flags, void *stream) {
+    if (!opt) return fail(HG_EINVAL, "opt is NULL");
+    if (count < 0) return fail(HG_EINVAL, "count = %lld < 0", (long long)count);
+    if (opt->step < 1) return fail(HG_EINVAL, "step %d < 1", opt->step);
+    if (!std::isfinite(opt->lr) || !std::isfinite(opt->eps) || opt->eps < 0.f)
+        return fail(HG_EINVAL, "lr and eps must be finite, eps >= 0");
+    if (!(opt->beta1 >= 0.f && opt->beta1 < 1.f) || !(opt->beta2 >= 0.f && opt->beta2 < 1.f))
+        return fail(HG_EINVAL, "betas must lie in [0, 1)");
+    if (flags & ~HG_ADAM_ZERO_GRAD) return fail(HG_EINVAL, "unknown flags 0x%x", flags);
+    if (count == 0) return ok();
+    if (!param || !m || !v || !grad) return fail(HG_EINVAL, "param, m, v and grad must be device pointers");
+    if (!aligned(param, 4) || !aligned(m, 4) || !aligned(v, 4) || !aligned(grad, 4) ||
+        (param_f16 && !aligned(param_f16, 2)))
+        return fail(HG_EINVAL, "misaligned buffer");
+    const hg::AdamParams a{opt->lr, opt->beta1, opt->beta2, opt->eps, opt->step};
+    return launch_status(hg::launch_adam(a, count, param, m, v, grad, param_f16, (flags & HG_ADAM_ZERO_GRAD) != 0,
+                                         (hipStream_t)stream),
+                         "adam");
 }
 
 int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint32_t *idx, float *w,

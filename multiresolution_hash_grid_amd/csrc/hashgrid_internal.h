@@ -2,6 +2,7 @@
 // libhashgrid.  Not part of the public ABI (include/hashgrid.h is).
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,6 +81,13 @@ hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, con
                           float *stage, hipStream_t stream);
 hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, const float *dout,
                            int64_t dout_stride, float *dtable, int lanes, hipStream_t stream);
+struct AdamParams {
+    float lr, beta1, beta2, eps;
+    int32_t step;
+};
+hipError_t launch_adam(const AdamParams &a, int64_t count, float *param, float *m, float *v, float *grad,
+                       void *param_f16, bool zero_grad, hipStream_t stream);
+
 hipError_t launch_debug_corners(const LaunchParams &lp, const float *x, int64_t n, uint32_t *idx,
                                 float *w, hipStream_t stream);
 

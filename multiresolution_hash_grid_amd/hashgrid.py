@@ -27,6 +27,9 @@ _DTYPES = {"f32": HG_F32, "f16": HG_F16}
 _TORCH_DTYPES = {HG_F32: torch.float32, HG_F16: torch.float16}
 
 
+HG_ADAM_ZERO_GRAD = 1
+
+
 class HashGridError(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"hashgrid error {code}: {message}")
@@ -37,6 +40,11 @@ class _Config(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "n_dims", "n_levels", "n_features", "log2_table_size", "base_resolution",
         "finest_resolution", "table_dtype", "grad_dtype")]
+
+
+class _Adam(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("step", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -104,6 +112,7 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
                 "hashgrid_backward": ([C, P, I64, P, I64, P, P, ctypes.c_size_t, P], ctypes.c_int),
                 "hashgrid_backward_workspace_size": ([C, I64, P, P], ctypes.c_int),
                 "hashgrid_debug_corners": ([C, P, I64, P, P, P], ctypes.c_int),
+                "hashgrid_adam_step": ([ctypes.POINTER(_Adam), I64, P, P, P, P, P, I32, P], ctypes.c_int),
                 "hashgrid_tune": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),
                 "hashgrid_tune_get": ([ctypes.c_int], ctypes.c_int),
             }
@@ -254,6 +263,58 @@ def hashgrid_debug_corners(cfg: HashGridConfig, x: torch.Tensor, stream=None):
     _check(load_library().hashgrid_debug_corners(ctypes.byref(c), x.data_ptr(), n, idx.data_ptr(),
                                                  w.data_ptr(), _stream(x, stream)))
     return idx, w
+
+
+def hashgrid_adam_step(param: torch.Tensor, m: torch.Tensor, v: torch.Tensor, grad: torch.Tensor, *,
+                       lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
+                       param_f16: torch.Tensor | None = None, zero_grad: bool = False, stream=None) -> None:
+    """One Adam update of ``param`` in place (fp32, any shape, contiguous),
+    with its moments ``m`` and ``v`` and gradient ``grad`` of the same shape;
+    ``step`` is the 1-based update index.  ``param_f16`` (fp16, same shape)
+    receives the updated values rounded to half; ``zero_grad`` clears ``grad``."""
+    for name, t in (("param", param), ("m", m), ("v", v), ("grad", grad)):
+        _dev(t, name, torch.float32)
+        if t.shape != param.shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous with the shape of param")
+    half_ptr = None
+    if param_f16 is not None:
+        _dev(param_f16, "param_f16", torch.float16)
+        if param_f16.shape != param.shape or not param_f16.is_contiguous():
+            raise ValueError("param_f16 must be contiguous with the shape of param")
+        half_ptr = param_f16.data_ptr()
+    opt = _Adam(lr, beta1, beta2, eps, step)
+    _check(load_library().hashgrid_adam_step(ctypes.byref(opt), param.numel(), param.data_ptr(), m.data_ptr(),
+                                             v.data_ptr(), grad.data_ptr(), half_ptr,
+                                             HG_ADAM_ZERO_GRAD if zero_grad else 0, _stream(param, stream)))
+
+
+class HashGridAdam(torch.optim.Optimizer):
+    """Adam over fp32 hash tables through hashgrid_adam_step (no weight decay:
+    the pages switch it off for the tables).  A drop-in for torch.optim.Adam on
+    such parameters; ``zero_grad_in_step`` clears each gradient inside the
+    update, so the next backward can accumulate into it directly."""
+
+    def __init__(self, params, lr=1e-2, betas=(0.9, 0.999), eps=1e-8, zero_grad_in_step=False):
+        super().__init__(params, dict(lr=lr, betas=betas, eps=eps))
+        self.zero_grad_in_step = zero_grad_in_step
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = closure() if closure is not None else None
+        for group in self.param_groups:
+            b1, b2 = group["betas"]
+            for p in group["params"]:
+                if p.grad is None:
+                    continue
+                st = self.state[p]
+                if not st:
+                    st["step"] = 0
+                    st["exp_avg"] = torch.zeros_like(p, memory_format=torch.contiguous_format)
+                    st["exp_avg_sq"] = torch.zeros_like(p, memory_format=torch.contiguous_format)
+                st["step"] += 1
+                hashgrid_adam_step(p, st["exp_avg"], st["exp_avg_sq"], p.grad, lr=group["lr"], step=st["step"],
+                                   beta1=b1, beta2=b2, eps=group["eps"], zero_grad=self.zero_grad_in_step)
+        return loss
 
 
 def hashgrid_tune(key: int, value: int) -> None:

@@ -189,3 +189,17 @@ def test_inputs_are_deterministic():
     assert a.min() >= 0.0 and a.max() < 1.0
     r = I.make_points(I.resized(I.WORKLOADS["ray"], 4 * 256))
     assert r.shape == (1024, 3) and r.min() >= 0.0 and r.max() < 1.0
+
+
+def test_adam_argument_errors(lib):
+    # Validation only: every call below is rejected (or is a count-0 no-op) before any launch.
+    opt = B._Adam(1e-2, 0.9, 0.999, 1e-8, 1)
+    assert lib.hashgrid_adam_step(ctypes.byref(opt), 0, None, None, None, None, None, 0, None) == B.HG_OK
+    assert lib.hashgrid_adam_step(None, 0, None, None, None, None, None, 0, None) == B.HG_EINVAL
+    assert lib.hashgrid_adam_step(ctypes.byref(opt), -1, None, None, None, None, None, 0, None) == B.HG_EINVAL
+    assert lib.hashgrid_adam_step(ctypes.byref(opt), 16, None, None, None, None, None, 0, None) == B.HG_EINVAL
+    assert lib.hashgrid_adam_step(ctypes.byref(opt), 0, None, None, None, None, None, 2, None) == B.HG_EINVAL
+    for bad in (B._Adam(1e-2, 0.9, 0.999, 1e-8, 0), B._Adam(1e-2, 1.0, 0.999, 1e-8, 1),
+                B._Adam(1e-2, 0.9, -0.1, 1e-8, 1), B._Adam(float("nan"), 0.9, 0.999, 1e-8, 1),
+                B._Adam(1e-2, 0.9, 0.999, -1.0, 1)):
+        assert lib.hashgrid_adam_step(ctypes.byref(bad), 0, None, None, None, None, None, 0, None) == B.HG_EINVAL
