@@ -218,3 +218,52 @@ int oracle_backward(const oracle_grid *g, const float *x, int64_t n, const float
     }
     return 0;
 }
+
+/* Gradient with respect to the points, dL/dx.  The pages imply it (ipipp.com
+ * section 3 places a learned canonical-space transform in front of the
+ * encoder, which needs it) but never write it down; it is the derivative of
+ * the blend of oracle_forward.  Inside a voxel the blend is multilinear in
+ * frac, and frac_d grows with x_d at the rate N_l (scaled = x * N_l), so
+ *   d out[l*F + j] / d x_d = N_l * sum_k (d w_k / d frac_d) * table[l][h(c_k)][j]
+ * where d w_k / d frac_d is +-1 (corner k on the upper / lower side in d) times
+ * the weight factors of the other dimensions.  On a voxel face (frac_d = 0)
+ * this is the derivative inside the voxel floor() chose, i.e. from above.
+ * dx[p][d] = sum_l sum_j dout[p][l*F + j] * d out[l*F + j] / d x_d, summed in
+ * level order; dx is [n][D] float64 and is WRITTEN. */
+int oracle_input_grad(const oracle_grid *g, const float *x, int64_t n, const void *table,
+                      const float *dout, int64_t dout_stride, double *dx) {
+    if (check_grid(g)) return -1;
+    int32_t res[ORACLE_MAX_LEVELS];
+    if (oracle_resolutions(g->n_levels, g->base_resolution, g->finest_resolution, res)) return -1;
+    const int D = g->n_dims, K = 1 << D, L = g->n_levels, F = g->n_features;
+    const int64_t T = (int64_t)1 << g->log2_table_size;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+    for (int64_t p = 0; p < n; ++p) {
+        double acc[ORACLE_MAX_DIMS];
+        for (int d = 0; d < D; ++d) acc[d] = 0.0;
+        for (int l = 0; l < L; ++l) {
+            int64_t v[ORACLE_MAX_DIMS], c[ORACLE_MAX_DIMS];
+            double frac[ORACLE_MAX_DIMS];
+            locate(x + p * D, D, res[l], v, frac);
+            for (int k = 0; k < K; ++k) {
+                corner(v, frac, D, k, c);
+                int64_t e = spatial_hash(c, D, T);
+                /* s = dL/dout of this level dotted with the corner's features */
+                double s = 0.0;
+                for (int j = 0; j < F; ++j)
+                    s += (double)dout[p * dout_stride + (int64_t)l * F + j] * table_value(g, table, l, e, j);
+                for (int d = 0; d < D; ++d) {
+                    double dw = 1.0;
+                    for (int q = 0; q < D; ++q) {
+                        int up = (k >> (D - 1 - q)) & 1;
+                        if (q == d) dw *= up ? 1.0 : -1.0;
+                        else dw *= up ? frac[q] : 1.0 - frac[q];
+                    }
+                    acc[d] += (double)res[l] * dw * s;
+                }
+            }
+        }
+        for (int d = 0; d < D; ++d) dx[p * D + d] = acc[d];
+    }
+    return 0;
+}

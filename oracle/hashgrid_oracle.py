@@ -57,6 +57,7 @@ def _lib():
             lib.oracle_corners.argtypes = [G, P, ctypes.c_int64, P, P]
             lib.oracle_forward.argtypes = [G, P, ctypes.c_int64, P, P]
             lib.oracle_backward.argtypes = [G, P, ctypes.c_int64, P, ctypes.c_int64, P]
+            lib.oracle_input_grad.argtypes = [G, P, ctypes.c_int64, P, P, ctypes.c_int64, P]
             lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
             lib.oracle_half_to_double.restype = ctypes.c_double
             lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -152,3 +153,17 @@ def backward(g: OracleGrid, x: np.ndarray, dout: np.ndarray, grad: np.ndarray | 
     if _lib().oracle_backward(ctypes.byref(g), _ptr(x), x.shape[0], _ptr(dout), dout.shape[1], _ptr(grad)):
         raise ValueError("invalid grid")
     return grad
+
+
+def input_grad(g: OracleGrid, x: np.ndarray, table: np.ndarray, dout: np.ndarray) -> np.ndarray:
+    """dL/dx [n, D] float64 of upstream dL/dout [n, >= L*F] (oracle_input_grad)."""
+    x = _points(g, x)
+    t = _table(g, table)
+    dout = np.ascontiguousarray(dout, dtype=np.float32)
+    n = x.shape[0]
+    if dout.ndim != 2 or dout.shape[0] != n or dout.shape[1] < g.n_levels * g.n_features:
+        raise ValueError("dout must be [n, >= L*F]")
+    dx = np.zeros((n, g.n_dims), dtype=np.float64)
+    if _lib().oracle_input_grad(ctypes.byref(g), _ptr(x), n, _ptr(t), _ptr(dout), dout.shape[1], _ptr(dx)):
+        raise ValueError("bad grid")
+    return dx

@@ -348,3 +348,62 @@ def test_out_of_domain_points_follow_the_same_formula(oracle):
     idx, wt = oracle.corners(g, x)
     assert idx[0, 0, 0] == (1 << 10) - 1 and idx[1, 0, 0] == 9
     assert np.all(wt[:, 0, 0] == 1.0)
+
+
+# ----------------------------------------------------------------------------- dL/dx
+
+def _dyadic_points(seed, n, dims, cells=256):
+    """Points (m + 1/4) / cells: x * N is exact in float32 for power-of-two N <= cells,
+    and x stays at least 1/(4 cells) away from every voxel face."""
+    rng = np.random.default_rng(seed)
+    return ((rng.integers(0, cells, size=(n, dims)) + 0.25) / cells).astype(np.float32)
+
+
+@pytest.mark.parametrize("dims", [2, 3, 4])
+def test_input_grad_equals_central_difference(oracle, dims):
+    # Inside a voxel the encoding is linear in each coordinate, so a central
+    # difference of the forward is exact up to rounding when x +- h stays in the
+    # voxel; power-of-two resolutions (4, 8, 16, 32) and dyadic x, h keep the
+    # float32 positions exact.
+    g = oracle.grid(4, 2, 12, 4, 32, n_dims=dims)
+    rng = np.random.default_rng(dims)
+    t = rng.uniform(-1, 1, (4, 1 << 12, 2)).astype(np.float32)
+    x = _dyadic_points(dims, 300, dims)
+    dout = rng.standard_normal((300, 8)).astype(np.float32)
+    dx = oracle.input_grad(g, x, t, dout)
+    h = 2.0 ** -16
+    for d in range(dims):
+        xp, xm = x.copy(), x.copy()
+        xp[:, d] += np.float32(h)
+        xm[:, d] -= np.float32(h)
+        fd = ((oracle.forward(g, xp, t) - oracle.forward(g, xm, t)) * dout).sum(1) / (2 * h)
+        assert np.max(np.abs(dx[:, d] - fd)) <= 1e-9 * np.max(np.abs(fd))
+
+
+def test_input_grad_of_linear_table(oracle):
+    # table[h(v)] = a . v + c on the collision-free level 0 of the standard grid and
+    # zero elsewhere: the encoding is a . (x N_0) + c there, so dL/dx = N_0 a^T dout.
+    w = I.WORKLOADS["standard"]
+    g = oracle.grid_of(w)
+    N = int(oracle.resolutions(w.n_levels, w.base_resolution, w.finest_resolution)[0])
+    ax = np.arange(N + 1)
+    v = np.stack(np.meshgrid(ax, ax, ax, indexing="ij"), -1).reshape(-1, 3)
+    h = _vertex_hash(oracle, v, w.log2_table_size, N=N)
+    a = np.array([[0.5, -0.25, 0.125], [-0.0625, 0.75, 0.375]])
+    t = np.zeros((w.n_levels, w.table_size, 2), dtype=np.float32)
+    t[0][h] = (v @ a.T + 0.25).astype(np.float32)
+    x = I.points_uniform(5, 2000)
+    dout = I.normal_f32(6, 2, 2000 * 32).reshape(2000, 32)
+    dx = oracle.input_grad(g, x, t, dout)
+    assert np.max(np.abs(dx - N * dout[:, 0:2].astype(np.float64) @ a)) < 1e-10
+
+
+def test_input_grad_half_table_equals_widened_float_table(oracle):
+    w = I.WORKLOADS["tiny"]
+    t16 = (np.random.default_rng(3).uniform(-1, 1, (w.n_levels, w.table_size, 2))).astype(np.float16)
+    x = I.points_uniform(4, 500)
+    dout = I.normal_f32(8, 2, 500 * 8).reshape(500, 8)
+    a = oracle.input_grad(oracle.grid(w.n_levels, 2, w.log2_table_size, w.base_resolution,
+                                      w.finest_resolution, "f16"), x, t16, dout)
+    b = oracle.input_grad(oracle.grid_of(w), x, t16.astype(np.float32), dout)
+    assert np.array_equal(a, b)
