@@ -90,6 +90,50 @@ def measure_adam(cfg, dev, iters: int) -> dict:
             "achieved_GBps": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
+def measure_input_grad(cfg, x, t, d, iters: int) -> dict:
+    """dL/dx of the standard workload (level-major with its stage): reads the
+    point, its L*F upstream values and 2^D x L x F table values, writes D
+    values -- 4D + 4LF + 2^D*4LF + 4D algorithmic bytes per point."""
+    import torch
+    import multiresolution_hash_grid_amd as hg
+    n = x.shape[0]
+    D, L, F = cfg.n_dims, cfg.n_levels, cfg.n_features
+    dx = torch.empty((n, D), device=x.device)
+    ws = torch.empty(hg.hashgrid_input_grad_workspace_size(cfg, n), dtype=torch.uint8, device=x.device)
+    ms = time_calls(lambda: hg.hashgrid_input_grad(cfg, x, t, d, dx=dx, workspace=ws), iters)
+    bpp = 4 * D + 4 * L * F + (1 << D) * 4 * L * F + 4 * D
+    gbs = bpp * n / (ms * 1e-3) / 1e9
+    return {"points": n, "us_per_call": ms * 1e3, "points_per_s": n / (ms * 1e-3),
+            "algorithmic_bytes_per_point": bpp, "achieved_GBps": gbs, "frac": gbs / HBM_PEAK_GBS}
+
+
+def measure_shapes(dev, n: int, iters: int) -> dict:
+    """Forward and backward (generic kernels, fp32 atomics) of other grid
+    shapes at the standard L, T and resolutions, n uniform points."""
+    import torch
+    import multiresolution_hash_grid_amd as hg
+    from multiresolution_hash_grid_amd import inputs
+    out = {}
+    for D, F in ((2, 2), (4, 2), (3, 1), (3, 4), (3, 8)):
+        w = inputs.resized(inputs.WORKLOADS["standard"], n, n_dims=D, n_features=F)
+        cfg = hg.HashGridConfig.of(w)
+        x = torch.from_numpy(inputs.make_points(w)).to(dev)
+        t = torch.from_numpy(inputs.make_table(w)).to(dev)
+        d = torch.from_numpy(inputs.make_dout(w)).to(dev)
+        o = torch.empty((n, cfg.out_features), device=dev)
+        g = torch.zeros(cfg.table_shape, device=dev)
+        fms = time_calls(lambda: hg.hashgrid_forward(cfg, x, t, out=o, workspace=None), iters)
+        bms = time_calls(lambda: hg.hashgrid_backward(cfg, x, d, g, workspace=None), iters)
+        L, K = cfg.n_levels, 1 << D
+        fb = 4 * D + K * 4 * L * F + 4 * L * F
+        bb = 4 * D + 4 * L * F + K * 4 * L * F
+        out[f"D{D}_F{F}"] = {"fwd_points_per_s": n / (fms * 1e-3), "bwd_points_per_s": n / (bms * 1e-3),
+                             "fwd_frac": fb * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del x, t, d, o, g
+    return out
+
+
 def cpu_baseline(w, x, t, d, budget_s: float) -> dict:
     """The CPU oracle, as it stands, on the same workload: forward + backward of
     all points, repeated until about `budget_s` seconds of work."""
@@ -217,7 +261,9 @@ def main() -> int:
         "roofline_fwd_bwd_frac": (bpp["fwd"] + bpp["bwd"]) * w.n_points * K / elapsed / 1e9 / HBM_PEAK_GBS,
     }
     # The table optimizer step that follows the backward (Adam over the tables).
-    result["next"] = {"adam": measure_adam(cfg, dev, 50)}
+    result["next"] = {"adam": measure_adam(cfg, dev, 50),
+                      "input_grad": measure_input_grad(cfg, x, t, d, 20),
+                      "shapes": measure_shapes(dev, w.n_points, 10)}
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x_h, t_h, d_h, args.cpu_seconds)

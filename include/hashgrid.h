@@ -12,6 +12,10 @@
  *     h(c) = (c_0 * 1) XOR (c_1 * 2654435761) XOR (c_2 * 805459861) mod T,
  *     the corner features are gathered and blended with multilinear weights;
  *   - the per-level F-vectors are concatenated level-major into L*F outputs.
+ * Other input dimensions (jsqmd.com HashEncoding, section 3: 2-D images,
+ * 4-D space-time) hash c_3 with 3674653429, the fourth of that page's primes;
+ * its section 4 runs F from 2 to 4.  D = 3, F = 2 (the pages' standard
+ * encoder) has tuned kernels; the other shapes run generic ones.
  *
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers (memory of the current HIP device)
@@ -57,9 +61,9 @@ extern "C" {
  * (n_levels, n_features_per_level, log2_hashmap_size, base_resolution,
  * finest_resolution). */
 typedef struct hg_config {
-    int32_t n_dims;            /* D, coordinates per point: 3                                   */
+    int32_t n_dims;            /* D, coordinates per point: 1..4                                */
     int32_t n_levels;          /* L, 1..64                                                      */
-    int32_t n_features;        /* F, features per table entry: 2                                */
+    int32_t n_features;        /* F, features per table entry: 1, 2, 4 or 8                     */
     int32_t log2_table_size;   /* T = 2^log2_table_size entries per level, 1..28                */
     int32_t base_resolution;   /* N_min >= 1                                                    */
     int32_t finest_resolution; /* N_max, N_min <= N_max < 2^24                                  */
@@ -154,6 +158,32 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
  * Either pointer may be NULL to skip that output.  Errors: as hashgrid_forward. */
 int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint32_t *idx,
                            float *w, void *stream);
+
+/* Bytes of device workspace that let hashgrid_input_grad stage per-level
+ * partial sums level-major: L * n * D * 4, rounded up to 256.  *bytes_out is
+ * a HOST size_t.  Errors: HG_EINVAL, HG_EUNSUPPORTED. */
+int hashgrid_input_grad_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out);
+
+/* Gradient of the loss with respect to the points, dL/dx.  The pages imply
+ * it (ipipp.com section 3 places a learned canonical-space transform in front
+ * of the encoder) but do not write it; it is the derivative of the forward's
+ * blend: inside a voxel the blend is multilinear in the fractions f and f_d
+ * moves with x_d at rate N_l, so
+ *   dx[p][d] = sum_l N_l sum_k (b_d ? 1 : -1) prod_{e != d} (b_e ? f_e : 1 - f_e)
+ *              * sum_j dout[p][l*F + j] * table[l][h(c_k)][j]
+ * over the corners c_k = v + b of the voxel floor() picked (on a voxel face,
+ * the derivative from that voxel), summed over levels in level order in fp32.
+ *   x, table : as hashgrid_forward;  dout : as hashgrid_backward.
+ *   dx       : float32 [n][D], 4-byte aligned; WRITTEN (not accumulated).
+ *   workspace: NULL, or hashgrid_input_grad_workspace_size bytes (256-byte
+ *              aligned) to run level-major (each level's table stays in L2)
+ *              and then sum the levels; without it one thread walks all levels
+ *              of a point.  The two give identical results.  Concurrent calls
+ *              must not share a workspace.
+ * Errors: as hashgrid_forward. */
+int hashgrid_input_grad(const hg_config *cfg, const float *x, int64_t n, const void *table, const float *dout,
+                        int64_t dout_row_stride, float *dx, void *workspace, size_t workspace_bytes,
+                        void *stream);
 
 /* Adam update of the tables (ipipp.com section 4: Adam, no weight decay on
  * the hash tables, whose learning rate is 5-10x the MLP's per section 3;

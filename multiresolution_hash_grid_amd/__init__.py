@@ -19,6 +19,8 @@ from .hashgrid import (  # noqa: F401
     forward_workspace,
     hashgrid_forward,
     hashgrid_forward_workspace_size,
+    hashgrid_input_grad,
+    hashgrid_input_grad_workspace_size,
     hashgrid_resolutions,
     hashgrid_tune,
     hashgrid_tune_get,

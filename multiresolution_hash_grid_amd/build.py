@@ -30,7 +30,7 @@ def hipcc() -> str:
 
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.
-COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
+COMMON = ["-O3", "-fPIC", "-std=c++20", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics", "-I", INCLUDE, "-I", CSRC]
 

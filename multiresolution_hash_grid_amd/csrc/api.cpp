@@ -74,8 +74,9 @@ int check_config(const hg_config *c) {
         return fail(HG_EINVAL, "table_dtype %d is neither HG_F32 nor HG_F16", c->table_dtype);
     if (c->grad_dtype != HG_F32 && c->grad_dtype != HG_F16)
         return fail(HG_EINVAL, "grad_dtype %d is neither HG_F32 nor HG_F16", c->grad_dtype);
-    if (c->n_dims != 3) return fail(HG_EUNSUPPORTED, "n_dims %d: only 3 is built", c->n_dims);
-    if (c->n_features != 2) return fail(HG_EUNSUPPORTED, "n_features %d: only 2 is built", c->n_features);
+    if (c->n_dims > 4) return fail(HG_EUNSUPPORTED, "n_dims %d: 1..4 are built", c->n_dims);
+    if (c->n_features != 1 && c->n_features != 2 && c->n_features != 4 && c->n_features != 8)
+        return fail(HG_EUNSUPPORTED, "n_features %d: 1, 2, 4 and 8 are built", c->n_features);
     if (c->grad_dtype != HG_F32) return fail(HG_EUNSUPPORTED, "grad_dtype must be HG_F32");
     return HG_OK;
 }
@@ -128,6 +129,11 @@ bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
 }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// The D = 3, F = 2 grid of the pages' standard encoder has tuned kernels
+// (lane pairs, staged forward, binned backward); other shapes take the
+// generic ones.
+bool standard_shape(const hg_config &c) { return c.n_dims == 3 && c.n_features == 2; }
 
 // Levels per binned group: as many as keep one group's records (written by
 // the bin kernel, read back by the accumulate kernel right after) within the
@@ -194,6 +200,10 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
     if (workspace && !aligned(workspace, 256)) return fail(HG_EINVAL, "workspace is not 256-byte aligned");
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
+    if (!standard_shape(*cfg))
+        return launch_status(hg::launch_forward_generic(lp, cfg->n_dims, cfg->n_features, x, n, table,
+                                                        cfg->table_dtype, out, out_row_stride, (hipStream_t)stream),
+                             "forward");
     const size_t stage_bytes = (size_t)n * cfg->n_levels * cfg->n_features * sizeof(float);
     float *stage = (g_tune.fwd_staged && workspace && workspace_bytes >= stage_bytes) ? (float *)workspace : nullptr;
     const hg::FwdTune ft{g_tune.fwd_lanes, g_tune.fwd_unroll, g_tune.fwd_nt};
@@ -246,9 +256,46 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
     }
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
+    if (!standard_shape(*cfg))
+        return launch_status(hg::launch_backward_generic(lp, cfg->n_dims, cfg->n_features, x, n, dout,
+                                                         dout_row_stride, dtable, (hipStream_t)stream),
+                             "backward");
     return launch_status(hg::launch_backward(lp, x, n, dout, dout_row_stride, dtable, g_tune.bwd_lanes,
                                              (hipStream_t)stream),
                          "backward");
+}
+
+int hashgrid_input_grad_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
+    if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
+    *bytes_out = round_up((size_t)n * cfg->n_levels * cfg->n_dims * sizeof(float), 256);
+    return ok();
+}
+
+int hashgrid_input_grad(const hg_config *cfg, const float *x, int64_t n, const void *table, const float *dout,
+                        int64_t dout_row_stride, float *dx, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n == 0) return ok();
+    if ((rc = check_points(n, x))) return rc;
+    const size_t esize = cfg->table_dtype == HG_F32 ? 4 : 2;
+    if (!table || !aligned(table, esize * cfg->n_features))
+        return fail(HG_EINVAL, "table is NULL or not %zu-byte aligned", esize * cfg->n_features);
+    if (!dout || !aligned(dout, 4)) return fail(HG_EINVAL, "dout is NULL or not 4-byte aligned");
+    if (dout_row_stride < (int64_t)cfg->n_levels * cfg->n_features)
+        return fail(HG_EINVAL, "dout_row_stride %lld < L*F", (long long)dout_row_stride);
+    if (!dx || !aligned(dx, 4)) return fail(HG_EINVAL, "dx is NULL or not 4-byte aligned");
+    if (workspace && !aligned(workspace, 256)) return fail(HG_EINVAL, "workspace is not 256-byte aligned");
+    hg::LaunchParams lp;
+    if ((rc = plan(*cfg, n, lp))) return rc;
+    const size_t stage_bytes = (size_t)n * cfg->n_levels * cfg->n_dims * sizeof(float);
+    float *stage = (workspace && workspace_bytes >= stage_bytes) ? (float *)workspace : nullptr;
+    return launch_status(hg::launch_input_grad(lp, cfg->n_dims, cfg->n_features, x, n, table, cfg->table_dtype,
+                                               dout, dout_row_stride, dx, stage, (hipStream_t)stream),
+                         "input_grad");
 }
 
 int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m, float *v, float *grad,
@@ -283,6 +330,9 @@ int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint
     if (n > ((int64_t)1 << 31) - 256) return fail(HG_EINVAL, "n too large for the debug export");
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
+    if (cfg->n_dims != 3)
+        return launch_status(hg::launch_debug_corners_generic(lp, cfg->n_dims, x, n, idx, w, (hipStream_t)stream),
+                             "debug_corners");
     return launch_status(hg::launch_debug_corners(lp, x, n, idx, w, (hipStream_t)stream), "debug_corners");
 }
 

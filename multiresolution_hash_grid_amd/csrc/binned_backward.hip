@@ -39,7 +39,7 @@
 // corner in its record and adds the x+1 corner with a global fp32 atomic.
 #include <algorithm>
 
-#include "hashgrid_internal.h"
+#include "device_common.h"
 
 namespace hg {
 namespace {
@@ -67,14 +67,6 @@ Space carve(void *ws, const BinParams &bp) {
     return s;
 }
 
-__device__ __forceinline__ void locate1b(float xd, float N, int32_t &v, float &f) {
-#pragma clang fp contract(off)
-    float s = xd * N;
-    float fl = floorf(s);
-    v = (int32_t)fl;
-    f = s - fl;
-}
-
 // The four corner pairs (dy, dz) of one point at one level.
 struct Pairs {
     uint32_t part[4];
@@ -89,9 +81,9 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
     const float N = (float)bp.res[l];
     int32_t v0, v1, v2;
     float a0, a1, a2;
-    locate1b(xp[0], N, v0, a0);
-    locate1b(xp[1], N, v1, a1);
-    locate1b(xp[2], N, v2, a2);
+    locate1(xp[0], N, v0, a0);
+    locate1(xp[1], N, v1, a1);
+    locate1(xp[2], N, v2, a2);
     const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hz0 = (uint32_t)v2 * kPrimeZ;
     const uint32_t cx0 = (uint32_t)v0, cx1 = cx0 + 1u;
     const uint32_t smask = (1u << bp.s_log2) - 1u;

@@ -19,46 +19,12 @@
 // two x-corners of one point to two adjacent lanes of the same load or atomic
 // instruction, so the memory pipeline sees about 4 distinct lines per
 // (point, level) instead of 8.
-#include "hashgrid_internal.h"
+#include "device_common.h"
 
 namespace hg {
 namespace {
 
 // ---------------------------------------------------------------- helpers
-
-struct Item {
-    int level;
-    int64_t p0;
-};
-
-__device__ __forceinline__ bool decode_item(const LaunchParams &lp, Item &it) {
-    int g = blockIdx.x;
-    int item = lp.xcd_map ? (g % kNumXcd) * lp.per_xcd + g / kNumXcd : g;
-    if (item >= lp.items) return false;
-    int pos = item / lp.chunks;
-    it.level = lp.level_order[pos];
-    it.p0 = (int64_t)(item - pos * lp.chunks) * lp.chunk_pts;
-    return true;
-}
-
-// Voxel of one coordinate: scaled position rounded to fp32, its floor as a
-// signed integer and the fraction s - floor(s), which is exact.  Contraction
-// is off here: fusing the multiply into the subtraction would compute the
-// fraction of the unrounded product and move the weights off the voxel that
-// floor(s) picked.
-__device__ __forceinline__ void locate1(float xd, float N, int32_t &v, float &f) {
-#pragma clang fp contract(off)
-    float s = xd * N;
-    float fl = floorf(s);
-    v = (int32_t)fl;
-    f = s - fl;
-}
-
-// Exchange a value with the other lane of an aligned lane pair (DPP
-// quad_perm [1,0,3,2]); the pair never leaves its quad.
-__device__ __forceinline__ float swap_pair(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
 
 // Table element pairs (F = 2).  fp16 entries are widened exactly (subnormals
 // included) and all arithmetic is fp32.

@@ -1,0 +1,327 @@
+// Generic-shape kernels of the hash-grid encoder for gfx950: any input
+// dimension D in 1..4 and F in {1, 2, 4, 8} features per entry, and the
+// gradient with respect to the points for every shape.
+//
+// Shapes: the jsqmd.com HashEncoding hashes d-dimensional points with its
+// list of seven primes (section 3; 2-D images, 4-D space-time) and its
+// experiment table runs 2 to 4 features per entry (section 4).  The method is
+// the same for every shape: per (point, level) the 2^D voxel corners
+// c = v + b (b in {0,1}^D, corner k has b_d = bit D-1-d of k, so the first
+// coordinate is the outermost loop), h(c) = XOR_d c_d * prime_d in uint32
+// masked to T, weights w_k = prod_d (b_d ? f_d : 1 - f_d), and
+// out[l*F + j] = sum_k w_k table[l][h(c_k)][j]; the backward adds
+// w_k dL/dout[l*F + j] into every entry a corner hashed to.  The D = 3, F = 2
+// grid has its own tuned kernels (encode_kernels.hip, binned_backward.hip);
+// these cover the other shapes with one thread per (point, level), direct row
+// writes and fp32 global atomics in the backward.
+//
+// Gradient with respect to the points (implied by ipipp.com section 3, which
+// puts a learned canonical-space transform before the encoder; never written
+// on the pages): inside a voxel the blend is multilinear in f and f_d moves
+// with x_d at rate N_l, so with s_k = sum_j dL/dout[l*F + j] table[l][h(c_k)][j]
+//   dL/dx_d = sum_l N_l sum_k (b_d ? 1 : -1) prod_{e != d} (b_e ? f_e : 1 - f_e) s_k.
+// Level-major work items write each level's D partial sums to a [L][n][D]
+// stage, which a second kernel sums over levels in level order; without a
+// stage one thread walks all levels of its point.  Both add the same fp32
+// terms in the same order (contraction off), so they agree bit for bit.
+#include <type_traits>
+
+#include "device_common.h"
+
+namespace hg {
+namespace {
+
+// Voxel of a D-dimensional point at resolution N: per coordinate the hash
+// terms of the lower and upper corner and the fraction.
+template <int D>
+struct Voxel {
+    uint32_t h0[D], h1[D];
+    float f[D];
+};
+
+template <int D>
+__device__ __forceinline__ void locate_point(const float *__restrict__ xp, float N, Voxel<D> &vx) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        int32_t v;
+        locate1(xp[d], N, v, vx.f[d]);
+        vx.h0[d] = (uint32_t)v * kPrimeList[d];
+        vx.h1[d] = vx.h0[d] + kPrimeList[d];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t corner_hash(const Voxel<D> &vx, int k, uint32_t mask) {
+    uint32_t h = 0;
+#pragma unroll
+    for (int d = 0; d < D; ++d) h ^= ((k >> (D - 1 - d)) & 1) ? vx.h1[d] : vx.h0[d];
+    return h & mask;
+}
+
+template <int D>
+__device__ __forceinline__ float corner_weight(const Voxel<D> &vx, int k) {
+    float w = 1.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) w *= ((k >> (D - 1 - d)) & 1) ? vx.f[d] : 1.f - vx.f[d];
+    return w;
+}
+
+// ---------------------------------------------------------------- forward
+
+template <int D, int F, int DT>
+__global__ __launch_bounds__(kBlock) void fwd_generic_kernel(const float *__restrict__ x, int64_t n,
+                                                             const void *__restrict__ table,
+                                                             float *__restrict__ out, int64_t ostride,
+                                                             LaunchParams lp) {
+    Item it;
+    if (!decode_item(lp, it)) return;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    for (int64_t p = it.p0 + threadIdx.x; p < end; p += kBlock) {
+        Voxel<D> vx;
+        locate_point<D>(x + p * D, N, vx);
+        float acc[F];
+#pragma unroll
+        for (int j = 0; j < F; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < (1 << D); ++k) {
+            float e[F];
+            load_features<F, DT>(table, lbase + corner_hash<D>(vx, k, lp.mask), e);
+            const float w = corner_weight<D>(vx, k);
+#pragma unroll
+            for (int j = 0; j < F; ++j) acc[j] += w * e[j];
+        }
+        float *orow = out + p * ostride + (int64_t)l * F;
+#pragma unroll
+        for (int j = 0; j < F; ++j) orow[j] = acc[j];
+    }
+}
+
+// ---------------------------------------------------------------- backward
+
+template <int D, int F>
+__global__ __launch_bounds__(kBlock) void bwd_generic_kernel(const float *__restrict__ x, int64_t n,
+                                                             const float *__restrict__ dout, int64_t dstride,
+                                                             float *__restrict__ grad, LaunchParams lp) {
+    Item it;
+    if (!decode_item(lp, it)) return;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    for (int64_t p = it.p0 + threadIdx.x; p < end; p += kBlock) {
+        Voxel<D> vx;
+        locate_point<D>(x + p * D, N, vx);
+        float g[F];
+#pragma unroll
+        for (int j = 0; j < F; ++j) g[j] = dout[p * dstride + (int64_t)l * F + j];
+#pragma unroll
+        for (int k = 0; k < (1 << D); ++k) {
+            float *e = grad + (lbase + corner_hash<D>(vx, k, lp.mask)) * F;
+            const float w = corner_weight<D>(vx, k);
+#pragma unroll
+            for (int j = 0; j < F; ++j) unsafeAtomicAdd(e + j, w * g[j]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- corners
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void corners_generic_kernel(const float *__restrict__ x, int64_t n,
+                                                                 uint32_t *__restrict__ idx, float *__restrict__ w,
+                                                                 LaunchParams lp) {
+    const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    const int l = blockIdx.y;
+    if (p >= n) return;
+    Voxel<D> vx;
+    locate_point<D>(x + p * D, (float)lp.res[l], vx);
+    const int64_t o = (p * lp.n_levels + l) << D;
+#pragma unroll
+    for (int k = 0; k < (1 << D); ++k) {
+        if (idx) idx[o + k] = corner_hash<D>(vx, k, lp.mask);
+        if (w) w[o + k] = corner_weight<D>(vx, k);
+    }
+}
+
+// ---------------------------------------------------------------- dL/dx
+
+// N_l * d(sum_j dout_j out_j)/dx_d of one (point, level) into g[0..D).
+template <int D, int F, int DT>
+__device__ __forceinline__ void level_input_grad(const float *__restrict__ xp, const void *__restrict__ table,
+                                                 const float *__restrict__ drow, int l, const LaunchParams &lp,
+                                                 float (&g)[D]) {
+#pragma clang fp contract(off)
+    const float N = (float)lp.res[l];
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    Voxel<D> vx;
+    locate_point<D>(xp, N, vx);
+    float dl[F];
+#pragma unroll
+    for (int j = 0; j < F; ++j) dl[j] = drow[(int64_t)l * F + j];
+#pragma unroll
+    for (int d = 0; d < D; ++d) g[d] = 0.f;
+#pragma unroll
+    for (int k = 0; k < (1 << D); ++k) {
+        float e[F];
+        load_features<F, DT>(table, lbase + corner_hash<D>(vx, k, lp.mask), e);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < F; ++j) s += dl[j] * e[j];
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            float dw = ((k >> (D - 1 - d)) & 1) ? 1.f : -1.f;
+#pragma unroll
+            for (int q = 0; q < D; ++q)
+                if (q != d) dw *= ((k >> (D - 1 - q)) & 1) ? vx.f[q] : 1.f - vx.f[q];
+            g[d] += dw * s;
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) g[d] = N * g[d];
+}
+
+template <int D, int F, int DT>
+__global__ __launch_bounds__(kBlock) void input_grad_level_kernel(const float *__restrict__ x, int64_t n,
+                                                                  const void *__restrict__ table,
+                                                                  const float *__restrict__ dout, int64_t dstride,
+                                                                  float *__restrict__ stage, LaunchParams lp) {
+    Item it;
+    if (!decode_item(lp, it)) return;
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    for (int64_t p = it.p0 + threadIdx.x; p < end; p += kBlock) {
+        float g[D];
+        level_input_grad<D, F, DT>(x + p * D, table, dout + p * dstride, it.level, lp, g);
+        float *dst = stage + ((int64_t)it.level * n + p) * D;
+#pragma unroll
+        for (int d = 0; d < D; ++d) dst[d] = g[d];
+    }
+}
+
+// dx[p][d] = sum over levels, in level order, of stage[l][p][d].
+__global__ __launch_bounds__(kBlock) void input_grad_reduce_kernel(const float *__restrict__ stage, int64_t nd,
+                                                                   int L, float *__restrict__ dx) {
+#pragma clang fp contract(off)
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= nd) return;
+    float acc = 0.f;
+    for (int l = 0; l < L; ++l) acc += stage[(int64_t)l * nd + i];
+    dx[i] = acc;
+}
+
+// One thread per point over all levels (no stage).
+template <int D, int F, int DT>
+__global__ __launch_bounds__(kBlock) void input_grad_point_kernel(const float *__restrict__ x, int64_t n,
+                                                                  const void *__restrict__ table,
+                                                                  const float *__restrict__ dout, int64_t dstride,
+                                                                  float *__restrict__ dx, LaunchParams lp) {
+#pragma clang fp contract(off)
+    const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (p >= n) return;
+    float acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = 0.f;
+    for (int l = 0; l < lp.n_levels; ++l) {
+        float g[D];
+        level_input_grad<D, F, DT>(x + p * D, table, dout + p * dstride, l, lp, g);
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] += g[d];
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) dx[p * D + d] = acc[d];
+}
+
+int grid_blocks(const LaunchParams &lp) { return lp.xcd_map ? kNumXcd * lp.per_xcd : lp.items; }
+
+// ---------------------------------------------------------------- dispatch
+
+// Calls fn.template operator()<D, F>() for the runtime shape; false if unbuilt.
+template <typename Fn>
+bool dispatch_shape(int D, int F, Fn &&fn) {
+    auto byF = [&](auto dc) {
+        constexpr int DD = decltype(dc)::value;
+        switch (F) {
+        case 1: fn.template operator()<DD, 1>(); return true;
+        case 2: fn.template operator()<DD, 2>(); return true;
+        case 4: fn.template operator()<DD, 4>(); return true;
+        case 8: fn.template operator()<DD, 8>(); return true;
+        default: return false;
+        }
+    };
+    switch (D) {
+    case 1: return byF(std::integral_constant<int, 1>{});
+    case 2: return byF(std::integral_constant<int, 2>{});
+    case 3: return byF(std::integral_constant<int, 3>{});
+    case 4: return byF(std::integral_constant<int, 4>{});
+    default: return false;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_forward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
+                                  const void *table, int table_dtype, float *out, int64_t out_stride,
+                                  hipStream_t stream) {
+    const dim3 grid(grid_blocks(lp)), block(kBlock);
+    const bool ok = dispatch_shape(D, F, [&]<int DD, int FF>() {
+        if (table_dtype == 0)
+            fwd_generic_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+        else
+            fwd_generic_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+    });
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
+                                   const float *dout, int64_t dout_stride, float *dtable, hipStream_t stream) {
+    const dim3 grid(grid_blocks(lp)), block(kBlock);
+    const bool ok = dispatch_shape(D, F, [&]<int DD, int FF>() {
+        bwd_generic_kernel<DD, FF><<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
+    });
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_debug_corners_generic(const LaunchParams &lp, int D, const float *x, int64_t n, uint32_t *idx,
+                                        float *w, hipStream_t stream) {
+    const dim3 grid((unsigned)((n + kBlock - 1) / kBlock), lp.n_levels), block(kBlock);
+    const bool ok = dispatch_shape(D, 1, [&]<int DD, int FF>() {
+        corners_generic_kernel<DD><<<grid, block, 0, stream>>>(x, n, idx, w, lp);
+    });
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_input_grad(const LaunchParams &lp, int D, int F, const float *x, int64_t n, const void *table,
+                             int table_dtype, const float *dout, int64_t dout_stride, float *dx, float *stage,
+                             hipStream_t stream) {
+    bool ok;
+    if (stage) {
+        const dim3 grid(grid_blocks(lp)), block(kBlock);
+        ok = dispatch_shape(D, F, [&]<int DD, int FF>() {
+            if (table_dtype == 0)
+                input_grad_level_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride,
+                                                                              stage, lp);
+            else
+                input_grad_level_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride,
+                                                                              stage, lp);
+        });
+        if (!ok) return hipErrorInvalidValue;
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t nd = n * D;
+        input_grad_reduce_kernel<<<(unsigned)((nd + kBlock - 1) / kBlock), kBlock, 0, stream>>>(stage, nd,
+                                                                                             lp.n_levels, dx);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((n + kBlock - 1) / kBlock)), block(kBlock);
+    ok = dispatch_shape(D, F, [&]<int DD, int FF>() {
+        if (table_dtype == 0)
+            input_grad_point_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride, dx, lp);
+        else
+            input_grad_point_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride, dx, lp);
+    });
+    return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+}  // namespace hg

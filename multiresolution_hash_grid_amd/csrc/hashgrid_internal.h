@@ -81,6 +81,20 @@ hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, con
                           float *stage, hipStream_t stream);
 hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, const float *dout,
                            int64_t dout_stride, float *dtable, int lanes, hipStream_t stream);
+// Shapes other than D = 3, F = 2 (generic_kernels.hip): D in 1..4,
+// F in {1, 2, 4, 8}; hipErrorInvalidValue for an unbuilt shape.
+hipError_t launch_forward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
+                                  const void *table, int table_dtype, float *out, int64_t out_stride,
+                                  hipStream_t stream);
+hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
+                                   const float *dout, int64_t dout_stride, float *dtable, hipStream_t stream);
+hipError_t launch_debug_corners_generic(const LaunchParams &lp, int D, const float *x, int64_t n, uint32_t *idx,
+                                        float *w, hipStream_t stream);
+// dL/dx of every shape; stage ([L][n][D] fp32) selects the level-major path.
+hipError_t launch_input_grad(const LaunchParams &lp, int D, int F, const float *x, int64_t n, const void *table,
+                             int table_dtype, const float *dout, int64_t dout_stride, float *dx, float *stage,
+                             hipStream_t stream);
+
 struct AdamParams {
     float lr, beta1, beta2, eps;
     int32_t step;

@@ -85,7 +85,7 @@ class HashGridConfig:
     def of(w) -> "HashGridConfig":
         """Config of a workload from ``multiresolution_hash_grid_amd.inputs``."""
         return HashGridConfig(w.n_levels, w.n_features, w.log2_table_size, w.base_resolution,
-                              w.finest_resolution, w.table_dtype)
+                              w.finest_resolution, w.table_dtype, n_dims=getattr(w, "n_dims", 3))
 
 
 _lock = threading.Lock()
@@ -112,6 +112,8 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
                 "hashgrid_backward": ([C, P, I64, P, I64, P, P, ctypes.c_size_t, P], ctypes.c_int),
                 "hashgrid_backward_workspace_size": ([C, I64, P, P], ctypes.c_int),
                 "hashgrid_debug_corners": ([C, P, I64, P, P, P], ctypes.c_int),
+                "hashgrid_input_grad": ([C, P, I64, P, P, I64, P, P, ctypes.c_size_t, P], ctypes.c_int),
+                "hashgrid_input_grad_workspace_size": ([C, I64, P], ctypes.c_int),
                 "hashgrid_adam_step": ([ctypes.POINTER(_Adam), I64, P, P, P, P, P, I32, P], ctypes.c_int),
                 "hashgrid_tune": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),
                 "hashgrid_tune_get": ([ctypes.c_int], ctypes.c_int),
@@ -265,6 +267,45 @@ def hashgrid_debug_corners(cfg: HashGridConfig, x: torch.Tensor, stream=None):
     return idx, w
 
 
+def hashgrid_input_grad_workspace_size(cfg: HashGridConfig, n: int) -> int:
+    """Bytes of the level-major stage of an input-gradient call over n points."""
+    out = ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().hashgrid_input_grad_workspace_size(ctypes.byref(c), n, ctypes.byref(out)))
+    return out.value
+
+
+def hashgrid_input_grad(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tensor, dout: torch.Tensor,
+                        dx: torch.Tensor | None = None, workspace="auto", stream=None) -> torch.Tensor:
+    """dL/dx [n, D] (fp32, written) of upstream ``dout`` [n, >= L*F].
+    ``workspace``: a uint8 GPU tensor, "auto" or None (point-major path)."""
+    _points(cfg, x)
+    n = x.shape[0]
+    _dev(table, "table", cfg.torch_table_dtype)
+    if tuple(table.shape) != cfg.table_shape or not table.is_contiguous():
+        raise ValueError(f"table must be a contiguous {cfg.table_shape} tensor")
+    _dev(dout, "dout", torch.float32)
+    if dout.dim() != 2 or dout.shape[0] != n or dout.stride(1) != 1 or dout.shape[1] < cfg.out_features:
+        raise ValueError("dout must be [n, >= L*F] with unit column stride")
+    if dx is None:
+        dx = torch.empty((n, cfg.n_dims), device=x.device, dtype=torch.float32)
+    _dev(dx, "dx", torch.float32)
+    if tuple(dx.shape) != (n, cfg.n_dims) or not dx.is_contiguous():
+        raise ValueError(f"dx must be a contiguous [n, {cfg.n_dims}] tensor")
+
+    def alloc():
+        if not n:
+            return None
+        return torch.empty(hashgrid_input_grad_workspace_size(cfg, n), dtype=torch.uint8, device=x.device)
+
+    ws_ptr, ws_bytes, _keep = _workspace(workspace, alloc, "workspace")
+    c = cfg.c()
+    _check(load_library().hashgrid_input_grad(ctypes.byref(c), x.data_ptr(), n, table.data_ptr(), dout.data_ptr(),
+                                              dout.stride(0), dx.data_ptr(), ws_ptr, ws_bytes,
+                                              _stream(x, stream)))
+    return dx
+
+
 def hashgrid_adam_step(param: torch.Tensor, m: torch.Tensor, v: torch.Tensor, grad: torch.Tensor, *,
                        lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
                        param_f16: torch.Tensor | None = None, zero_grad: bool = False, stream=None) -> None:
@@ -329,36 +370,43 @@ def hashgrid_tune_get(key: int) -> int:
 
 
 class HashGridFunction(torch.autograd.Function):
-    """Autograd wrapper: forward through hashgrid_forward, table gradient through
-    hashgrid_backward into a zeroed fp32 buffer.  No gradient flows to x."""
+    """Autograd wrapper: forward through hashgrid_forward; the table gradient
+    through hashgrid_backward into a zeroed fp32 buffer and, when x requires
+    grad, dL/dx through hashgrid_input_grad."""
 
     @staticmethod
     def forward(ctx, x, table, cfg):
         ctx.cfg = cfg
-        ctx.save_for_backward(x)
-        return hashgrid_forward(cfg, x.contiguous(), table.contiguous())
+        x, table = x.contiguous(), table.contiguous()
+        ctx.save_for_backward(x, table)
+        return hashgrid_forward(cfg, x, table)
 
     @staticmethod
     def backward(ctx, dout):
-        (x,) = ctx.saved_tensors
+        x, table = ctx.saved_tensors
         cfg = ctx.cfg
-        grad = torch.zeros(cfg.table_shape, device=x.device, dtype=torch.float32)
-        hashgrid_backward(cfg, x, dout.contiguous(), grad)
-        if cfg.table_dtype == "f16":
-            grad = grad.to(torch.float16)
-        return None, grad, None
+        dout = dout.contiguous()
+        dx = grad = None
+        if ctx.needs_input_grad[0]:
+            dx = hashgrid_input_grad(cfg, x, table, dout)
+        if ctx.needs_input_grad[1]:
+            grad = torch.zeros(cfg.table_shape, device=x.device, dtype=torch.float32)
+            hashgrid_backward(cfg, x, dout, grad)
+            if cfg.table_dtype == "f16":
+                grad = grad.to(torch.float16)
+        return dx, grad, None
 
 
 class HashGridEncoder(torch.nn.Module):
     """Multiresolution hash-grid encoder with the pages' constructor arguments
-    (ipipp.com HashGridEncoder): ``forward(x [N, 3]) -> [N, L*F]``.  The L
+    (ipipp.com HashGridEncoder): ``forward(x [N, D]) -> [N, L*F]`` (D = 3 by default).  The L
     tables live in one [L, T, F] parameter initialised uniform(-1e-4, 1e-4)."""
 
     def __init__(self, n_levels=16, n_features_per_level=2, log2_hashmap_size=19,
-                 base_resolution=16, finest_resolution=512, table_dtype="f32", device="cuda"):
+                 base_resolution=16, finest_resolution=512, table_dtype="f32", device="cuda", n_dims=3):
         super().__init__()
         self.cfg = HashGridConfig(n_levels, n_features_per_level, log2_hashmap_size,
-                                  base_resolution, finest_resolution, table_dtype)
+                                  base_resolution, finest_resolution, table_dtype, n_dims=n_dims)
         self.resolutions = hashgrid_resolutions(self.cfg)
         t = torch.empty(self.cfg.table_shape, dtype=torch.float32, device=device).uniform_(-1e-4, 1e-4)
         self.embeddings = torch.nn.Parameter(t.to(self.cfg.torch_table_dtype))

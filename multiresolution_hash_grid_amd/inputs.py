@@ -123,8 +123,8 @@ def normal_f32(seed: int, stream: int, count: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- shapes
 
-def points_uniform(seed: int, n: int) -> np.ndarray:
-    return uniform_f32(seed, STREAM_POINTS, 3 * n).reshape(n, 3)
+def points_uniform(seed: int, n: int, dims: int = 3) -> np.ndarray:
+    return uniform_f32(seed, STREAM_POINTS, dims * n).reshape(n, dims)
 
 
 def table_uniform(seed: int, n_levels: int, table_size: int, n_features: int,
@@ -214,6 +214,7 @@ class Workload:
     n_rays: int = 0
     samples_per_ray: int = 0
     mlp: tuple = field(default=())
+    n_dims: int = 3
 
     @property
     def table_size(self) -> int:
@@ -249,7 +250,7 @@ def resized(w: Workload, n_points: int | None = None, **kw) -> Workload:
 def make_points(w: Workload) -> np.ndarray:
     if w.structure == "rays":
         return points_rays(w.seed, w.n_rays, w.samples_per_ray)
-    return points_uniform(w.seed, w.n_points)
+    return points_uniform(w.seed, w.n_points, w.n_dims)
 
 
 def make_table(w: Workload) -> np.ndarray:

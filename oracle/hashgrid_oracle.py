@@ -87,7 +87,7 @@ def grid(n_levels, n_features, log2_table_size, base_resolution, finest_resoluti
 def grid_of(w) -> OracleGrid:
     """Grid of a workload from the shared input module."""
     return grid(w.n_levels, w.n_features, w.log2_table_size, w.base_resolution,
-                w.finest_resolution, w.table_dtype)
+                w.finest_resolution, w.table_dtype, n_dims=getattr(w, "n_dims", 3))
 
 
 def resolutions(n_levels: int, base_resolution: int, finest_resolution: int) -> np.ndarray:

@@ -203,3 +203,21 @@ def test_adam_argument_errors(lib):
                 B._Adam(1e-2, 0.9, -0.1, 1e-8, 1), B._Adam(float("nan"), 0.9, 0.999, 1e-8, 1),
                 B._Adam(1e-2, 0.9, 0.999, -1.0, 1)):
         assert lib.hashgrid_adam_step(ctypes.byref(bad), 0, None, None, None, None, None, 0, None) == B.HG_EINVAL
+
+
+def test_input_grad_workspace_and_argument_errors(lib):
+    cfg = hg.HashGridConfig()
+    assert hg.hashgrid_input_grad_workspace_size(cfg, 1 << 18) == 16 * 3 * 4 << 18
+    assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=2, n_features=4), 10) == 1280  # 16*10*2*4
+    assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=1, n_levels=1), 3) == 256    # 12 -> 256
+    c = cfg.c()
+    # n == 0 is a no-op; NULL points / dout / dx are rejected before any launch
+    assert lib.hashgrid_input_grad(ctypes.byref(c), None, 0, None, None, 32, None, None, 0, None) == B.HG_OK
+    assert lib.hashgrid_input_grad(ctypes.byref(c), None, 4, None, None, 32, None, None, 0, None) == B.HG_EINVAL
+
+
+@pytest.mark.parametrize("D,F", [(1, 1), (2, 2), (2, 8), (4, 4), (3, 8)])
+def test_other_shapes_are_accepted(lib, D, F):
+    cfg = hg.HashGridConfig(n_dims=D, n_features=F)
+    assert hg.hashgrid_resolutions(cfg)[0] == 16
+    assert hg.hashgrid_input_grad_workspace_size(cfg, 64) == 16 * 64 * D * 4

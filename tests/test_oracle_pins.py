@@ -407,3 +407,55 @@ def test_input_grad_half_table_equals_widened_float_table(oracle):
                                       w.finest_resolution, "f16"), x, t16, dout)
     b = oracle.input_grad(oracle.grid_of(w), x, t16.astype(np.float32), dout)
     assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------------------- other shapes
+
+@pytest.mark.parametrize("dims", [1, 2, 4])
+def test_hash_of_other_dimensions_uses_page_primes(oracle, page, dims):
+    # jsqmd.com HashEncoding hashes d coordinates with the first d entries of its prime list.
+    primes = page["primes_7d"]["values"][:dims]
+    log2T = 16
+    N = 8
+    g = oracle.grid(1, 1, log2T, N, N, n_dims=dims)
+    rng = np.random.default_rng(dims)
+    v = rng.integers(0, N, size=(500, dims))
+    idx, _ = oracle.corners(g, (v / N).astype(np.float32))
+    for p in range(len(v)):
+        h = 0
+        for d in range(dims):
+            h ^= int(v[p, d]) * primes[d]
+        assert int(idx[p, 0, 0]) == h % (1 << log2T)
+
+
+@pytest.mark.parametrize("dims,F", [(2, 4), (4, 1), (1, 8)])
+def test_other_shapes_match_library_interpolation(oracle, dims, F):
+    # As the 3-D test: the dense vertex grid read back at vertex points, then
+    # scipy's N-dimensional linear RegularGridInterpolator at the fp32 position.
+    g = oracle.grid(3, F, 12, 4, 16, n_dims=dims)
+    t = np.random.default_rng(dims + F).uniform(-1, 1, (3, 1 << 12, F)).astype(np.float32)
+    res = oracle.resolutions(3, 4, 16)
+    x = I.points_uniform(13, 800, dims)
+    out = oracle.forward(g, x, t)
+    for l, N in enumerate(res):
+        ax = np.arange(N + 1)
+        v = np.stack(np.meshgrid(*([ax] * dims), indexing="ij"), -1).reshape(-1, dims)
+        G = oracle.forward(g, (v / N).astype(np.float32), t)[:, F * l:F * l + F]
+        G = G.reshape(*([N + 1] * dims), F)
+        pos = (x * np.float32(N)).astype(np.float64)
+        ref = RegularGridInterpolator(tuple([ax] * dims), G, method="linear")(pos)
+        assert np.max(np.abs(out[:, F * l:F * l + F] - ref)) <= 1e-14
+
+
+@pytest.mark.parametrize("dims,F", [(2, 1), (4, 8)])
+def test_other_shapes_constant_table_and_adjoint(oracle, dims, F):
+    g = oracle.grid(4, F, 10, 4, 32, n_dims=dims)
+    x = I.points_uniform(17, 700, dims)
+    const = np.full((4, 1 << 10, F), -0.625, dtype=np.float32)
+    assert np.max(np.abs(oracle.forward(g, x, const) + 0.625)) < 1e-15
+    rng = np.random.default_rng(dims * F)
+    t = rng.uniform(-1, 1, (4, 1 << 10, F)).astype(np.float32)
+    dout = rng.standard_normal((700, 4 * F)).astype(np.float32)
+    lhs = float(np.sum(dout.astype(np.float64) * oracle.forward(g, x, t)))
+    rhs = float(np.sum(oracle.backward(g, x, dout) * t.astype(np.float64)))
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))

@@ -1,0 +1,124 @@
+"""GPU parity of the other grid shapes (input dimension D in 1..4, F in
+{1, 2, 4, 8} features per entry; jsqmd.com HashEncoding sections 3 and 4)
+and of the gradient with respect to the points, against the CPU oracle.
+
+Bars as for the standard grid: corner indices bit-exact; forward
+<= 1e-6 * max|table| (fp32; fp16 tables are widened exactly, so the same bar
+holds and the 1e-3 relative bound with it); backward <= 1e-5 * max|oracle
+gradient| per level.  dL/dx (not bounded on the pages): its fp32 sum of
+2^D signed products per level rounds to ~1e-7 of the sum of their
+magnitudes, which for these tables is within a few times |dL/dx|, so the
+bar is <= 1e-5 * max|oracle dL/dx| per coordinate."""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import multiresolution_hash_grid_amd as hg  # noqa: E402
+from multiresolution_hash_grid_amd import inputs as I  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _threads(oracle):
+    oracle.set_threads(min(16, os.cpu_count() or 1))
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def shape_workload(D, F, dtype, n=3 * 1024 + 77, L=8, log2T=14, nmin=4, nmax=128):
+    return I.Workload(f"d{D}f{F}{dtype}", L, F, log2T, nmin, nmax, dtype, n, "uniform",
+                      seed=2000 + 10 * D + F, n_dims=D)
+
+
+SHAPES = [(1, 2, "f32"), (2, 1, "f32"), (2, 2, "f16"), (2, 4, "f32"), (3, 1, "f32"), (3, 4, "f32"),
+          (3, 8, "f16"), (3, 8, "f32"), (4, 2, "f32"), (4, 4, "f16"), (4, 8, "f32")]
+
+
+def input_grad_check(dx, ref):
+    for d in range(ref.shape[1]):
+        scale = float(np.max(np.abs(ref[:, d])))
+        err = float(np.max(np.abs(dx[:, d].astype(np.float64) - ref[:, d])))
+        assert err <= 1e-5 * scale, f"coordinate {d}: dL/dx err {err:.3g} > 1e-5 * {scale:.3g}"
+
+
+@pytest.mark.parametrize("D,F,dtype", SHAPES)
+def test_shape_forward_backward_corners(oracle, D, F, dtype):
+    w = shape_workload(D, F, dtype)
+    cfg = hg.HashGridConfig.of(w)
+    g = oracle.grid_of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    # forward
+    out = hg.hashgrid_forward(cfg, dev(x), dev(t)).cpu().numpy()
+    ref = oracle.forward(g, x, t)
+    tmax = float(np.max(np.abs(t.astype(np.float64))))
+    assert float(np.max(np.abs(out - ref))) <= 1e-6 * tmax
+    # backward (accumulates into a non-zero buffer)
+    base = np.random.default_rng(D * 10 + F).uniform(-1, 1, cfg.table_shape).astype(np.float32)
+    grad = dev(base)
+    hg.hashgrid_backward(cfg, dev(x), dev(d), grad)
+    gref = oracle.backward(g, x, d)
+    got = grad.cpu().numpy().astype(np.float64) - base
+    for l in range(w.n_levels):
+        assert np.max(np.abs(got[l] - gref[l])) <= 1e-5 * np.max(np.abs(gref[l])) + 4e-7
+    # corners
+    idx, wt = hg.hashgrid_debug_corners(cfg, dev(x))
+    ridx, rw = oracle.corners(g, x)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ridx)
+    assert np.max(np.abs(wt.cpu().numpy() - rw)) <= 2.5e-7
+
+
+@pytest.mark.parametrize("D,F,dtype", SHAPES + [(3, 2, "f32"), (3, 2, "f16")])
+def test_shape_input_grad(oracle, D, F, dtype):
+    w = shape_workload(D, F, dtype)
+    cfg = hg.HashGridConfig.of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    ref = oracle.input_grad(oracle.grid_of(w), x, t, d)
+    staged = hg.hashgrid_input_grad(cfg, dev(x), dev(t), dev(d)).cpu().numpy()
+    direct = hg.hashgrid_input_grad(cfg, dev(x), dev(t), dev(d), workspace=None).cpu().numpy()
+    input_grad_check(staged, ref)
+    assert np.array_equal(staged, direct)  # same fp32 terms in the same level order
+
+
+@pytest.mark.parametrize("name,n", [("standard", None), ("ray", 1 << 18), ("large_f16", 1 << 16)])
+def test_input_grad_workloads(oracle, name, n):
+    w = I.WORKLOADS[name] if n is None else I.resized(I.WORKLOADS[name], n)
+    cfg = hg.HashGridConfig.of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    ref = oracle.input_grad(oracle.grid_of(w), x, t, d)
+    input_grad_check(hg.hashgrid_input_grad(cfg, dev(x), dev(t), dev(d)).cpu().numpy(), ref)
+
+
+def test_input_grad_strided_upstream_and_ragged(oracle):
+    w = I.resized(I.WORKLOADS["standard"], 1000 + 3)
+    cfg = hg.HashGridConfig.of(w)
+    x, t = I.make_points(w), I.make_table(w)
+    wide = I.dout_normal(77, w.n_points, 40)          # rows of 40 values, the first 32 used
+    ref = oracle.input_grad(oracle.grid_of(w), x, t, wide)
+    got = hg.hashgrid_input_grad(cfg, dev(x), dev(t), dev(wide)).cpu().numpy()
+    input_grad_check(got, ref)
+    empty = torch.empty((0, 3), device=DEV)
+    assert hg.hashgrid_input_grad(cfg, empty, dev(t), torch.empty((0, 32), device=DEV)).shape == (0, 3)
+
+
+def test_autograd_gives_point_and_table_gradients(oracle):
+    w = I.resized(I.WORKLOADS["standard"], 2000)
+    enc = hg.HashGridEncoder(device=DEV)
+    t = I.make_table(w)
+    with torch.no_grad():
+        enc.embeddings.copy_(dev(t))
+    x = dev(I.make_points(w)).requires_grad_(True)
+    d = I.make_dout(w)
+    enc(x).backward(dev(d))
+    g = oracle.grid_of(w)
+    input_grad_check(x.grad.cpu().numpy(), oracle.input_grad(g, I.make_points(w), t, d))
+    ref = oracle.backward(g, I.make_points(w), d)
+    got = enc.embeddings.grad.cpu().numpy()
+    for l in range(w.n_levels):
+        assert np.max(np.abs(got[l] - ref[l])) <= 1e-5 * np.max(np.abs(ref[l]))
