@@ -134,6 +134,41 @@ def measure_shapes(dev, n: int, iters: int) -> dict:
     return out
 
 
+def measure_fused_mlp(dev, iters: int) -> dict:
+    """Encoder + MLP head (2^22 uniform points, standard grid with binary16
+    tables, 32-64-64-4): forward = binary16 encoding stage + head, backward =
+    head backward + weight-gradient reduction + table backward.  Algorithmic
+    bytes per point: forward 12 (x) + 8 L F 2 (binary16 corners) + 16 (y);
+    backward 12 (x) + 16 (dL/dy) + 2 L F (the stage) + 8 L F 4 (table
+    gradient additions)."""
+    import torch
+    import multiresolution_hash_grid_amd as hg
+    from multiresolution_hash_grid_amd import inputs
+    w = inputs.WORKLOADS["fused_mlp"]
+    cfg = hg.HashGridConfig.of(w)
+    n = w.n_points
+    x = torch.from_numpy(inputs.make_points(w)).to(dev)
+    t = torch.from_numpy(inputs.make_table(w)).to(dev)
+    P = [torch.from_numpy(a).to(dev) for a in inputs.mlp_params(w.seed, bias_scale=0.1)]
+    dy = torch.from_numpy(inputs.dout_normal(w.seed + 7, n, 4)).to(dev)
+    st_bytes, bw_bytes = hg.hashgrid_mlp_workspace_size(cfg, n)
+    stage = torch.empty(st_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(bw_bytes, dtype=torch.uint8, device=dev)
+    y = torch.empty((n, 4), device=dev)
+    grads = [torch.zeros(hg.hashgrid.MLP_SHAPES[k], device=dev) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+    dtable = torch.zeros(cfg.table_shape, device=dev)
+    fms = time_calls(lambda: hg.hashgrid_mlp_forward(cfg, x, t, P, y=y, stage=stage), iters)
+    bms = time_calls(lambda: hg.hashgrid_mlp_backward(cfg, x, stage, P, dy, grads, dtable, workspace=ws), iters)
+    L, F = cfg.n_levels, cfg.n_features
+    fb = 12 + 8 * L * F * 2 + 16
+    bb = 12 + 16 + 2 * L * F + 8 * L * F * 4
+    return {"points": n, "fwd_points_per_s": n / (fms * 1e-3), "bwd_points_per_s": n / (bms * 1e-3),
+            "step_points_per_s": n / ((fms + bms) * 1e-3), "fwd_us": fms * 1e3, "bwd_us": bms * 1e3,
+            "algorithmic_bytes_per_point": {"fwd": fb, "bwd": bb},
+            "fwd_frac": fb * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(w, x, t, d, budget_s: float) -> dict:
     """The CPU oracle, as it stands, on the same workload: forward + backward of
     all points, repeated until about `budget_s` seconds of work."""
@@ -263,7 +298,8 @@ def main() -> int:
     # The table optimizer step that follows the backward (Adam over the tables).
     result["next"] = {"adam": measure_adam(cfg, dev, 50),
                       "input_grad": measure_input_grad(cfg, x, t, d, 20),
-                      "shapes": measure_shapes(dev, w.n_points, 10)}
+                      "shapes": measure_shapes(dev, w.n_points, 10),
+                      "fused_mlp": measure_fused_mlp(dev, 5)}
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x_h, t_h, d_h, args.cpu_seconds)

@@ -159,6 +159,62 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
 int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint32_t *idx,
                            float *w, void *stream);
 
+/* MLP head after the encoder: the NeRFace head of ipipp.com (section 3
+ * listing), Linear(32, 64), ReLU, Linear(64, 64), ReLU, Linear(64, 4) with
+ * biases,  y = W3 relu(W2 relu(W1 e + b1) + b2) + b3,  where e is the 32-wide
+ * encoding of a point (grids with D = 3, F = 2, L = 16).  It runs on the
+ * matrix cores: binary16 operands (the encoding, the hidden activations and,
+ * in the backward, dL/dy and the pre-activation gradients are rounded to
+ * binary16 where they enter a product), fp32 accumulation.  The encoding is
+ * computed once, in the forward, into a binary16 stage the backward reuses.
+ * Weights are binary16 [out][in] (nn.Linear layout), biases fp32. */
+typedef struct {
+    const void *w1;  /* binary16 [64][32], 8-byte aligned  */
+    const float *b1; /* [64]                               */
+    const void *w2;  /* binary16 [64][64]                   */
+    const float *b2; /* [64]                               */
+    const void *w3;  /* binary16 [4][64]                    */
+    const float *b3; /* [4]                                */
+} hg_mlp_params;
+
+/* fp32 gradients of the weights and biases, same shapes; ACCUMULATED. */
+typedef struct {
+    float *dw1, *db1, *dw2, *db2, *dw3, *db3;
+} hg_mlp_grads;
+
+/* Workspace sizes of the MLP head over n points (HOST size_t outputs):
+ *   *stage_bytes_out : the binary16 encoding stage, n * 64 bytes (rounded);
+ *                      written by hashgrid_mlp_forward, read by the backward;
+ *   *bwd_bytes_out   : the backward's workspace: dL/de (n * 128 bytes), the
+ *                      per-wave weight-gradient partials, and the binned table
+ *                      backward's workspace.
+ * Errors: HG_EINVAL, HG_EUNSUPPORTED (a grid other than D = 3, L * F = 32). */
+int hashgrid_mlp_workspace_size(const hg_config *cfg, int64_t n, size_t *stage_bytes_out, size_t *bwd_bytes_out);
+
+/* Forward of encoder + MLP head: y [n][4] fp32 (16-byte aligned), WRITTEN.
+ *   x, table : as hashgrid_forward.
+ *   stage    : device buffer of stage_bytes >= n * 64 (256-byte aligned) that
+ *              receives the binary16 encoding [L][n][2]; keep it for the
+ *              backward.
+ * Errors: as hashgrid_forward, plus HG_EINVAL for parameter pointers. */
+int hashgrid_mlp_forward(const hg_config *cfg, const float *x, int64_t n, const void *table,
+                         const hg_mlp_params *params, float *y, void *stage, size_t stage_bytes, void *stream);
+
+/* Backward of encoder + MLP head for upstream dy = dL/dy [n][4] fp32
+ * (16-byte aligned): adds the weight and bias gradients into *grads and the
+ * table gradient into dtable ([L][T][F] fp32, as hashgrid_backward).
+ *   stage     : the stage the forward of the same x, table and params wrote.
+ *   workspace : hashgrid_mlp_workspace_size's bwd bytes (256-byte aligned);
+ *               at least the dL/de rows and partials are required, and with
+ *               less than the full size the table gradient takes the smaller
+ *               binned groups or the atomic scatter, as in hashgrid_backward.
+ * The weight gradients are summed per wave in registers and the wave
+ * partials added in a fixed order: results do not depend on scheduling.
+ * Errors: as hashgrid_backward. */
+int hashgrid_mlp_backward(const hg_config *cfg, const float *x, int64_t n, const void *stage,
+                          const hg_mlp_params *params, const float *dy, const hg_mlp_grads *grads, float *dtable,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace that let hashgrid_input_grad stage per-level
  * partial sums level-major: L * n * D * 4, rounded up to 256.  *bytes_out is
  * a HOST size_t.  Errors: HG_EINVAL, HG_EUNSUPPORTED. */

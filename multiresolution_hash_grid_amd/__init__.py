@@ -10,6 +10,8 @@ from .hashgrid import (  # noqa: F401
     HashGridEncoder,
     HashGridError,
     HashGridFunction,
+    HashGridMLP,
+    HashGridMLPFunction,
     abi_version,
     backward_workspace,
     hashgrid_adam_step,
@@ -20,6 +22,9 @@ from .hashgrid import (  # noqa: F401
     hashgrid_forward,
     hashgrid_forward_workspace_size,
     hashgrid_input_grad,
+    hashgrid_mlp_backward,
+    hashgrid_mlp_forward,
+    hashgrid_mlp_workspace_size,
     hashgrid_input_grad_workspace_size,
     hashgrid_resolutions,
     hashgrid_tune,

@@ -138,12 +138,16 @@ bool standard_shape(const hg_config &c) { return c.n_dims == 3 && c.n_features =
 // Levels per binned group: as many as keep one group's records (written by
 // the bin kernel, read back by the accumulate kernel right after) within the
 // budget, so that they can stay in the 256 MB last-level cache of the
-// MI355X; groups are then made equal.
+// MI355X -- but at least enough levels for 512 accumulate workgroups (two per
+// CU), which large batches need more than cache residency; groups are then
+// made equal.
 int binned_group(const hg::BinParams &bp, int n_levels) {
     if (g_tune.bwd_group_mib <= 0) return n_levels;
     const size_t rec_bytes = (size_t)bp.level_records * 16;
     const size_t budget = (size_t)g_tune.bwd_group_mib << 20;
-    const int cap = (int)std::max<size_t>(1, std::min<size_t>(n_levels, budget / std::max<size_t>(rec_bytes, 1)));
+    const int fill = (512 + bp.parts - 1) / bp.parts;
+    const int cap = (int)std::min<size_t>(
+        n_levels, std::max<size_t>({(size_t)1, (size_t)fill, budget / std::max<size_t>(rec_bytes, 1)}));
     const int ngroups = (n_levels + cap - 1) / cap;
     return (n_levels + ngroups - 1) / ngroups;
 }
@@ -158,6 +162,60 @@ int check_points(int64_t n, const float *x) {
 int launch_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(HG_EHIP, "%s launch failed: %s", what, hipGetErrorString(e));
     return ok();
+}
+
+// The table gradient of upstream rows dout (validated by the caller).
+int table_backward(const hg_config *cfg, const float *x, int64_t n, const float *dout, int64_t dout_row_stride,
+                   float *dtable, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc;
+    hg::BinParams bp;
+    if (g_tune.bwd_binned && workspace && aligned(dtable, 16) && plan_binned(*cfg, n, bp)) {
+        const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
+        if (workspace_bytes >= per_level) {
+            // Whole levels per group; the launcher splits the workspace itself.
+            const size_t usable = workspace_bytes / per_level * hg::binned_level_bytes(bp);
+            return launch_status(hg::launch_binned_backward(bp, cfg->n_levels, binned_group(bp, cfg->n_levels), x,
+                                                            n, dout, dout_row_stride, dtable, workspace, usable,
+                                                            (hipStream_t)stream),
+                                 "binned backward");
+        }
+    }
+    hg::LaunchParams lp;
+    if ((rc = plan(*cfg, n, lp))) return rc;
+    if (!standard_shape(*cfg))
+        return launch_status(hg::launch_backward_generic(lp, cfg->n_dims, cfg->n_features, x, n, dout,
+                                                         dout_row_stride, dtable, (hipStream_t)stream),
+                             "backward");
+    return launch_status(hg::launch_backward(lp, x, n, dout, dout_row_stride, dtable, g_tune.bwd_lanes,
+                                             (hipStream_t)stream),
+                         "backward");
+}
+
+// Binned-backward workspace of n points: (bytes for the default level groups, one level's bytes).
+void table_backward_workspace(const hg_config &c, int64_t n, size_t &full, size_t &least) {
+    hg::BinParams bp;
+    full = least = 0;
+    if (n > 0 && plan_binned(c, n, bp)) {
+        least = round_up(hg::binned_level_bytes(bp), 256);
+        full = least * (size_t)binned_group(bp, c.n_levels);
+    }
+}
+
+bool mlp_shape(const hg_config &c) { return standard_shape(c) && c.n_levels * c.n_features == 32; }
+
+int check_mlp_params(const hg_mlp_params *mp) {
+    if (!mp) return fail(HG_EINVAL, "params is NULL");
+    if (!mp->w1 || !mp->w2 || !mp->w3 || !mp->b1 || !mp->b2 || !mp->b3)
+        return fail(HG_EINVAL, "every weight and bias must be a device pointer");
+    if (!aligned(mp->w1, 8) || !aligned(mp->w2, 8) || !aligned(mp->w3, 8) || !aligned(mp->b1, 4) ||
+        !aligned(mp->b2, 4) || !aligned(mp->b3, 4))
+        return fail(HG_EINVAL, "weights must be 8-byte and biases 4-byte aligned");
+    return HG_OK;
+}
+
+hg::MlpParams mlp_params(const hg_mlp_params *mp) {
+    return hg::MlpParams{(const _Float16 *)mp->w1, (const _Float16 *)mp->w2, (const _Float16 *)mp->w3,
+                         mp->b1, mp->b2, mp->b3};
 }
 
 }  // namespace
@@ -218,15 +276,10 @@ int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *by
     if (rc) return rc;
     if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
     if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
-    hg::BinParams bp;
-    size_t per_level = 0;
-    int group = 0;
-    if (n > 0 && plan_binned(*cfg, n, bp)) {
-        per_level = round_up(hg::binned_level_bytes(bp), 256);
-        group = binned_group(bp, cfg->n_levels);
-    }
-    *bytes_out = per_level * (size_t)group;
-    if (min_bytes_out) *min_bytes_out = per_level;
+    size_t full, least;
+    table_backward_workspace(*cfg, n, full, least);
+    *bytes_out = full;
+    if (min_bytes_out) *min_bytes_out = least;
     return ok();
 }
 
@@ -242,27 +295,75 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
     if (dout_row_stride < (int64_t)cfg->n_levels * cfg->n_features)
         return fail(HG_EINVAL, "dout_row_stride %lld < L*F", (long long)dout_row_stride);
     if (workspace && !aligned(workspace, 256)) return fail(HG_EINVAL, "workspace is not 256-byte aligned");
-    hg::BinParams bp;
-    if (g_tune.bwd_binned && workspace && aligned(dtable, 16) && plan_binned(*cfg, n, bp)) {
-        const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
-        if (workspace_bytes >= per_level) {
-            // Whole levels per group; the launcher splits the workspace itself.
-            const size_t usable = workspace_bytes / per_level * hg::binned_level_bytes(bp);
-            return launch_status(hg::launch_binned_backward(bp, cfg->n_levels, binned_group(bp, cfg->n_levels), x,
-                                                            n, dout, dout_row_stride,
-                                                            dtable, workspace, usable, (hipStream_t)stream),
-                                 "binned backward");
-        }
-    }
+    return table_backward(cfg, x, n, dout, dout_row_stride, dtable, workspace, workspace_bytes, stream);
+}
+
+int hashgrid_mlp_workspace_size(const hg_config *cfg, int64_t n, size_t *stage_bytes_out, size_t *bwd_bytes_out) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!mlp_shape(*cfg)) return fail(HG_EUNSUPPORTED, "the MLP head takes the 32 features of D = 3, L*F = 32 grids");
+    if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
+    if (!stage_bytes_out || !bwd_bytes_out) return fail(HG_EINVAL, "output pointers must be non-NULL");
+    *stage_bytes_out = round_up((size_t)n * 32 * 2, 256);
+    size_t full, least;
+    table_backward_workspace(*cfg, n, full, least);
+    *bwd_bytes_out = n ? round_up((size_t)n * 32 * 4, 256) + round_up(hg::mlp_partials_bytes(n), 256) + full : 0;
+    return ok();
+}
+
+int hashgrid_mlp_forward(const hg_config *cfg, const float *x, int64_t n, const void *table,
+                         const hg_mlp_params *params, float *y, void *stage, size_t stage_bytes, void *stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!mlp_shape(*cfg)) return fail(HG_EUNSUPPORTED, "the MLP head takes the 32 features of D = 3, L*F = 32 grids");
+    if (n == 0) return ok();
+    if ((rc = check_points(n, x))) return rc;
+    if ((rc = check_mlp_params(params))) return rc;
+    const size_t esize = cfg->table_dtype == HG_F32 ? 4 : 2;
+    if (!table || !aligned(table, esize * 2)) return fail(HG_EINVAL, "table is NULL or misaligned");
+    if (!y || !aligned(y, 16)) return fail(HG_EINVAL, "y is NULL or not 16-byte aligned");
+    if (!stage || !aligned(stage, 256) || stage_bytes < (size_t)n * 64)
+        return fail(HG_EINVAL, "stage must be 256-byte aligned and hold n * 64 bytes");
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
-    if (!standard_shape(*cfg))
-        return launch_status(hg::launch_backward_generic(lp, cfg->n_dims, cfg->n_features, x, n, dout,
-                                                         dout_row_stride, dtable, (hipStream_t)stream),
-                             "backward");
-    return launch_status(hg::launch_backward(lp, x, n, dout, dout_row_stride, dtable, g_tune.bwd_lanes,
-                                             (hipStream_t)stream),
-                         "backward");
+    hipError_t e = hg::launch_encode_stage_f16(lp, x, n, table, cfg->table_dtype, (_Float16 *)stage,
+                                               (hipStream_t)stream);
+    if (e != hipSuccess) return launch_status(e, "encode stage");
+    return launch_status(hg::launch_mlp_forward((const _Float16 *)stage, n, mlp_params(params), y,
+                                                (hipStream_t)stream),
+                         "mlp forward");
+}
+
+int hashgrid_mlp_backward(const hg_config *cfg, const float *x, int64_t n, const void *stage,
+                          const hg_mlp_params *params, const float *dy, const hg_mlp_grads *grads, float *dtable,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!mlp_shape(*cfg)) return fail(HG_EUNSUPPORTED, "the MLP head takes the 32 features of D = 3, L*F = 32 grids");
+    if (n == 0) return ok();
+    if ((rc = check_points(n, x))) return rc;
+    if ((rc = check_mlp_params(params))) return rc;
+    if (!stage || !aligned(stage, 256)) return fail(HG_EINVAL, "stage is NULL or not 256-byte aligned");
+    if (!dy || !aligned(dy, 16)) return fail(HG_EINVAL, "dy is NULL or not 16-byte aligned");
+    if (!grads || !grads->dw1 || !grads->db1 || !grads->dw2 || !grads->db2 || !grads->dw3 || !grads->db3)
+        return fail(HG_EINVAL, "every gradient must be a device pointer");
+    if (!dtable || !aligned(dtable, 4)) return fail(HG_EINVAL, "dtable is NULL or not 4-byte aligned");
+    const size_t de_bytes = round_up((size_t)n * 32 * 4, 256);
+    const size_t part_bytes = round_up(hg::mlp_partials_bytes(n), 256);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < de_bytes + part_bytes)
+        return fail(HG_EINVAL, "workspace must be 256-byte aligned and hold at least n * 128 bytes plus the "
+                               "weight-gradient partials (hashgrid_mlp_workspace_size)");
+    float *de = (float *)workspace;
+    float *partials = (float *)((char *)workspace + de_bytes);
+    const hg::MlpGrads g{grads->dw1, grads->db1, grads->dw2, grads->db2, grads->dw3, grads->db3};
+    hipError_t e = hg::launch_mlp_backward((const _Float16 *)stage, n, mlp_params(params), dy, de, partials, g,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return launch_status(e, "mlp backward");
+    // The encoder's table gradient with dL/de as the upstream rows; the rest of
+    // the workspace goes to the binned backward.
+    const size_t used = de_bytes + part_bytes;
+    void *rest = workspace_bytes > used ? (char *)workspace + used : nullptr;
+    return table_backward(cfg, x, n, de, 32, dtable, rest, workspace_bytes - used, stream);
 }
 
 int hashgrid_input_grad_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out) {

@@ -126,10 +126,10 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_kernel(const float *__restrict_
 // Output element (p, l, j) is out[p * ostride + l * lstride + j]: lstride = 2
 // writes the [n][L*F] rows directly, ostride = 2 with lstride = 2 n writes a
 // level-major [L][n][F] staging array whose stores are fully coalesced.
-template <int DT, int U, bool NT>
+template <int DT, int U, bool NT, typename OutT = float>
 __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__restrict__ x, int64_t n,
                                                              const void *__restrict__ table,
-                                                             float *__restrict__ out, int64_t ostride,
+                                                             OutT *__restrict__ out, int64_t ostride,
                                                              int64_t lstride, LaunchParams lp) {
     Item it;
     if (!decode_item(lp, it)) return;
@@ -175,9 +175,9 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
             // lane 0 keeps feature 0 and needs lane 1's x-half; lane 1 the reverse.
             const float v = (sub ? ry : rx) + swap_pair(sub ? rx : ry);
             if (ok[u]) {
-                float *dst = out + (p0 + (int64_t)u * kPairs) * ostride + (int64_t)l * lstride + sub;
-                if (NT) __builtin_nontemporal_store(v, dst);
-                else *dst = v;
+                OutT *dst = out + (p0 + (int64_t)u * kPairs) * ostride + (int64_t)l * lstride + sub;
+                if constexpr (NT) __builtin_nontemporal_store((OutT)v, dst);
+                else *dst = (OutT)v;  // binary16 stage: round to nearest even
             }
         }
     }
@@ -328,6 +328,16 @@ hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, con
     const unsigned blocks = (unsigned)((n + kTransposePts - 1) / kTransposePts);
     const size_t lds = (size_t)kTransposePts * (2 * lp.n_levels + 1) * sizeof(float);
     transpose_kernel<<<blocks, kBlock, lds, stream>>>(stage, n, lp.n_levels, out, out_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_stage_f16(const LaunchParams &lp, const float *x, int64_t n, const void *table,
+                                   int table_dtype, _Float16 *stage, hipStream_t stream) {
+    dim3 grid(grid_blocks(lp)), block(kBlock);
+    if (table_dtype == 0)
+        fwd_f2_pair_kernel<0, 4, false, _Float16><<<grid, block, 0, stream>>>(x, n, table, stage, 2, 2 * n, lp);
+    else
+        fwd_f2_pair_kernel<1, 4, false, _Float16><<<grid, block, 0, stream>>>(x, n, table, stage, 2, 2 * n, lp);
     return hipGetLastError();
 }
 

@@ -95,6 +95,23 @@ hipError_t launch_input_grad(const LaunchParams &lp, int D, int F, const float *
                              int table_dtype, const float *dout, int64_t dout_stride, float *dx, float *stage,
                              hipStream_t stream);
 
+// MLP head 32 -> 64 -> 64 -> 4 (mlp_kernels.hip).  Weights binary16 [out][in],
+// biases and gradients fp32.
+struct MlpParams {
+    const _Float16 *w1, *w2, *w3;
+    const float *b1, *b2, *b3;
+};
+struct MlpGrads {
+    float *dw1, *db1, *dw2, *db2, *dw3, *db3;
+};
+// Encoding of the standard grid as a binary16 level-major stage [L][n][2].
+hipError_t launch_encode_stage_f16(const LaunchParams &lp, const float *x, int64_t n, const void *table,
+                                   int table_dtype, _Float16 *stage, hipStream_t stream);
+size_t mlp_partials_bytes(int64_t n);
+hipError_t launch_mlp_forward(const _Float16 *stage, int64_t n, const MlpParams &mp, float *y, hipStream_t stream);
+hipError_t launch_mlp_backward(const _Float16 *stage, int64_t n, const MlpParams &mp, const float *dy, float *de,
+                               float *partials, const MlpGrads &g, hipStream_t stream);
+
 struct AdamParams {
     float lr, beta1, beta2, eps;
     int32_t step;

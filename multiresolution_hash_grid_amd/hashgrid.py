@@ -47,6 +47,17 @@ class _Adam(ctypes.Structure):
                 ("eps", ctypes.c_float), ("step", ctypes.c_int32)]
 
 
+class _MlpParams(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+
+
+class _MlpGrads(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in ("dw1", "db1", "dw2", "db2", "dw3", "db3")]
+
+
+MLP_SHAPES = {"w1": (64, 32), "b1": (64,), "w2": (64, 64), "b2": (64,), "w3": (4, 64), "b3": (4,)}
+
+
 @dataclass(frozen=True)
 class HashGridConfig:
     """Grid description; defaults are the pages' standard grid (L=16, F=2,
@@ -114,6 +125,11 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
                 "hashgrid_debug_corners": ([C, P, I64, P, P, P], ctypes.c_int),
                 "hashgrid_input_grad": ([C, P, I64, P, P, I64, P, P, ctypes.c_size_t, P], ctypes.c_int),
                 "hashgrid_input_grad_workspace_size": ([C, I64, P], ctypes.c_int),
+                "hashgrid_mlp_workspace_size": ([C, I64, P, P], ctypes.c_int),
+                "hashgrid_mlp_forward": ([C, P, I64, P, ctypes.POINTER(_MlpParams), P, P, ctypes.c_size_t, P],
+                                         ctypes.c_int),
+                "hashgrid_mlp_backward": ([C, P, I64, P, ctypes.POINTER(_MlpParams), P, ctypes.POINTER(_MlpGrads),
+                                           P, P, ctypes.c_size_t, P], ctypes.c_int),
                 "hashgrid_adam_step": ([ctypes.POINTER(_Adam), I64, P, P, P, P, P, I32, P], ctypes.c_int),
                 "hashgrid_tune": ([ctypes.c_int, ctypes.c_int], ctypes.c_int),
                 "hashgrid_tune_get": ([ctypes.c_int], ctypes.c_int),
@@ -306,6 +322,84 @@ def hashgrid_input_grad(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tenso
     return dx
 
 
+def hashgrid_mlp_workspace_size(cfg: HashGridConfig, n: int) -> tuple:
+    """(binary16 encoding stage bytes, backward workspace bytes) of the MLP head."""
+    st, bw = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    c = cfg.c()
+    _check(load_library().hashgrid_mlp_workspace_size(ctypes.byref(c), n, ctypes.byref(st), ctypes.byref(bw)))
+    return st.value, bw.value
+
+
+def _mlp_params(params) -> _MlpParams:
+    """[w1, b1, w2, b2, w3, b3]: binary16 weights [out][in], fp32 biases, contiguous GPU tensors."""
+    names = ("w1", "b1", "w2", "b2", "w3", "b3")
+    if len(params) != 6:
+        raise ValueError("params must be [w1, b1, w2, b2, w3, b3]")
+    ptrs = []
+    for name, t in zip(names, params):
+        _dev(t, name, torch.float16 if name[0] == "w" else torch.float32)
+        if tuple(t.shape) != MLP_SHAPES[name] or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {MLP_SHAPES[name]} tensor")
+        ptrs.append(t.data_ptr())
+    return _MlpParams(*ptrs)
+
+
+def hashgrid_mlp_forward(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tensor, params,
+                         y: torch.Tensor | None = None, stage: torch.Tensor | None = None, stream=None):
+    """Encoder + MLP head forward.  Returns (y [n, 4] fp32, stage), the stage
+    (uint8, the binary16 encoding) being what hashgrid_mlp_backward needs."""
+    _points(cfg, x)
+    n = x.shape[0]
+    _dev(table, "table", cfg.torch_table_dtype)
+    if tuple(table.shape) != cfg.table_shape or not table.is_contiguous():
+        raise ValueError(f"table must be a contiguous {cfg.table_shape} tensor")
+    mp = _mlp_params(params)
+    st_bytes, _ = hashgrid_mlp_workspace_size(cfg, n)
+    if stage is None:
+        stage = torch.empty(max(st_bytes, 1), dtype=torch.uint8, device=x.device)
+    _dev(stage, "stage", torch.uint8)
+    if y is None:
+        y = torch.empty((n, 4), device=x.device, dtype=torch.float32)
+    _dev(y, "y", torch.float32)
+    if tuple(y.shape) != (n, 4) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [n, 4] tensor")
+    c = cfg.c()
+    _check(load_library().hashgrid_mlp_forward(ctypes.byref(c), x.data_ptr(), n, table.data_ptr(), ctypes.byref(mp),
+                                               y.data_ptr(), stage.data_ptr(), stage.numel(), _stream(x, stream)))
+    return y, stage
+
+
+def hashgrid_mlp_backward(cfg: HashGridConfig, x: torch.Tensor, stage: torch.Tensor, params, dy: torch.Tensor,
+                          grads, dtable: torch.Tensor, workspace="auto", stream=None) -> None:
+    """Accumulate the MLP's weight and bias gradients into ``grads`` ([dw1, db1,
+    dw2, db2, dw3, db3], fp32) and the table gradient into ``dtable``."""
+    _points(cfg, x)
+    n = x.shape[0]
+    mp = _mlp_params(params)
+    _dev(stage, "stage", torch.uint8)
+    _dev(dy, "dy", torch.float32)
+    if tuple(dy.shape) != (n, 4) or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous [n, 4] tensor")
+    names = ("dw1", "db1", "dw2", "db2", "dw3", "db3")
+    if len(grads) != 6:
+        raise ValueError("grads must be [dw1, db1, dw2, db2, dw3, db3]")
+    for name, t in zip(names, grads):
+        _dev(t, name, torch.float32)
+        if tuple(t.shape) != MLP_SHAPES[name[1:]] or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {MLP_SHAPES[name[1:]]} tensor")
+    g = _MlpGrads(*[t.data_ptr() for t in grads])
+    _dev(dtable, "dtable", torch.float32)
+    if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
+        raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
+    ws_ptr, ws_bytes, _keep = _workspace(
+        workspace, lambda: torch.empty(max(1, hashgrid_mlp_workspace_size(cfg, n)[1]), dtype=torch.uint8,
+                                       device=x.device), "workspace")
+    c = cfg.c()
+    _check(load_library().hashgrid_mlp_backward(ctypes.byref(c), x.data_ptr(), n, stage.data_ptr(), ctypes.byref(mp),
+                                                dy.data_ptr(), ctypes.byref(g), dtable.data_ptr(), ws_ptr, ws_bytes,
+                                                _stream(x, stream)))
+
+
 def hashgrid_adam_step(param: torch.Tensor, m: torch.Tensor, v: torch.Tensor, grad: torch.Tensor, *,
                        lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8,
                        param_f16: torch.Tensor | None = None, zero_grad: bool = False, stream=None) -> None:
@@ -413,3 +507,55 @@ class HashGridEncoder(torch.nn.Module):
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         return HashGridFunction.apply(x, self.embeddings, self.cfg)
+
+
+class HashGridMLPFunction(torch.autograd.Function):
+    """Autograd of encoder + MLP head: the forward keeps the binary16 encoding
+    stage, the backward gives the table gradient and the fp32 gradients of the
+    (fp32 master) weights and biases; no gradient flows to x."""
+
+    @staticmethod
+    def forward(ctx, x, table, w1, b1, w2, b2, w3, b3, cfg):
+        x, table = x.contiguous(), table.contiguous()
+        params = [w1.to(torch.float16).contiguous(), b1.float().contiguous(), w2.to(torch.float16).contiguous(),
+                  b2.float().contiguous(), w3.to(torch.float16).contiguous(), b3.float().contiguous()]
+        y, stage = hashgrid_mlp_forward(cfg, x, table, params)
+        ctx.cfg = cfg
+        ctx.save_for_backward(x, stage, *params)
+        ctx.dtypes = [t.dtype for t in (w1, b1, w2, b2, w3, b3)]
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, stage, *params = ctx.saved_tensors
+        cfg = ctx.cfg
+        grads = [torch.zeros(MLP_SHAPES[k], device=x.device) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+        dtable = torch.zeros(cfg.table_shape, device=x.device)
+        hashgrid_mlp_backward(cfg, x, stage, params, dy.contiguous().float(), grads, dtable)
+        if cfg.table_dtype == "f16":
+            dtable = dtable.to(torch.float16)
+        return (None, dtable, *[g.to(dt) for g, dt in zip(grads, ctx.dtypes)], None)
+
+
+class HashGridMLP(torch.nn.Module):
+    """The encoder followed by the NeRFace head of ipipp.com section 3:
+    Linear(32, 64), ReLU, Linear(64, 64), ReLU, Linear(64, 4) with biases;
+    ``forward(x [N, 3]) -> [N, 4]`` (density and colour channels).  Weights
+    are fp32 masters initialised Xavier-uniform, biases zero; the matrix cores
+    read them as binary16."""
+
+    def __init__(self, table_dtype="f16", device="cuda", **encoder_kw):
+        super().__init__()
+        self.encoder = HashGridEncoder(table_dtype=table_dtype, device=device, **encoder_kw)
+        if self.encoder.cfg.out_features != 32:
+            raise ValueError("the MLP head takes 32 encoded features (L * F = 32)")
+        layers = []
+        for fin, fout in ((32, 64), (64, 64), (64, 4)):
+            w = torch.empty((fout, fin), device=device)
+            torch.nn.init.xavier_uniform_(w)
+            layers += [torch.nn.Parameter(w), torch.nn.Parameter(torch.zeros(fout, device=device))]
+        self.w1, self.b1, self.w2, self.b2, self.w3, self.b3 = layers
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return HashGridMLPFunction.apply(x, self.encoder.embeddings, self.w1, self.b1, self.w2, self.b2, self.w3,
+                                         self.b3, self.encoder.cfg)

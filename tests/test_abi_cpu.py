@@ -137,8 +137,12 @@ def test_backward_workspace_size():
     try:
         hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 0)      # one group of all levels
         assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 16, least)
-        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 48)     # 3 levels per group -> 6 groups of 3 (16 = 3*5 + 1)
-        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 3, least)
+        # 48 MiB holds 3 levels, but a group keeps at least 512 / 128 partitions = 4
+        # levels so that the accumulate grid fills the chip: 4 groups of 4.
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 48)
+        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 4, least)
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 96)     # 6 levels -> groups 6 + 6 + 4, sized for 6
+        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 6, least)
     finally:
         hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, old)
     assert least >= 64 * (1 << 18) and least < 64 * (1 << 18) + (1 << 20)
