@@ -198,6 +198,9 @@ def main() -> int:
     ap.add_argument("--workload", default="standard")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--section", choices=("all", "main", "next"), default="all",
+                    help="main: the standard fwd+bwd step only; next: only the figures of the "
+                         "optimizer, input-gradient, shape and MLP-head paths (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -229,6 +232,13 @@ def main() -> int:
     def step():
         hg.hashgrid_forward(cfg, x, t, out=out, workspace=fws)
         hg.hashgrid_backward(cfg, x, d, grad, workspace=ws)
+
+    if args.section == "next":
+        print(json.dumps({"next": {"adam": measure_adam(cfg, dev, 50),
+                                   "input_grad": measure_input_grad(cfg, x, t, d, 20),
+                                   "shapes": measure_shapes(dev, w.n_points, 10),
+                                   "fused_mlp": measure_fused_mlp(dev, 5)}}), flush=True)
+        return 0
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -295,11 +305,14 @@ def main() -> int:
         "roofline_fwd_frac": bpp["fwd"] * w.n_points / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline_fwd_bwd_frac": (bpp["fwd"] + bpp["bwd"]) * w.n_points * K / elapsed / 1e9 / HBM_PEAK_GBS,
     }
-    # The table optimizer step that follows the backward (Adam over the tables).
-    result["next"] = {"adam": measure_adam(cfg, dev, 50),
-                      "input_grad": measure_input_grad(cfg, x, t, d, 20),
-                      "shapes": measure_shapes(dev, w.n_points, 10),
-                      "fused_mlp": measure_fused_mlp(dev, 5)}
+    # The paths after the encoder's own step: Adam over the tables, dL/dx,
+    # other grid shapes, the MLP head.
+    if args.section in ("all", "next"):
+        print("[bench] optimizer, input gradient, shapes, MLP head", file=sys.stderr, flush=True)
+        result["next"] = {"adam": measure_adam(cfg, dev, 50),
+                          "input_grad": measure_input_grad(cfg, x, t, d, 20),
+                          "shapes": measure_shapes(dev, w.n_points, 10),
+                          "fused_mlp": measure_fused_mlp(dev, 5)}
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x_h, t_h, d_h, args.cpu_seconds)

@@ -45,7 +45,33 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
+def _unmangle(name: str) -> str:
+    """Kernel name and template arguments of a mangled hg:: kernel symbol that
+    the profiler left mangled (e.g. ones with _Float16 arguments)."""
+    m = re.match(r"_ZN2hg12_GLOBAL__N_1(\d+)", name)
+    if not m:
+        return name
+    k = int(m.group(1))
+    rest = name[m.end():]
+    ident, rest = rest[:k], rest[k:]
+    if not rest.startswith("I"):
+        return ident
+    args = []
+    for tok in re.finditer(r"Li(-?\d+)E|Lb([01])E|DF16_|f(?=[EL])", rest[1:rest.find("EE") + 1]):
+        if tok.group(1) is not None:
+            args.append(tok.group(1))
+        elif tok.group(2) is not None:
+            args.append("true" if tok.group(2) == "1" else "false")
+        elif tok.group(0) == "DF16_":
+            args.append("_Float16")
+        else:
+            args.append("float")
+    return f"{ident}<{', '.join(args)}>"
+
+
 def short_name(name: str) -> str:
+    if name.startswith("_ZN"):
+        return _unmangle(name)
     name = name.replace("hg::(anonymous namespace)::", "").replace("void ", "")
     return re.sub(r"\(.*", "", name)
 
@@ -76,10 +102,12 @@ def stats(args) -> None:
         avg = float(r["AverageNs"]) / 1e3
         lines.append(f"| `{short_name(r['Name'])}` | {p or '-'} | {r['Calls']} | {avg:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} |")
-        if p:
+        if p and args.passes > 0:
             per_pass[p] += avg * int(r["Calls"]) / args.passes
-    lines += ["", f"Kernel time per call of each entry point ({args.passes} calls each, us): " +
-              ", ".join(f"{p} {v:.1f}" for p, v in sorted(per_pass.items())), ""]
+    if args.passes > 0:
+        lines += ["", f"Kernel time per call of each entry point ({args.passes} calls each, us): " +
+                  ", ".join(f"{p} {v:.1f}" for p, v in sorted(per_pass.items()))]
+    lines.append("")
     text = "\n".join(lines)
     with open(args.out, "w") as f:
         f.write(text)
@@ -164,7 +192,8 @@ def main() -> int:
     s.add_argument("--out", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--title", default="rocprofv3 --kernel-trace --stats")
-    s.add_argument("--passes", type=int, required=True, help="calls of each entry point in the run")
+    s.add_argument("--passes", type=int, required=True,
+                   help="calls of each entry point in the run (0: list the kernels only)")
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write", "out"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
