@@ -293,6 +293,9 @@ __device__ __forceinline__ int fixed_exponent(uint32_t dmax_bits) {
 // batches of kAccBatch steps are in flight: the next batch is requested
 // before the current one is added.
 constexpr int kAccBatch = 2;
+// float4 gradient values per thread of a partition: S / 2 <= kFlushPer * THREADS
+// for the partition size each workgroup width serves (launch_accumulate checks).
+constexpr int kFlushPer = 4;
 constexpr int kMapWindow = 1024;  // positions per map window, a multiple of 64 * kAccBatch
 static_assert(kMapWindow % (64 * kAccBatch) == 0, "map windows must hold whole batches");
 
@@ -347,6 +350,29 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     const int l = bp.level0 + g;
     const int S = 1 << bp.s_log2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t *truns = sp.runs + (int64_t)g * bp.tiles * (bp.parts + 1) + part;
+    const int tl = lane * kWaves + wave;  // this lane's tile within a chunk
+    // Run start and length of tile chunk + tl (0, 0 past the last tile).
+    auto load_run = [&](int chunk, uint32_t &s, uint32_t &len) {
+        s = len = 0;
+        if (chunk + tl < bp.tiles) {
+            const uint32_t *r = truns + (int64_t)(chunk + tl) * (bp.parts + 1);
+            s = r[0];
+            len = r[1] - s;
+        }
+    };
+    uint32_t s_next, len_next;
+    load_run(0, s_next, len_next);
+    // The partition's entries [part * S, (part + 1) * S) of level l: only this
+    // workgroup writes them, so their current values can be read now and the
+    // read's latency hidden behind the record loop.
+    float4 *gl = reinterpret_cast<float4 *>(grad + ((((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * 2));
+    float4 gv[kFlushPer];
+#pragma unroll
+    for (int u = 0; u < kFlushPer; ++u) {
+        const int j = threadIdx.x + u * THREADS;
+        if (j < S / 2) gv[u] = gl[j];
+    }
     for (int i = threadIdx.x; i < 2 * S; i += THREADS) slice[i] = 0ull;
     if (threadIdx.x == 0) touched = 0;
     // The level's max |dL/dout| over the tiles' maxima.
@@ -355,7 +381,6 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     for (int off = 32; off > 0; off >>= 1) dm = max(dm, __shfl_xor(dm, off, 64));
     if (lane == 0) wmax[wave] = dm;
     const uint4 *grec = sp.records + (int64_t)g * bp.level_records;
-    const uint32_t *truns = sp.runs + (int64_t)g * bp.tiles * (bp.parts + 1) + part;
     uint4 *map = maps[wave];
     const uint8_t *mapb = reinterpret_cast<const uint8_t *>(map);
     __syncthreads();
@@ -363,14 +388,8 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     for (int w = 1; w < kWaves; ++w) dm = max(dm, wmax[w]);
     const int k = fixed_exponent(dm);
     for (int chunk = 0; chunk < bp.tiles; chunk += THREADS) {
-        const int tl = lane * kWaves + wave;  // tile within the chunk
-        const int t = chunk + tl;
-        uint32_t s = 0, len = 0;
-        if (t < bp.tiles) {
-            const uint32_t *r = truns + (int64_t)t * (bp.parts + 1);
-            s = r[0];
-            len = r[1] - s;
-        }
+        const uint32_t s = s_next, len = len_next;
+        if (chunk + THREADS < bp.tiles) load_run(chunk + THREADS, s_next, len_next);
         const uint32_t incl = wave_inclusive_scan(len);
         const uint32_t pre = incl - len;
         const uint32_t total = __shfl(incl, 63, 64);
@@ -416,11 +435,12 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     }
     __syncthreads();
     if (!touched) return;  // no corner of this batch fell in the partition: nothing to add
-    // The partition's entries are [part * S, (part + 1) * S) of level l.
-    float4 *gl = reinterpret_cast<float4 *>(grad + ((((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * 2));
     const long long *sl = reinterpret_cast<const long long *>(slice);
-    for (int j = threadIdx.x; j < S / 2; j += THREADS) {
-        float4 a = gl[j];
+#pragma unroll
+    for (int u = 0; u < kFlushPer; ++u) {
+        const int j = threadIdx.x + u * THREADS;
+        if (j >= S / 2) break;
+        float4 a = gv[u];
         a.x += (float)ldexp((double)sl[4 * j + 0], -k);
         a.y += (float)ldexp((double)sl[4 * j + 1], -k);
         a.z += (float)ldexp((double)sl[4 * j + 2], -k);
@@ -432,6 +452,7 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
 template <int THREADS>
 hipError_t launch_accumulate(const BinParams &bp, const Space &sp, float *dtable, hipStream_t stream) {
     const size_t lds = ((size_t)2 << bp.s_log2) * sizeof(unsigned long long);
+    if (((size_t)1 << bp.s_log2) / 2 > (size_t)kFlushPer * THREADS) return hipErrorInvalidValue;
     // The partition slice can exceed the default 64 KB of dynamic LDS.
     hipError_t e = hipFuncSetAttribute((const void *)accumulate_kernel<THREADS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

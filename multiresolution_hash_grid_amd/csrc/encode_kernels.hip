@@ -273,24 +273,49 @@ int grid_blocks(const LaunchParams &lp) {
 
 // Level-major staging [L][n][2] -> rows out[p * ostride + l * 2 + j], 64
 // points per workgroup through LDS so that both sides move whole lines.
+// VEC moves 16 bytes per access on both sides (n even, L even, rows and
+// output 16-byte aligned); otherwise 4 bytes.
 constexpr int kTransposePts = 64;
 
+template <bool VEC>
 __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restrict__ stage, int64_t n, int L,
                                                            float *__restrict__ out, int64_t ostride) {
-    extern __shared__ float tile[];  // [kTransposePts][2L + 1]
-    const int row = 2 * L + 1;
+    extern __shared__ float tile[];  // [kTransposePts][2L + 4]: rows 16-byte aligned
+    const int row = 2 * L + 4;
     const int64_t p0 = (int64_t)blockIdx.x * kTransposePts;
     const int np = (int)min((int64_t)kTransposePts, n - p0);
-    const int total = kTransposePts * 2 * L;
-    for (int e = threadIdx.x; e < total; e += kBlock) {
-        const int l = e / (2 * kTransposePts), r = e - l * 2 * kTransposePts;
-        const int i = r >> 1, j = r & 1;
-        if (i < np) tile[i * row + 2 * l + j] = stage[((int64_t)l * n + p0 + i) * 2 + j];
-    }
-    __syncthreads();
-    for (int e = threadIdx.x; e < total; e += kBlock) {
-        const int i = e / (2 * L), c = e - i * 2 * L;
-        if (i < np) out[(p0 + i) * ostride + c] = tile[i * row + c];
+    if constexpr (VEC) {
+        // Level l of this block is 2 np contiguous floats: np / 2 float4 (np even: n is).
+        const int q_per_level = kTransposePts / 2;
+        for (int e = threadIdx.x; e < L * q_per_level; e += kBlock) {
+            const int l = e / q_per_level, qd = e - l * q_per_level;
+            if (2 * qd < np) {
+                const float4 v = *reinterpret_cast<const float4 *>(stage + ((int64_t)l * n + p0) * 2 + 4 * qd);
+                // points 2 qd and 2 qd + 1, features 0 and 1 of level l
+                *reinterpret_cast<float2 *>(&tile[(2 * qd) * row + 2 * l]) = make_float2(v.x, v.y);
+                *reinterpret_cast<float2 *>(&tile[(2 * qd + 1) * row + 2 * l]) = make_float2(v.z, v.w);
+            }
+        }
+        __syncthreads();
+        const int q_per_row = L / 2;  // float4 per output row
+        for (int e = threadIdx.x; e < kTransposePts * q_per_row; e += kBlock) {
+            const int i = e / q_per_row, c = e - i * q_per_row;
+            if (i < np)
+                *reinterpret_cast<float4 *>(out + (p0 + i) * ostride + 4 * c) =
+                    *reinterpret_cast<const float4 *>(&tile[i * row + 4 * c]);
+        }
+    } else {
+        const int total = kTransposePts * 2 * L;
+        for (int e = threadIdx.x; e < total; e += kBlock) {
+            const int l = e / (2 * kTransposePts), r = e - l * 2 * kTransposePts;
+            const int i = r >> 1, j = r & 1;
+            if (i < np) tile[i * row + 2 * l + j] = stage[((int64_t)l * n + p0 + i) * 2 + j];
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < total; e += kBlock) {
+            const int i = e / (2 * L), c = e - i * 2 * L;
+            if (i < np) out[(p0 + i) * ostride + c] = tile[i * row + c];
+        }
     }
 }
 
@@ -326,8 +351,11 @@ hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, con
                          : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream);
     if (e != hipSuccess) return e;
     const unsigned blocks = (unsigned)((n + kTransposePts - 1) / kTransposePts);
-    const size_t lds = (size_t)kTransposePts * (2 * lp.n_levels + 1) * sizeof(float);
-    transpose_kernel<<<blocks, kBlock, lds, stream>>>(stage, n, lp.n_levels, out, out_stride);
+    const size_t lds = (size_t)kTransposePts * (2 * lp.n_levels + 4) * sizeof(float);
+    const bool vec = n % 2 == 0 && lp.n_levels % 2 == 0 && out_stride % 4 == 0 && ((uintptr_t)out & 15) == 0 &&
+                     ((uintptr_t)stage & 15) == 0;
+    if (vec) transpose_kernel<true><<<blocks, kBlock, lds, stream>>>(stage, n, lp.n_levels, out, out_stride);
+    else transpose_kernel<false><<<blocks, kBlock, lds, stream>>>(stage, n, lp.n_levels, out, out_stride);
     return hipGetLastError();
 }
 
