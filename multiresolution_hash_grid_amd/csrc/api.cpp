@@ -143,7 +143,7 @@ bool standard_shape(const hg_config &c) { return c.n_dims == 3 && c.n_features =
 // made equal.
 int binned_group(const hg::BinParams &bp, int n_levels) {
     if (g_tune.bwd_group_mib <= 0) return n_levels;
-    const size_t rec_bytes = (size_t)bp.level_records * 16;
+    const size_t rec_bytes = (size_t)bp.level_records * hg::kRecordBytes;
     const size_t budget = (size_t)g_tune.bwd_group_mib << 20;
     const int fill = (512 + bp.parts - 1) / bp.parts;
     const int cap = (int)std::min<size_t>(

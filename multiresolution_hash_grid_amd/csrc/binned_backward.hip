@@ -11,11 +11,12 @@
 //
 //   bin        : per (level, tile of 512 points), each corner pair (the two
 //                x-corners of one (dy, dz), which share a table partition of
-//                2^s entries unless x+1 carries above bit s) becomes a 16-byte
-//                record {local index of both corners, f_x, w_y w_z g_0,
-//                w_y w_z g_1}; the tile's 2048 records are counting-sorted by
-//                partition in LDS and written contiguously to the tile's own
-//                region together with the run offsets of every partition;
+//                2^s entries unless x+1 carries above bit s) becomes a 12-byte
+//                record {local index of the x corner, the x+1 corner's offset
+//                code, f_x, w_y w_z g_0, w_y w_z g_1}; the tile's 2048 records
+//                are counting-sorted by partition in LDS and written
+//                contiguously to the tile's own region together with the run
+//                offsets of every partition;
 //   accumulate : one workgroup per (level, partition) gathers its run from
 //                every tile, adds the records into the partition's gradient
 //                held in LDS, then adds the partition into dtable with plain
@@ -37,6 +38,19 @@
 // A corner pair whose x+1 corner lands in another partition (only when the
 // low s bits of the x coordinate are all ones, e.g. x = -1) keeps the x
 // corner in its record and adds the x+1 corner with a global fp32 atomic.
+//
+// Record packing (96 bits; the records are three quarters of the backward's
+// memory traffic, written once and read once):
+//   bits  0..12  lo0, the x corner's index inside the partition (s <= 13);
+//   bits 13..16  t = min(trailing ones of v_x, 15): the x+1 corner's index is
+//                lo0 XOR (2^(t+1) - 1) within the partition, because
+//                v_x XOR (v_x + 1) = 2^(t+1) - 1 and the x prime is 1;
+//   bits 17..39  f_x * 2^23: exact, as f_x is a multiple of the ulp of the
+//                fp32 position, >= 2^-23 once the position is >= 1 (below 1,
+//                i.e. in the first voxel, it is rounded to 2^-24);
+//   bits 40..67  w_y w_z g_0 and bits 68..95 w_y w_z g_1, each an fp32 value
+//                rounded to nearest on its 4 lowest mantissa bits (relative
+//                error <= 2^-21, far inside the gradient's 1e-5 bound).
 #include <algorithm>
 
 #include "device_common.h"
@@ -49,9 +63,24 @@ constexpr int kPtsPerThread = kBinTile / kBinThreads;  // 2
 constexpr int kRecPerTile = kBinTile * 4;              // 4 corner pairs per point
 constexpr int kLevelsPerBlock = 4;                     // levels per bin workgroup
 
+// One corner-pair record (see the packing above); 4-byte aligned, 12 bytes.
+struct Rec {
+    uint32_t a, b, c;
+};
+static_assert(sizeof(Rec) == kRecordBytes, "records are 12 bytes");
+
+// fp32 bits rounded to nearest on the 4 lowest mantissa bits, as 28 bits.
+__device__ __forceinline__ uint32_t pack28(float v) { return (__float_as_uint(v) + 8u) >> 4; }
+__device__ __forceinline__ float unpack28(uint32_t v) { return __uint_as_float(v << 4); }
+
+__device__ __forceinline__ Rec pack_record(uint32_t lo0, uint32_t t, uint32_t fx23, float A, float B) {
+    const uint32_t a28 = pack28(A), b28 = pack28(B);
+    return Rec{lo0 | (t << 13) | (fx23 << 17), (fx23 >> 15) | (a28 << 8), (a28 >> 24) | (b28 << 4)};
+}
+
 // Workspace of one launch group.
 struct Space {
-    uint4 *records;     // [group][tiles][kRecPerTile], each tile's records sorted by partition
+    Rec *records;       // [group][tiles][kRecPerTile], each tile's records sorted by partition
     uint32_t *runs;     // [group][tiles][parts + 1], start of every partition's run in the tile
     uint32_t *dmax;     // [group][tiles], bits of each tile's max |dL/dout| (non-negative floats order as uints)
 };
@@ -59,8 +88,8 @@ struct Space {
 Space carve(void *ws, const BinParams &bp) {
     Space s;
     char *p = reinterpret_cast<char *>(ws);
-    s.records = reinterpret_cast<uint4 *>(p);
-    p += (size_t)bp.group * bp.level_records * sizeof(uint4);
+    s.records = reinterpret_cast<Rec *>(p);
+    p += (size_t)bp.group * bp.level_records * sizeof(Rec);
     s.runs = reinterpret_cast<uint32_t *>(p);
     p += (size_t)bp.group * bp.tiles * (bp.parts + 1) * sizeof(uint32_t);
     s.dmax = reinterpret_cast<uint32_t *>(p);
@@ -70,7 +99,7 @@ Space carve(void *ws, const BinParams &bp) {
 // The four corner pairs (dy, dz) of one point at one level.
 struct Pairs {
     uint32_t part[4];
-    uint4 rec[4];
+    Rec rec[4];
     uint32_t split_idx[4];  // table entry of an x+1 corner outside the pair's partition, or ~0u
     float2 split_val[4];
     float dabs;             // max(|g_0|, |g_1|)
@@ -88,6 +117,10 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
     const uint32_t cx0 = (uint32_t)v0, cx1 = cx0 + 1u;
     const uint32_t smask = (1u << bp.s_log2) - 1u;
     out.dabs = fmaxf(fabsf(d0), fabsf(d1));
+    // trailing ones of v_x (bit 31 set keeps ctz defined for v_x = -1)
+    const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 15u);
+    // f_x * 2^23 (exact for positions >= 1; the first voxel's fraction rounds)
+    const uint32_t fx23 = min(__float2uint_rn(a0 * 8388608.f), 8388607u);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const uint32_t dy = (uint32_t)(c >> 1), dz = (uint32_t)(c & 1);
@@ -98,14 +131,13 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
         const float A = wyz * d0, B = wyz * d1;
         out.part[c] = p0;
         if ((i1 >> bp.s_log2) == p0) {
-            out.rec[c] = make_uint4((i0 & smask) | ((i1 & smask) << 16), __float_as_uint(a0),
-                                    __float_as_uint(A), __float_as_uint(B));
+            out.rec[c] = pack_record(i0 & smask, t, fx23, A, B);
             out.split_idx[c] = ~0u;
             out.split_val[c] = make_float2(0.f, 0.f);
         } else {
+            // f_x = 0 in the record: only the x corner, with its weight folded in.
             const float w0 = 1.f - a0;
-            out.rec[c] = make_uint4((i0 & smask) | ((i0 & smask) << 16), 0u, __float_as_uint(w0 * A),
-                                    __float_as_uint(w0 * B));
+            out.rec[c] = pack_record(i0 & smask, 0u, 0u, w0 * A, w0 * B);
             out.split_idx[c] = i1;
             out.split_val[c] = make_float2(a0 * A, a0 * B);
         }
@@ -190,7 +222,7 @@ __device__ __forceinline__ void load_points(const float *__restrict__ x, int64_t
 __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restrict__ x, int64_t n,
                                                           const float *__restrict__ dout, int64_t dstride,
                                                           BinParams bp, Space sp, float *__restrict__ grad) {
-    __shared__ uint4 stage[kRecPerTile];
+    __shared__ Rec stage[kRecPerTile];
     __shared__ uint32_t wmax[kBinThreads / 64];
     __shared__ uint32_t wsum[kBinThreads / 64];
     extern __shared__ uint32_t dyn[];  // cnt[parts], base[parts + 1]
@@ -246,7 +278,7 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
         }
         __syncthreads();
         const uint32_t total = base[bp.parts];
-        uint4 *trec = sp.records + (int64_t)g * bp.level_records + (int64_t)tile * kRecPerTile;
+        Rec *trec = sp.records + (int64_t)g * bp.level_records + (int64_t)tile * kRecPerTile;
         for (uint32_t i = threadIdx.x; i < total; i += kBinThreads) trec[i] = stage[i];
         __syncthreads();
     }
@@ -259,9 +291,12 @@ __device__ __forceinline__ unsigned long long to_fixed(float c, int k) {
     return (unsigned long long)(long long)(int32_t)rintf(ldexpf(c, k));
 }
 
-__device__ __forceinline__ void apply_record(unsigned long long *slice, const uint4 r, int k) {
-    const uint32_t lo0 = r.x & 0xFFFFu, lo1 = r.x >> 16;
-    const float fx = __uint_as_float(r.y), A = __uint_as_float(r.z), B = __uint_as_float(r.w);
+__device__ __forceinline__ void apply_record(unsigned long long *slice, const Rec r, int k, uint32_t smask) {
+    const uint32_t lo0 = r.a & 0x1FFFu, t = (r.a >> 13) & 0xFu;
+    const uint32_t lo1 = lo0 ^ (((2u << t) - 1u) & smask);
+    const uint32_t fx23 = (r.a >> 17) | ((r.b & 0xFFu) << 15);
+    const float fx = (float)fx23 * 0x1p-23f;  // exact: fx23 < 2^23
+    const float A = unpack28((r.b >> 8) | ((r.c & 0xFu) << 24)), B = unpack28(r.c >> 4);
     const float w0 = 1.f - fx;
     atomicAdd(slice + 2 * lo0, to_fixed(w0 * A, k));
     atomicAdd(slice + 2 * lo0 + 1, to_fixed(w0 * B, k));
@@ -380,7 +415,8 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     for (int t = threadIdx.x; t < bp.tiles; t += THREADS) dm = max(dm, sp.dmax[(int64_t)g * bp.tiles + t]);
     for (int off = 32; off > 0; off >>= 1) dm = max(dm, __shfl_xor(dm, off, 64));
     if (lane == 0) wmax[wave] = dm;
-    const uint4 *grec = sp.records + (int64_t)g * bp.level_records;
+    const Rec *grec = sp.records + (int64_t)g * bp.level_records;
+    const uint32_t smask = (uint32_t)S - 1u;
     uint4 *map = maps[wave];
     const uint8_t *mapb = reinterpret_cast<const uint8_t *>(map);
     __syncthreads();
@@ -394,12 +430,12 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
         const uint32_t pre = incl - len;
         const uint32_t total = __shfl(incl, 63, 64);
         // Records of the chunk's tiles, relative to the first of them.
-        const uint4 *trec = grec + (int64_t)chunk * kRecPerTile;
+        const Rec *trec = grec + (int64_t)chunk * kRecPerTile;
         offs[wave][lane] = tl * kRecPerTile + (int32_t)s - (int32_t)pre;
         if (total && lane == 0) touched = 1;
         // Run holding position i (the window that holds i is in the map).
         uint32_t carry = 0;
-        auto fetch = [&](uint32_t i) -> uint4 {
+        auto fetch = [&](uint32_t i) -> Rec {
             const uint32_t m = mapb[i % kMapWindow];
             const int j = m ? (int)m - 1 : (int)carry;
             return trec[offs[wave][j] + (int32_t)i];
@@ -410,7 +446,7 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
             build_run_map(map, w0, pre, len);
         };
         if (total) open_window(0);
-        uint4 cur[kAccBatch], nxt[kAccBatch];
+        Rec cur[kAccBatch], nxt[kAccBatch];
 #pragma unroll
         for (int u = 0; u < kAccBatch; ++u) {
             const uint32_t i = u * 64 + lane;
@@ -427,7 +463,7 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
             }
 #pragma unroll
             for (int u = 0; u < kAccBatch; ++u)
-                if (b0 + u * 64 + lane < total) apply_record(slice, cur[u], k);
+                if (b0 + u * 64 + lane < total) apply_record(slice, cur[u], k, smask);
 #pragma unroll
             for (int u = 0; u < kAccBatch; ++u) cur[u] = nxt[u];
         }
@@ -464,7 +500,7 @@ hipError_t launch_accumulate(const BinParams &bp, const Space &sp, float *dtable
 }  // namespace
 
 size_t binned_level_bytes(const BinParams &bp) {
-    const size_t recs = (size_t)bp.level_records * sizeof(uint4);
+    const size_t recs = (size_t)bp.level_records * sizeof(Rec);
     const size_t words = (size_t)bp.tiles * (bp.parts + 2);
     return recs + words * sizeof(uint32_t);
 }
