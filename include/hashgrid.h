@@ -114,11 +114,11 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
 
 /* Bytes of device workspace that let hashgrid_backward route the whole
  * gradient of n points through its binned (atomic-free) path at full speed:
- * per level, 64 * ceil(n / 512) * 512 bytes of records plus small counters
- * (about 17 MB for n = 2^18), times the number of levels binned together.
+ * per level, 48 * ceil(n / 512) * 512 bytes of records plus small counters
+ * (about 12.9 MB for n = 2^18), times the number of levels binned together.
  * That group is sized so its records fit the MI355X last-level cache (the
  * HG_TUNE_BWD_GROUP_MIB budget, 160 MiB by default: 8 levels for n = 2^18,
- * about 136 MB).  *bytes_out is a HOST size_t.  A workspace of at least
+ * about 103 MB).  *bytes_out is a HOST size_t.  A workspace of at least
  * *min_bytes_out (one level's share; may be NULL) also works -- the levels
  * are then processed in smaller groups.  Returns 0 bytes when the
  * configuration has no binned path (more than 4096 partitions of 2^13

@@ -127,27 +127,27 @@ def test_zero_points_is_a_no_op(lib):
 
 
 def test_backward_workspace_size():
-    # 64 bytes per point, level and corner pair slot (tiles of 512 points) plus counters.
+    # 48 bytes per point and level (four 12-byte corner-pair records, tiles of 512 points) plus counters.
     cfg = hg.HashGridConfig()
     full, least = hg.hashgrid_backward_workspace_size(cfg, 1 << 18)
-    # 16 MiB of records per level: the 160 MiB group budget takes 10 levels,
-    # so the 16 levels run as two equal groups of 8.
+    # 12 MiB of records per level (2^20 records of 12 bytes): the 160 MiB group
+    # budget takes 13 levels, so the 16 levels run as two equal groups of 8.
     assert least * 8 == full
     old = hg.hashgrid_tune_get(B.HG_TUNE_BWD_GROUP_MIB)
     try:
         hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 0)      # one group of all levels
         assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 16, least)
-        # 48 MiB holds 3 levels, but a group keeps at least 512 / 128 partitions = 4
+        # 36 MiB holds 3 levels, but a group keeps at least 512 / 128 partitions = 4
         # levels so that the accumulate grid fills the chip: 4 groups of 4.
-        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 48)
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 36)
         assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 4, least)
-        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 96)     # 6 levels -> groups 6 + 6 + 4, sized for 6
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 72)     # 6 levels -> groups 6 + 6 + 4, sized for 6
         assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 6, least)
     finally:
         hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, old)
-    assert least >= 64 * (1 << 18) and least < 64 * (1 << 18) + (1 << 20)
+    assert least >= 48 * (1 << 18) and least < 48 * (1 << 18) + (1 << 20)
     assert hg.hashgrid_backward_workspace_size(cfg, 0) == (0, 0)
-    assert hg.hashgrid_backward_workspace_size(cfg, 1)[1] >= 64 * 512
+    assert hg.hashgrid_backward_workspace_size(cfg, 1)[1] >= 48 * 512
     big = hg.HashGridConfig(log2_table_size=28)   # beyond 4096 partitions: atomic path only
     assert hg.hashgrid_backward_workspace_size(big, 1000) == (0, 0)
     with pytest.raises(hg.HashGridError):
