@@ -115,14 +115,17 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
 /* Bytes of device workspace that let hashgrid_backward route the whole
  * gradient of n points through its binned (atomic-free) path at full speed:
  * per level, 48 * ceil(n / 512) * 512 bytes of records plus small counters
- * (about 12.9 MB for n = 2^18), times the number of levels binned together.
+ * (about 12.9 MB for n = 2^18) for the D = 3, F = 2 grid; for other shapes
+ * (2 + F) * 4 bytes per corner pair, 2^(D-1) pairs per point -- times the
+ * number of levels binned together.
  * That group is sized so its records fit the MI355X last-level cache (the
  * HG_TUNE_BWD_GROUP_MIB budget, 160 MiB by default: 8 levels for n = 2^18,
  * about 103 MB).  *bytes_out is a HOST size_t.  A workspace of at least
  * *min_bytes_out (one level's share; may be NULL) also works -- the levels
  * are then processed in smaller groups.  Returns 0 bytes when the
- * configuration has no binned path (more than 4096 partitions of 2^13
- * entries, i.e. T > 2^25, or n >= 2^29).
+ * configuration has no binned path (more than 4096 partitions: T > 2^25 for
+ * the D = 3, F = 2 grid, partitions of 8192 / F entries for other shapes; or
+ * n >= 2^29).
  * Errors: HG_EINVAL, HG_EUNSUPPORTED. */
 int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out,
                                      size_t *min_bytes_out);

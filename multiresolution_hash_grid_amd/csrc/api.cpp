@@ -105,14 +105,25 @@ int plan(const hg_config &c, int64_t n, hg::LaunchParams &lp) {
 // Binned backward layout; returns false when the configuration has no binned
 // path (partition count or record count beyond the kernels' index widths).
 bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
-    if (c.n_dims != 3 || c.n_features != 2) return false;
-    // Partition of 2^12 entries (32 KB of accumulators, 512-thread owners) for
-    // tables up to 2^20 entries; 2^13 (1024 threads) for larger tables, whose
-    // runs per tile would otherwise get short.
-    const int want = g_tune.bwd_part_log2 ? g_tune.bwd_part_log2 : (c.log2_table_size <= 20 ? 12 : 13);
+    const bool std_shape = c.n_dims == 3 && c.n_features == 2;
+    int want, tile_pts, rec_per_tile, rec_bytes;
+    if (std_shape) {
+        // Partition of 2^12 entries (32 KB of accumulators, 512-thread owners) for
+        // tables up to 2^20 entries; 2^13 (1024 threads) for larger tables, whose
+        // runs per tile would otherwise get short.
+        want = g_tune.bwd_part_log2 ? g_tune.bwd_part_log2 : (c.log2_table_size <= 20 ? 12 : 13);
+        tile_pts = hg::kBinTile;
+        rec_per_tile = hg::kBinTile * 4;
+        rec_bytes = hg::kRecordBytes;
+    } else {
+        want = hg::generic_s_log2(c.n_features);
+        tile_pts = hg::generic_tile(c.n_dims, c.n_features);
+        rec_per_tile = hg::generic_rec_per_tile(c.n_dims, c.n_features);
+        rec_bytes = hg::generic_rec_bytes(c.n_features);
+    }
     const int s_log2 = c.log2_table_size < want ? c.log2_table_size : want;
     const int64_t parts = (int64_t)1 << (c.log2_table_size - s_log2);
-    const int64_t tiles = (n + hg::kBinTile - 1) / hg::kBinTile;
+    const int64_t tiles = (n + tile_pts - 1) / tile_pts;
     if (parts > hg::kMaxParts || n >= ((int64_t)1 << 29)) return false;
     bp.level0 = 0;
     bp.group = c.n_levels;
@@ -121,9 +132,11 @@ bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
     bp.s_log2 = s_log2;
     bp.log2_table_size = c.log2_table_size;
     bp.mask = (uint32_t)((1ull << c.log2_table_size) - 1);
-    bp.pad_ = 0;
+    bp.tile_pts = tile_pts;
     bp.n = n;
-    bp.level_records = tiles * hg::kBinTile * 4;
+    bp.level_records = tiles * rec_per_tile;
+    bp.rec_per_tile = rec_per_tile;
+    bp.rec_bytes = rec_bytes;
     resolutions(c, bp.res);
     return true;
 }
@@ -143,7 +156,7 @@ bool standard_shape(const hg_config &c) { return c.n_dims == 3 && c.n_features =
 // made equal.
 int binned_group(const hg::BinParams &bp, int n_levels) {
     if (g_tune.bwd_group_mib <= 0) return n_levels;
-    const size_t rec_bytes = (size_t)bp.level_records * hg::kRecordBytes;
+    const size_t rec_bytes = (size_t)bp.level_records * bp.rec_bytes;
     const size_t budget = (size_t)g_tune.bwd_group_mib << 20;
     const int fill = (512 + bp.parts - 1) / bp.parts;
     const int cap = (int)std::min<size_t>(
@@ -174,9 +187,14 @@ int table_backward(const hg_config *cfg, const float *x, int64_t n, const float 
         if (workspace_bytes >= per_level) {
             // Whole levels per group; the launcher splits the workspace itself.
             const size_t usable = workspace_bytes / per_level * hg::binned_level_bytes(bp);
-            return launch_status(hg::launch_binned_backward(bp, cfg->n_levels, binned_group(bp, cfg->n_levels), x,
-                                                            n, dout, dout_row_stride, dtable, workspace, usable,
-                                                            (hipStream_t)stream),
+            const int group = binned_group(bp, cfg->n_levels);
+            if (!standard_shape(*cfg))
+                return launch_status(hg::launch_binned_backward_generic(bp, cfg->n_dims, cfg->n_features, cfg->n_levels,
+                                                                        group, x, n, dout, dout_row_stride, dtable,
+                                                                        workspace, usable, (hipStream_t)stream),
+                                     "binned backward");
+            return launch_status(hg::launch_binned_backward(bp, cfg->n_levels, group, x, n, dout, dout_row_stride,
+                                                            dtable, workspace, usable, (hipStream_t)stream),
                                  "binned backward");
         }
     }

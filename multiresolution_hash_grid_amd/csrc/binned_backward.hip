@@ -53,10 +53,12 @@
 //                error <= 2^-21, far inside the gradient's 1e-5 bound).
 #include <algorithm>
 
-#include "device_common.h"
+#include "binned_common.h"
 
 namespace hg {
 namespace {
+
+using namespace binned;
 
 constexpr int kBinThreads = 256;
 constexpr int kPtsPerThread = kBinTile / kBinThreads;  // 2
@@ -64,10 +66,12 @@ constexpr int kRecPerTile = kBinTile * 4;              // 4 corner pairs per poi
 constexpr int kLevelsPerBlock = 4;                     // levels per bin workgroup
 
 // One corner-pair record (see the packing above); 4-byte aligned, 12 bytes.
-struct Rec {
+struct Rec12 {
     uint32_t a, b, c;
 };
-static_assert(sizeof(Rec) == kRecordBytes, "records are 12 bytes");
+static_assert(sizeof(Rec12) == kRecordBytes, "records are 12 bytes");
+using Rec = Rec12;
+using StdSpace = binned::Space<Rec>;
 
 // fp32 bits rounded to nearest on the 4 lowest mantissa bits, as 28 bits.
 __device__ __forceinline__ uint32_t pack28(float v) { return (__float_as_uint(v) + 8u) >> 4; }
@@ -76,24 +80,6 @@ __device__ __forceinline__ float unpack28(uint32_t v) { return __uint_as_float(v
 __device__ __forceinline__ Rec pack_record(uint32_t lo0, uint32_t t, uint32_t fx23, float A, float B) {
     const uint32_t a28 = pack28(A), b28 = pack28(B);
     return Rec{lo0 | (t << 13) | (fx23 << 17), (fx23 >> 15) | (a28 << 8), (a28 >> 24) | (b28 << 4)};
-}
-
-// Workspace of one launch group.
-struct Space {
-    Rec *records;       // [group][tiles][kRecPerTile], each tile's records sorted by partition
-    uint32_t *runs;     // [group][tiles][parts + 1], start of every partition's run in the tile
-    uint32_t *dmax;     // [group][tiles], bits of each tile's max |dL/dout| (non-negative floats order as uints)
-};
-
-Space carve(void *ws, const BinParams &bp) {
-    Space s;
-    char *p = reinterpret_cast<char *>(ws);
-    s.records = reinterpret_cast<Rec *>(p);
-    p += (size_t)bp.group * bp.level_records * sizeof(Rec);
-    s.runs = reinterpret_cast<uint32_t *>(p);
-    p += (size_t)bp.group * bp.tiles * (bp.parts + 1) * sizeof(uint32_t);
-    s.dmax = reinterpret_cast<uint32_t *>(p);
-    return s;
 }
 
 // The four corner pairs (dy, dz) of one point at one level.
@@ -144,37 +130,6 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
     }
 }
 
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(v, off, 64);
-        if (lane >= off) v += t;
-    }
-    return v;
-}
-
-// Exclusive prefix of cnt[0..count) into base[0..count] (base[count] = total)
-// by all kBinThreads threads: each thread sums a contiguous slice, the wave
-// sums are combined through wsum, and every thread writes its slice.
-__device__ __forceinline__ void block_exclusive_scan(const uint32_t *cnt, int count, uint32_t *base,
-                                                     uint32_t *wsum) {
-    const int per = (count + kBinThreads - 1) / kBinThreads;
-    const int b = per * threadIdx.x, e = min(count, b + per);
-    uint32_t s = 0;
-    for (int i = b; i < e; ++i) s += cnt[i];
-    const uint32_t incl = wave_inclusive_scan(s);
-    if ((threadIdx.x & 63) == 63) wsum[threadIdx.x >> 6] = incl;
-    __syncthreads();
-    uint32_t run = incl - s;
-    for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) run += wsum[w];
-    for (int i = b; i < e; ++i) {
-        base[i] = run;
-        run += cnt[i];
-    }
-    if (threadIdx.x == kBinThreads - 1) base[count] = run;
-}
-
 // ---------------------------------------------------------------- loads
 
 // The coordinates and the block's dL/dout of one thread's points, loaded once
@@ -221,7 +176,7 @@ __device__ __forceinline__ void load_points(const float *__restrict__ x, int64_t
 // Workgroup (tile, block of kLevelsPerBlock consecutive levels).
 __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restrict__ x, int64_t n,
                                                           const float *__restrict__ dout, int64_t dstride,
-                                                          BinParams bp, Space sp, float *__restrict__ grad) {
+                                                          BinParams bp, StdSpace sp, float *__restrict__ grad) {
     __shared__ Rec stage[kRecPerTile];
     __shared__ uint32_t wmax[kBinThreads / 64];
     __shared__ uint32_t wsum[kBinThreads / 64];
@@ -261,7 +216,7 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
         if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = __float_as_uint(dm);
         __syncthreads();
         // Run starts of the tile's partitions, published for the owners.
-        block_exclusive_scan(cnt, bp.parts, base, wsum);
+        block_exclusive_scan<kBinThreads>(cnt, bp.parts, base, wsum);
         if (threadIdx.x == 0) {
             uint32_t m = wmax[0];
             for (int w = 1; w < kBinThreads / 64; ++w) m = max(m, wmax[w]);
@@ -286,221 +241,31 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
 
 // ---------------------------------------------------------------- accumulate
 
-// c * 2^k rounded to nearest; |c * 2^k| < 2^31 by the choice of k.
-__device__ __forceinline__ unsigned long long to_fixed(float c, int k) {
-    return (unsigned long long)(long long)(int32_t)rintf(ldexpf(c, k));
-}
-
-__device__ __forceinline__ void apply_record(unsigned long long *slice, const Rec r, int k, uint32_t smask) {
-    const uint32_t lo0 = r.a & 0x1FFFu, t = (r.a >> 13) & 0xFu;
-    const uint32_t lo1 = lo0 ^ (((2u << t) - 1u) & smask);
-    const uint32_t fx23 = (r.a >> 17) | ((r.b & 0xFFu) << 15);
-    const float fx = (float)fx23 * 0x1p-23f;  // exact: fx23 < 2^23
-    const float A = unpack28((r.b >> 8) | ((r.c & 0xFu) << 24)), B = unpack28(r.c >> 4);
-    const float w0 = 1.f - fx;
-    atomicAdd(slice + 2 * lo0, to_fixed(w0 * A, k));
-    atomicAdd(slice + 2 * lo0 + 1, to_fixed(w0 * B, k));
-    if (fx != 0.f) {
-        atomicAdd(slice + 2 * lo1, to_fixed(fx * A, k));
-        atomicAdd(slice + 2 * lo1 + 1, to_fixed(fx * B, k));
-    }
-}
-
-// Fixed-point exponent of a level: max|dL/dout| < 2^e  ->  k = 30 - e.
-__device__ __forceinline__ int fixed_exponent(uint32_t dmax_bits) {
-    const float m = __uint_as_float(dmax_bits);
-    if (!(m > 0.f) || !isfinite(m)) return 0;
-    int e;
-    frexpf(m, &e);  // m < 2^e
-    return 30 - e;
-}
-
-// Workgroup (level, partition) of THREADS threads.  The tiles are walked in
-// chunks of THREADS: lane i of wave w takes tile chunk + i * waves + w (the
-// waves share out a short chunk evenly) and the wave works through the
-// concatenation of its tiles' runs, 64 records per step.  The
-// run that holds concatenation position i comes from a byte map built per
-// window of kMapWindow positions: every run that starts inside the window
-// marks its start with its lane index + 1, and a max-scan along the window
-// spreads each mark to the positions up to the next start (0 stays where the
-// run in progress when the window opened continues).  A record address is
-// then two LDS reads away (map entry, run offset) instead of a search.  Two
-// batches of kAccBatch steps are in flight: the next batch is requested
-// before the current one is added.
-constexpr int kAccBatch = 2;
-// float4 gradient values per thread of a partition: S / 2 <= kFlushPer * THREADS
-// for the partition size each workgroup width serves (launch_accumulate checks).
-constexpr int kFlushPer = 4;
-constexpr int kMapWindow = 1024;  // positions per map window, a multiple of 64 * kAccBatch
-static_assert(kMapWindow % (64 * kAccBatch) == 0, "map windows must hold whole batches");
-
-// LDS order between lanes of one wave (the wave's LDS operations complete in
-// issue order; this keeps the compiler from moving them across).
-__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
-
-// Byte map of window [w0, w0 + kMapWindow) of a wave's run concatenation.
-// pre / len: this lane's run offset and length.
-__device__ __forceinline__ void build_run_map(uint4 *map, uint32_t w0, uint32_t pre, uint32_t len) {
-    const int lane = threadIdx.x & 63;
-    map[lane] = make_uint4(0u, 0u, 0u, 0u);
-    wave_lds_fence();
-    if (len > 0 && pre > w0 && pre < w0 + kMapWindow) reinterpret_cast<uint8_t *>(map)[pre - w0] = (uint8_t)(lane + 1);
-    wave_lds_fence();
-    const uint4 q = map[lane];
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t run = 0;
-    uint32_t loc[16];
-#pragma unroll
-    for (int b = 0; b < 16; ++b) {
-        run = max(run, (w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
-        loc[b] = run;
-    }
-    // Largest mark in the lanes below (the window positions before this lane's 16).
-    uint32_t incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl = max(incl, t);
-    }
-    uint32_t below = __shfl_up(incl, 1, 64);
-    if (lane == 0) below = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-        w[m] = max(loc[4 * m], below) | (max(loc[4 * m + 1], below) << 8) | (max(loc[4 * m + 2], below) << 16) |
-               (max(loc[4 * m + 3], below) << 24);
-    map[lane] = make_uint4(w[0], w[1], w[2], w[3]);
-    wave_lds_fence();
-}
-
-template <int THREADS>
-__global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space sp, float *__restrict__ grad) {
-    constexpr int kWaves = THREADS / 64;
-    extern __shared__ unsigned long long slice[];       // [2^s][2] fixed-point accumulators
-    __shared__ int32_t offs[kWaves][64];                // per run: record index minus concatenation position
-    __shared__ uint4 maps[kWaves][kMapWindow / 16];     // per wave: byte map of the current window
-    __shared__ uint32_t touched;
-    __shared__ uint32_t wmax[kWaves];
-    const int g = blockIdx.x / bp.parts;
-    const int part = blockIdx.x - g * bp.parts;
-    const int l = bp.level0 + g;
-    const int S = 1 << bp.s_log2;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t *truns = sp.runs + (int64_t)g * bp.tiles * (bp.parts + 1) + part;
-    const int tl = lane * kWaves + wave;  // this lane's tile within a chunk
-    // Run start and length of tile chunk + tl (0, 0 past the last tile).
-    auto load_run = [&](int chunk, uint32_t &s, uint32_t &len) {
-        s = len = 0;
-        if (chunk + tl < bp.tiles) {
-            const uint32_t *r = truns + (int64_t)(chunk + tl) * (bp.parts + 1);
-            s = r[0];
-            len = r[1] - s;
+// The records of this grid for the shared accumulate kernel.
+struct StdPolicy {
+    using Rec = Rec12;
+    static constexpr int F = 2;
+    static constexpr int kRecPerTile = kBinTile * 4;
+    static __device__ __forceinline__ void apply(unsigned long long *slice, const Rec r, int k, uint32_t smask) {
+        const uint32_t lo0 = r.a & 0x1FFFu, t = (r.a >> 13) & 0xFu;
+        const uint32_t lo1 = lo0 ^ (((2u << t) - 1u) & smask);
+        const uint32_t fx23 = (r.a >> 17) | ((r.b & 0xFFu) << 15);
+        const float fx = (float)fx23 * 0x1p-23f;  // exact: fx23 < 2^23
+        const float A = unpack28((r.b >> 8) | ((r.c & 0xFu) << 24)), B = unpack28(r.c >> 4);
+        const float w0 = 1.f - fx;
+        atomicAdd(slice + 2 * lo0, to_fixed(w0 * A, k));
+        atomicAdd(slice + 2 * lo0 + 1, to_fixed(w0 * B, k));
+        if (fx != 0.f) {
+            atomicAdd(slice + 2 * lo1, to_fixed(fx * A, k));
+            atomicAdd(slice + 2 * lo1 + 1, to_fixed(fx * B, k));
         }
-    };
-    uint32_t s_next, len_next;
-    load_run(0, s_next, len_next);
-    // The partition's entries [part * S, (part + 1) * S) of level l: only this
-    // workgroup writes them, so their current values can be read now and the
-    // read's latency hidden behind the record loop.
-    float4 *gl = reinterpret_cast<float4 *>(grad + ((((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * 2));
-    float4 gv[kFlushPer];
-#pragma unroll
-    for (int u = 0; u < kFlushPer; ++u) {
-        const int j = threadIdx.x + u * THREADS;
-        if (j < S / 2) gv[u] = gl[j];
     }
-    for (int i = threadIdx.x; i < 2 * S; i += THREADS) slice[i] = 0ull;
-    if (threadIdx.x == 0) touched = 0;
-    // The level's max |dL/dout| over the tiles' maxima.
-    uint32_t dm = 0;
-    for (int t = threadIdx.x; t < bp.tiles; t += THREADS) dm = max(dm, sp.dmax[(int64_t)g * bp.tiles + t]);
-    for (int off = 32; off > 0; off >>= 1) dm = max(dm, __shfl_xor(dm, off, 64));
-    if (lane == 0) wmax[wave] = dm;
-    const Rec *grec = sp.records + (int64_t)g * bp.level_records;
-    const uint32_t smask = (uint32_t)S - 1u;
-    uint4 *map = maps[wave];
-    const uint8_t *mapb = reinterpret_cast<const uint8_t *>(map);
-    __syncthreads();
-    dm = wmax[0];
-    for (int w = 1; w < kWaves; ++w) dm = max(dm, wmax[w]);
-    const int k = fixed_exponent(dm);
-    for (int chunk = 0; chunk < bp.tiles; chunk += THREADS) {
-        const uint32_t s = s_next, len = len_next;
-        if (chunk + THREADS < bp.tiles) load_run(chunk + THREADS, s_next, len_next);
-        const uint32_t incl = wave_inclusive_scan(len);
-        const uint32_t pre = incl - len;
-        const uint32_t total = __shfl(incl, 63, 64);
-        // Records of the chunk's tiles, relative to the first of them.
-        const Rec *trec = grec + (int64_t)chunk * kRecPerTile;
-        offs[wave][lane] = tl * kRecPerTile + (int32_t)s - (int32_t)pre;
-        if (total && lane == 0) touched = 1;
-        // Run holding position i (the window that holds i is in the map).
-        uint32_t carry = 0;
-        auto fetch = [&](uint32_t i) -> Rec {
-            const uint32_t m = mapb[i % kMapWindow];
-            const int j = m ? (int)m - 1 : (int)carry;
-            return trec[offs[wave][j] + (int32_t)i];
-        };
-        auto open_window = [&](uint32_t w0) {
-            // The run in progress at w0: the last run starting at or before it.
-            carry = (uint32_t)__popcll(__ballot(pre <= w0)) - 1u;
-            build_run_map(map, w0, pre, len);
-        };
-        if (total) open_window(0);
-        Rec cur[kAccBatch], nxt[kAccBatch];
-#pragma unroll
-        for (int u = 0; u < kAccBatch; ++u) {
-            const uint32_t i = u * 64 + lane;
-            if (i < total) cur[u] = fetch(i);
-        }
-        for (uint32_t b0 = 0; b0 < total; b0 += 64 * kAccBatch) {
-            const uint32_t b1 = b0 + 64 * kAccBatch;
-            // The batch in flight already has its addresses: the map may move on.
-            if (b1 < total && b1 % kMapWindow == 0) open_window(b1);
-#pragma unroll
-            for (int u = 0; u < kAccBatch; ++u) {
-                const uint32_t i = b1 + u * 64 + lane;
-                if (i < total) nxt[u] = fetch(i);
-            }
-#pragma unroll
-            for (int u = 0; u < kAccBatch; ++u)
-                if (b0 + u * 64 + lane < total) apply_record(slice, cur[u], k, smask);
-#pragma unroll
-            for (int u = 0; u < kAccBatch; ++u) cur[u] = nxt[u];
-        }
-        wave_lds_fence();
-    }
-    __syncthreads();
-    if (!touched) return;  // no corner of this batch fell in the partition: nothing to add
-    const long long *sl = reinterpret_cast<const long long *>(slice);
-#pragma unroll
-    for (int u = 0; u < kFlushPer; ++u) {
-        const int j = threadIdx.x + u * THREADS;
-        if (j >= S / 2) break;
-        float4 a = gv[u];
-        a.x += (float)ldexp((double)sl[4 * j + 0], -k);
-        a.y += (float)ldexp((double)sl[4 * j + 1], -k);
-        a.z += (float)ldexp((double)sl[4 * j + 2], -k);
-        a.w += (float)ldexp((double)sl[4 * j + 3], -k);
-        gl[j] = a;
-    }
-}
-
-template <int THREADS>
-hipError_t launch_accumulate(const BinParams &bp, const Space &sp, float *dtable, hipStream_t stream) {
-    const size_t lds = ((size_t)2 << bp.s_log2) * sizeof(unsigned long long);
-    if (((size_t)1 << bp.s_log2) / 2 > (size_t)kFlushPer * THREADS) return hipErrorInvalidValue;
-    // The partition slice can exceed the default 64 KB of dynamic LDS.
-    hipError_t e = hipFuncSetAttribute((const void *)accumulate_kernel<THREADS>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    accumulate_kernel<THREADS><<<bp.group * bp.parts, THREADS, lds, stream>>>(bp, sp, dtable);
-    return hipGetLastError();
-}
+};
 
 }  // namespace
 
 size_t binned_level_bytes(const BinParams &bp) {
-    const size_t recs = (size_t)bp.level_records * sizeof(Rec);
+    const size_t recs = (size_t)bp.level_records * bp.rec_bytes;
     const size_t words = (size_t)bp.tiles * (bp.parts + 2);
     return recs + words * sizeof(uint32_t);
 }
@@ -517,16 +282,16 @@ hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, con
     for (int l0 = 0; l0 < n_levels; l0 += group) {
         bp.level0 = l0;
         bp.group = min(group, n_levels - l0);
-        const Space sp = carve(workspace, bp);
+        const StdSpace sp = carve<Rec>(workspace, bp);
         const dim3 tgrid(bp.tiles, (bp.group + kLevelsPerBlock - 1) / kLevelsPerBlock);
         bin_kernel<<<tgrid, kBinThreads, (2 * bp.parts + 1) * sizeof(uint32_t), stream>>>(x, n, dout, dout_stride,
                                                                                          bp, sp, dtable);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         // Larger partitions (longer runs per tile) take more LDS and more threads.
-        if (bp.s_log2 >= 13) e = launch_accumulate<1024>(bp, sp, dtable, stream);
-        else if (bp.s_log2 == 12) e = launch_accumulate<512>(bp, sp, dtable, stream);
-        else e = launch_accumulate<256>(bp, sp, dtable, stream);
+        if (bp.s_log2 >= 13) e = launch_accumulate<1024, StdPolicy>(bp, sp, dtable, stream);
+        else if (bp.s_log2 == 12) e = launch_accumulate<512, StdPolicy>(bp, sp, dtable, stream);
+        else e = launch_accumulate<256, StdPolicy>(bp, sp, dtable, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

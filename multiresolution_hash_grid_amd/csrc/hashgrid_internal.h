@@ -47,19 +47,36 @@ constexpr int kMaxSLog2 = 13;     // largest partition: 2^13 entries = 128 KB of
 struct BinParams {
     int32_t level0;          // first level of this launch group
     int32_t group;           // levels in this launch group
-    int32_t tiles;           // ceil(n / kBinTile)
+    int32_t tiles;           // ceil(n / tile_pts)
     int32_t parts;           // partitions per level = T >> s_log2
     int32_t s_log2;          // log2 entries per partition
     int32_t log2_table_size;
     uint32_t mask;           // T - 1
-    int32_t pad_;
+    int32_t tile_pts;        // points per bin tile
     int64_t n;
-    int64_t level_records;   // record slots per level = tiles * kBinTile * 4
+    int64_t level_records;   // record slots per level = tiles * rec_per_tile
+    int32_t rec_per_tile;    // record slots of one tile (points x corner pairs)
+    int32_t rec_bytes;       // bytes of one record
     int32_t res[kMaxLevels];
 };
 
+// Binned backward of the other shapes (generic_binned.hip): records of
+// 2 + F words (corner code, f_x, F upstream products), at most 32 KB of them
+// per tile, tiles of at most 1024 points, and partitions of S entries with
+// S * F * 8 = 64 KB of fixed-point accumulators.
+constexpr int generic_max_recs(int F) { return F <= 2 ? 2048 : (F == 4 ? 1024 : 512); }
+constexpr int generic_tile(int D, int F) {
+    return (generic_max_recs(F) >> (D - 1)) > 1024 ? 1024 : (generic_max_recs(F) >> (D - 1));
+}
+constexpr int generic_rec_per_tile(int D, int F) { return generic_tile(D, F) << (D - 1); }
+constexpr int generic_rec_bytes(int F) { return (2 + F) * 4; }
+constexpr int generic_s_log2(int F) { return F == 1 ? 13 : F == 2 ? 12 : F == 4 ? 11 : 10; }
+
 // Workspace bytes of one level (records, run starts, tile maxima).
 size_t binned_level_bytes(const BinParams &bp);
+hipError_t launch_binned_backward_generic(BinParams bp, int D, int F, int n_levels, int max_group, const float *x,
+                                          int64_t n, const float *dout, int64_t dout_stride, float *dtable,
+                                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 // Levels are binned and accumulated in equal groups of at most max_group
 // levels (and no more than the workspace holds).
 hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, const float *x, int64_t n,

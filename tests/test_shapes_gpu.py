@@ -122,3 +122,31 @@ def test_autograd_gives_point_and_table_gradients(oracle):
     got = enc.embeddings.grad.cpu().numpy()
     for l in range(w.n_levels):
         assert np.max(np.abs(got[l] - ref[l])) <= 1e-5 * np.max(np.abs(ref[l]))
+
+
+@pytest.mark.parametrize("D,F,log2T", [(2, 1, 10), (4, 8, 10), (1, 4, 12), (3, 8, 16), (2, 2, 13)])
+def test_shape_binned_backward_edge_cases(oracle, D, F, log2T):
+    # The binned path of the other shapes against the oracle: points partly
+    # outside [0,1) (negative voxel coordinates have all-ones low bits, so
+    # their x+1 corner leaves its partition and takes the atomic side path),
+    # one-partition tables (log2 T below the partition size), the smallest
+    # workspace (one level per group) and an accumulating, non-zero buffer.
+    w = shape_workload(D, F, "f32", n=2 * 4096 + 5, log2T=log2T)
+    cfg = hg.HashGridConfig.of(w)
+    g = oracle.grid_of(w)
+    x = (I.make_points(w).astype(np.float64) * 1.5 - 0.25).astype(np.float32)
+    d = I.make_dout(w)
+    full, least = hg.hashgrid_backward_workspace_size(cfg, w.n_points)
+    assert full > 0 and least > 0
+    base = np.random.default_rng(D + F).uniform(-1, 1, cfg.table_shape).astype(np.float32)
+    ref = oracle.backward(g, x, d)
+    for ws in (torch.empty(full, dtype=torch.uint8, device=DEV), torch.empty(least, dtype=torch.uint8, device=DEV)):
+        grad = dev(base)
+        hg.hashgrid_backward(cfg, dev(x), dev(d), grad, workspace=ws)
+        got = grad.cpu().numpy().astype(np.float64) - base
+        for l in range(w.n_levels):
+            assert np.max(np.abs(got[l] - ref[l])) <= 1e-5 * np.max(np.abs(ref[l])) + 4e-7, (l, ws.numel())
+    atomic = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_backward(cfg, dev(x), dev(d), atomic, workspace=None)
+    for l in range(w.n_levels):
+        assert np.max(np.abs(atomic.cpu().numpy()[l] - ref[l])) <= 1e-5 * np.max(np.abs(ref[l]))
