@@ -219,8 +219,10 @@ int hashgrid_mlp_backward(const hg_config *cfg, const float *x, int64_t n, const
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace that let hashgrid_input_grad stage per-level
- * partial sums level-major: L * n * D * 4, rounded up to 256.  *bytes_out is
- * a HOST size_t.  Errors: HG_EINVAL, HG_EUNSUPPORTED. */
+ * partial sums level-major: L * n * D * 4, rounded up to 256, plus for the
+ * D = 3, F = 2 grid L * n * 2 * 4 for a level-major copy of the upstream rows
+ * (a workspace holding only the stage also works).  *bytes_out is a HOST
+ * size_t.  Errors: HG_EINVAL, HG_EUNSUPPORTED. */
 int hashgrid_input_grad_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out);
 
 /* Gradient of the loss with respect to the points, dL/dx.  The pages imply

@@ -389,7 +389,10 @@ int hashgrid_input_grad_workspace_size(const hg_config *cfg, int64_t n, size_t *
     if (rc) return rc;
     if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
     if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
-    *bytes_out = round_up((size_t)n * cfg->n_levels * cfg->n_dims * sizeof(float), 256);
+    // The [L][n][D] stage, and for the D = 3, F = 2 grid a level-major copy of the upstream rows.
+    const size_t stage = round_up((size_t)n * cfg->n_levels * cfg->n_dims * sizeof(float), 256);
+    const size_t copy = standard_shape(*cfg) ? round_up((size_t)n * cfg->n_levels * 2 * sizeof(float), 256) : 0;
+    *bytes_out = stage + copy;
     return ok();
 }
 
@@ -410,10 +413,14 @@ int hashgrid_input_grad(const hg_config *cfg, const float *x, int64_t n, const v
     if (workspace && !aligned(workspace, 256)) return fail(HG_EINVAL, "workspace is not 256-byte aligned");
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
-    const size_t stage_bytes = (size_t)n * cfg->n_levels * cfg->n_dims * sizeof(float);
+    const size_t stage_bytes = round_up((size_t)n * cfg->n_levels * cfg->n_dims * sizeof(float), 256);
+    const size_t copy_bytes = (size_t)n * cfg->n_levels * 2 * sizeof(float);
     float *stage = (workspace && workspace_bytes >= stage_bytes) ? (float *)workspace : nullptr;
+    float *dlm = (stage && standard_shape(*cfg) && workspace_bytes >= stage_bytes + copy_bytes)
+                     ? (float *)((char *)workspace + stage_bytes)
+                     : nullptr;
     return launch_status(hg::launch_input_grad(lp, cfg->n_dims, cfg->n_features, x, n, table, cfg->table_dtype,
-                                               dout, dout_row_stride, dx, stage, (hipStream_t)stream),
+                                               dout, dout_row_stride, dx, stage, dlm, (hipStream_t)stream),
                          "input_grad");
 }
 

@@ -23,7 +23,8 @@
 // Level-major work items write each level's D partial sums to a [L][n][D]
 // stage, which a second kernel sums over levels in level order; without a
 // stage one thread walks all levels of its point.  Both add the same fp32
-// terms in the same order (contraction off), so they agree bit for bit.
+// terms in the same order (contraction off), so they agree bit for bit.  The
+// D = 3, F = 2 grid uses the forward's lane pairs for the level-major pass.
 #include <type_traits>
 
 #include "device_common.h"
@@ -233,6 +234,184 @@ __global__ __launch_bounds__(kBlock) void input_grad_point_kernel(const float *_
     for (int d = 0; d < D; ++d) dx[p * D + d] = acc[d];
 }
 
+// ---------------------------------------------------------------- dL/dx, D = 3, F = 2
+
+// The part of a level's dL/dx (before the factor N_l) that the four corners
+// with x offset `sub` give, from their features e[(dy, dz)] (order 00, 01,
+// 10, 11) and the level's upstream pair (d0, d1).  A level's derivative is
+// half(0) + half(1), added in that order by both the lane-pair kernel and the
+// point kernel so that the two agree bit for bit.
+__device__ __forceinline__ void half_input_grad(float a0, float a1, float a2, const float2 (&e)[4], float d0,
+                                                float d1, uint32_t sub, float (&h)[3]) {
+#pragma clang fp contract(off)
+    float s[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[c] = d0 * e[c].x + d1 * e[c].y;
+    const float wy0 = 1.f - a1, wz0 = 1.f - a2;
+    const float wx = sub ? a0 : 1.f - a0;
+    const float hx = wy0 * (wz0 * s[0] + a2 * s[1]) + a1 * (wz0 * s[2] + a2 * s[3]);
+    h[0] = sub ? hx : -hx;
+    h[1] = wx * (wz0 * (s[2] - s[0]) + a2 * (s[3] - s[1]));
+    h[2] = wx * (wy0 * (s[1] - s[0]) + a1 * (s[3] - s[2]));
+}
+
+template <int DT>
+__device__ __forceinline__ void corner_pairs(const void *__restrict__ table, uint64_t lbase, uint32_t mask,
+                                             uint32_t cx, uint32_t hy0, uint32_t hz0, float2 (&e)[4]) {
+    const uint32_t hy1 = hy0 + kPrimeList[1], hz1 = hz0 + kPrimeList[2];
+    float v[2];
+    load_features<2, DT>(table, lbase + ((cx ^ hy0 ^ hz0) & mask), v);
+    e[0] = make_float2(v[0], v[1]);
+    load_features<2, DT>(table, lbase + ((cx ^ hy0 ^ hz1) & mask), v);
+    e[1] = make_float2(v[0], v[1]);
+    load_features<2, DT>(table, lbase + ((cx ^ hy1 ^ hz0) & mask), v);
+    e[2] = make_float2(v[0], v[1]);
+    load_features<2, DT>(table, lbase + ((cx ^ hy1 ^ hz1) & mask), v);
+    e[3] = make_float2(v[0], v[1]);
+}
+
+// Upstream rows [n][>= 2L] (row stride dstride) -> level-major [L][n][2], 64
+// points per workgroup through LDS, so that the level-major pass reads its
+// level's 8 bytes per point contiguously instead of every XCD fetching all of
+// the 128-byte rows for the two levels it works on.
+constexpr int kRowPts = 64;
+
+template <bool VEC>
+__global__ __launch_bounds__(kBlock) void rows_to_levels_kernel(const float *__restrict__ dout, int64_t dstride,
+                                                                int64_t n, int L, float *__restrict__ dlm) {
+    extern __shared__ float tile[];  // [kRowPts][2L + 4]
+    const int row = 2 * L + 4;
+    const int64_t p0 = (int64_t)blockIdx.x * kRowPts;
+    const int np = (int)min((int64_t)kRowPts, n - p0);
+    if constexpr (VEC) {  // rows and dlm 16-byte aligned, L even, n even
+        const int q_per_row = L / 2;
+        for (int e = threadIdx.x; e < kRowPts * q_per_row; e += kBlock) {
+            const int i = e / q_per_row, c = e - i * q_per_row;
+            if (i < np)
+                *reinterpret_cast<float4 *>(&tile[i * row + 4 * c]) =
+                    *reinterpret_cast<const float4 *>(dout + (p0 + i) * dstride + 4 * c);
+        }
+        __syncthreads();
+        const int q_per_level = kRowPts / 2;
+        for (int e = threadIdx.x; e < L * q_per_level; e += kBlock) {
+            const int l = e / q_per_level, qd = e - l * q_per_level;
+            if (2 * qd < np) {
+                const float2 a = *reinterpret_cast<const float2 *>(&tile[(2 * qd) * row + 2 * l]);
+                const float2 b = *reinterpret_cast<const float2 *>(&tile[(2 * qd + 1) * row + 2 * l]);
+                *reinterpret_cast<float4 *>(dlm + ((int64_t)l * n + p0) * 2 + 4 * qd) = make_float4(a.x, a.y, b.x, b.y);
+            }
+        }
+    } else {
+        const int total = kRowPts * 2 * L;
+        for (int e = threadIdx.x; e < total; e += kBlock) {
+            const int i = e / (2 * L), c = e - i * 2 * L;
+            if (i < np) tile[i * row + c] = dout[(p0 + i) * dstride + c];
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < total; e += kBlock) {
+            const int l = e / (2 * kRowPts), r = e - l * 2 * kRowPts;
+            const int i = r >> 1, j = r & 1;
+            if (i < np) dlm[((int64_t)l * n + p0 + i) * 2 + j] = tile[i * row + 2 * l + j];
+        }
+    }
+}
+
+// Level-major, as the forward: two adjacent lanes per point (lane `sub`
+// gathers the corners with x offset sub, which share a cache line with the
+// other lane's 15 times in 16), U points per pair in flight; the pair swaps
+// its halves and lane 0 writes (dx, dy), lane 1 dz of stage[l][p][0..2].
+// The level's upstream pair of point q is dl[q * pstride + l * lstride + 0..1]:
+// (dstride, 2) for the rows, (2, 2 n) for a level-major copy.
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void input_grad_pair_kernel(const float *__restrict__ x, int64_t n,
+                                                                 const void *__restrict__ table,
+                                                                 const float *__restrict__ dl, int64_t pstride,
+                                                                 int64_t lstride, float *__restrict__ stage,
+                                                                 LaunchParams lp) {
+#pragma clang fp contract(off)
+    Item it;
+    if (!decode_item(lp, it)) return;
+    constexpr int kPairs = kBlock / 2;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    const uint32_t sub = threadIdx.x & 1;
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    for (int64_t p0 = it.p0 + (threadIdx.x >> 1); p0 < end; p0 += (int64_t)kPairs * U) {
+        float2 e[U][4];
+        float a0[U], a1[U], a2[U], d0[U], d1[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t p = p0 + (int64_t)u * kPairs;
+            ok[u] = p < end;
+            const int64_t q = ok[u] ? p : p0;  // p0 < end: always a valid point
+            int32_t v0, v1, v2;
+            locate1(x[3 * q + 0], N, v0, a0[u]);
+            locate1(x[3 * q + 1], N, v1, a1[u]);
+            locate1(x[3 * q + 2], N, v2, a2[u]);
+            d0[u] = dl[q * pstride + l * lstride];
+            d1[u] = dl[q * pstride + l * lstride + 1];
+            corner_pairs<DT>(table, lbase, lp.mask, (uint32_t)v0 + sub, (uint32_t)v1 * kPrimeList[1],
+                             (uint32_t)v2 * kPrimeList[2], e[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float h[3];
+            half_input_grad(a0[u], a1[u], a2[u], e[u], d0[u], d1[u], sub, h);
+            float g[3];
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                const float o = swap_pair(h[d]);
+                g[d] = N * (sub ? o + h[d] : h[d] + o);  // half(0) + half(1) on both lanes
+            }
+            if (ok[u]) {
+                float *dst = stage + ((int64_t)l * n + p0 + (int64_t)u * kPairs) * 3;
+                if (sub) {
+                    dst[2] = g[2];
+                } else {
+                    dst[0] = g[0];
+                    dst[1] = g[1];
+                }
+            }
+        }
+    }
+}
+
+// One thread per point over all levels, with the same arithmetic.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void input_grad_point_pair_kernel(const float *__restrict__ x, int64_t n,
+                                                                       const void *__restrict__ table,
+                                                                       const float *__restrict__ dout, int64_t dstride,
+                                                                       float *__restrict__ dx, LaunchParams lp) {
+#pragma clang fp contract(off)
+    const int64_t p = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (p >= n) return;
+    float acc[3] = {0.f, 0.f, 0.f};
+    for (int l = 0; l < lp.n_levels; ++l) {
+        const float N = (float)lp.res[l];
+        const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+        int32_t v0, v1, v2;
+        float a0, a1, a2;
+        locate1(x[3 * p + 0], N, v0, a0);
+        locate1(x[3 * p + 1], N, v1, a1);
+        locate1(x[3 * p + 2], N, v2, a2);
+        const float d0 = dout[p * dstride + 2 * l], d1 = dout[p * dstride + 2 * l + 1];
+        float2 e0[4], e1[4];
+        corner_pairs<DT>(table, lbase, lp.mask, (uint32_t)v0, (uint32_t)v1 * kPrimeList[1],
+                         (uint32_t)v2 * kPrimeList[2], e0);
+        corner_pairs<DT>(table, lbase, lp.mask, (uint32_t)v0 + 1u, (uint32_t)v1 * kPrimeList[1],
+                         (uint32_t)v2 * kPrimeList[2], e1);
+        float h0[3], h1[3];
+        half_input_grad(a0, a1, a2, e0, d0, d1, 0, h0);
+        half_input_grad(a0, a1, a2, e1, d0, d1, 1, h1);
+#pragma unroll
+        for (int d = 0; d < 3; ++d) acc[d] += N * (h0[d] + h1[d]);
+    }
+#pragma unroll
+    for (int d = 0; d < 3; ++d) dx[p * 3 + d] = acc[d];
+}
+
 int grid_blocks(const LaunchParams &lp) { return lp.xcd_map ? kNumXcd * lp.per_xcd : lp.items; }
 
 // ---------------------------------------------------------------- dispatch
@@ -294,8 +473,44 @@ hipError_t launch_debug_corners_generic(const LaunchParams &lp, int D, const flo
 
 hipError_t launch_input_grad(const LaunchParams &lp, int D, int F, const float *x, int64_t n, const void *table,
                              int table_dtype, const float *dout, int64_t dout_stride, float *dx, float *stage,
-                             hipStream_t stream) {
+                             float *dlm, hipStream_t stream) {
     bool ok;
+    if (D == 3 && F == 2) {  // lane pairs, as the forward
+        if (stage) {
+            const dim3 grid(grid_blocks(lp)), block(kBlock);
+            const float *dl = dout;
+            int64_t pstride = dout_stride, lstride = 2;
+            if (dlm) {
+                const unsigned blocks = (unsigned)((n + kRowPts - 1) / kRowPts);
+                const size_t lds = (size_t)kRowPts * (2 * lp.n_levels + 4) * sizeof(float);
+                const bool vec = n % 2 == 0 && lp.n_levels % 2 == 0 && dout_stride % 4 == 0 &&
+                                 ((uintptr_t)dout & 15) == 0 && ((uintptr_t)dlm & 15) == 0;
+                if (vec)
+                    rows_to_levels_kernel<true><<<blocks, kBlock, lds, stream>>>(dout, dout_stride, n, lp.n_levels, dlm);
+                else
+                    rows_to_levels_kernel<false><<<blocks, kBlock, lds, stream>>>(dout, dout_stride, n, lp.n_levels, dlm);
+                dl = dlm;
+                pstride = 2;
+                lstride = 2 * n;
+            }
+            if (table_dtype == 0)
+                input_grad_pair_kernel<0, 4><<<grid, block, 0, stream>>>(x, n, table, dl, pstride, lstride, stage, lp);
+            else
+                input_grad_pair_kernel<1, 4><<<grid, block, 0, stream>>>(x, n, table, dl, pstride, lstride, stage, lp);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int64_t nd = n * 3;
+            input_grad_reduce_kernel<<<(unsigned)((nd + kBlock - 1) / kBlock), kBlock, 0, stream>>>(stage, nd,
+                                                                                                 lp.n_levels, dx);
+            return hipGetLastError();
+        }
+        const dim3 grid((unsigned)((n + kBlock - 1) / kBlock)), block(kBlock);
+        if (table_dtype == 0)
+            input_grad_point_pair_kernel<0><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride, dx, lp);
+        else
+            input_grad_point_pair_kernel<1><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride, dx, lp);
+        return hipGetLastError();
+    }
     if (stage) {
         const dim3 grid(grid_blocks(lp)), block(kBlock);
         ok = dispatch_shape(D, F, [&]<int DD, int FF>() {

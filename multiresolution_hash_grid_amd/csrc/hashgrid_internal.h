@@ -108,10 +108,12 @@ hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const f
                                    const float *dout, int64_t dout_stride, float *dtable, hipStream_t stream);
 hipError_t launch_debug_corners_generic(const LaunchParams &lp, int D, const float *x, int64_t n, uint32_t *idx,
                                         float *w, hipStream_t stream);
-// dL/dx of every shape; stage ([L][n][D] fp32) selects the level-major path.
+// dL/dx of every shape; stage ([L][n][D] fp32) selects the level-major path,
+// dlm ([L][n][2] fp32, D = 3 and F = 2 only, or NULL) a level-major copy of
+// the upstream rows for it.
 hipError_t launch_input_grad(const LaunchParams &lp, int D, int F, const float *x, int64_t n, const void *table,
                              int table_dtype, const float *dout, int64_t dout_stride, float *dx, float *stage,
-                             hipStream_t stream);
+                             float *dlm, hipStream_t stream);
 
 // MLP head 32 -> 64 -> 64 -> 4 (mlp_kernels.hip).  Weights binary16 [out][in],
 // biases and gradients fp32.

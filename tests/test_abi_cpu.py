@@ -211,7 +211,8 @@ def test_adam_argument_errors(lib):
 
 def test_input_grad_workspace_and_argument_errors(lib):
     cfg = hg.HashGridConfig()
-    assert hg.hashgrid_input_grad_workspace_size(cfg, 1 << 18) == 16 * 3 * 4 << 18
+    # the [L][n][3] stage plus a level-major copy [L][n][2] of the upstream rows
+    assert hg.hashgrid_input_grad_workspace_size(cfg, 1 << 18) == 16 * (3 + 2) * 4 << 18
     assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=2, n_features=4), 10) == 1280  # 16*10*2*4
     assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=1, n_levels=1), 3) == 256    # 12 -> 256
     c = cfg.c()

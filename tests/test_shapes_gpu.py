@@ -150,3 +150,23 @@ def test_shape_binned_backward_edge_cases(oracle, D, F, log2T):
     hg.hashgrid_backward(cfg, dev(x), dev(d), atomic, workspace=None)
     for l in range(w.n_levels):
         assert np.max(np.abs(atomic.cpu().numpy()[l] - ref[l])) <= 1e-5 * np.max(np.abs(ref[l]))
+
+
+@pytest.mark.parametrize("n", [4096 + 2, 1001])
+def test_input_grad_workspace_variants_agree(oracle, n):
+    # Full workspace (stage + level-major copy of the upstream rows), stage only
+    # (the level pass reads the rows), none (point-major): the same fp32 terms
+    # in the same order, so the same bits; even and odd n take the 16-byte and
+    # the 4-byte copy kernels.
+    w = I.resized(I.WORKLOADS["standard"], n)
+    cfg = hg.HashGridConfig.of(w)
+    x, t, d = dev(I.make_points(w)), dev(I.make_table(w)), dev(I.make_dout(w))
+    full = hg.hashgrid_input_grad_workspace_size(cfg, n)
+    stage_only = (n * cfg.n_levels * 3 * 4 + 255) // 256 * 256
+    assert full > stage_only
+    outs = [hg.hashgrid_input_grad(cfg, x, t, d, workspace=ws).cpu().numpy()
+            for ws in (torch.empty(full, dtype=torch.uint8, device=DEV),
+                       torch.empty(stage_only, dtype=torch.uint8, device=DEV), None)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    input_grad_check(outs[0], oracle.input_grad(oracle.grid_of(w), I.make_points(w), I.make_table(w),
+                                                I.make_dout(w)))
