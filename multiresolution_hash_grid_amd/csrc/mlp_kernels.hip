@@ -139,12 +139,15 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 
     FwdWeights w;
     load_fwd_weights(mp, q, c, w);
     const int64_t nwaves = (int64_t)gridDim.x * kMlpWaves;
-    for (int64_t t = (int64_t)blockIdx.x * kMlpWaves + (threadIdx.x >> 6); t < tiles; t += nwaves) {
+    half4_t eb_next[2];
+    int64_t t = (int64_t)blockIdx.x * kMlpWaves + (threadIdx.x >> 6);
+    if (t < tiles) load_encoding(stage, n, min(t * 16 + c, n - 1), q, eb_next);
+    for (; t < tiles; t += nwaves) {
         const int64_t p = t * 16 + c;
         const bool ok = p < n;
-        half4_t eb[2], h1[4], h2[4];
+        half4_t eb[2] = {eb_next[0], eb_next[1]}, h1[4], h2[4];
+        if (t + nwaves < tiles) load_encoding(stage, n, min((t + nwaves) * 16 + c, n - 1), q, eb_next);
         uint32_t m1, m2;
-        load_encoding(stage, n, ok ? p : n - 1, q, eb);
         hidden_layers(w, eb, h1, h2, m1, m2);
         float4_t o = w.b3;
 #pragma unroll
@@ -217,16 +220,29 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 
     }
     gb3 = float4_t{0.f, 0.f, 0.f, 0.f};
     const int64_t nwaves = (int64_t)gridDim.x * kMlpWaves;
-    for (int64_t t = (int64_t)blockIdx.x * kMlpWaves + wave; t < tiles; t += nwaves) {
+    // The next tile's encoding and dL/dy are requested before the current tile
+    // is worked on (one wave per SIMD at this register count: the loads must
+    // not stall it).
+    auto load_tile = [&](int64_t t, half4_t (&eb)[2], float4 &g) {
         const int64_t p = t * 16 + c;
         const bool ok = p < n;
-        half4_t eb[2], h1[4], h2[4], dz1[4], dz2[4], g3;
-        uint32_t m1, m2;
         load_encoding(stage, n, ok ? p : n - 1, q, eb);
-        hidden_layers(w, eb, h1, h2, m1, m2);
         // dL/dy of the point as the B operand (k = output 0..3 on lanes q = 0); points past n give 0.
-        float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+        g = make_float4(0.f, 0.f, 0.f, 0.f);
         if (q == 0 && ok) g = *reinterpret_cast<const float4 *>(dy + p * kOut);
+    };
+    half4_t eb_next[2];
+    float4 g_next;
+    int64_t t = (int64_t)blockIdx.x * kMlpWaves + wave;
+    if (t < tiles) load_tile(t, eb_next, g_next);
+    for (; t < tiles; t += nwaves) {
+        const int64_t p = t * 16 + c;
+        const bool ok = p < n;
+        half4_t eb[2] = {eb_next[0], eb_next[1]}, h1[4], h2[4], dz1[4], dz2[4], g3;
+        const float4 g = g_next;
+        if (t + nwaves < tiles) load_tile(t + nwaves, eb_next, g_next);
+        uint32_t m1, m2;
+        hidden_layers(w, eb, h1, h2, m1, m2);
         g3 = half4_t{(_Float16)g.x, (_Float16)g.y, (_Float16)g.z, (_Float16)g.w};
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
