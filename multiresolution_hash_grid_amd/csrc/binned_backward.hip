@@ -42,15 +42,28 @@
 // Record packing (96 bits; the records are three quarters of the backward's
 // memory traffic, written once and read once):
 //   bits  0..12  lo0, the x corner's index inside the partition (s <= 13);
-//   bits 13..16  t = min(trailing ones of v_x, 15): the x+1 corner's index is
+//   bits 13..16  t = min(trailing ones of v_x, 14): the x+1 corner's index is
 //                lo0 XOR (2^(t+1) - 1) within the partition, because
-//                v_x XOR (v_x + 1) = 2^(t+1) - 1 and the x prime is 1;
+//                v_x XOR (v_x + 1) = 2^(t+1) - 1 and the x prime is 1 (the
+//                cap is exact as partitions have at most 2^13 entries);
 //   bits 17..39  f_x * 2^23: exact, as f_x is a multiple of the ulp of the
 //                fp32 position, >= 2^-23 once the position is >= 1 (below 1,
 //                i.e. in the first voxel, it is rounded to 2^-24);
 //   bits 40..67  w_y w_z g_0 and bits 68..95 w_y w_z g_1, each an fp32 value
 //                rounded to nearest on its 4 lowest mantissa bits (relative
 //                error <= 2^-21, far inside the gradient's 1e-5 bound).
+// t = 15 marks a single-corner record instead: bits 0..12 the corner's index
+// in the partition, words 1 and 2 its two fp32 sums.
+//
+// Wave pre-reduction: the 64 lanes of a wave hold 64 consecutive points.
+// Where consecutive points fall in the same voxel of a level (coarse levels
+// of ray-ordered batches, where a ray crosses one voxel in many samples), the
+// run of lanes shares all 8 corners: a segmented scan across the wave adds
+// the run's 16 corner contributions (8 corners x 2 features, in lane order),
+// and the run's first and last lanes emit 4 single-corner records each in
+// place of the run's 4 pair records per lane.  This cuts the records, and the
+// same-entry LDS atomics in the owners, by the run length; a run of 2 breaks
+// even.
 #include <algorithm>
 
 #include "binned_common.h"
@@ -65,7 +78,7 @@ constexpr int kPtsPerThread = kBinTile / kBinThreads;  // 2
 constexpr int kRecPerTile = kBinTile * 4;              // 4 corner pairs per point
 constexpr int kLevelsPerBlock = 4;                     // levels per bin workgroup
 
-// One corner-pair record (see the packing above); 4-byte aligned, 12 bytes.
+// One corner-pair or single-corner record (see the packing above); 4-byte aligned, 12 bytes.
 struct Rec12 {
     uint32_t a, b, c;
 };
@@ -82,17 +95,26 @@ __device__ __forceinline__ Rec pack_record(uint32_t lo0, uint32_t t, uint32_t fx
     return Rec{lo0 | (t << 13) | (fx23 << 17), (fx23 >> 15) | (a28 << 8), (a28 >> 24) | (b28 << 4)};
 }
 
-// The four corner pairs (dy, dz) of one point at one level.
+constexpr uint32_t kSingle = 15u;  // t of a single-corner record
+
+__device__ __forceinline__ Rec single_record(uint32_t lo, float A, float B) {
+    return Rec{lo | (kSingle << 13), __float_as_uint(A), __float_as_uint(B)};
+}
+
+// The records of one point at one level: the four corner pairs (dy, dz), or
+// none or four single corners after the wave pre-reduction.
 struct Pairs {
     uint32_t part[4];
     Rec rec[4];
+    uint32_t nrec;          // 4, or 0 / 4 inside a pre-reduced run of lanes
     uint32_t split_idx[4];  // table entry of an x+1 corner outside the pair's partition, or ~0u
     float2 split_val[4];
     float dabs;             // max(|g_0|, |g_1|)
 };
 
+// wbuf: this wave's 16 x 64 floats of LDS, free while the records are made.
 __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1, int l, const BinParams &bp,
-                                           Pairs &out) {
+                                           bool valid, float *wbuf, Pairs &out) {
     const float N = (float)bp.res[l];
     int32_t v0, v1, v2;
     float a0, a1, a2;
@@ -103,8 +125,9 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
     const uint32_t cx0 = (uint32_t)v0, cx1 = cx0 + 1u;
     const uint32_t smask = (1u << bp.s_log2) - 1u;
     out.dabs = fmaxf(fabsf(d0), fabsf(d1));
+    out.nrec = valid ? 4u : 0u;
     // trailing ones of v_x (bit 31 set keeps ctz defined for v_x = -1)
-    const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 15u);
+    const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 14u);
     // f_x * 2^23 (exact for positions >= 1; the first voxel's fraction rounds)
     const uint32_t fx23 = min(__float2uint_rn(a0 * 8388608.f), 8388607u);
 #pragma unroll
@@ -127,6 +150,55 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
             out.split_idx[c] = i1;
             out.split_val[c] = make_float2(a0 * A, a0 * B);
         }
+    }
+    // Wave pre-reduction of runs of consecutive lanes in one voxel.
+    const int lane = threadIdx.x & 63;
+    // Every lane takes part in the shuffles (a short-circuited shuffle would read inactive lanes).
+    const int32_t u0 = __shfl_up(v0, 1, 64), u1 = __shfl_up(v1, 1, 64), u2 = __shfl_up(v2, 1, 64);
+    const bool same = valid && lane > 0 && u0 == v0 && u1 == v1 && u2 == v2;
+    const uint64_t dup = __ballot(same);
+    if (dup == 0) return;  // wave-uniform: no two neighbouring points share a voxel
+    const uint64_t heads = ~dup, tails = (heads >> 1) | (1ull << 63);
+    const int start = 63 - __builtin_clzll(heads & ((2ull << lane) - 1ull));  // first lane of this lane's run
+    const int end = __builtin_ctzll(tails & (~0ull << lane));                // last lane of this lane's run
+    // Each lane parks its 16 corner contributions (corner (dx, c), c = 2 dy + dz,
+    // feature j at wbuf[(8 dx + 2 c + j) * 64 + lane]); the run's first lane
+    // sums the x corners over the run and its last lane the x+1 corners, in
+    // lane order.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float wyz = ((c >> 1) ? a1 : 1.f - a1) * ((c & 1) ? a2 : 1.f - a2);
+        const float w0 = (1.f - a0) * wyz, w1 = a0 * wyz;
+        wbuf[(2 * c + 0) * 64 + lane] = w0 * d0;
+        wbuf[(2 * c + 1) * 64 + lane] = w0 * d1;
+        wbuf[(8 + 2 * c + 0) * 64 + lane] = w1 * d0;
+        wbuf[(8 + 2 * c + 1) * 64 + lane] = w1 * d1;
+    }
+    wave_lds_fence();
+    if (start == end) return;  // a run of one lane keeps its pair records
+    // A run of m >= 2 lanes emits 8 single-corner records in place of 4 m pair
+    // records: 4 from its first lane, 4 from its last.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out.split_idx[c] = ~0u;
+    const bool first = lane == start;
+    out.nrec = first || lane == end ? 4u : 0u;
+    if (!out.nrec) return;
+    const float *src = wbuf + (first ? 0 : 8 * 64);
+    float sum[4][2] = {};
+    for (int i = start; i <= end; ++i) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            sum[c][0] += src[(2 * c + 0) * 64 + i];
+            sum[c][1] += src[(2 * c + 1) * 64 + i];
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t dy = (uint32_t)(c >> 1), dz = (uint32_t)(c & 1);
+        const uint32_t K = (hy0 + dy * kPrimeY) ^ (hz0 + dz * kPrimeZ);
+        const uint32_t i = ((first ? cx0 : cx1) ^ K) & bp.mask;
+        out.part[c] = i >> bp.s_log2;
+        out.rec[c] = single_record(i & smask, sum[c][0], sum[c][1]);
     }
 }
 
@@ -186,6 +258,9 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
     const int tile = blockIdx.x;
     const int gb = blockIdx.y * kLevelsPerBlock;
     const int nlev = min(bp.group - gb, kLevelsPerBlock);
+    // The wave pre-reduction borrows the stage before the records are sorted into it.
+    static_assert(kBinThreads / 64 * 16 * 64 * sizeof(float) <= sizeof(Rec) * kRecPerTile, "stage too small");
+    float *wbuf = reinterpret_cast<float *>(stage) + (threadIdx.x >> 6) * (16 * 64);
     TilePoints tp;
     load_points<true>(x, n, dout, dstride, tile, bp.level0 + gb, nlev, tp);
 #pragma unroll
@@ -200,11 +275,12 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
         float dm = 0.f;
 #pragma unroll
         for (int k = 0; k < kPtsPerThread; ++k) {
-            make_pairs(tp.xs[k], tp.dv[k][j][0], tp.dv[k][j][1], l, bp, pr[k]);
+            make_pairs(tp.xs[k], tp.dv[k][j][0], tp.dv[k][j][1], l, bp, tp.valid[k], wbuf, pr[k]);
             if (tp.valid[k]) dm = fmaxf(dm, pr[k].dabs);
 #pragma unroll
+            for (int c = 0; c < 4; ++c) rank[k][c] = c < (int)pr[k].nrec ? atomicAdd(&cnt[pr[k].part[c]], 1u) : 0u;
+#pragma unroll
             for (int c = 0; c < 4; ++c) {
-                rank[k][c] = tp.valid[k] ? atomicAdd(&cnt[pr[k].part[c]], 1u) : 0u;
                 if (tp.valid[k] && pr[k].split_idx[c] != ~0u) {
                     float *e = grad + (((uint64_t)l << bp.log2_table_size) + pr[k].split_idx[c]) * 2;
                     unsafeAtomicAdd(e, pr[k].split_val[c].x);
@@ -229,7 +305,7 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
         for (int k = 0; k < kPtsPerThread; ++k) {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (tp.valid[k]) stage[base[pr[k].part[c]] + rank[k][c]] = pr[k].rec[c];
+                if (c < (int)pr[k].nrec) stage[base[pr[k].part[c]] + rank[k][c]] = pr[k].rec[c];
         }
         __syncthreads();
         const uint32_t total = base[bp.parts];
@@ -248,6 +324,11 @@ struct StdPolicy {
     static constexpr int kRecPerTile = kBinTile * 4;
     static __device__ __forceinline__ void apply(unsigned long long *slice, const Rec r, int k, uint32_t smask) {
         const uint32_t lo0 = r.a & 0x1FFFu, t = (r.a >> 13) & 0xFu;
+        if (t == kSingle) {  // a pre-reduced run's corner: its sums may exceed max|dL/dout|
+            atomicAdd(slice + 2 * lo0, to_fixed_wide(__uint_as_float(r.b), k));
+            atomicAdd(slice + 2 * lo0 + 1, to_fixed_wide(__uint_as_float(r.c), k));
+            return;
+        }
         const uint32_t lo1 = lo0 ^ (((2u << t) - 1u) & smask);
         const uint32_t fx23 = (r.a >> 17) | ((r.b & 0xFFu) << 15);
         const float fx = (float)fx23 * 0x1p-23f;  // exact: fx23 < 2^23

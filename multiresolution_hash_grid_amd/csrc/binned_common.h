@@ -74,6 +74,15 @@ __device__ __forceinline__ unsigned long long to_fixed(float c, int k) {
     return (unsigned long long)(long long)(int32_t)rintf(ldexpf(c, k));
 }
 
+// The same for |c * 2^k| < 2^39 (sums of up to 2^8 contributions): past 2^31
+// the rounded value is an fp32 integer whose ulp is at least 2^8, so it is
+// 2^8 times an integer below 2^31.
+__device__ __forceinline__ unsigned long long to_fixed_wide(float c, int k) {
+    const float v = rintf(ldexpf(c, k));
+    if (fabsf(v) < 2147483648.f) return (unsigned long long)(long long)(int32_t)v;
+    return (unsigned long long)((long long)(int32_t)(v * 0x1p-8f) * 256);
+}
+
 // Fixed-point exponent of a level: max|dL/dout| < 2^e  ->  k = 30 - e.
 __device__ __forceinline__ int fixed_exponent(uint32_t dmax_bits) {
     const float m = __uint_as_float(dmax_bits);

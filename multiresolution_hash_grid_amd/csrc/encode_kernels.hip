@@ -186,7 +186,8 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
 // ---------------------------------------------------------------- backward
 
 // LANES = 4: lane (dx, j) = (sub >> 1, sub & 1) adds feature j of the four
-// corners with that dx; the four lanes of a point hit one or two lines.
+// corners with that dx; the four lanes of a point hit one or two lines (the
+// default atomic path, bwd_f2_quad_kernel, adds the wave pre-reduction to it).
 // LANES = 2: lane dx adds both features of its four corners.
 // LANES = 1: one lane adds all sixteen values.
 template <int LANES>
@@ -241,6 +242,75 @@ __global__ __launch_bounds__(kBlock) void bwd_f2_kernel(const float *__restrict_
                 fadd(g + 2 * i11, g0 * w11);
                 fadd(g + 2 * i11 + 1, g1 * w11);
             }
+        }
+    }
+}
+
+// Four lanes (dx, j) per point, 16 consecutive points per wave, with the
+// wave pre-reduction of duplicate coarse-level corners: a run of consecutive
+// points in one voxel (ray samples at coarse levels) shares all 8 corners.
+// Each lane parks its 4 contributions (feature j of the corners (dx, dy, dz))
+// in LDS; the lanes of the run's first point add the run's sums, in point
+// order, and the other points of the run add nothing, so a run of m points
+// costs 16 atomics instead of 16 m.  The four lanes of a point hit one or two
+// lines, so each atomic instruction makes few requests.
+__global__ __launch_bounds__(kBlock) void bwd_f2_quad_kernel(const float *__restrict__ x, int64_t n,
+                                                             const float *__restrict__ dout, int64_t dstride,
+                                                             float *__restrict__ grad, LaunchParams lp) {
+    __shared__ float park[kBlock / 64][4 * 64];
+    Item it;
+    if (!decode_item(lp, it)) return;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint32_t mask = lp.mask;
+    float *__restrict__ g = grad + 2 * ((uint64_t)l << lp.log2_table_size);
+    const int lane = threadIdx.x & 63, sub = lane & 3;
+    const int dx = sub >> 1, j = sub & 1;
+    float *wbuf = park[threadIdx.x >> 6];
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    // wave-uniform loop over the wave's 16 points: every lane runs the shuffles and the ballot
+    for (int64_t pw = it.p0 + (threadIdx.x >> 2 & ~15); pw < end; pw += kBlock / 4) {
+        const int64_t p = pw + (lane >> 2);
+        const bool valid = p < end;
+        const int64_t q = valid ? p : pw;
+        int32_t v0, v1, v2;
+        float a0, a1, a2;
+        locate1(x[3 * q + 0], N, v0, a0);
+        locate1(x[3 * q + 1], N, v1, a1);
+        locate1(x[3 * q + 2], N, v2, a2);
+        const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hy1 = hy0 + kPrimeY;
+        const uint32_t hz0 = (uint32_t)v2 * kPrimeZ, hz1 = hz0 + kPrimeZ;
+        const float gw = dout[q * dstride + 2 * l + j] * (dx ? a0 : 1.f - a0);
+        const float wy0 = 1.f - a1, wz0 = 1.f - a2;
+        float c[4] = {gw * (wy0 * wz0), gw * (wy0 * a2), gw * (a1 * wz0), gw * (a1 * a2)};
+        const int32_t u0 = __shfl_up(v0, 4, 64), u1 = __shfl_up(v1, 4, 64), u2 = __shfl_up(v2, 4, 64);
+        const bool same = valid && lane >= 4 && u0 == v0 && u1 == v1 && u2 == v2;
+        const uint64_t dup = __ballot(same);  // the 4 lanes of a point agree
+        bool emit = valid;
+        if (dup != 0) {
+            const uint64_t heads = ~dup, tails = (heads >> 4) | (0xFull << 60);
+            const int first = (63 - __builtin_clzll(heads & ((2ull << lane) - 1ull))) >> 2;  // run's first point
+            const int last = __builtin_ctzll(tails & (~0ull << lane)) >> 2;                  // run's last point
+#pragma unroll
+            for (int k = 0; k < 4; ++k) wbuf[k * 64 + lane] = c[k];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            emit = valid && first == (lane >> 2);
+            if (emit && last > first) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) c[k] = 0.f;
+                for (int i = first; i <= last; ++i)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) c[k] += wbuf[k * 64 + 4 * i + sub];
+            }
+            // the next pass overwrites this wave's parked values after these reads
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+        if (emit) {
+            const uint32_t cx = (uint32_t)v0 + (uint32_t)dx;
+            fadd(g + 2 * ((cx ^ hy0 ^ hz0) & mask) + j, c[0]);
+            fadd(g + 2 * ((cx ^ hy0 ^ hz1) & mask) + j, c[1]);
+            fadd(g + 2 * ((cx ^ hy1 ^ hz0) & mask) + j, c[2]);
+            fadd(g + 2 * ((cx ^ hy1 ^ hz1) & mask) + j, c[3]);
         }
     }
 }
@@ -372,7 +442,7 @@ hipError_t launch_encode_stage_f16(const LaunchParams &lp, const float *x, int64
 hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, const float *dout,
                            int64_t dout_stride, float *dtable, int lanes, hipStream_t stream) {
     dim3 grid(grid_blocks(lp)), block(kBlock);
-    if (lanes == 4) bwd_f2_kernel<4><<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
+    if (lanes == 4) bwd_f2_quad_kernel<<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
     else if (lanes == 2) bwd_f2_kernel<2><<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
     else bwd_f2_kernel<1><<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
     return hipGetLastError();

@@ -74,4 +74,5 @@ def test_adam_optimizer_class_matches_torch_adam():
         oa.step()
         ob.step()
     torch.cuda.synchronize()
+    a, b = a.detach(), b.detach()
     assert float((a - b).abs().max()) <= 1e-6 * float(b.abs().max()) + 1e-7

@@ -206,6 +206,43 @@ def test_backward_exact_dyadic_case(oracle):
     assert np.array_equal(grad.astype(np.float64), ref)
 
 
+def runs_of_points(seed, n, max_run=100, jitter=2e-4):
+    # Consecutive points that share a voxel at the coarse levels, as ray samples
+    # do: runs of 1..max_run points around one base point each, and one run of
+    # 200 identical points in the middle.
+    rng = np.random.default_rng(seed)
+    x = np.empty((n, 3), dtype=np.float64)
+    i = 0
+    while i < n:
+        m = min(int(rng.integers(1, max_run + 1)), n - i)
+        x[i:i + m] = rng.uniform(0.01, 0.99, 3) + rng.uniform(-jitter, jitter, (m, 3))
+        i += m
+    mid = n // 2
+    x[mid:mid + 200] = x[mid]
+    return np.clip(x, 0.0, 0.999).astype(np.float32)
+
+
+@pytest.mark.parametrize("name,n", [("standard", 3 * 1024 + 37), ("standard", 4096), ("tiny", 2 * 512 + 63)])
+def test_backward_runs_of_points_in_one_voxel(oracle, name, n):
+    # Runs of consecutive points in one voxel are summed inside the wave before
+    # they become records: runs crossing wave and tile boundaries and the ragged
+    # end, runs of identical points whose sums exceed max|dL/dout| many times,
+    # and the one-partition table of the tiny grid.
+    w = I.resized(I.WORKLOADS[name], n)
+    print(f"backward runs {name} n={n}", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    x, d = runs_of_points(n, n), I.make_dout(w)
+    ref = oracle.backward(oracle.grid_of(w), x, d)
+    bwd_check(run_backward(cfg, x, d), ref, w.n_levels)
+    old = hg.hashgrid_tune_get(B.HG_TUNE_BWD_LANES)
+    try:
+        for lanes in (1, 2, 4):  # the atomic kernels; one lane per point pre-reduces the runs
+            hg.hashgrid_tune(B.HG_TUNE_BWD_LANES, lanes)
+            bwd_check(run_backward(cfg, x, d, workspace=None), ref, w.n_levels)
+    finally:
+        hg.hashgrid_tune(B.HG_TUNE_BWD_LANES, old)
+
+
 def test_backward_accumulates_and_reads_strided_rows(oracle):
     w = I.resized(I.WORKLOADS["standard"], 2000)
     cfg = hg.HashGridConfig.of(w)
