@@ -72,7 +72,7 @@ def _unmangle(name: str) -> str:
 def short_name(name: str) -> str:
     if name.startswith("_ZN"):
         return _unmangle(name)
-    name = name.replace("hg::(anonymous namespace)::", "").replace("void ", "")
+    name = re.sub(r"hg::(\(anonymous namespace\)::|binned::)+", "", name).replace("void ", "")
     return re.sub(r"\(.*", "", name)
 
 
