@@ -278,7 +278,8 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
     if ((rc = plan(*cfg, n, lp))) return rc;
     if (!standard_shape(*cfg))
         return launch_status(hg::launch_forward_generic(lp, cfg->n_dims, cfg->n_features, x, n, table,
-                                                        cfg->table_dtype, out, out_row_stride, (hipStream_t)stream),
+                                                        cfg->table_dtype, out, out_row_stride, g_tune.fwd_lanes,
+                                                        (hipStream_t)stream),
                              "forward");
     const size_t stage_bytes = (size_t)n * cfg->n_levels * cfg->n_features * sizeof(float);
     float *stage = (g_tune.fwd_staged && workspace && workspace_bytes >= stage_bytes) ? (float *)workspace : nullptr;

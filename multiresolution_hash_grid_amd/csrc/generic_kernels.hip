@@ -100,6 +100,78 @@ __global__ __launch_bounds__(kBlock) void fwd_generic_kernel(const float *__rest
     }
 }
 
+// Points per lane pair in flight: the 2^(D-1) corner loads of U points are
+// issued before the first blend, within about 32 registers of features.
+constexpr int pair_unroll(int D, int F) {
+    const int per = (1 << (D - 1)) * F;
+    return per <= 8 ? 4 : per <= 16 ? 2 : 1;
+}
+
+// Lane-pair forward of every shape: lane sub of a pair takes the corners whose
+// first coordinate is v_0 + sub.  The first prime is 1, so the two corners of
+// an x-pair differ in the low index bits and mostly share a 128-byte line: the
+// pair's two loads are one line request where one thread per point makes two.
+// The halves' partial sums are exchanged with a DPP swap and each lane writes
+// half of the level's F features (F = 1: lane 0 writes).
+template <int D, int F, int DT>
+__global__ __launch_bounds__(kBlock) void fwd_generic_pair_kernel(const float *__restrict__ x, int64_t n,
+                                                                  const void *__restrict__ table,
+                                                                  float *__restrict__ out, int64_t ostride,
+                                                                  LaunchParams lp) {
+    constexpr int U = pair_unroll(D, F), H = 1 << (D - 1), kPairs = kBlock / 2;
+    Item it;
+    if (!decode_item(lp, it)) return;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    const int sub = threadIdx.x & 1;
+    const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
+    for (int64_t p0 = it.p0 + (threadIdx.x >> 1); p0 < end; p0 += (int64_t)kPairs * U) {
+        float e[U][H][F];
+        Voxel<D> vx[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t p = p0 + (int64_t)u * kPairs;
+            ok[u] = p < end;
+            locate_point<D>(x + (ok[u] ? p : p0) * D, N, vx[u]);  // p0 < end: always a valid point
+#pragma unroll
+            for (int h = 0; h < H; ++h)
+                load_features<F, DT>(table, lbase + corner_hash<D>(vx[u], sub * H + h, lp.mask), e[u][h]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float part[F];
+#pragma unroll
+            for (int j = 0; j < F; ++j) part[j] = 0.f;
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                const float w = corner_weight<D>(vx[u], sub * H + h);
+#pragma unroll
+                for (int j = 0; j < F; ++j) part[j] += w * e[u][h][j];
+            }
+            float *orow = out + (p0 + (int64_t)u * kPairs) * ostride + (int64_t)l * F;
+            if constexpr (F == 1) {
+                const float v = part[0] + swap_pair(part[0]);
+                if (ok[u] && sub == 0) orow[0] = v;
+            } else {
+                constexpr int HF = F / 2;
+                float v[HF];
+#pragma unroll
+                for (int i = 0; i < HF; ++i) {
+                    // lane 0 writes features [0, F/2) and sends the upper half; lane 1 the reverse
+                    const float mine = sub ? part[HF + i] : part[i];
+                    v[i] = mine + swap_pair(sub ? part[i] : part[HF + i]);
+                }
+                if (ok[u]) {
+#pragma unroll
+                    for (int i = 0; i < HF; ++i) orow[sub * HF + i] = v[i];
+                }
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- backward
 
 template <int D, int F>
@@ -441,14 +513,20 @@ bool dispatch_shape(int D, int F, Fn &&fn) {
 }  // namespace
 
 hipError_t launch_forward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
-                                  const void *table, int table_dtype, float *out, int64_t out_stride,
+                                  const void *table, int table_dtype, float *out, int64_t out_stride, int lanes,
                                   hipStream_t stream) {
     const dim3 grid(grid_blocks(lp)), block(kBlock);
     const bool ok = dispatch_shape(D, F, [&]<int DD, int FF>() {
-        if (table_dtype == 0)
-            fwd_generic_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
-        else
-            fwd_generic_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+        if (lanes == 1) {  // one thread per (point, level)
+            if (table_dtype == 0)
+                fwd_generic_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+            else
+                fwd_generic_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+        } else if (table_dtype == 0) {
+            fwd_generic_pair_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+        } else {
+            fwd_generic_pair_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+        }
     });
     return ok ? hipGetLastError() : hipErrorInvalidValue;
 }

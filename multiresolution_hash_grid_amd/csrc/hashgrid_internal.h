@@ -102,7 +102,7 @@ hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, co
 // Shapes other than D = 3, F = 2 (generic_kernels.hip): D in 1..4,
 // F in {1, 2, 4, 8}; hipErrorInvalidValue for an unbuilt shape.
 hipError_t launch_forward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
-                                  const void *table, int table_dtype, float *out, int64_t out_stride,
+                                  const void *table, int table_dtype, float *out, int64_t out_stride, int lanes,
                                   hipStream_t stream);
 hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
                                    const float *dout, int64_t dout_stride, float *dtable, hipStream_t stream);

@@ -17,6 +17,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import multiresolution_hash_grid_amd as hg  # noqa: E402
+from multiresolution_hash_grid_amd import hashgrid as B  # noqa: E402
 from multiresolution_hash_grid_amd import inputs as I  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -72,6 +73,24 @@ def test_shape_forward_backward_corners(oracle, D, F, dtype):
     ridx, rw = oracle.corners(g, x)
     assert np.array_equal(idx.cpu().numpy().view(np.uint32), ridx)
     assert np.max(np.abs(wt.cpu().numpy() - rw)) <= 2.5e-7
+
+
+@pytest.mark.parametrize("D,F,dtype", SHAPES)
+def test_shape_forward_one_lane_per_point(oracle, D, F, dtype):
+    # The default forward of these shapes uses lane pairs (one lane per x
+    # offset); one thread per (point, level) is the other launch shape.
+    w = shape_workload(D, F, dtype)
+    cfg = hg.HashGridConfig.of(w)
+    x, t = I.make_points(w), I.make_table(w)
+    ref = oracle.forward(oracle.grid_of(w), x, t)
+    tmax = float(np.max(np.abs(t.astype(np.float64))))
+    old = hg.hashgrid_tune_get(B.HG_TUNE_FWD_LANES)
+    try:
+        hg.hashgrid_tune(B.HG_TUNE_FWD_LANES, 1)
+        one = hg.hashgrid_forward(cfg, dev(x), dev(t)).cpu().numpy()
+    finally:
+        hg.hashgrid_tune(B.HG_TUNE_FWD_LANES, old)
+    assert one.shape == ref.shape and float(np.max(np.abs(one - ref))) <= 1e-6 * tmax
 
 
 @pytest.mark.parametrize("D,F,dtype", SHAPES + [(3, 2, "f32"), (3, 2, "f16")])
