@@ -108,8 +108,9 @@ def measure_input_grad(cfg, x, t, d, iters: int) -> dict:
 
 
 def measure_shapes(dev, n: int, iters: int) -> dict:
-    """Forward (generic kernel) and backward (generic binned path) of other
-    grid shapes at the standard L, T and resolutions, n uniform points."""
+    """Forward (lane-pair kernel, staged for F <= 4) and backward (generic
+    binned path) of other grid shapes at the standard L, T and resolutions, n
+    uniform points."""
     import torch
     import multiresolution_hash_grid_amd as hg
     from multiresolution_hash_grid_amd import inputs
@@ -123,7 +124,8 @@ def measure_shapes(dev, n: int, iters: int) -> dict:
         o = torch.empty((n, cfg.out_features), device=dev)
         g = torch.zeros(cfg.table_shape, device=dev)
         ws = hg.backward_workspace(cfg, n, dev)
-        fms = time_calls(lambda: hg.hashgrid_forward(cfg, x, t, out=o, workspace=None), iters)
+        fws = hg.forward_workspace(cfg, n, dev)
+        fms = time_calls(lambda: hg.hashgrid_forward(cfg, x, t, out=o, workspace=fws), iters)
         bms = time_calls(lambda: hg.hashgrid_backward(cfg, x, d, g, workspace=ws), iters)
         L, K = cfg.n_levels, 1 << D
         fb = 4 * D + K * 4 * L * F + 4 * L * F
@@ -131,7 +133,7 @@ def measure_shapes(dev, n: int, iters: int) -> dict:
         out[f"D{D}_F{F}"] = {"fwd_points_per_s": n / (fms * 1e-3), "bwd_points_per_s": n / (bms * 1e-3),
                              "fwd_frac": fb * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del x, t, d, o, g, ws
+        del x, t, d, o, g, ws, fws
     return out
 
 

@@ -102,8 +102,10 @@ int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *byt
  *           hashgrid_forward_workspace_size bytes each level's encodings are
  *           first written level-major (whole cache lines, so the level's table
  *           stays in L2) and then transposed into the rows; without it every
- *           level writes its F values straight into the rows.  Results are
- *           identical either way.  Concurrent calls must not share a workspace.
+ *           level writes its F values straight into the rows.  F = 8 grids
+ *           always write the rows directly (32 bytes per level and row).
+ *           Results are identical either way.  Concurrent calls must not share
+ *           a workspace.
  *   The blend of level l is sum_k w_k * table[l][h(corner_k)][j] computed in
  *   fp32, with w_k the trilinear weight of corner k.
  * Errors: HG_EINVAL (config, NULL, alignment, n < 0, stride), HG_EUNSUPPORTED,

@@ -276,13 +276,14 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
     if (workspace && !aligned(workspace, 256)) return fail(HG_EINVAL, "workspace is not 256-byte aligned");
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
+    const size_t stage_bytes = (size_t)n * cfg->n_levels * cfg->n_features * sizeof(float);
+    float *stage = (g_tune.fwd_staged && workspace && workspace_bytes >= stage_bytes) ? (float *)workspace : nullptr;
+    // F = 8 rows take 32 bytes per level, whole enough that staging costs more than it saves.
     if (!standard_shape(*cfg))
         return launch_status(hg::launch_forward_generic(lp, cfg->n_dims, cfg->n_features, x, n, table,
                                                         cfg->table_dtype, out, out_row_stride, g_tune.fwd_lanes,
-                                                        (hipStream_t)stream),
+                                                        cfg->n_features <= 4 ? stage : nullptr, (hipStream_t)stream),
                              "forward");
-    const size_t stage_bytes = (size_t)n * cfg->n_levels * cfg->n_features * sizeof(float);
-    float *stage = (g_tune.fwd_staged && workspace && workspace_bytes >= stage_bytes) ? (float *)workspace : nullptr;
     const hg::FwdTune ft{g_tune.fwd_lanes, g_tune.fwd_unroll, g_tune.fwd_nt};
     return launch_status(hg::launch_forward(lp, x, n, table, cfg->table_dtype, out, out_row_stride, ft, stage,
                                             (hipStream_t)stream),

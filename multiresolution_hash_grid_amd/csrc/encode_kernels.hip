@@ -19,6 +19,8 @@
 // two x-corners of one point to two adjacent lanes of the same load or atomic
 // instruction, so the memory pipeline sees about 4 distinct lines per
 // (point, level) instead of 8.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace hg {
@@ -341,52 +343,75 @@ int grid_blocks(const LaunchParams &lp) {
     return lp.xcd_map ? kNumXcd * lp.per_xcd : lp.items;
 }
 
-// Level-major staging [L][n][2] -> rows out[p * ostride + l * 2 + j], 64
+// Level-major staging [L][n][F] -> rows out[p * ostride + l * F + j], pts
 // points per workgroup through LDS so that both sides move whole lines.
-// VEC moves 16 bytes per access on both sides (n even, L even, rows and
-// output 16-byte aligned); otherwise 4 bytes.
-constexpr int kTransposePts = 64;
-
-template <bool VEC>
+// VEC moves 16 bytes per access on both sides (F n and F L multiples of 4,
+// rows and output 16-byte aligned); otherwise 4 bytes.
+template <int F, bool VEC>
 __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restrict__ stage, int64_t n, int L,
-                                                           float *__restrict__ out, int64_t ostride) {
-    extern __shared__ float tile[];  // [kTransposePts][2L + 4]: rows 16-byte aligned
-    const int row = 2 * L + 4;
-    const int64_t p0 = (int64_t)blockIdx.x * kTransposePts;
-    const int np = (int)min((int64_t)kTransposePts, n - p0);
+                                                           int pts, float *__restrict__ out, int64_t ostride) {
+    extern __shared__ float tile[];  // [pts][F L + 4]: rows 16-byte aligned when F L is a multiple of 4
+    const int row = F * L + 4;
+    const int64_t p0 = (int64_t)blockIdx.x * pts;
+    const int np = (int)min((int64_t)pts, n - p0);
     if constexpr (VEC) {
-        // Level l of this block is 2 np contiguous floats: np / 2 float4 (np even: n is).
-        const int q_per_level = kTransposePts / 2;
+        // Level l of this block is F np contiguous floats, F np / 4 float4 (pts is a multiple of 4).
+        const int q_per_level = F * pts / 4;
         for (int e = threadIdx.x; e < L * q_per_level; e += kBlock) {
             const int l = e / q_per_level, qd = e - l * q_per_level;
-            if (2 * qd < np) {
-                const float4 v = *reinterpret_cast<const float4 *>(stage + ((int64_t)l * n + p0) * 2 + 4 * qd);
-                // points 2 qd and 2 qd + 1, features 0 and 1 of level l
-                *reinterpret_cast<float2 *>(&tile[(2 * qd) * row + 2 * l]) = make_float2(v.x, v.y);
-                *reinterpret_cast<float2 *>(&tile[(2 * qd + 1) * row + 2 * l]) = make_float2(v.z, v.w);
+            if (4 * qd < F * np) {
+                const float4 v = *reinterpret_cast<const float4 *>(stage + ((int64_t)l * n + p0) * F + 4 * qd);
+                if constexpr (F == 1) {
+                    tile[(4 * qd + 0) * row + l] = v.x;
+                    tile[(4 * qd + 1) * row + l] = v.y;
+                    tile[(4 * qd + 2) * row + l] = v.z;
+                    tile[(4 * qd + 3) * row + l] = v.w;
+                } else if constexpr (F == 2) {
+                    // points 2 qd and 2 qd + 1, features 0 and 1 of level l
+                    *reinterpret_cast<float2 *>(&tile[(2 * qd) * row + 2 * l]) = make_float2(v.x, v.y);
+                    *reinterpret_cast<float2 *>(&tile[(2 * qd + 1) * row + 2 * l]) = make_float2(v.z, v.w);
+                } else {
+                    // features 4 qd mod F .. + 3 of point 4 qd / F
+                    const int i = 4 * qd / F, f = 4 * qd - i * F;
+                    *reinterpret_cast<float4 *>(&tile[i * row + F * l + f]) = v;
+                }
             }
         }
         __syncthreads();
-        const int q_per_row = L / 2;  // float4 per output row
-        for (int e = threadIdx.x; e < kTransposePts * q_per_row; e += kBlock) {
+        const int q_per_row = F * L / 4;  // float4 per output row
+        for (int e = threadIdx.x; e < pts * q_per_row; e += kBlock) {
             const int i = e / q_per_row, c = e - i * q_per_row;
             if (i < np)
                 *reinterpret_cast<float4 *>(out + (p0 + i) * ostride + 4 * c) =
                     *reinterpret_cast<const float4 *>(&tile[i * row + 4 * c]);
         }
     } else {
-        const int total = kTransposePts * 2 * L;
+        const int total = pts * F * L;
         for (int e = threadIdx.x; e < total; e += kBlock) {
-            const int l = e / (2 * kTransposePts), r = e - l * 2 * kTransposePts;
-            const int i = r >> 1, j = r & 1;
-            if (i < np) tile[i * row + 2 * l + j] = stage[((int64_t)l * n + p0 + i) * 2 + j];
+            const int l = e / (F * pts), r = e - l * F * pts;
+            const int i = r / F, j = r - i * F;
+            if (i < np) tile[i * row + F * l + j] = stage[((int64_t)l * n + p0 + i) * F + j];
         }
         __syncthreads();
         for (int e = threadIdx.x; e < total; e += kBlock) {
-            const int i = e / (2 * L), c = e - i * 2 * L;
+            const int i = e / (F * L), c = e - i * F * L;
             if (i < np) out[(p0 + i) * ostride + c] = tile[i * row + c];
         }
     }
+}
+
+template <int F>
+hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, int64_t ostride,
+                              hipStream_t stream) {
+    // Points per workgroup: 64, fewer for wide rows so that the tile stays near 32 KB.
+    const int pts = std::max(4, std::min(64, 8192 / (F * L + 4)) / 4 * 4);
+    const unsigned blocks = (unsigned)((n + pts - 1) / pts);
+    const size_t lds = (size_t)pts * (F * L + 4) * sizeof(float);
+    const bool vec = (n * F) % 4 == 0 && (F * L) % 4 == 0 && ostride % 4 == 0 && ((uintptr_t)out & 15) == 0 &&
+                     ((uintptr_t)stage & 15) == 0;
+    if (vec) transpose_kernel<F, true><<<blocks, kBlock, lds, stream>>>(stage, n, L, pts, out, ostride);
+    else transpose_kernel<F, false><<<blocks, kBlock, lds, stream>>>(stage, n, L, pts, out, ostride);
+    return hipGetLastError();
 }
 
 template <int DT>
@@ -420,13 +445,18 @@ hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, con
     e = table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, stage, 2, 2 * n, ft, stream)
                          : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream);
     if (e != hipSuccess) return e;
-    const unsigned blocks = (unsigned)((n + kTransposePts - 1) / kTransposePts);
-    const size_t lds = (size_t)kTransposePts * (2 * lp.n_levels + 4) * sizeof(float);
-    const bool vec = n % 2 == 0 && lp.n_levels % 2 == 0 && out_stride % 4 == 0 && ((uintptr_t)out & 15) == 0 &&
-                     ((uintptr_t)stage & 15) == 0;
-    if (vec) transpose_kernel<true><<<blocks, kBlock, lds, stream>>>(stage, n, lp.n_levels, out, out_stride);
-    else transpose_kernel<false><<<blocks, kBlock, lds, stream>>>(stage, n, lp.n_levels, out, out_stride);
-    return hipGetLastError();
+    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream);
+}
+
+hipError_t launch_transpose(int F, const float *stage, int64_t n, int L, float *out, int64_t ostride,
+                            hipStream_t stream) {
+    switch (F) {
+    case 1: return launch_transpose_f<1>(stage, n, L, out, ostride, stream);
+    case 2: return launch_transpose_f<2>(stage, n, L, out, ostride, stream);
+    case 4: return launch_transpose_f<4>(stage, n, L, out, ostride, stream);
+    case 8: return launch_transpose_f<8>(stage, n, L, out, ostride, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_encode_stage_f16(const LaunchParams &lp, const float *x, int64_t n, const void *table,

@@ -12,8 +12,10 @@
 // out[l*F + j] = sum_k w_k table[l][h(c_k)][j]; the backward adds
 // w_k dL/dout[l*F + j] into every entry a corner hashed to.  The D = 3, F = 2
 // grid has its own tuned kernels (encode_kernels.hip, binned_backward.hip);
-// these cover the other shapes with one thread per (point, level), direct row
-// writes and fp32 global atomics in the backward.
+// these cover the other shapes: a lane-pair forward (written level-major and
+// transposed into the rows for F <= 4), a one-thread-per-(point, level)
+// forward, the fp32-atomic backward used without a workspace (the binned one
+// is generic_binned.hip) and the corner export.
 //
 // Gradient with respect to the points (implied by ipipp.com section 3, which
 // puts a learned canonical-space transform before the encoder; never written
@@ -69,11 +71,14 @@ __device__ __forceinline__ float corner_weight(const Voxel<D> &vx, int k) {
 
 // ---------------------------------------------------------------- forward
 
+// Output element (p, l, j) is out[p * ostride + l * lstride + j]: lstride = F
+// writes [n][L*F] rows, ostride = F with lstride = F n a level-major [L][n][F]
+// stage whose stores are whole lines.
 template <int D, int F, int DT>
 __global__ __launch_bounds__(kBlock) void fwd_generic_kernel(const float *__restrict__ x, int64_t n,
                                                              const void *__restrict__ table,
                                                              float *__restrict__ out, int64_t ostride,
-                                                             LaunchParams lp) {
+                                                             int64_t lstride, LaunchParams lp) {
     Item it;
     if (!decode_item(lp, it)) return;
     const int l = it.level;
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(kBlock) void fwd_generic_kernel(const float *__rest
 #pragma unroll
             for (int j = 0; j < F; ++j) acc[j] += w * e[j];
         }
-        float *orow = out + p * ostride + (int64_t)l * F;
+        float *orow = out + p * ostride + (int64_t)l * lstride;
 #pragma unroll
         for (int j = 0; j < F; ++j) orow[j] = acc[j];
     }
@@ -112,12 +117,13 @@ constexpr int pair_unroll(int D, int F) {
 // an x-pair differ in the low index bits and mostly share a 128-byte line: the
 // pair's two loads are one line request where one thread per point makes two.
 // The halves' partial sums are exchanged with a DPP swap and each lane writes
-// half of the level's F features (F = 1: lane 0 writes).
+// half of the level's F features (F = 1: lane 0 writes); output layout as
+// fwd_generic_kernel.
 template <int D, int F, int DT>
 __global__ __launch_bounds__(kBlock) void fwd_generic_pair_kernel(const float *__restrict__ x, int64_t n,
                                                                   const void *__restrict__ table,
                                                                   float *__restrict__ out, int64_t ostride,
-                                                                  LaunchParams lp) {
+                                                                  int64_t lstride, LaunchParams lp) {
     constexpr int U = pair_unroll(D, F), H = 1 << (D - 1), kPairs = kBlock / 2;
     Item it;
     if (!decode_item(lp, it)) return;
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void fwd_generic_pair_kernel(const float *_
 #pragma unroll
                 for (int j = 0; j < F; ++j) part[j] += w * e[u][h][j];
             }
-            float *orow = out + (p0 + (int64_t)u * kPairs) * ostride + (int64_t)l * F;
+            float *orow = out + (p0 + (int64_t)u * kPairs) * ostride + (int64_t)l * lstride;
             if constexpr (F == 1) {
                 const float v = part[0] + swap_pair(part[0]);
                 if (ok[u] && sub == 0) orow[0] = v;
@@ -514,21 +520,26 @@ bool dispatch_shape(int D, int F, Fn &&fn) {
 
 hipError_t launch_forward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
                                   const void *table, int table_dtype, float *out, int64_t out_stride, int lanes,
-                                  hipStream_t stream) {
+                                  float *stage, hipStream_t stream) {
     const dim3 grid(grid_blocks(lp)), block(kBlock);
+    float *dst = stage ? stage : out;
+    const int64_t os = stage ? F : out_stride, ls = stage ? (int64_t)F * n : F;
     const bool ok = dispatch_shape(D, F, [&]<int DD, int FF>() {
         if (lanes == 1) {  // one thread per (point, level)
             if (table_dtype == 0)
-                fwd_generic_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+                fwd_generic_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, dst, os, ls, lp);
             else
-                fwd_generic_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+                fwd_generic_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, dst, os, ls, lp);
         } else if (table_dtype == 0) {
-            fwd_generic_pair_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+            fwd_generic_pair_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, dst, os, ls, lp);
         } else {
-            fwd_generic_pair_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, out, out_stride, lp);
+            fwd_generic_pair_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, dst, os, ls, lp);
         }
     });
-    return ok ? hipGetLastError() : hipErrorInvalidValue;
+    if (!ok) return hipErrorInvalidValue;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !stage) return e;
+    return launch_transpose(F, stage, n, lp.n_levels, out, out_stride, stream);
 }
 
 hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,

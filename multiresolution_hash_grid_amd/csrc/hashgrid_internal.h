@@ -103,7 +103,10 @@ hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, co
 // F in {1, 2, 4, 8}; hipErrorInvalidValue for an unbuilt shape.
 hipError_t launch_forward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
                                   const void *table, int table_dtype, float *out, int64_t out_stride, int lanes,
-                                  hipStream_t stream);
+                                  float *stage, hipStream_t stream);
+// [L][n][F] level-major stage -> rows out[p * ostride + l * F + j].
+hipError_t launch_transpose(int F, const float *stage, int64_t n, int L, float *out, int64_t ostride,
+                            hipStream_t stream);
 hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
                                    const float *dout, int64_t dout_stride, float *dtable, hipStream_t stream);
 hipError_t launch_debug_corners_generic(const LaunchParams &lp, int D, const float *x, int64_t n, uint32_t *idx,

@@ -93,6 +93,24 @@ def test_shape_forward_one_lane_per_point(oracle, D, F, dtype):
     assert one.shape == ref.shape and float(np.max(np.abs(one - ref))) <= 1e-6 * tmax
 
 
+@pytest.mark.parametrize("D,F,dtype", SHAPES)
+def test_shape_forward_staged_equals_direct(D, F, dtype):
+    # With a workspace the levels are written level-major and transposed into
+    # the rows (16-byte moves when F n and F L are multiples of 4, 4-byte moves
+    # for a wide output buffer or an odd n); the same arithmetic either way.
+    for n in (3 * 1024 + 77, 4096):
+        w = shape_workload(D, F, dtype, n=n)
+        cfg = hg.HashGridConfig.of(w)
+        x, t = dev(I.make_points(w)), dev(I.make_table(w))
+        direct = hg.hashgrid_forward(cfg, x, t, workspace=None).cpu().numpy()
+        staged = hg.hashgrid_forward(cfg, x, t, workspace="auto").cpu().numpy()
+        wide = torch.full((n, cfg.out_features + 3), 7.0, device=DEV)
+        hg.hashgrid_forward(cfg, x, t, out=wide, workspace="auto")
+        wide = wide.cpu().numpy()
+        assert np.array_equal(direct, staged) and np.array_equal(direct, wide[:, :cfg.out_features])
+        assert np.all(wide[:, cfg.out_features:] == 7.0)
+
+
 @pytest.mark.parametrize("D,F,dtype", SHAPES + [(3, 2, "f32"), (3, 2, "f16")])
 def test_shape_input_grad(oracle, D, F, dtype):
     w = shape_workload(D, F, dtype)
