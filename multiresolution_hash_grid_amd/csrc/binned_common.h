@@ -111,6 +111,8 @@ constexpr int kAccBatch = 2;
 constexpr int kFlushPer = 4;
 constexpr int kMapWindow = 1024;  // positions per map window, a multiple of 64 * kAccBatch
 static_assert(kMapWindow % (64 * kAccBatch) == 0, "map windows must hold whole batches");
+// build_run_map gives each of the 64 lanes one uint4 (16 positions) of the map.
+static_assert(kMapWindow == 64 * 16, "a map window is 16 positions per lane");
 
 // LDS order between lanes of one wave (the wave's LDS operations complete in
 // issue order; this keeps the compiler from moving them across).
