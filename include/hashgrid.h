@@ -122,7 +122,10 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
  * number of levels binned together.
  * That group is sized so its records fit the MI355X last-level cache (the
  * HG_TUNE_BWD_GROUP_MIB budget, 160 MiB by default: 8 levels for n = 2^18,
- * about 103 MB).  *bytes_out is a HOST size_t.  A workspace of at least
+ * about 103 MB) when such groups still give the accumulate kernel at least
+ * 1024 workgroups; otherwise (larger batches: 2^20 points and up at T = 2^19)
+ * it holds all levels, e.g. about 3.1 GiB for n = 2^22 and L = 16.
+ * *bytes_out is a HOST size_t.  A workspace of at least
  * *min_bytes_out (one level's share; may be NULL) also works -- the levels
  * are then processed in smaller groups.  Returns 0 bytes when the
  * configuration has no binned path (more than 4096 partitions: T > 2^25 for

@@ -148,19 +148,20 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // generic ones.
 bool standard_shape(const hg_config &c) { return c.n_dims == 3 && c.n_features == 2; }
 
-// Levels per binned group: as many as keep one group's records (written by
-// the bin kernel, read back by the accumulate kernel right after) within the
-// budget, so that they can stay in the 256 MB last-level cache of the
-// MI355X -- but at least enough levels for 512 accumulate workgroups (two per
-// CU), which large batches need more than cache residency; groups are then
-// made equal.
+// Levels per binned group.  Where the budget (sized for the 256 MB last-level
+// cache of the MI355X) holds enough levels for at least 1024 accumulate
+// workgroups (two rounds of two per CU), groups take as many levels as keep
+// their records (written by the bin kernel, read back by the accumulate
+// kernel right after) within it, made equal.  Otherwise, for large batches
+// whose records cannot stay in the cache in groups that fill the chip, all
+// levels form one group: the accumulate grid of every level at once balances
+// the uneven partitions of coarse levels and of structured batches.
 int binned_group(const hg::BinParams &bp, int n_levels) {
     if (g_tune.bwd_group_mib <= 0) return n_levels;
     const size_t rec_bytes = (size_t)bp.level_records * bp.rec_bytes;
     const size_t budget = (size_t)g_tune.bwd_group_mib << 20;
-    const int fill = (512 + bp.parts - 1) / bp.parts;
-    const int cap = (int)std::min<size_t>(
-        n_levels, std::max<size_t>({(size_t)1, (size_t)fill, budget / std::max<size_t>(rec_bytes, 1)}));
+    const int cap = (int)std::min<size_t>(n_levels, std::max<size_t>(1, budget / std::max<size_t>(rec_bytes, 1)));
+    if ((int64_t)cap * bp.parts < 1024) return n_levels;
     const int ngroups = (n_levels + cap - 1) / cap;
     return (n_levels + ngroups - 1) / ngroups;
 }

@@ -137,12 +137,18 @@ def test_backward_workspace_size():
     try:
         hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 0)      # one group of all levels
         assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 16, least)
-        # 36 MiB holds 3 levels, but a group keeps at least 512 / 128 partitions = 4
-        # levels so that the accumulate grid fills the chip: 4 groups of 4.
+        # 96 MiB holds 8 levels, 8 x 128 partitions = 1024 accumulate workgroups:
+        # groups of 8.  95 MiB holds 7 (896 workgroups), too few to fill two
+        # rounds, and so does 36 MiB (3 levels): then all 16 levels form one group.
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 96)
+        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 8, least)
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 95)
+        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 16, least)
         hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 36)
-        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 4, least)
-        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 72)     # 6 levels -> groups 6 + 6 + 4, sized for 6
-        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 6, least)
+        assert hg.hashgrid_backward_workspace_size(cfg, 1 << 18) == (least * 16, least)
+        hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, 160)    # 2^20 points: 48 MiB per level, 3 levels -> all 16
+        full20, least20 = hg.hashgrid_backward_workspace_size(cfg, 1 << 20)
+        assert full20 == least20 * 16
     finally:
         hg.hashgrid_tune(B.HG_TUNE_BWD_GROUP_MIB, old)
     assert least >= 48 * (1 << 18) and least < 48 * (1 << 18) + (1 << 20)

@@ -313,8 +313,10 @@ def test_backward_binned_reused_workspace_and_dirty_contents(oracle):
                                        (B.HG_TUNE_BWD_BINNED, 0), (B.HG_TUNE_FWD_UNROLL, 2),
                                        (B.HG_TUNE_FWD_UNROLL, 4), (B.HG_TUNE_FWD_NT, 1),
                                        (B.HG_TUNE_BWD_PART_LOG2, 11), (B.HG_TUNE_BWD_PART_LOG2, 12),
-                                       (B.HG_TUNE_BWD_GROUP_MIB, 0), (B.HG_TUNE_BWD_GROUP_MIB, 1)])
+                                       (B.HG_TUNE_BWD_GROUP_MIB, 0), (B.HG_TUNE_BWD_GROUP_MIB, 3)])
 def test_launch_variants_match_oracle(oracle, key, value):
+    # (GROUP_MIB, 3): 270 KB of records per level at this n, so 3 MiB holds 11
+    # levels (1408 accumulate workgroups): two groups of 8; 0: one group.
     w = I.resized(I.WORKLOADS["standard"], 5 * 1024 + 77)
     cfg = hg.HashGridConfig.of(w)
     x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
