@@ -24,8 +24,36 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_standard.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_standard_mlp.json")
 PASS_KERNELS = {"forward": "fwd_f2_pair_kernel + transpose_kernel",
                 "backward": "bin_kernel + accumulate_kernel per level group"}
+
+
+def load_counters():
+    """The committed rocprofv3 counter summary (L2 hit and request rates of the
+    standard workload's kernels, MFMA utilisation of the MLP head's), each part
+    None when it was taken on other kernel source."""
+    from multiresolution_hash_grid_amd import profile_summary as ps
+    try:
+        with open(COUNTERS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    l2 = rec.get("l2") if rec.get("source_sha256") == ps.source_digest() else None
+    mfma = rec.get("mfma") if rec.get("mlp_source_sha256") == ps.source_digest(ps.MLP_SOURCES) else None
+    return l2, mfma
+
+
+def cache_summary(l2) -> dict | None:
+    """L2 hit rate and request rate of the standard step's kernels, by pass."""
+    if not l2:
+        return None
+    out = {}
+    for name, k in l2.items():
+        if k.get("pass"):
+            out[name] = {"pass": k["pass"], "l2_hit_rate": k["hit_rate"],
+                         "l2_requests_per_dispatch": k["requests"], "l2_requests_per_s": k["requests_per_s"]}
+    return out
 
 
 def algorithmic_bytes_per_point(w, table_esize: int) -> dict:
@@ -165,11 +193,16 @@ def measure_fused_mlp(dev, iters: int) -> dict:
     L, F = cfg.n_levels, cfg.n_features
     fb = 12 + 8 * L * F * 2 + 16
     bb = 12 + 16 + 2 * L * F + 8 * L * F * 4
+    _, mfma = load_counters()
     return {"points": n, "fwd_points_per_s": n / (fms * 1e-3), "bwd_points_per_s": n / (bms * 1e-3),
             "step_points_per_s": n / ((fms + bms) * 1e-3), "fwd_us": fms * 1e3, "bwd_us": bms * 1e3,
             "algorithmic_bytes_per_point": {"fwd": fb, "bwd": bb},
             "fwd_frac": fb * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            # rocprofv3 MfmaUtil and fp16 MFMA throughput of the head kernels (committed summary)
+            "mfma": None if mfma is None else {
+                k: {"util_pct": v["mfma_util_pct"], "tflops": v["tflops"], "peak_tflops": 2500.0}
+                for k, v in mfma.items() if k.startswith("mlp_")}}
 
 
 def cpu_baseline(w, x, t, d, budget_s: float) -> dict:
@@ -201,9 +234,10 @@ def main() -> int:
     ap.add_argument("--workload", default="standard")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--section", choices=("all", "main", "next"), default="all",
+    ap.add_argument("--section", choices=("all", "main", "next", "mlp"), default="all",
                     help="main: the standard fwd+bwd step only; next: only the figures of the "
-                         "optimizer, input-gradient, shape and MLP-head paths (for profiling runs)")
+                         "optimizer, input-gradient, shape and MLP-head paths; mlp: the MLP head "
+                         "only (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -236,6 +270,9 @@ def main() -> int:
         hg.hashgrid_forward(cfg, x, t, out=out, workspace=fws)
         hg.hashgrid_backward(cfg, x, d, grad, workspace=ws)
 
+    if args.section == "mlp":
+        print(json.dumps({"next": {"fused_mlp": measure_fused_mlp(dev, 5)}}), flush=True)
+        return 0
     if args.section == "next":
         print(json.dumps({"next": {"adam": measure_adam(cfg, dev, 50),
                                    "input_grad": measure_input_grad(cfg, x, t, d, 20),
@@ -305,6 +342,8 @@ def main() -> int:
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
         },
+        # L2 hit and request rates of the step's kernels (committed rocprofv3 counter summary)
+        "cache": cache_summary(load_counters()[0]),
         "roofline_fwd_frac": bpp["fwd"] * w.n_points / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline_fwd_bwd_frac": (bpp["fwd"] + bpp["bwd"]) * w.n_points * K / elapsed / 1e9 / HBM_PEAK_GBS,
     }

@@ -12,6 +12,12 @@
     # the calibration workload itself: a device-to-device copy of B bytes
     python -m multiresolution_hash_grid_amd.profile_summary copy --bytes B
 
+    # L2 (TCC) hit rate and request rate per kernel from a --pmc TCC_HIT_sum
+    # TCC_MISS_sum TCC_REQ_sum run, MFMA utilisation from a --pmc MfmaUtil
+    # SQ_INSTS_VALU_MFMA_MOPS_F16 run; durations from kernel-trace --stats runs
+    python -m multiresolution_hash_grid_amd.profile_summary counters --l2 D1 --l2-stats S1 \
+        --mfma D2 --mfma-stats S2 --out FILE.json
+
 A pass is the group of kernels one library call launches: the forward is the
 gather plus the level-major transpose, the backward the binned path's bin and
 accumulate kernels, once per level group (or the atomic scatter).  Per-pass
@@ -33,13 +39,15 @@ PASSES = {
     "backward": ("bin_kernel", "accumulate_kernel", "bwd_f2_kernel"),
 }
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCES = ("encode_kernels.hip", "binned_backward.hip")
+SOURCES = ("device_common.h", "hashgrid_internal.h", "encode_kernels.hip", "binned_common.h",
+           "binned_backward.hip")
+MLP_SOURCES = SOURCES + ("mlp_kernels.hip",)
 
 
-def source_digest() -> str:
-    """sha256 over the kernel sources (the traffic figures are only valid for them)."""
+def source_digest(files=SOURCES) -> str:
+    """sha256 over the kernel sources (counter figures are only valid for them)."""
     h = hashlib.sha256()
-    for f in SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "multiresolution_hash_grid_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -173,6 +181,52 @@ def traffic(args) -> None:
     print(json.dumps(rec, indent=1))
 
 
+def _durations_us(d: str) -> dict:
+    """{kernel short name: average duration in us} of a --kernel-trace --stats run."""
+    return {short_name(r["Name"]): float(r["AverageNs"]) / 1e3
+            for r in csv.DictReader(open(_find(d, "kernel_stats.csv")))}
+
+
+def counters(args) -> None:
+    hit = _counter_per_dispatch(args.l2, "TCC_HIT_sum")
+    miss = _counter_per_dispatch(args.l2, "TCC_MISS_sum")
+    req = _counter_per_dispatch(args.l2, "TCC_REQ_sum")
+    dur = _durations_us(args.l2_stats)
+    l2 = {}
+    for name in hit:
+        sn = short_name(name)
+        h, m, r = _avg(hit[name]), _avg(miss.get(name, [0.0])), _avg(req.get(name, [0.0]))
+        us = dur.get(sn)
+        l2[sn] = {"pass": pass_of(name), "hit_rate": h / (h + m) if h + m else None, "requests": r,
+                  "hits": h, "misses": m, "duration_us": us,
+                  "requests_per_s": r / (us * 1e-6) if us else None}
+    util = _counter_per_dispatch(args.mfma, "MfmaUtil")
+    mops = _counter_per_dispatch(args.mfma, "SQ_INSTS_VALU_MFMA_MOPS_F16")
+    mdur = _durations_us(args.mfma_stats)
+    mfma = {}
+    for name in mops:
+        sn = short_name(name)
+        ops = _avg(mops[name])
+        if ops <= 0:
+            continue
+        us = mdur.get(sn)
+        flops = ops * 512.0  # the counter counts fp16 MFMA work in units of 512 flops
+        mfma[sn] = {"mfma_util_pct": _avg(util[name]) if name in util else None, "fp16_flops": flops,
+                    "duration_us": us, "tflops": flops / (us * 1e-6) / 1e12 if us else None}
+    rec = {
+        "about": "Per-kernel L2 (TCC) hit rate, requests per dispatch and request rate of the standard "
+                 "workload's kernels; MFMA utilisation (busy cycles over SIMD cycles) and fp16 MFMA "
+                 "throughput of the MLP head's kernels. Durations are the kernel-trace averages of "
+                 "runs without counters.",
+        "command_l2": args.command_l2, "command_mfma": args.command_mfma,
+        "source_sha256": source_digest(), "mlp_source_sha256": source_digest(MLP_SOURCES),
+        "l2": l2, "mfma": mfma,
+    }
+    with open(args.out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def copy(args) -> None:
     import torch
     n = args.bytes // 4
@@ -201,10 +255,15 @@ def main() -> int:
     t.add_argument("--passes", type=int, required=True, help="calls of each entry point in the run")
     t.add_argument("--command-fetch", default="")
     t.add_argument("--command-write", default="")
+    k = sub.add_parser("counters")
+    for a in ("l2", "l2_stats", "mfma", "mfma_stats", "out"):
+        k.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
+    k.add_argument("--command-l2", default="")
+    k.add_argument("--command-mfma", default="")
     c = sub.add_parser("copy")
     c.add_argument("--bytes", type=int, default=256 << 20)
     args = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "copy": copy}[args.cmd](args)
+    {"stats": stats, "traffic": traffic, "counters": counters, "copy": copy}[args.cmd](args)
     return 0
 
 
