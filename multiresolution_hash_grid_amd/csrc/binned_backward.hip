@@ -369,9 +369,10 @@ hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, con
                                                                                          bp, sp, dtable);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        // Larger partitions (longer runs per tile) take more LDS and more threads.
-        if (bp.s_log2 >= 13) e = launch_accumulate<1024, StdPolicy>(bp, sp, dtable, stream);
-        else if (bp.s_log2 == 12) e = launch_accumulate<512, StdPolicy>(bp, sp, dtable, stream);
+        // 2^12- and 2^13-entry partitions: 1024 threads (16 waves) on one slice;
+        // with 64 KB slices two workgroups share a CU, 32 waves to hide the
+        // record loads.  Smaller partitions (short runs per tile): 256.
+        if (bp.s_log2 >= 12) e = launch_accumulate<1024, StdPolicy>(bp, sp, dtable, stream);
         else e = launch_accumulate<256, StdPolicy>(bp, sp, dtable, stream);
         if (e != hipSuccess) return e;
     }

@@ -109,33 +109,52 @@ constexpr int kAccBatch = 2;
 // THREADS for the partition size each workgroup width serves (launch_accumulate
 // checks).
 constexpr int kFlushPer = 4;
-constexpr int kMapWindow = 1024;  // positions per map window, a multiple of 64 * kAccBatch
-static_assert(kMapWindow % (64 * kAccBatch) == 0, "map windows must hold whole batches");
-// build_run_map gives each of the 64 lanes one uint4 (16 positions) of the map.
-static_assert(kMapWindow == 64 * 16, "a map window is 16 positions per lane");
+// A wave's run map holds PPL positions per lane: 16 (one uint4, windows of
+// 1024 positions) or 8 (one uint2, windows of 512), a multiple of 64 *
+// kAccBatch either way.
+template <int PPL>
+struct MapVec;
+template <>
+struct MapVec<16> {
+    using T = uint4;
+    static __device__ __forceinline__ void split(const T v, uint32_t (&w)[4]) { w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w; }
+    static __device__ __forceinline__ T join(const uint32_t (&w)[4]) { return make_uint4(w[0], w[1], w[2], w[3]); }
+};
+template <>
+struct MapVec<8> {
+    using T = uint2;
+    static __device__ __forceinline__ void split(const T v, uint32_t (&w)[2]) { w[0] = v.x, w[1] = v.y; }
+    static __device__ __forceinline__ T join(const uint32_t (&w)[2]) { return make_uint2(w[0], w[1]); }
+};
 
 // LDS order between lanes of one wave (the wave's LDS operations complete in
 // issue order; this keeps the compiler from moving them across).
 __device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-// Byte map of window [w0, w0 + kMapWindow) of a wave's run concatenation.
-// pre / len: this lane's run offset and length.
-__device__ __forceinline__ void build_run_map(uint4 *map, uint32_t w0, uint32_t pre, uint32_t len) {
+// Byte map of window [w0, w0 + 64 PPL) of a wave's run concatenation; lane l
+// owns bytes [l PPL, (l + 1) PPL).  pre / len: this lane's run offset and length.
+template <int PPL>
+__device__ __forceinline__ void build_run_map(typename MapVec<PPL>::T *map, uint32_t w0, uint32_t pre, uint32_t len) {
+    using M = MapVec<PPL>;
+    constexpr int W = PPL / 4;
+    constexpr uint32_t kWindow = 64 * PPL;
     const int lane = threadIdx.x & 63;
-    map[lane] = make_uint4(0u, 0u, 0u, 0u);
-    wave_lds_fence();
-    if (len > 0 && pre > w0 && pre < w0 + kMapWindow) reinterpret_cast<uint8_t *>(map)[pre - w0] = (uint8_t)(lane + 1);
-    wave_lds_fence();
-    const uint4 q = map[lane];
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t run = 0;
-    uint32_t loc[16];
+    uint32_t w[W];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
+    for (int m = 0; m < W; ++m) w[m] = 0;
+    map[lane] = M::join(w);
+    wave_lds_fence();
+    if (len > 0 && pre > w0 && pre < w0 + kWindow) reinterpret_cast<uint8_t *>(map)[pre - w0] = (uint8_t)(lane + 1);
+    wave_lds_fence();
+    M::split(map[lane], w);
+    uint32_t run = 0;
+    uint32_t loc[PPL];
+#pragma unroll
+    for (int b = 0; b < PPL; ++b) {
         run = max(run, (w[b >> 2] >> (8 * (b & 3))) & 0xFFu);
         loc[b] = run;
     }
-    // Largest mark in the lanes below (the window positions before this lane's 16).
+    // Largest mark in the lanes below (the window positions before this lane's PPL).
     uint32_t incl = run;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -145,10 +164,10 @@ __device__ __forceinline__ void build_run_map(uint4 *map, uint32_t w0, uint32_t 
     uint32_t below = __shfl_up(incl, 1, 64);
     if (lane == 0) below = 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < W; ++m)
         w[m] = max(loc[4 * m], below) | (max(loc[4 * m + 1], below) << 8) | (max(loc[4 * m + 2], below) << 16) |
                (max(loc[4 * m + 3], below) << 24);
-    map[lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    map[lane] = M::join(w);
     wave_lds_fence();
 }
 
@@ -159,9 +178,15 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     constexpr int F = P::F;
     constexpr int kRecPerTile = P::kRecPerTile;
     constexpr int kWaves = THREADS / 64;
+    // 1024-thread workgroups keep their 16 maps at 512 B so that two fit a CU
+    // next to 64 KB slices (32 waves per CU).
+    constexpr int PPL = THREADS >= 1024 ? 8 : 16;
+    constexpr uint32_t kMapWindow = 64 * PPL;
+    static_assert(kMapWindow % (64 * kAccBatch) == 0, "map windows must hold whole batches");
+    using MapT = typename MapVec<PPL>::T;
     extern __shared__ unsigned long long slice[];       // [2^s][F] fixed-point accumulators
     __shared__ int32_t offs[kWaves][64];                // per run: record index minus concatenation position
-    __shared__ uint4 maps[kWaves][kMapWindow / 16];     // per wave: byte map of the current window
+    __shared__ MapT maps[kWaves][64];                    // per wave: byte map of the current window
     __shared__ uint32_t touched;
     __shared__ uint32_t wmax[kWaves];
     const int g = blockIdx.x / bp.parts;
@@ -196,7 +221,7 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     if (lane == 0) wmax[wave] = dm;
     const Rec *grec = sp.records + (int64_t)g * bp.level_records;
     const uint32_t smask = (uint32_t)S - 1u;
-    uint4 *map = maps[wave];
+    MapT *map = maps[wave];
     const uint8_t *mapb = reinterpret_cast<const uint8_t *>(map);
     __syncthreads();
     dm = wmax[0];
@@ -222,7 +247,7 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
         auto open_window = [&](uint32_t w0) {
             // The run in progress at w0: the last run starting at or before it.
             carry = (uint32_t)__popcll(__ballot(pre <= w0)) - 1u;
-            build_run_map(map, w0, pre, len);
+            build_run_map<PPL>(map, w0, pre, len);
         };
         if (total) open_window(0);
         Rec cur[kAccBatch], nxt[kAccBatch];
