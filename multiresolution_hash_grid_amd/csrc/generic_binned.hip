@@ -25,7 +25,11 @@ namespace {
 using namespace binned;
 
 constexpr int kGenThreads = 256;  // bin workgroup
-constexpr int kGenAccThreads = 512;  // accumulate workgroup: S * F / 4 = 2048 float4, 4 per thread
+// Accumulate workgroup width: 1024 threads (two per CU next to the 64 KB
+// slices, 32 waves) where the kernel stays within 64 VGPRs (F <= 2); the
+// F = 4 and F = 8 kernels need 70 and 92, so there 512 threads keep two
+// workgroups per CU.  S * F / 4 = 2048 float4 either way.
+constexpr int gen_acc_threads(int F) { return F <= 2 ? 1024 : 512; }
 
 template <int F>
 struct RecG {
@@ -167,7 +171,7 @@ hipError_t launch_shape(BinParams bp, int n_levels, int max_group, const float *
                                    stream>>>(x, n, dout, dout_stride, bp, sp, dtable);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        e = launch_accumulate<kGenAccThreads, GenPolicy<F, R>>(bp, sp, dtable, stream);
+        e = launch_accumulate<gen_acc_threads(F), GenPolicy<F, R>>(bp, sp, dtable, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
