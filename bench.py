@@ -23,6 +23,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+# L2 request peak: 8 XCDs x 16 L2 channels, each serving one 128-byte request
+# per clock, at 2.4 GHz.
+L2_REQ_PEAK_PER_S = 8 * 16 * 2.4e9
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_standard.json")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_standard_mlp.json")
 PASS_KERNELS = {"forward": "fwd_f2_pair_kernel + transpose_kernel",
@@ -51,8 +54,11 @@ def cache_summary(l2) -> dict | None:
     out = {}
     for name, k in l2.items():
         if k.get("pass"):
+            rps = k["requests_per_s"]
             out[name] = {"pass": k["pass"], "l2_hit_rate": k["hit_rate"],
-                         "l2_requests_per_dispatch": k["requests"], "l2_requests_per_s": k["requests_per_s"]}
+                         "l2_requests_per_dispatch": k["requests"], "l2_requests_per_s": rps,
+                         "l2_request_peak_per_s": L2_REQ_PEAK_PER_S,
+                         "l2_request_frac": None if rps is None else rps / L2_REQ_PEAK_PER_S}
     return out
 
 
@@ -205,9 +211,21 @@ def measure_fused_mlp(dev, iters: int) -> dict:
                 for k, v in mfma.items() if k.startswith("mlp_")}}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, t, d, budget_s: float) -> dict:
     """The CPU oracle, as it stands, on the same workload: forward + backward of
-    all points, repeated until about `budget_s` seconds of work."""
+    all points, repeated until about `budget_s` seconds of work, with OpenMP over
+    the levels; and single-threaded on the first 2^14 points (median of 3)."""
     from oracle import hashgrid_oracle as oracle
 
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -220,10 +238,22 @@ def cpu_baseline(w, x, t, d, budget_s: float) -> dict:
         oracle.backward(g, x, d)
         spent += time.perf_counter() - t0
         reps += 1
+    oracle.set_threads(1)
+    m = min(len(x), 1 << 14)
+    one = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.forward(g, x[:m], t)
+        oracle.backward(g, x[:m], d[:m])
+        one.append(time.perf_counter() - t0)
+    oracle.set_threads(threads)
     return {"value": w.n_points * reps / spent, "unit": "points/s", "cores": min(threads, w.n_levels),
             "kind": "oracle",
             "sample": f"full workload ({w.n_points} points) forward+backward x{reps}, {spent:.1f} s, "
-                      f"OpenMP over levels"}
+                      f"OpenMP over levels",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+            "single_thread": {"value": m / sorted(one)[1], "unit": "points/s",
+                              "sample": f"first {m} points forward+backward, median of 3"}}
 
 
 def main() -> int:
