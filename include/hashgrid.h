@@ -226,8 +226,10 @@ int hashgrid_mlp_backward(const hg_config *cfg, const float *x, int64_t n, const
 /* Bytes of device workspace that let hashgrid_input_grad stage per-level
  * partial sums level-major: L * n * D * 4, rounded up to 256, plus for the
  * D = 3, F = 2 grid L * n * 2 * 4 for a level-major copy of the upstream rows
- * (a workspace holding only the stage also works).  *bytes_out is a HOST
- * size_t.  Errors: HG_EINVAL, HG_EUNSUPPORTED. */
+ * (a workspace holding only the stage also works).  0 for D <= 2: a level
+ * there holds at most (N_l + 1)^2 corners, the tables stay in cache, and the
+ * point-major path is faster with or without a workspace.  *bytes_out is a
+ * HOST size_t.  Errors: HG_EINVAL, HG_EUNSUPPORTED. */
 int hashgrid_input_grad_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out);
 
 /* Gradient of the loss with respect to the points, dL/dx.  The pages imply
@@ -243,9 +245,9 @@ int hashgrid_input_grad_workspace_size(const hg_config *cfg, int64_t n, size_t *
  *   dx       : float32 [n][D], 4-byte aligned; WRITTEN (not accumulated).
  *   workspace: NULL, or hashgrid_input_grad_workspace_size bytes (256-byte
  *              aligned) to run level-major (each level's table stays in L2)
- *              and then sum the levels; without it one thread walks all levels
- *              of a point.  The two give identical results.  Concurrent calls
- *              must not share a workspace.
+ *              and then sum the levels; without it (and for D <= 2) one thread
+ *              walks all levels of a point.  The two give identical results.
+ *              Concurrent calls must not share a workspace.
  * Errors: as hashgrid_forward. */
 int hashgrid_input_grad(const hg_config *cfg, const float *x, int64_t n, const void *table, const float *dout,
                         int64_t dout_row_stride, float *dx, void *workspace, size_t workspace_bytes,

@@ -392,7 +392,12 @@ int hashgrid_input_grad_workspace_size(const hg_config *cfg, int64_t n, size_t *
     if (rc) return rc;
     if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
     if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
-    // The [L][n][D] stage, and for the D = 3, F = 2 grid a level-major copy of the upstream rows.
+    // The [L][n][D] stage, and for the D = 3, F = 2 grid a level-major copy of
+    // the upstream rows.  D <= 2 runs point-major whatever the workspace.
+    if (cfg->n_dims <= 2) {
+        *bytes_out = 0;
+        return ok();
+    }
     const size_t stage = round_up((size_t)n * cfg->n_levels * cfg->n_dims * sizeof(float), 256);
     const size_t copy = standard_shape(*cfg) ? round_up((size_t)n * cfg->n_levels * 2 * sizeof(float), 256) : 0;
     *bytes_out = stage + copy;

@@ -26,7 +26,8 @@
 // stage, which a second kernel sums over levels in level order; without a
 // stage one thread walks all levels of its point.  Both add the same fp32
 // terms in the same order (contraction off), so they agree bit for bit.  The
-// D = 3, F = 2 grid uses the forward's lane pairs for the level-major pass.
+// level-major pass uses the forward's lane pairs: a level's derivative is
+// N_l (half(0) + half(1)), half(b) the corners with first-coordinate offset b.
 #include <type_traits>
 
 #include "device_common.h"
@@ -59,6 +60,26 @@ __device__ __forceinline__ uint32_t corner_hash(const Voxel<D> &vx, int k, uint3
 #pragma unroll
     for (int d = 0; d < D; ++d) h ^= ((k >> (D - 1 - d)) & 1) ? vx.h1[d] : vx.h0[d];
     return h & mask;
+}
+
+// Corner h of the half with first-coordinate offset b (corner k = b 2^(D-1) + h):
+// only the first coordinate's choice depends on the runtime b, so the other
+// terms stay compile-time register picks (a runtime k for every coordinate
+// made the compiler index the Voxel arrays through scratch memory).
+template <int D>
+__device__ __forceinline__ uint32_t half_corner_hash(const Voxel<D> &vx, int b, int h, uint32_t mask) {
+    uint32_t v = b ? vx.h1[0] : vx.h0[0];
+#pragma unroll
+    for (int d = 1; d < D; ++d) v ^= ((h >> (D - 1 - d)) & 1) ? vx.h1[d] : vx.h0[d];
+    return v & mask;
+}
+
+template <int D>
+__device__ __forceinline__ float half_corner_weight(const Voxel<D> &vx, int b, int h) {
+    float w = b ? vx.f[0] : 1.f - vx.f[0];
+#pragma unroll
+    for (int d = 1; d < D; ++d) w *= ((h >> (D - 1 - d)) & 1) ? vx.f[d] : 1.f - vx.f[d];
+    return w;
 }
 
 template <int D>
@@ -143,7 +164,7 @@ __global__ __launch_bounds__(kBlock) void fwd_generic_pair_kernel(const float *_
             locate_point<D>(x + (ok[u] ? p : p0) * D, N, vx[u]);  // p0 < end: always a valid point
 #pragma unroll
             for (int h = 0; h < H; ++h)
-                load_features<F, DT>(table, lbase + corner_hash<D>(vx[u], sub * H + h, lp.mask), e[u][h]);
+                load_features<F, DT>(table, lbase + half_corner_hash<D>(vx[u], sub, h, lp.mask), e[u][h]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -152,7 +173,7 @@ __global__ __launch_bounds__(kBlock) void fwd_generic_pair_kernel(const float *_
             for (int j = 0; j < F; ++j) part[j] = 0.f;
 #pragma unroll
             for (int h = 0; h < H; ++h) {
-                const float w = corner_weight<D>(vx[u], sub * H + h);
+                const float w = half_corner_weight<D>(vx[u], sub, h);
 #pragma unroll
                 for (int j = 0; j < F; ++j) part[j] += w * e[u][h][j];
             }
@@ -227,12 +248,60 @@ __global__ __launch_bounds__(kBlock) void corners_generic_kernel(const float *__
 
 // ---------------------------------------------------------------- dL/dx
 
+// Corner hh of the half with first-coordinate offset b (corner k = b 2^(D-1)
+// + hh) adds its term to that half's sums h[0..D): with s = sum_j dl_j e_j,
+// h[d] += (b_d ? 1 : -1) prod_{q != d} (b_q ? f_q : 1 - f_q) s.  A level's
+// dL/dx is N_l (half(0) + half(1)), each half summed over hh in order: the
+// lane-pair kernel and the point kernel both go through this function, so
+// they agree bit for bit.
+template <int D, int F>
+__device__ __forceinline__ void corner_grad_term(const Voxel<D> &vx, const float (&e)[F], const float (&dl)[F],
+                                                 int b, int hh, float (&h)[D]) {
+#pragma clang fp contract(off)
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < F; ++j) s += dl[j] * e[j];
+    // bit of coordinate d: b for d = 0, bit D-1-d of hh otherwise
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        const bool bd = d == 0 ? b != 0 : ((hh >> (D - 1 - d)) & 1) != 0;
+        float dw = bd ? 1.f : -1.f;
+#pragma unroll
+        for (int q = 0; q < D; ++q) {
+            if (q == d) continue;
+            const bool bq = q == 0 ? b != 0 : ((hh >> (D - 1 - q)) & 1) != 0;
+            dw *= bq ? vx.f[q] : 1.f - vx.f[q];
+        }
+        h[d] += dw * s;
+    }
+}
+
+// One half's sums from its corners' features e[hh].
+template <int D, int F>
+__device__ __forceinline__ void half_grad(const Voxel<D> &vx, const float (&e)[1 << (D - 1)][F],
+                                          const float (&dl)[F], int b, float (&h)[D]) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) h[d] = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < (1 << (D - 1)); ++hh) corner_grad_term<D, F>(vx, e[hh], dl, b, hh, h);
+}
+
+// Features of the corners with first-coordinate offset b.
+template <int D, int F, int DT>
+__device__ __forceinline__ void load_half(const void *__restrict__ table, uint64_t lbase, uint32_t mask,
+                                          const Voxel<D> &vx, int b, float (&e)[1 << (D - 1)][F]) {
+    constexpr int H = 1 << (D - 1);
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh) load_features<F, DT>(table, lbase + half_corner_hash<D>(vx, b, hh, mask), e[hh]);
+}
+
 // N_l * d(sum_j dout_j out_j)/dx_d of one (point, level) into g[0..D).
 template <int D, int F, int DT>
 __device__ __forceinline__ void level_input_grad(const float *__restrict__ xp, const void *__restrict__ table,
                                                  const float *__restrict__ drow, int l, const LaunchParams &lp,
                                                  float (&g)[D]) {
 #pragma clang fp contract(off)
+    constexpr int H = 1 << (D - 1);
     const float N = (float)lp.res[l];
     const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
     Voxel<D> vx;
@@ -240,42 +309,71 @@ __device__ __forceinline__ void level_input_grad(const float *__restrict__ xp, c
     float dl[F];
 #pragma unroll
     for (int j = 0; j < F; ++j) dl[j] = drow[(int64_t)l * F + j];
+    // Corner by corner into the two half sums.
+    float h0[D], h1[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) g[d] = 0.f;
+    for (int d = 0; d < D; ++d) h0[d] = h1[d] = 0.f;
 #pragma unroll
-    for (int k = 0; k < (1 << D); ++k) {
+    for (int k = 0; k < 2 * H; ++k) {
         float e[F];
-        load_features<F, DT>(table, lbase + corner_hash<D>(vx, k, lp.mask), e);
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < F; ++j) s += dl[j] * e[j];
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            float dw = ((k >> (D - 1 - d)) & 1) ? 1.f : -1.f;
-#pragma unroll
-            for (int q = 0; q < D; ++q)
-                if (q != d) dw *= ((k >> (D - 1 - q)) & 1) ? vx.f[q] : 1.f - vx.f[q];
-            g[d] += dw * s;
-        }
+        load_features<F, DT>(table, lbase + half_corner_hash<D>(vx, k / H, k % H, lp.mask), e);
+        if (k < H) corner_grad_term<D, F>(vx, e, dl, 0, k, h0);
+        else corner_grad_term<D, F>(vx, e, dl, 1, k - H, h1);
     }
 #pragma unroll
-    for (int d = 0; d < D; ++d) g[d] = N * g[d];
+    for (int d = 0; d < D; ++d) g[d] = N * (h0[d] + h1[d]);
 }
 
+// Level-major, as the forward: two adjacent lanes per point, lane sub takes
+// the corners with first-coordinate offset sub (the first prime is 1, so the
+// two corners of an x-pair mostly share a line and the pair's loads make one
+// request), U points per pair in flight.  The pair swaps its halves; lane 0
+// writes coordinates [0, ceil(D/2)) of stage[l][p][0..D), lane 1 the rest.
 template <int D, int F, int DT>
-__global__ __launch_bounds__(kBlock) void input_grad_level_kernel(const float *__restrict__ x, int64_t n,
-                                                                  const void *__restrict__ table,
-                                                                  const float *__restrict__ dout, int64_t dstride,
-                                                                  float *__restrict__ stage, LaunchParams lp) {
+__global__ __launch_bounds__(kBlock) void input_grad_generic_pair_kernel(const float *__restrict__ x, int64_t n,
+                                                                         const void *__restrict__ table,
+                                                                         const float *__restrict__ dout,
+                                                                         int64_t dstride, float *__restrict__ stage,
+                                                                         LaunchParams lp) {
+#pragma clang fp contract(off)
+    constexpr int U = pair_unroll(D, F), H = 1 << (D - 1), kPairs = kBlock / 2, DA = (D + 1) / 2;
     Item it;
     if (!decode_item(lp, it)) return;
+    const int l = it.level;
+    const float N = (float)lp.res[l];
+    const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+    const int sub = threadIdx.x & 1;
     const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
-    for (int64_t p = it.p0 + threadIdx.x; p < end; p += kBlock) {
-        float g[D];
-        level_input_grad<D, F, DT>(x + p * D, table, dout + p * dstride, it.level, lp, g);
-        float *dst = stage + ((int64_t)it.level * n + p) * D;
+    for (int64_t p0 = it.p0 + (threadIdx.x >> 1); p0 < end; p0 += (int64_t)kPairs * U) {
+        float e[U][H][F], dl[U][F];
+        Voxel<D> vx[U];
+        bool ok[U];
 #pragma unroll
-        for (int d = 0; d < D; ++d) dst[d] = g[d];
+        for (int u = 0; u < U; ++u) {
+            const int64_t p = p0 + (int64_t)u * kPairs;
+            ok[u] = p < end;
+            const int64_t q = ok[u] ? p : p0;  // p0 < end: always a valid point
+            locate_point<D>(x + q * D, N, vx[u]);
+#pragma unroll
+            for (int j = 0; j < F; ++j) dl[u][j] = dout[q * dstride + (int64_t)l * F + j];
+            load_half<D, F, DT>(table, lbase, lp.mask, vx[u], sub, e[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float h[D], g[D];
+            half_grad<D, F>(vx[u], e[u], dl[u], sub, h);
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const float o = swap_pair(h[d]);
+                g[d] = N * (sub ? o + h[d] : h[d] + o);  // half(0) + half(1) on both lanes
+            }
+            if (ok[u]) {
+                float *dst = stage + ((int64_t)l * n + p0 + (int64_t)u * kPairs) * D;
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    if ((d < DA) == (sub == 0)) dst[d] = g[d];
+            }
+        }
     }
 }
 
@@ -600,15 +698,18 @@ hipError_t launch_input_grad(const LaunchParams &lp, int D, int F, const float *
             input_grad_point_pair_kernel<1><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride, dx, lp);
         return hipGetLastError();
     }
-    if (stage) {
+    // D <= 2: a level holds at most (N_l + 1)^2 corners, so the tables stay in
+    // cache without level-major passes, and one thread walking its point's
+    // levels beats staging (D1F2 23 vs 87 us, D2F2 72 vs 98 us at 2^18 points).
+    if (stage && D >= 3) {
         const dim3 grid(grid_blocks(lp)), block(kBlock);
         ok = dispatch_shape(D, F, [&]<int DD, int FF>() {
             if (table_dtype == 0)
-                input_grad_level_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride,
-                                                                              stage, lp);
+                input_grad_generic_pair_kernel<DD, FF, 0><<<grid, block, 0, stream>>>(x, n, table, dout,
+                                                                                      dout_stride, stage, lp);
             else
-                input_grad_level_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, dout, dout_stride,
-                                                                              stage, lp);
+                input_grad_generic_pair_kernel<DD, FF, 1><<<grid, block, 0, stream>>>(x, n, table, dout,
+                                                                                      dout_stride, stage, lp);
         });
         if (!ok) return hipErrorInvalidValue;
         hipError_t e = hipGetLastError();

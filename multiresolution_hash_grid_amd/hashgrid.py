@@ -310,9 +310,8 @@ def hashgrid_input_grad(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tenso
         raise ValueError(f"dx must be a contiguous [n, {cfg.n_dims}] tensor")
 
     def alloc():
-        if not n:
-            return None
-        return torch.empty(hashgrid_input_grad_workspace_size(cfg, n), dtype=torch.uint8, device=x.device)
+        size = hashgrid_input_grad_workspace_size(cfg, n) if n else 0
+        return torch.empty(size, dtype=torch.uint8, device=x.device) if size else None
 
     ws_ptr, ws_bytes, _keep = _workspace(workspace, alloc, "workspace")
     c = cfg.c()

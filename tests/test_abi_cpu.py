@@ -219,8 +219,11 @@ def test_input_grad_workspace_and_argument_errors(lib):
     cfg = hg.HashGridConfig()
     # the [L][n][3] stage plus a level-major copy [L][n][2] of the upstream rows
     assert hg.hashgrid_input_grad_workspace_size(cfg, 1 << 18) == 16 * (3 + 2) * 4 << 18
-    assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=2, n_features=4), 10) == 1280  # 16*10*2*4
-    assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=1, n_levels=1), 3) == 256    # 12 -> 256
+    assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=4, n_features=4), 10) == 2560  # 16*10*4*4
+    assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=3, n_levels=1, n_features=1), 3) == 256
+    # D <= 2 runs point-major with or without a workspace: none is asked for.
+    assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=2, n_features=4), 10) == 0
+    assert hg.hashgrid_input_grad_workspace_size(hg.HashGridConfig(n_dims=1, n_levels=1), 3) == 0
     c = cfg.c()
     # n == 0 is a no-op; NULL points / dout / dx are rejected before any launch
     assert lib.hashgrid_input_grad(ctypes.byref(c), None, 0, None, None, 32, None, None, 0, None) == B.HG_OK
@@ -231,4 +234,4 @@ def test_input_grad_workspace_and_argument_errors(lib):
 def test_other_shapes_are_accepted(lib, D, F):
     cfg = hg.HashGridConfig(n_dims=D, n_features=F)
     assert hg.hashgrid_resolutions(cfg)[0] == 16
-    assert hg.hashgrid_input_grad_workspace_size(cfg, 64) == 16 * 64 * D * 4
+    assert hg.hashgrid_input_grad_workspace_size(cfg, 64) == (16 * 64 * D * 4 if D >= 3 else 0)
