@@ -142,9 +142,9 @@ def measure_input_grad(cfg, x, t, d, iters: int) -> dict:
 
 
 def measure_shapes(dev, n: int, iters: int) -> dict:
-    """Forward (lane-pair kernel, staged for F <= 4) and backward (generic
-    binned path) of other grid shapes at the standard L, T and resolutions, n
-    uniform points."""
+    """Forward (lane-pair kernel, staged for F <= 4), backward (generic binned
+    path) and dL/dx (lane pairs level-major for D >= 3) of other grid shapes at
+    the standard L, T and resolutions, n uniform points."""
     import torch
     import multiresolution_hash_grid_amd as hg
     from multiresolution_hash_grid_amd import inputs
@@ -159,15 +159,22 @@ def measure_shapes(dev, n: int, iters: int) -> dict:
         g = torch.zeros(cfg.table_shape, device=dev)
         ws = hg.backward_workspace(cfg, n, dev)
         fws = hg.forward_workspace(cfg, n, dev)
+        isz = hg.hashgrid_input_grad_workspace_size(cfg, n)
+        iws = torch.empty(isz, dtype=torch.uint8, device=dev) if isz else None
+        dx = torch.empty((n, D), device=dev)
         fms = time_calls(lambda: hg.hashgrid_forward(cfg, x, t, out=o, workspace=fws), iters)
         bms = time_calls(lambda: hg.hashgrid_backward(cfg, x, d, g, workspace=ws), iters)
+        ims = time_calls(lambda: hg.hashgrid_input_grad(cfg, x, t, d, dx=dx, workspace=iws), iters)
         L, K = cfg.n_levels, 1 << D
         fb = 4 * D + K * 4 * L * F + 4 * L * F
         bb = 4 * D + 4 * L * F + K * 4 * L * F
+        ib = 4 * D + 4 * L * F + K * 4 * L * F + 4 * D  # x, dout, corner gathers, dx
         out[f"D{D}_F{F}"] = {"fwd_points_per_s": n / (fms * 1e-3), "bwd_points_per_s": n / (bms * 1e-3),
+                             "input_grad_points_per_s": n / (ims * 1e-3),
                              "fwd_frac": fb * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del x, t, d, o, g, ws, fws
+                             "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "input_grad_frac": ib * n / (ims * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del x, t, d, o, g, ws, fws, iws, dx
     return out
 
 
