@@ -243,6 +243,31 @@ def test_backward_runs_of_points_in_one_voxel(oracle, name, n):
         hg.hashgrid_tune(B.HG_TUNE_BWD_LANES, old)
 
 
+@pytest.mark.parametrize("name,kw", [
+    # the largest table the binned backward takes: 2^25 / 2^13 = 4096 partitions, resolution 2^20
+    ("max_binned_table", dict(n_levels=1, log2_table_size=25, base_resolution=1 << 20, finest_resolution=1 << 20)),
+    # past it (8192 partitions): the atomic path only
+    ("beyond_binned_table", dict(n_levels=1, log2_table_size=26, base_resolution=1 << 12, finest_resolution=1 << 12)),
+    # the most levels, up to resolution 2^23
+    ("max_levels", dict(n_levels=64, log2_table_size=10, base_resolution=2, finest_resolution=1 << 23)),
+])
+def test_limit_configurations_match_oracle(oracle, name, kw):
+    w = I.resized(I.WORKLOADS["standard"], 2000 + 37, **kw)
+    print(f"limits {name}", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    g = oracle.grid_of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    assert fwd_err(run_forward(cfg, x, t), oracle.forward(g, x, t), t) <= FWD_TOL
+    full, _ = hg.hashgrid_backward_workspace_size(cfg, w.n_points)
+    assert (full > 0) == (name != "beyond_binned_table")
+    ref = oracle.backward(g, x, d)
+    bwd_check(run_backward(cfg, x, d), ref, w.n_levels)
+    bwd_check(run_backward(cfg, x, d, workspace=None), ref, w.n_levels)
+    idx, _ = hg.hashgrid_debug_corners(cfg, dev(x))
+    ridx, _ = oracle.corners(g, x)
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), ridx)
+
+
 def test_backward_accumulates_and_reads_strided_rows(oracle):
     w = I.resized(I.WORKLOADS["standard"], 2000)
     cfg = hg.HashGridConfig.of(w)
