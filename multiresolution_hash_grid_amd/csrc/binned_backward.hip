@@ -360,14 +360,16 @@ hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, con
     // Equal groups: 16 levels in groups of at most 6 run as 6 + 5 + 5.
     const int ngroups = (n_levels + group - 1) / group;
     group = (n_levels + ngroups - 1) / ngroups;
+    const size_t dyn = (2 * (size_t)bp.parts + 1) * sizeof(uint32_t);  // run counters: 32 KB at 4096 partitions
+    hipError_t e = hipFuncSetAttribute((const void *)bin_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
     for (int l0 = 0; l0 < n_levels; l0 += group) {
         bp.level0 = l0;
         bp.group = min(group, n_levels - l0);
         const StdSpace sp = carve<Rec>(workspace, bp);
         const dim3 tgrid(bp.tiles, (bp.group + kLevelsPerBlock - 1) / kLevelsPerBlock);
-        bin_kernel<<<tgrid, kBinThreads, (2 * bp.parts + 1) * sizeof(uint32_t), stream>>>(x, n, dout, dout_stride,
-                                                                                         bp, sp, dtable);
-        hipError_t e = hipGetLastError();
+        bin_kernel<<<tgrid, kBinThreads, dyn, stream>>>(x, n, dout, dout_stride, bp, sp, dtable);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
         // 2^12- and 2^13-entry partitions: 1024 threads (16 waves) on one slice;
         // with 64 KB slices two workgroups share a CU, 32 waves to hide the

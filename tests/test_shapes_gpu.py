@@ -189,6 +189,32 @@ def test_shape_binned_backward_edge_cases(oracle, D, F, log2T):
         assert np.max(np.abs(atomic.cpu().numpy()[l] - ref[l])) <= 1e-5 * np.max(np.abs(ref[l]))
 
 
+@pytest.mark.parametrize("D,F,log2T,res", [(2, 2, 24, 1 << 20), (4, 8, 22, 1 << 10), (1, 1, 25, 1 << 22),
+                                          (3, 4, 23, 1 << 16)])
+def test_shape_limits_match_oracle(oracle, D, F, log2T, res):
+    # 4096 partitions of 8192 / F entries, the largest tables the binned
+    # backward takes (its counters and record stage pass 64 KB of LDS for F = 2),
+    # at high resolutions.
+    w = shape_workload(D, F, "f32", n=2000 + 37, L=1, log2T=log2T, nmin=res, nmax=res)
+    print(f"shape limits D{D} F{F} T=2^{log2T} N={res}", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    g = oracle.grid_of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    tmax = float(np.max(np.abs(t.astype(np.float64))))
+    assert float(np.max(np.abs(hg.hashgrid_forward(cfg, dev(x), dev(t)).cpu().numpy() - oracle.forward(g, x, t)))) \
+        <= 1e-6 * tmax
+    full, _ = hg.hashgrid_backward_workspace_size(cfg, w.n_points)
+    assert full > 0
+    ref = oracle.backward(g, x, d)
+    for ws in ("auto", None):
+        grad = torch.zeros(cfg.table_shape, device=DEV)
+        hg.hashgrid_backward(cfg, dev(x), dev(d), grad, workspace=ws)
+        assert np.max(np.abs(grad.cpu().numpy()[0] - ref[0])) <= 1e-5 * np.max(np.abs(ref[0])), ws
+    idx, _ = hg.hashgrid_debug_corners(cfg, dev(x))
+    assert np.array_equal(idx.cpu().numpy().view(np.uint32), oracle.corners(g, x)[0])
+    input_grad_check(hg.hashgrid_input_grad(cfg, dev(x), dev(t), dev(d)).cpu().numpy(), oracle.input_grad(g, x, t, d))
+
+
 @pytest.mark.parametrize("n", [4096 + 2, 1001])
 def test_input_grad_workspace_variants_agree(oracle, n):
     # Full workspace (stage + level-major copy of the upstream rows), stage only
