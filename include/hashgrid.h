@@ -143,9 +143,16 @@ int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *by
  *            element (p, l*F + j) is read, other columns are ignored.
  *   dtable : float32 [L][T][F], 4-byte aligned.  ACCUMULATED INTO:
  *            dtable[l][h(corner_k)][j] += w_k * dout[p][l*F + j] for every point,
- *            level and corner.  Additions happen in an unspecified order, so
- *            results can differ from run to run in the last bits.  The caller
- *            zeroes the buffer when it wants the gradient of one batch alone.
+ *            level and corner.  The caller zeroes the buffer when it wants the
+ *            gradient of one batch alone.  On the binned path each contribution
+ *            is rounded to 64-bit fixed point (a step below 2^-29 max|dout| of
+ *            the level) and the integer sums do not depend on the order of the
+ *            additions: for points in [0,1)^D the result is reproducible bit for
+ *            bit.  The atomic path adds in fp32 in an unspecified order, so its
+ *            results can differ from run to run in the last bits.  Both paths
+ *            first sum, inside each wavefront, runs of consecutive points that
+ *            share a voxel (ray samples at coarse levels) for the D = 3, F = 2
+ *            grid.
  *   workspace, workspace_bytes : caller-owned device scratch (contents need
  *            not be initialised and are clobbered).  With at least the minimum
  *            of hashgrid_backward_workspace_size and a 16-byte aligned dtable
