@@ -268,6 +268,22 @@ def test_limit_configurations_match_oracle(oracle, name, kw):
     assert np.array_equal(idx.cpu().numpy().view(np.uint32), ridx)
 
 
+@pytest.mark.parametrize("name", ["standard", "ray"])
+def test_backward_binned_is_reproducible(name):
+    # Fixed-point accumulation: the binned gradient does not depend on the
+    # order in which workgroups add their records, so two runs agree bit for bit.
+    w = I.WORKLOADS[name]
+    cfg = hg.HashGridConfig.of(w)
+    x, d = dev(I.make_points(w)), dev(I.make_dout(w))
+    ws = hg.backward_workspace(cfg, w.n_points, DEV)
+    runs = []
+    for _ in range(2):
+        g = torch.zeros(cfg.table_shape, device=DEV)
+        hg.hashgrid_backward(cfg, x, d, g, workspace=ws)
+        runs.append(g.cpu().numpy())
+    assert np.array_equal(runs[0], runs[1])
+
+
 def test_backward_accumulates_and_reads_strided_rows(oracle):
     w = I.resized(I.WORKLOADS["standard"], 2000)
     cfg = hg.HashGridConfig.of(w)
