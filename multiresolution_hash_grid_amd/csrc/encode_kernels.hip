@@ -54,11 +54,9 @@ __device__ __forceinline__ void fadd(float *p, float v) { unsafeAtomicAdd(p, v);
 
 // ---------------------------------------------------------------- forward
 
-// LANES = 2: lane `sub` of a pair takes the corners with dx = sub, blends
-// its four (dy, dz) corners with weight w_x(sub) * w_y * w_z, and the pair
-// adds its two halves; lane sub then writes feature sub.
-// LANES = 1: one lane takes all eight corners.
-template <int DT, int LANES>
+// One lane per (point, level) takes all eight corners (the lane-pair kernel
+// below is the default; this one is the HG_TUNE_FWD_LANES = 1 launch shape).
+template <int DT>
 __global__ __launch_bounds__(kBlock) void fwd_f2_kernel(const float *__restrict__ x, int64_t n,
                                                         const void *__restrict__ table,
                                                         float *__restrict__ out, int64_t ostride,
@@ -69,9 +67,8 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_kernel(const float *__restrict_
     const float N = (float)lp.res[l];
     const uint32_t mask = lp.mask;
     const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
-    const int sub = threadIdx.x % LANES;
     const int64_t end = min(it.p0 + (int64_t)lp.chunk_pts, n);
-    for (int64_t p = it.p0 + threadIdx.x / LANES; p < end; p += kBlock / LANES) {
+    for (int64_t p = it.p0 + threadIdx.x; p < end; p += kBlock) {
         int32_t v0, v1, v2;
         float a0, a1, a2;
         locate1(x[3 * p + 0], N, v0, a0);
@@ -80,44 +77,30 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_kernel(const float *__restrict_
         const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hy1 = hy0 + kPrimeY;
         const uint32_t hz0 = (uint32_t)v2 * kPrimeZ, hz1 = hz0 + kPrimeZ;
         const float wy0 = 1.f - a1, wz0 = 1.f - a2;
-        float* orow = out + p * ostride + (int64_t)l * 2;
-        if (LANES == 2) {
-            const uint32_t cx = (uint32_t)v0 + (uint32_t)sub;
-            const float2 e00 = Table2<DT>::load(table, lbase + ((cx ^ hy0 ^ hz0) & mask));
-            const float2 e01 = Table2<DT>::load(table, lbase + ((cx ^ hy0 ^ hz1) & mask));
-            const float2 e10 = Table2<DT>::load(table, lbase + ((cx ^ hy1 ^ hz0) & mask));
-            const float2 e11 = Table2<DT>::load(table, lbase + ((cx ^ hy1 ^ hz1) & mask));
-            const float wx = sub ? a0 : 1.f - a0;
-            const float rx = wx * (wy0 * (wz0 * e00.x + a2 * e01.x) + a1 * (wz0 * e10.x + a2 * e11.x));
-            const float ry = wx * (wy0 * (wz0 * e00.y + a2 * e01.y) + a1 * (wz0 * e10.y + a2 * e11.y));
-            // lane 0 keeps feature 0 and needs lane 1's x-half; lane 1 the reverse.
-            const float recv = swap_pair(sub ? rx : ry);
-            orow[sub] = (sub ? ry : rx) + recv;
-        } else {
-            const uint32_t c0 = (uint32_t)v0, c1 = c0 + 1u;
-            float2 e[8];
-            e[0] = Table2<DT>::load(table, lbase + ((c0 ^ hy0 ^ hz0) & mask));
-            e[1] = Table2<DT>::load(table, lbase + ((c0 ^ hy0 ^ hz1) & mask));
-            e[2] = Table2<DT>::load(table, lbase + ((c0 ^ hy1 ^ hz0) & mask));
-            e[3] = Table2<DT>::load(table, lbase + ((c0 ^ hy1 ^ hz1) & mask));
-            e[4] = Table2<DT>::load(table, lbase + ((c1 ^ hy0 ^ hz0) & mask));
-            e[5] = Table2<DT>::load(table, lbase + ((c1 ^ hy0 ^ hz1) & mask));
-            e[6] = Table2<DT>::load(table, lbase + ((c1 ^ hy1 ^ hz0) & mask));
-            e[7] = Table2<DT>::load(table, lbase + ((c1 ^ hy1 ^ hz1) & mask));
-            const float wx0 = 1.f - a0;
-            float r[2];
+        float *orow = out + p * ostride + (int64_t)l * 2;
+        const uint32_t c0 = (uint32_t)v0, c1 = c0 + 1u;
+        float2 e[8];
+        e[0] = Table2<DT>::load(table, lbase + ((c0 ^ hy0 ^ hz0) & mask));
+        e[1] = Table2<DT>::load(table, lbase + ((c0 ^ hy0 ^ hz1) & mask));
+        e[2] = Table2<DT>::load(table, lbase + ((c0 ^ hy1 ^ hz0) & mask));
+        e[3] = Table2<DT>::load(table, lbase + ((c0 ^ hy1 ^ hz1) & mask));
+        e[4] = Table2<DT>::load(table, lbase + ((c1 ^ hy0 ^ hz0) & mask));
+        e[5] = Table2<DT>::load(table, lbase + ((c1 ^ hy0 ^ hz1) & mask));
+        e[6] = Table2<DT>::load(table, lbase + ((c1 ^ hy1 ^ hz0) & mask));
+        e[7] = Table2<DT>::load(table, lbase + ((c1 ^ hy1 ^ hz1) & mask));
+        const float wx0 = 1.f - a0;
+        float r[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float ej[8] = {j ? e[0].y : e[0].x, j ? e[1].y : e[1].x, j ? e[2].y : e[2].x,
-                                     j ? e[3].y : e[3].x, j ? e[4].y : e[4].x, j ? e[5].y : e[5].x,
-                                     j ? e[6].y : e[6].x, j ? e[7].y : e[7].x};
-                const float lo = wy0 * (wz0 * ej[0] + a2 * ej[1]) + a1 * (wz0 * ej[2] + a2 * ej[3]);
-                const float hi = wy0 * (wz0 * ej[4] + a2 * ej[5]) + a1 * (wz0 * ej[6] + a2 * ej[7]);
-                r[j] = wx0 * lo + a0 * hi;
-            }
-            orow[0] = r[0];
-            orow[1] = r[1];
+        for (int j = 0; j < 2; ++j) {
+            const float ej[8] = {j ? e[0].y : e[0].x, j ? e[1].y : e[1].x, j ? e[2].y : e[2].x,
+                                 j ? e[3].y : e[3].x, j ? e[4].y : e[4].x, j ? e[5].y : e[5].x,
+                                 j ? e[6].y : e[6].x, j ? e[7].y : e[7].x};
+            const float lo = wy0 * (wz0 * ej[0] + a2 * ej[1]) + a1 * (wz0 * ej[2] + a2 * ej[3]);
+            const float hi = wy0 * (wz0 * ej[4] + a2 * ej[5]) + a1 * (wz0 * ej[6] + a2 * ej[7]);
+            r[j] = wx0 * lo + a0 * hi;
         }
+        orow[0] = r[0];
+        orow[1] = r[1];
     }
 }
 
@@ -187,11 +170,10 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
 
 // ---------------------------------------------------------------- backward
 
-// LANES = 4: lane (dx, j) = (sub >> 1, sub & 1) adds feature j of the four
-// corners with that dx; the four lanes of a point hit one or two lines (the
-// default atomic path, bwd_f2_quad_kernel, adds the wave pre-reduction to it).
-// LANES = 2: lane dx adds both features of its four corners.
-// LANES = 1: one lane adds all sixteen values.
+// Other launch shapes of the atomic backward (the default is
+// bwd_f2_quad_kernel, four lanes (dx, feature) per point with the wave
+// pre-reduction):  LANES = 2: lane dx adds both features of its four
+// corners.  LANES = 1: one lane adds all sixteen values.
 template <int LANES>
 __global__ __launch_bounds__(kBlock) void bwd_f2_kernel(const float *__restrict__ x, int64_t n,
                                                         const float *__restrict__ dout,
@@ -217,33 +199,23 @@ __global__ __launch_bounds__(kBlock) void bwd_f2_kernel(const float *__restrict_
         const float wy0 = 1.f - a1, wz0 = 1.f - a2;
         const float w00 = wy0 * wz0, w01 = wy0 * a2, w10 = a1 * wz0, w11 = a1 * a2;
         const float *drow = dout + p * dstride + (int64_t)l * 2;
-        if (LANES == 4) {
-            const int dx = sub >> 1, j = sub & 1;
-            const uint32_t cx = (uint32_t)v0 + (uint32_t)dx;
-            const float gw = drow[j] * (dx ? a0 : 1.f - a0);
-            fadd(g + 2 * ((cx ^ hy0 ^ hz0) & mask) + j, gw * w00);
-            fadd(g + 2 * ((cx ^ hy0 ^ hz1) & mask) + j, gw * w01);
-            fadd(g + 2 * ((cx ^ hy1 ^ hz0) & mask) + j, gw * w10);
-            fadd(g + 2 * ((cx ^ hy1 ^ hz1) & mask) + j, gw * w11);
-        } else {
-            const float d0 = drow[0], d1 = drow[1];
+        const float d0 = drow[0], d1 = drow[1];
 #pragma unroll
-            for (int dx = 0; dx < 2; ++dx) {
-                if (LANES == 2 && dx != sub) continue;
-                const uint32_t cx = (uint32_t)v0 + (uint32_t)dx;
-                const float wx = dx ? a0 : 1.f - a0;
-                const float g0 = d0 * wx, g1 = d1 * wx;
-                const uint32_t i00 = (cx ^ hy0 ^ hz0) & mask, i01 = (cx ^ hy0 ^ hz1) & mask;
-                const uint32_t i10 = (cx ^ hy1 ^ hz0) & mask, i11 = (cx ^ hy1 ^ hz1) & mask;
-                fadd(g + 2 * i00, g0 * w00);
-                fadd(g + 2 * i00 + 1, g1 * w00);
-                fadd(g + 2 * i01, g0 * w01);
-                fadd(g + 2 * i01 + 1, g1 * w01);
-                fadd(g + 2 * i10, g0 * w10);
-                fadd(g + 2 * i10 + 1, g1 * w10);
-                fadd(g + 2 * i11, g0 * w11);
-                fadd(g + 2 * i11 + 1, g1 * w11);
-            }
+        for (int dx = 0; dx < 2; ++dx) {
+            if (LANES == 2 && dx != sub) continue;
+            const uint32_t cx = (uint32_t)v0 + (uint32_t)dx;
+            const float wx = dx ? a0 : 1.f - a0;
+            const float g0 = d0 * wx, g1 = d1 * wx;
+            const uint32_t i00 = (cx ^ hy0 ^ hz0) & mask, i01 = (cx ^ hy0 ^ hz1) & mask;
+            const uint32_t i10 = (cx ^ hy1 ^ hz0) & mask, i11 = (cx ^ hy1 ^ hz1) & mask;
+            fadd(g + 2 * i00, g0 * w00);
+            fadd(g + 2 * i00 + 1, g1 * w00);
+            fadd(g + 2 * i01, g0 * w01);
+            fadd(g + 2 * i01 + 1, g1 * w01);
+            fadd(g + 2 * i10, g0 * w10);
+            fadd(g + 2 * i10 + 1, g1 * w10);
+            fadd(g + 2 * i11, g0 * w11);
+            fadd(g + 2 * i11 + 1, g1 * w11);
         }
     }
 }
@@ -419,7 +391,7 @@ hipError_t launch_gather_dt(const LaunchParams &lp, const float *x, int64_t n, c
                             int64_t ostride, int64_t lstride, const FwdTune &ft, hipStream_t stream) {
     dim3 grid(grid_blocks(lp)), block(kBlock);
     if (lstride == 2 && ft.lanes == 1) {
-        fwd_f2_kernel<DT, 1><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lp);
+        fwd_f2_kernel<DT><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lp);
     } else if (ft.nt) {
         if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
         else if (ft.unroll == 2) fwd_f2_pair_kernel<DT, 2, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
