@@ -108,9 +108,9 @@ bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
     const bool std_shape = c.n_dims == 3 && c.n_features == 2;
     int want, tile_pts, rec_per_tile, rec_bytes;
     if (std_shape) {
-        // Partition of 2^12 entries (32 KB of accumulators, 512-thread owners) for
-        // tables up to 2^20 entries; 2^13 (1024 threads) for larger tables, whose
-        // runs per tile would otherwise get short.
+        // Partitions of 2^12 entries (64 KB of 64-bit accumulators, 1024-thread
+        // owners, two per CU) for tables up to 2^20 entries; 2^13 (128 KB, one
+        // per CU) for larger tables, whose runs per tile would otherwise get short.
         want = g_tune.bwd_part_log2 ? g_tune.bwd_part_log2 : (c.log2_table_size <= 20 ? 12 : 13);
         tile_pts = hg::kBinTile;
         rec_per_tile = hg::kBinTile * 4;
