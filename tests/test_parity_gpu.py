@@ -373,6 +373,53 @@ def test_launch_variants_match_oracle(oracle, key, value):
     bwd_check(grad, oracle.backward(g, x, d), w.n_levels)
 
 
+# ----------------------------------------------------------------------------- graph capture
+
+@pytest.mark.parametrize("workspace", ["binned", "atomic"])
+def test_step_captured_in_a_graph_replays_like_eager(workspace):
+    # The library allocates nothing, never synchronises and issues no memsets,
+    # so a forward + backward can be captured in a HIP graph.  Every replay,
+    # with eager work and synchronisations in between, matches the eager result:
+    # bit for bit on the binned path (fixed-point sums), to fp32 rounding on the
+    # atomic path (its additions happen in an unspecified order).
+    w = I.resized(I.WORKLOADS["standard"], 1 << 16)
+    cfg = hg.HashGridConfig.of(w)
+    x, t, d = dev(I.make_points(w)), dev(I.make_table(w)), dev(I.make_dout(w))
+    out = torch.empty((w.n_points, cfg.out_features), device=DEV)
+    grad = torch.zeros(cfg.table_shape, device=DEV)
+    ws = hg.backward_workspace(cfg, w.n_points, DEV) if workspace == "binned" else None
+    fws = hg.forward_workspace(cfg, w.n_points, DEV)
+
+    def step():
+        hg.hashgrid_forward(cfg, x, t, out=out, workspace=fws)
+        hg.hashgrid_backward(cfg, x, d, grad, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_grad = out.clone(), grad.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        grad.zero_()
+        out.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
+        if workspace == "binned":
+            assert torch.equal(grad, ref_grad)
+        else:
+            scale = float(ref_grad.abs().max())
+            assert float((grad - ref_grad).abs().max()) <= 1e-6 * scale
+
+
 # ----------------------------------------------------------------------------- module
 
 def test_encoder_module_autograd(oracle):
