@@ -8,8 +8,10 @@
 //   h(c) = (c_x ^ c_y * 2654435761 ^ c_z * 805459861) mod 2^log2T in uint32,
 //   out[l*F + j] = sum over the 8 corners of w_c * table[l][h(c)][j],
 //   w_c = prod_d (d-th offset ? f_d : 1 - f_d).
-// The backward scatters dL/dout * w_c back into every table entry a corner
-// hashed to (the adjoint of the gather) with fp32 atomic adds.
+// The backward here (used without a workspace; binned_backward.hip holds the
+// default one) scatters dL/dout * w_c back into every table entry a corner
+// hashed to (the adjoint of the gather) with fp32 atomic adds, after a wave
+// has summed runs of consecutive points that share a voxel.
 //
 // Memory behaviour on MI355X.  The corner gathers are the traffic: 8 random
 // F-vectors per point and level.  Because the x prime is 1, the corners
