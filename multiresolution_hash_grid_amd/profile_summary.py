@@ -44,12 +44,20 @@ SOURCES = ("device_common.h", "hashgrid_internal.h", "encode_kernels.hip", "binn
 MLP_SOURCES = SOURCES + ("mlp_kernels.hip",)
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace runs collapsed: edits
+    to comments or layout do not change the code the figures belong to."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(files=SOURCES) -> str:
-    """sha256 over the kernel sources (counter figures are only valid for them)."""
+    """sha256 over the code of the kernel sources (counter figures are only valid for it)."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "multiresolution_hash_grid_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "multiresolution_hash_grid_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
