@@ -66,3 +66,11 @@ def test_committed_summaries_parse():
     c = json.load(open(os.path.join(ROOT, "profiles", "counters_standard_mlp.json")))
     assert 0.0 <= c["l2"]["fwd_f2_pair_kernel<0, 4, false, float>"]["hit_rate"] <= 1.0
     assert set(c["mfma"]) >= {"mlp_fwd_kernel", "mlp_bwd_kernel"}
+
+
+def test_source_digest_ignores_comments_and_layout():
+    a = "int f(int x) {  // twice\n    return 2 * x; /* the result */\n}\n"
+    b = "int f(int x)\n{\n  return 2 * x;\n}  // another comment\n"
+    c = "int f(int x) { return 3 * x; }"
+    assert ps._code_only(a) == ps._code_only(b)
+    assert ps._code_only(a) != ps._code_only(c)
