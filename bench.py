@@ -218,6 +218,36 @@ def measure_fused_mlp(dev, iters: int) -> dict:
                 for k, v in mfma.items() if k.startswith("mlp_")}}
 
 
+def measure_other_configs(dev, iters: int) -> dict:
+    """Forward and backward (with workspaces) of the other full-size grids the
+    parity tests run: the ray batch (ray-major samples, whose coarse levels the
+    wave pre-reduction folds) and the large binary16 grid."""
+    import torch
+    import multiresolution_hash_grid_amd as hg
+    from multiresolution_hash_grid_amd import inputs
+    out = {}
+    for name in ("ray", "large_f16"):
+        w = inputs.WORKLOADS[name]
+        cfg = hg.HashGridConfig.of(w)
+        n = w.n_points
+        x = torch.from_numpy(inputs.make_points(w)).to(dev)
+        t = torch.from_numpy(inputs.make_table(w)).to(dev)
+        d = torch.from_numpy(inputs.make_dout(w)).to(dev)
+        o = torch.empty((n, cfg.out_features), device=dev)
+        g = torch.zeros(cfg.table_shape, device=dev)
+        ws = hg.backward_workspace(cfg, n, dev)
+        fws = hg.forward_workspace(cfg, n, dev)
+        fms = time_calls(lambda: hg.hashgrid_forward(cfg, x, t, out=o, workspace=fws), iters)
+        bms = time_calls(lambda: hg.hashgrid_backward(cfg, x, d, g, workspace=ws), iters)
+        bpp = algorithmic_bytes_per_point(w, 2 if w.table_dtype == "f16" else 4)
+        out[name] = {"points": n, "fwd_us": fms * 1e3, "bwd_us": bms * 1e3,
+                     "fwd_points_per_s": n / (fms * 1e-3), "bwd_points_per_s": n / (bms * 1e-3),
+                     "fwd_frac": bpp["fwd"] * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "bwd_frac": bpp["bwd"] * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del x, t, d, o, g, ws, fws
+    return out
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -314,7 +344,8 @@ def main() -> int:
         print(json.dumps({"next": {"adam": measure_adam(cfg, dev, 50),
                                    "input_grad": measure_input_grad(cfg, x, t, d, 20),
                                    "shapes": measure_shapes(dev, w.n_points, 10),
-                                   "fused_mlp": measure_fused_mlp(dev, 5)}}), flush=True)
+                                   "fused_mlp": measure_fused_mlp(dev, 5),
+                                   "other_configs": measure_other_configs(dev, 5)}}), flush=True)
         return 0
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
@@ -397,7 +428,8 @@ def main() -> int:
         result["next"] = {"adam": measure_adam(cfg, dev, 50),
                           "input_grad": measure_input_grad(cfg, x, t, d, 20),
                           "shapes": measure_shapes(dev, w.n_points, 10),
-                          "fused_mlp": measure_fused_mlp(dev, 5)}
+                          "fused_mlp": measure_fused_mlp(dev, 5),
+                          "other_configs": measure_other_configs(dev, 5)}
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, x_h, t_h, d_h, args.cpu_seconds)
