@@ -292,10 +292,13 @@ typedef struct {
 int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m, float *v,
                        float *grad, void *param_f16, int32_t flags, void *stream);
 
-/* Performance knobs (launch shapes).  They never change results beyond the
- * unspecified order of the backward's atomic adds.  Process-wide; not
- * thread-safe against concurrent launches.  Returns HG_EINVAL for an unknown
- * key or an out-of-range value. */
+/* Performance knobs (launch shapes).  Two change results within rounding:
+ * HG_TUNE_FWD_LANES (the order in which the blend's eight terms are added) and
+ * HG_TUNE_BWD_BINNED (fixed-point binned accumulation or fp32 atomics, whose
+ * order is unspecified), as do the atomic path's HG_TUNE_BWD_LANES shapes.
+ * The others give identical results.  Process-wide; not thread-safe against
+ * concurrent launches.  Returns HG_EINVAL for an unknown key or an
+ * out-of-range value. */
 #define HG_TUNE_FWD_LANES 0    /* lanes per (point, level) in the forward: 1 or 2        */
 #define HG_TUNE_BWD_LANES 1    /* lanes per (point, level) in the backward: 1, 2 or 4    */
 #define HG_TUNE_CHUNK_POINTS 2 /* points per workgroup work item: 64..65536, power of 2  */
