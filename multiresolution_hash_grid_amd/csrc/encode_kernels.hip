@@ -155,10 +155,12 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
         for (int u = 0; u < U; ++u) {
             const float wy0 = 1.f - a1[u], wz0 = 1.f - a2[u];
             const float wx = sub ? a0[u] : 1.f - a0[u];
-            const float rx = wx * (wy0 * (wz0 * e[u][0].x + a2[u] * e[u][1].x) +
-                                   a1[u] * (wz0 * e[u][2].x + a2[u] * e[u][3].x));
-            const float ry = wx * (wy0 * (wz0 * e[u][0].y + a2[u] * e[u][1].y) +
-                                   a1[u] * (wz0 * e[u][2].y + a2[u] * e[u][3].y));
+            // Explicit fused multiply-adds: the rounding does not depend on
+            // how the compiler contracts each unroll depth.
+            const float rx = wx * fmaf(a1[u], fmaf(a2[u], e[u][3].x, wz0 * e[u][2].x),
+                                       wy0 * fmaf(a2[u], e[u][1].x, wz0 * e[u][0].x));
+            const float ry = wx * fmaf(a1[u], fmaf(a2[u], e[u][3].y, wz0 * e[u][2].y),
+                                       wy0 * fmaf(a2[u], e[u][1].y, wz0 * e[u][0].y));
             // lane 0 keeps feature 0 and needs lane 1's x-half; lane 1 the reverse.
             const float v = (sub ? ry : rx) + swap_pair(sub ? rx : ry);
             if (ok[u]) {

@@ -373,6 +373,27 @@ def test_launch_variants_match_oracle(oracle, key, value):
     bwd_check(grad, oracle.backward(g, x, d), w.n_levels)
 
 
+@pytest.mark.parametrize("key,value", [(B.HG_TUNE_CHUNK_POINTS, 64), (B.HG_TUNE_CHUNK_POINTS, 8192),
+                                       (B.HG_TUNE_XCD_MAP, 0), (B.HG_TUNE_FWD_UNROLL, 1), (B.HG_TUNE_FWD_NT, 1),
+                                       (B.HG_TUNE_FWD_STAGED, 0), (B.HG_TUNE_BWD_PART_LOG2, 11),
+                                       (B.HG_TUNE_BWD_PART_LOG2, 13), (B.HG_TUNE_BWD_GROUP_MIB, 0),
+                                       (B.HG_TUNE_BWD_GROUP_MIB, 3)])
+def test_result_neutral_knobs_give_identical_results(key, value):
+    # The launch shapes that the header documents as result-neutral reproduce
+    # the default's forward and binned backward bit for bit.
+    w = I.resized(I.WORKLOADS["standard"], 5 * 1024 + 77)
+    cfg = hg.HashGridConfig.of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    ref_out, ref_grad = run_forward(cfg, x, t), run_backward(cfg, x, d)
+    old = hg.hashgrid_tune_get(key)
+    try:
+        hg.hashgrid_tune(key, value)
+        out, grad = run_forward(cfg, x, t), run_backward(cfg, x, d)
+    finally:
+        hg.hashgrid_tune(key, old)
+    assert np.array_equal(out, ref_out) and np.array_equal(grad, ref_grad)
+
+
 # ----------------------------------------------------------------------------- graph capture
 
 @pytest.mark.parametrize("workspace", ["binned", "atomic"])
