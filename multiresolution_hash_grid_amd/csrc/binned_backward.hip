@@ -255,8 +255,10 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
     extern __shared__ uint32_t dyn[];  // cnt[parts], base[parts + 1]
     uint32_t *cnt = dyn;
     uint32_t *base = dyn + bp.parts;
-    const int tile = blockIdx.x;
-    const int gb = blockIdx.y * kLevelsPerBlock;
+    const BinSlot slot = bin_slot((bp.group + kLevelsPerBlock - 1) / kLevelsPerBlock);
+    if (slot.tile >= bp.tiles) return;
+    const int tile = slot.tile;
+    const int gb = slot.block * kLevelsPerBlock;
     const int nlev = min(bp.group - gb, kLevelsPerBlock);
     // The wave pre-reduction borrows the stage before the records are sorted into it.
     static_assert(kBinThreads / 64 * 16 * 64 * sizeof(float) <= sizeof(Rec) * kRecPerTile, "stage too small");
@@ -367,7 +369,7 @@ hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, con
         bp.level0 = l0;
         bp.group = min(group, n_levels - l0);
         const StdSpace sp = carve<Rec>(workspace, bp);
-        const dim3 tgrid(bp.tiles, (bp.group + kLevelsPerBlock - 1) / kLevelsPerBlock);
+        const dim3 tgrid(bin_grid(bp.tiles, (bp.group + kLevelsPerBlock - 1) / kLevelsPerBlock));
         bin_kernel<<<tgrid, kBinThreads, dyn, stream>>>(x, n, dout, dout_stride, bp, sp, dtable);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -37,6 +37,24 @@ Space<Rec> carve(void *ws, const BinParams &bp) {
     return s;
 }
 
+// Bin workgroup -> (tile, block of levels).  The nb blocks of one tile read
+// the same points and the same dout rows (each a slice of every row).
+// Workgroups are dispatched to the XCDs round-robin, so workgroup ids w,
+// w + 8, w + 16 ... run back to back on one XCD: giving a tile's blocks those
+// ids lets the later blocks find the rows in that XCD's L2.
+struct BinSlot {
+    int tile, block;
+};
+__device__ __forceinline__ BinSlot bin_slot(int nb) {
+    const int k = (int)(blockIdx.x / kNumXcd);
+    return {(k / nb) * kNumXcd + (int)(blockIdx.x % kNumXcd), k % nb};
+}
+// Grid of the bin kernels: every tile below tiles rounded up to a multiple of
+// kNumXcd, nb blocks each (workgroups past the last tile return at once).
+inline unsigned bin_grid(int tiles, int nb) {
+    return (unsigned)(((int64_t)tiles + kNumXcd - 1) / kNumXcd * kNumXcd * nb);
+}
+
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
