@@ -206,6 +206,53 @@ def test_vertex_points_return_the_vertex_feature(oracle):
         assert np.array_equal(out[:, 2 * l:2 * l + 2], expect)
 
 
+def _fp32_vertex_coordinate(k, N):
+    """An fp32 x with fl32(x * N) == k, preferring one whose exact product is
+    not k (then only a position rounded to fp32 lands on the vertex)."""
+    x0 = np.float32(k / N)
+    cands = [x0]
+    up = down = x0
+    for _ in range(4):
+        up, down = np.nextafter(up, np.float32(np.inf)), np.nextafter(down, np.float32(-np.inf))
+        cands += [up, down]
+    hits = [x for x in cands if np.float32(x) * np.float32(N) == np.float32(k)]
+    inexact = [x for x in hits if float(x) * N != k]
+    if not hits:
+        return None, False  # the fp32 products step over k
+    return (inexact or hits)[0], bool(inexact)
+
+
+def test_vertex_points_at_resolutions_that_are_not_powers_of_two(oracle):
+    # The position is one fp32 multiply (reading of p1's x * N_l with fp32 x): where
+    # fl32(x * N_l) is the integer vertex v, all weight sits on v even when the exact
+    # product x * N_l is not v.  Non-power-of-two levels of the standard grid make
+    # such points common; a fraction taken from the unrounded product fails here.
+    w = I.WORKLOADS["standard"]
+    g = oracle.grid_of(w)
+    t = I.make_table(w)
+    res = oracle.resolutions(w.n_levels, w.base_resolution, w.finest_resolution)
+    rng = np.random.default_rng(12)
+    n_inexact = 0
+    for l, N in enumerate(res):
+        N = int(N)
+        if N & (N - 1) == 0:
+            continue
+        coord = {k: _fp32_vertex_coordinate(k, N) for k in range(N + 1)}
+        reachable = np.array([k for k, (xk, _) in coord.items() if xk is not None])
+        v = rng.choice(reachable, size=(200, 3))
+        x = np.zeros((200, 3), dtype=np.float32)
+        for i in range(200):
+            for d in range(3):
+                x[i, d], inexact = coord[int(v[i, d])]
+                n_inexact += inexact
+        assert np.array_equal(np.floor(x * np.float32(N)).astype(np.int64), v)
+        out = oracle.forward(g, x, t)
+        idx, _ = oracle.corners(g, x)
+        expect = t[l][idx[:, l, 0]].astype(np.float64)
+        assert np.array_equal(out[:, 2 * l:2 * l + 2], expect)
+    assert n_inexact > 1000  # most coordinates exercise the rounding
+
+
 def test_matches_library_trilinear_interpolation(oracle):
     # Dense vertex grid G_l[v] = table[h(v)] read back at vertex points, then scipy's
     # RegularGridInterpolator (linear) evaluated at the float32 scaled position.
