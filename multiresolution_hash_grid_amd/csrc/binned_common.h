@@ -49,8 +49,10 @@ __device__ __forceinline__ BinSlot bin_slot(int nb) {
     const int k = (int)(blockIdx.x / kNumXcd);
     return {(k / nb) * kNumXcd + (int)(blockIdx.x % kNumXcd), k % nb};
 }
-// Grid of the bin kernels: every tile below tiles rounded up to a multiple of
-// kNumXcd, nb blocks each (workgroups past the last tile return at once).
+// Grid for bin_slot: tiles rounded up to a multiple of kNumXcd, nb blocks each
+// (workgroups past the last tile return at once).  The standard grid's bin
+// kernel uses it; the generic bin kernels keep a (tile, level) grid in tile
+// order, where this order measured slower for some shapes.
 inline unsigned bin_grid(int tiles, int nb) {
     return (unsigned)(((int64_t)tiles + kNumXcd - 1) / kNumXcd * kNumXcd * nb);
 }
