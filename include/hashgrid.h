@@ -129,8 +129,8 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
  * *min_bytes_out (one level's share; may be NULL) also works -- the levels
  * are then processed in smaller groups.  Returns 0 bytes when the
  * configuration has no binned path (more than 4096 partitions: T > 2^25 for
- * the D = 3, F = 2 grid, partitions of 8192 / F entries for other shapes; or
- * n >= 2^29).
+ * the D = 3, F = 2 grid, partitions of 8192 / F entries for other shapes;
+ * n >= 2^29; or a 2-entry table with F = 1).
  * Errors: HG_EINVAL, HG_EUNSUPPORTED. */
 int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out,
                                      size_t *min_bytes_out);

@@ -1,0 +1,118 @@
+"""GPU parity on seeded random grid configurations.
+
+Each case draws a grid (D in 1..4 inputs, F in {1, 2, 4, 8}, 1..20 levels,
+T = 2^1..2^18, N_min 1..64 up to N_max <= 64 N_min, fp32 or binary16 tables),
+a point count from 1 to 6000 and, for half of them, points spread over
+[-0.25, 1.25) so that voxels outside the unit cube (negative coordinates,
+x = 1) occur, then checks every entry point against the CPU oracle at the
+bars of the other parity tests:
+  - corner indices of the debug export bit-exact, weights to 1e-6;
+  - forward <= 1e-6 * max|table|;
+  - backward, binned (sized workspace) and atomic (no workspace), <= 1e-5 *
+    max|oracle gradient| per level, added into a non-zero buffer;
+  - dL/dx <= 1e-5 * max|oracle dL/dx| per coordinate.
+The draws are fixed by the case number, so a failure names a reproducible
+configuration (printed before each case runs).
+"""
+import os
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import multiresolution_hash_grid_amd as hg  # noqa: E402
+from multiresolution_hash_grid_amd import inputs as I  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+CASES = 24
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _threads(oracle):
+    oracle.set_threads(min(16, os.cpu_count() or 1))
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def draw(case):
+    rng = np.random.default_rng(90_000 + case)
+    D = int(rng.integers(1, 5))
+    F = int(rng.choice([1, 2, 4, 8]))
+    if case % 6 == 0:
+        D, F = 3, 2  # the tuned shape, at odd sizes
+    L = int(rng.integers(1, 21))
+    log2T = int(rng.integers(1, 19))
+    nmin = int(rng.integers(1, 65))
+    nmax = int(rng.integers(nmin, 64 * nmin + 1))
+    dtype = "f16" if rng.random() < 0.3 else "f32"
+    n = int(rng.integers(1, 6001))
+    spread = bool(case % 2)
+    w = I.Workload(f"random{case}", L, F, log2T, nmin, nmax, dtype, n, "uniform", seed=3000 + case, n_dims=D)
+    return w, spread
+
+
+# Hand-picked corners of the parameter space: 2-entry tables (for F = 1 the
+# binned path would hold partitions of fewer than one float4, so those take the
+# atomic path), one level, N_min = N_max, resolution 1, a single point.
+EDGES = [
+    # D, F, L, log2T, N_min, N_max, dtype, n, spread
+    (2, 1, 4, 1, 2, 8, "f32", 3001, True),
+    (3, 1, 3, 1, 4, 64, "f32", 2049, False),
+    (3, 2, 5, 1, 1, 40, "f16", 1500, True),
+    (4, 8, 2, 1, 3, 9, "f32", 700, True),
+    (1, 1, 1, 5, 7, 7, "f32", 513, True),
+    (3, 2, 1, 19, 512, 512, "f32", 4096, False),
+    (3, 2, 6, 12, 1, 1, "f32", 1000, True),
+    (2, 4, 7, 3, 16, 16, "f16", 1, False),
+]
+
+
+def edge_workload(i):
+    D, F, L, log2T, nmin, nmax, dtype, n, spread = EDGES[i]
+    return I.Workload(f"edge{i}", L, F, log2T, nmin, nmax, dtype, n, "uniform", seed=4000 + i, n_dims=D), spread
+
+
+@pytest.mark.parametrize("case", range(CASES + len(EDGES)))
+def test_random_configuration_matches_oracle(oracle, case):
+    w, spread = draw(case) if case < CASES else edge_workload(case - CASES)
+    print(f"[config {case}] D={w.n_dims} F={w.n_features} L={w.n_levels} log2T={w.log2_table_size} "
+          f"N={w.base_resolution}..{w.finest_resolution} {w.table_dtype} n={w.n_points} spread={spread}",
+          flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    g = oracle.grid_of(w)
+    x = I.make_points(w)
+    if spread:
+        x = (x.astype(np.float64) * 1.5 - 0.25).astype(np.float32)
+    t = I.make_table(w)
+    d = I.make_dout(w)
+    xd, td, dd = dev(x), dev(t), dev(d)
+
+    idx_ref, w_ref = oracle.corners(g, x)
+    idx, wt = hg.hashgrid_debug_corners(cfg, xd)
+    assert np.array_equal(idx.cpu().numpy().astype(np.uint32).reshape(idx_ref.shape), idx_ref)
+    assert np.max(np.abs(wt.cpu().numpy().astype(np.float64).reshape(w_ref.shape) - w_ref)) <= 1e-6
+
+    ref = oracle.forward(g, x, t)
+    scale = float(np.max(np.abs(t.astype(np.float64))))
+    for workspace in ("auto", None):
+        out = hg.hashgrid_forward(cfg, xd, td, workspace=workspace).cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(out - ref)) <= 1e-6 * scale, workspace
+
+    gref = oracle.backward(g, x, d)
+    base = np.random.default_rng(case).uniform(-1, 1, cfg.table_shape).astype(np.float32)
+    for workspace in ("auto", None):
+        grad = dev(base)
+        hg.hashgrid_backward(cfg, xd, dd, grad, workspace=workspace)
+        got = grad.cpu().numpy().astype(np.float64) - base
+        for l in range(w.n_levels):
+            bound = 1e-5 * float(np.max(np.abs(gref[l]))) + 4e-7  # + the rounding of the fp32 base
+            assert np.max(np.abs(got[l] - gref[l])) <= bound, (workspace, l)
+
+    dxref = oracle.input_grad(g, x, t, d)
+    dx = hg.hashgrid_input_grad(cfg, xd, td, dd).cpu().numpy().astype(np.float64)
+    for c in range(w.n_dims):
+        assert np.max(np.abs(dx[:, c] - dxref[:, c])) <= 1e-5 * float(np.max(np.abs(dxref[:, c]))), c
