@@ -125,9 +125,6 @@ bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
     const int64_t parts = (int64_t)1 << (c.log2_table_size - s_log2);
     const int64_t tiles = (n + tile_pts - 1) / tile_pts;
     if (parts > hg::kMaxParts || n >= ((int64_t)1 << 29)) return false;
-    // The owners add their partition into the table in whole float4s: a
-    // partition of fewer than 4 values (T = 2 with F = 1) takes the atomic path.
-    if (((int64_t)c.n_features << s_log2) < 4) return false;
     bp.level0 = 0;
     bp.group = c.n_levels;
     bp.tiles = (int32_t)tiles;

@@ -231,7 +231,8 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     // workgroup writes them.  They are read at the flush: holding them in
     // registers through the record loop (87 instead of 63 VGPRs) cost more
     // than the exposed read latency (standard backward 162 -> 158 us without).
-    float4 *gl = reinterpret_cast<float4 *>(grad + ((((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * F));
+    float *gbase = grad + ((((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * F);
+    float4 *gl = reinterpret_cast<float4 *>(gbase);
     for (int i = threadIdx.x; i < S * F; i += THREADS) slice[i] = 0ull;
     if (threadIdx.x == 0) touched = 0;
     // The level's max |dL/dout| over the tiles' maxima.
@@ -296,6 +297,10 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     __syncthreads();
     if (!touched) return;  // no corner of this batch fell in the partition: nothing to add
     const long long *sl = reinterpret_cast<const long long *>(slice);
+    if (S * F < 4) {  // a 2-entry table with one feature: two floats, less than a float4
+        if (threadIdx.x < S * F) gbase[threadIdx.x] += (float)ldexp((double)sl[threadIdx.x], -k);
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < kFlushPer; ++u) {
         const int j = threadIdx.x + u * THREADS;

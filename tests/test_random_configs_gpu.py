@@ -55,9 +55,9 @@ def draw(case):
     return w, spread
 
 
-# Hand-picked corners of the parameter space: 2-entry tables (for F = 1 the
-# binned path would hold partitions of fewer than one float4, so those take the
-# atomic path), one level, N_min = N_max, resolution 1, a single point.
+# Hand-picked corners of the parameter space: 2-entry tables (with F = 1 a
+# partition holds two floats, less than the float4 the owners flush), one
+# level, N_min = N_max, resolution 1, a single point.
 EDGES = [
     # D, F, L, log2T, N_min, N_max, dtype, n, spread
     (2, 1, 4, 1, 2, 8, "f32", 3001, True),
