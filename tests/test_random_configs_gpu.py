@@ -11,7 +11,9 @@ bars of the other parity tests:
   - backward, binned (sized workspace) and atomic (no workspace), <= 1e-5 *
     max|oracle gradient| per level, added into a non-zero buffer;
   - dL/dx <= 1e-5 * max|oracle dL/dx| per coordinate.
-The draws are fixed by the case number, so a failure names a reproducible
+Eight more draws use the D = 3, F = 2 grid with the points sorted by a coarse
+cell, so that the wave pre-reduction meets long runs on random grids.  The
+draws are fixed by the case number, so a failure names a reproducible
 configuration (printed before each case runs).
 """
 import os
@@ -76,17 +78,49 @@ def edge_workload(i):
     return I.Workload(f"edge{i}", L, F, log2T, nmin, nmax, dtype, n, "uniform", seed=4000 + i, n_dims=D), spread
 
 
-@pytest.mark.parametrize("case", range(CASES + len(EDGES)))
+COHERENT = 8  # D = 3, F = 2 draws with the points sorted by a coarse cell
+
+
+def _spread_bits(v):
+    """The 10 low bits of v moved to every third bit (a Morton interleave)."""
+    v = v.astype(np.uint64) & np.uint64(0x3FF)
+    for shift, mask in ((16, 0x030000FF), (8, 0x0300F00F), (4, 0x030C30C3), (2, 0x09249249)):
+        v = (v | (v << np.uint64(shift))) & np.uint64(mask)
+    return v
+
+
+def coherent_order(x):
+    """Points in Morton order on a 1024^3 grid over [-1/4, 5/4)^3, so that
+    consecutive points share voxels at the coarse levels as ray samples do:
+    long runs for the wave pre-reduction, on random grids."""
+    q = np.clip(np.floor((x.astype(np.float64) + 0.25) / 1.5 * 1024), 0, 1023).astype(np.int64)
+    key = (_spread_bits(q[:, 0]) << np.uint64(2)) | (_spread_bits(q[:, 1]) << np.uint64(1)) | _spread_bits(q[:, 2])
+    return np.ascontiguousarray(x[np.argsort(key, kind="stable")])
+
+
+@pytest.mark.parametrize("case", range(CASES + len(EDGES) + COHERENT))
 def test_random_configuration_matches_oracle(oracle, case):
-    w, spread = draw(case) if case < CASES else edge_workload(case - CASES)
+    coherent = case >= CASES + len(EDGES)
+    if coherent:
+        w, spread = draw(1000 + case)
+        rng = np.random.default_rng(95_000 + case)
+        # Tables of at least 2^10 entries: below that, 10^4 points put more than
+        # 10^4 fp32 additions on an entry of the atomic path, past its 1e-5 bar.
+        w = I.replace(w, name=f"coherent{case}", n_dims=3, n_features=2, base_resolution=int(rng.integers(1, 9)),
+                      n_points=int(rng.integers(8000, 20001)), log2_table_size=max(10, w.log2_table_size))
+    else:
+        w, spread = draw(case) if case < CASES else edge_workload(case - CASES)
     print(f"[config {case}] D={w.n_dims} F={w.n_features} L={w.n_levels} log2T={w.log2_table_size} "
-          f"N={w.base_resolution}..{w.finest_resolution} {w.table_dtype} n={w.n_points} spread={spread}",
+          f"N={w.base_resolution}..{w.finest_resolution} {w.table_dtype} n={w.n_points} spread={spread} "
+          f"coherent={coherent}",
           flush=True)
     cfg = hg.HashGridConfig.of(w)
     g = oracle.grid_of(w)
     x = I.make_points(w)
     if spread:
         x = (x.astype(np.float64) * 1.5 - 0.25).astype(np.float32)
+    if coherent:
+        x = coherent_order(x)
     t = I.make_table(w)
     d = I.make_dout(w)
     xd, td, dd = dev(x), dev(t), dev(d)
