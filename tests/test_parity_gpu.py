@@ -441,6 +441,75 @@ def test_step_captured_in_a_graph_replays_like_eager(workspace):
             assert float((grad - ref_grad).abs().max()) <= 1e-6 * scale
 
 
+def test_head_input_grad_and_adam_captured_in_a_graph_replay_like_eager():
+    # The other entry points under graph capture: encoder + MLP head forward and
+    # backward, dL/dx and the Adam step, with every buffer (stages, workspaces)
+    # allocated before capture.  Each replay starts from the same state, set by
+    # eager copies between replays, and matches the eager step bit for bit: the
+    # binned table sums are exact and the weight gradients are reduced in a
+    # fixed order.
+    w = I.resized(I.WORKLOADS["fused_mlp"], 1 << 14)
+    cfg = hg.HashGridConfig.of(w)
+    n = w.n_points
+    x, t = dev(I.make_points(w)), dev(I.make_table(w))
+    P = [dev(a) for a in I.mlp_params(w.seed, bias_scale=0.1)]
+    dy = dev(I.dout_normal(w.seed + 7, n, 4))
+    st_bytes, bw_bytes = hg.hashgrid_mlp_workspace_size(cfg, n)
+    stage = torch.empty(st_bytes, dtype=torch.uint8, device=DEV)
+    mws = torch.empty(bw_bytes, dtype=torch.uint8, device=DEV)
+    y = torch.empty((n, 4), device=DEV)
+    grads = [torch.zeros(hg.hashgrid.MLP_SHAPES[k], device=DEV) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+    dtable = torch.zeros(cfg.table_shape, device=DEV)
+    ws = I.resized(I.WORKLOADS["standard"], n)
+    scfg = hg.HashGridConfig.of(ws)
+    st, sd = dev(I.make_table(ws)), dev(I.make_dout(ws))
+    iws = torch.empty(hg.hashgrid_input_grad_workspace_size(scfg, n), dtype=torch.uint8, device=DEV)
+    dx = torch.empty((n, 3), device=DEV)
+    p0 = torch.from_numpy(np.random.default_rng(3).uniform(-1, 1, 1 << 16).astype(np.float32)).to(DEV)
+    g0 = torch.from_numpy(np.random.default_rng(4).normal(size=1 << 16).astype(np.float32)).to(DEV)
+    param, m, v, gr = p0.clone(), torch.zeros_like(p0), torch.zeros_like(p0), g0.clone()
+
+    def reset():
+        for a in grads:
+            a.zero_()
+        dtable.zero_()
+        y.fill_(-1.0)
+        dx.fill_(-1.0)
+        param.copy_(p0)
+        m.zero_()
+        v.zero_()
+        gr.copy_(g0)
+
+    def step():
+        hg.hashgrid_mlp_forward(cfg, x, t, P, y=y, stage=stage)
+        hg.hashgrid_mlp_backward(cfg, x, stage, P, dy, grads, dtable, workspace=mws)
+        hg.hashgrid_input_grad(scfg, x, st, sd, dx=dx, workspace=iws)
+        hg.hashgrid_adam_step(param, m, v, gr, lr=1e-2, step=1)
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    ref = [y.clone(), dtable.clone(), dx.clone(), param.clone(), m.clone(), v.clone()] + [a.clone() for a in grads]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [y, dtable, dx, param, m, v] + grads
+        for name, a, b in zip(("y", "dtable", "dx", "param", "m", "v", "dw1", "db1", "dw2", "db2", "dw3", "db3"),
+                              got, ref):
+            assert torch.equal(a, b), name
+
+
 # ----------------------------------------------------------------------------- module
 
 def test_encoder_module_autograd(oracle):
