@@ -38,6 +38,13 @@ MUTANTS = {
     "weights_flipped": (C, "        w *= up ? frac[d] : 1.0 - frac[d];", "        w *= up ? 1.0 - frac[d] : frac[d];"),
     "corner_offset_from_wrong_bit": (C, "int up = (k >> (dims - 1 - d)) & 1;\n        c[d]",
                                      "int up = (k >> d) & 1;\n        c[d]"),
+    "resolution_in_fp32": (C, "double b = exp((log((double)n_max) - log((double)n_min)) / (double)(n_levels - 1));\n"
+                                 "    for (int l = 0; l < n_levels; ++l) res[l] = (int32_t)floor((double)n_min * pow(b, (double)l));",
+                           "float b = expf((logf((float)n_max) - logf((float)n_min)) / (float)(n_levels - 1));\n"
+                           "    for (int l = 0; l < n_levels; ++l) res[l] = (int32_t)floorf((float)n_min * powf(b, (float)l));"),
+    "negative_voxels_clamped": (C, "v[d] = (int64_t)fl;", "v[d] = fl < 0 ? 0 : (int64_t)fl;"),
+    "weights_y_flipped": (C, "        w *= up ? frac[d] : 1.0 - frac[d];",
+                          "        w *= (up ^ (d == 1)) ? frac[d] : 1.0 - frac[d];"),
     # forward
     "forward_drops_last_corner": (C, "for (int k = 0; k < K; ++k) {\n                double wk = corner(v, frac, D, k, c);\n"
                                      "                int64_t e = spatial_hash(c, D, T);\n                for (int j = 0; j < F; ++j) acc[j]",
@@ -54,7 +61,15 @@ MUTANTS = {
                                  "wk * (double)dout[p * dout_stride + (int64_t)l * F];"),
     "backward_ignores_row_stride": (C, "wk * (double)dout[p * dout_stride + (int64_t)l * F + j];",
                                     "wk * (double)dout[p * (int64_t)L * F + (int64_t)l * F + j];"),
+    "backward_drops_last_corner": (C, "for (int k = 0; k < K; ++k) {\n                double wk = corner(v, frac, D, k, c);\n"
+                                      "                int64_t e = spatial_hash(c, D, T);\n                for (int j = 0; j < F; ++j)\n"
+                                      "                    grad",
+                                   "for (int k = 0; k < K - 1; ++k) {\n                double wk = corner(v, frac, D, k, c);\n"
+                                   "                int64_t e = spatial_hash(c, D, T);\n                for (int j = 0; j < F; ++j)\n"
+                                   "                    grad"),
     # dL/dx
+    "input_grad_weight_of_wrong_axis": (C, "else dw *= up ? frac[q] : 1.0 - frac[q];",
+                                        "else dw *= up ? frac[d] : 1.0 - frac[d];"),
     "input_grad_sign": (C, "if (q == d) dw *= up ? 1.0 : -1.0;", "if (q == d) dw *= up ? -1.0 : 1.0;"),
     "input_grad_missing_chain_factor": (C, "acc[d] += (double)res[l] * dw * s;", "acc[d] += dw * s;"),
     "input_grad_other_weights_flipped": (C, "else dw *= up ? frac[q] : 1.0 - frac[q];",
