@@ -510,6 +510,50 @@ def test_head_input_grad_and_adam_captured_in_a_graph_replay_like_eager():
             assert torch.equal(a, b), name
 
 
+def test_concurrent_calls_from_host_threads_on_their_own_streams():
+    # The library keeps no per-call state (the last error is thread-local), so
+    # host threads may call it at once, each on its own stream with its own
+    # buffers and workspaces: every thread's forward and binned backward equal
+    # the single-threaded results bit for bit.
+    import threading
+    w = I.resized(I.WORKLOADS["standard"], 20000 + 13)
+    cfg = hg.HashGridConfig.of(w)
+    x, t, d = dev(I.make_points(w)), dev(I.make_table(w)), dev(I.make_dout(w))
+    ref_out = hg.hashgrid_forward(cfg, x, t)
+    ref_grad = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_backward(cfg, x, d, ref_grad)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(k):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                out = torch.empty_like(ref_out)
+                grad = torch.zeros_like(ref_grad)
+                fws = hg.forward_workspace(cfg, w.n_points, DEV)
+                bws = hg.backward_workspace(cfg, w.n_points, DEV)
+                for _ in range(5):
+                    grad.zero_()
+                    hg.hashgrid_forward(cfg, x, t, out=out, workspace=fws)
+                    hg.hashgrid_backward(cfg, x, d, grad, workspace=bws)
+            stream.synchronize()
+            results[k] = (out, grad)
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for k in range(4):
+        out, grad = results[k]
+        assert torch.equal(out, ref_out), k
+        assert torch.equal(grad, ref_grad), k
+
+
 # ----------------------------------------------------------------------------- module
 
 def test_encoder_module_autograd(oracle):
