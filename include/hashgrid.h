@@ -107,7 +107,11 @@ int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *byt
  *           Results are identical either way.  Concurrent calls must not share
  *           a workspace.
  *   The blend of level l is sum_k w_k * table[l][h(corner_k)][j] computed in
- *   fp32, with w_k the trilinear weight of corner k.
+ *   fp32, with w_k the trilinear weight of corner k.  For the D = 3, F = 2
+ *   grid a level whose table exceeds 4 MiB (fp32 T >= 2^20, binary16
+ *   T >= 2^21) is gathered one table half per pass, so that the half fits one
+ *   XCD's L2, and the two partial blends are added; staged and direct outputs
+ *   still agree bit for bit.
  * Errors: HG_EINVAL (config, NULL, alignment, n < 0, stride), HG_EUNSUPPORTED,
  *         HG_EHIP. */
 int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void *table,

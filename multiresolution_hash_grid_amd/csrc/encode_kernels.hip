@@ -113,11 +113,16 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_kernel(const float *__restrict_
 // Output element (p, l, j) is out[p * ostride + l * lstride + j]: lstride = 2
 // writes the [n][L*F] rows directly, ostride = 2 with lstride = 2 n writes a
 // level-major [L][n][F] staging array whose stores are fully coalesced.
-template <int DT, int U, bool NT, typename OutT = float>
+// SPLIT: one half of every level's table, the entries whose index has top bit
+// `half` (T = 2^s entries, so the bit is idx >> (s - 1)); the other half's
+// corners count as zero.  Half 0 writes its partial blend and half 1 adds its
+// own to it, so two launches give the blend while each XCD's L2 holds only
+// half of a level's table at a time.
+template <int DT, int U, bool NT, typename OutT = float, bool SPLIT = false>
 __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__restrict__ x, int64_t n,
                                                              const void *__restrict__ table,
                                                              OutT *__restrict__ out, int64_t ostride,
-                                                             int64_t lstride, LaunchParams lp) {
+                                                             int64_t lstride, LaunchParams lp, int half) {
     Item it;
     if (!decode_item(lp, it)) return;
     constexpr int kPairs = kBlock / 2;
@@ -146,10 +151,16 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
             const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hy1 = hy0 + kPrimeY;
             const uint32_t hz0 = (uint32_t)v2 * kPrimeZ, hz1 = hz0 + kPrimeZ;
             const uint32_t cx = (uint32_t)v0 + sub;
-            e[u][0] = Table2<DT>::load(table, lbase + ((cx ^ hy0 ^ hz0) & mask));
-            e[u][1] = Table2<DT>::load(table, lbase + ((cx ^ hy0 ^ hz1) & mask));
-            e[u][2] = Table2<DT>::load(table, lbase + ((cx ^ hy1 ^ hz0) & mask));
-            e[u][3] = Table2<DT>::load(table, lbase + ((cx ^ hy1 ^ hz1) & mask));
+            auto corner = [&](uint32_t idx) -> float2 {
+                if constexpr (SPLIT) {
+                    if ((idx >> (lp.log2_table_size - 1)) != (uint32_t)half) return make_float2(0.f, 0.f);
+                }
+                return Table2<DT>::load(table, lbase + idx);
+            };
+            e[u][0] = corner((cx ^ hy0 ^ hz0) & mask);
+            e[u][1] = corner((cx ^ hy0 ^ hz1) & mask);
+            e[u][2] = corner((cx ^ hy1 ^ hz0) & mask);
+            e[u][3] = corner((cx ^ hy1 ^ hz1) & mask);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -162,9 +173,12 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
             const float ry = wx * fmaf(a1[u], fmaf(a2[u], e[u][3].y, wz0 * e[u][2].y),
                                        wy0 * fmaf(a2[u], e[u][1].y, wz0 * e[u][0].y));
             // lane 0 keeps feature 0 and needs lane 1's x-half; lane 1 the reverse.
-            const float v = (sub ? ry : rx) + swap_pair(sub ? rx : ry);
+            float v = (sub ? ry : rx) + swap_pair(sub ? rx : ry);
             if (ok[u]) {
                 OutT *dst = out + (p0 + (int64_t)u * kPairs) * ostride + (int64_t)l * lstride + sub;
+                if constexpr (SPLIT) {
+                    if (half) v += NT ? __builtin_nontemporal_load(dst) : *dst;
+                }
                 if constexpr (NT) __builtin_nontemporal_store((OutT)v, dst);
                 else *dst = (OutT)v;  // binary16 stage: round to nearest even
             }
@@ -390,20 +404,32 @@ hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, 
     return hipGetLastError();
 }
 
+// A level's table above one XCD's L2 (4 MiB) is gathered in two launches,
+// one per half (fwd_f2_pair_kernel SPLIT): measured on the 8 MiB levels of a
+// binary16 T = 2^21 grid, 2.07 against 2.29 ms; quarters cost more in
+// instructions than they gain (3.8 ms).
+constexpr size_t kSplitTableBytes = (size_t)4 << 20;
+
 template <int DT>
 hipError_t launch_gather_dt(const LaunchParams &lp, const float *x, int64_t n, const void *table, float *out,
                             int64_t ostride, int64_t lstride, const FwdTune &ft, hipStream_t stream) {
     dim3 grid(grid_blocks(lp)), block(kBlock);
+    const size_t level_bytes = (DT == 0 ? sizeof(float2) : sizeof(uint32_t)) << lp.log2_table_size;
     if (lstride == 2 && ft.lanes == 1) {
         fwd_f2_kernel<DT><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lp);
+    } else if (level_bytes > kSplitTableBytes) {
+        for (int half = 0; half < 2; ++half) {
+            if (ft.nt) fwd_f2_pair_kernel<DT, 4, true, float, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, half);
+            else fwd_f2_pair_kernel<DT, 4, false, float, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, half);
+        }
     } else if (ft.nt) {
-        if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
-        else if (ft.unroll == 2) fwd_f2_pair_kernel<DT, 2, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
-        else fwd_f2_pair_kernel<DT, 4, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
+        if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, 0);
+        else if (ft.unroll == 2) fwd_f2_pair_kernel<DT, 2, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, 0);
+        else fwd_f2_pair_kernel<DT, 4, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, 0);
     } else {
-        if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
-        else if (ft.unroll == 2) fwd_f2_pair_kernel<DT, 2, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
-        else fwd_f2_pair_kernel<DT, 4, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp);
+        if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, 0);
+        else if (ft.unroll == 2) fwd_f2_pair_kernel<DT, 2, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, 0);
+        else fwd_f2_pair_kernel<DT, 4, false><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, 0);
     }
     return hipGetLastError();
 }
@@ -439,9 +465,9 @@ hipError_t launch_encode_stage_f16(const LaunchParams &lp, const float *x, int64
                                    int table_dtype, _Float16 *stage, hipStream_t stream) {
     dim3 grid(grid_blocks(lp)), block(kBlock);
     if (table_dtype == 0)
-        fwd_f2_pair_kernel<0, 4, false, _Float16><<<grid, block, 0, stream>>>(x, n, table, stage, 2, 2 * n, lp);
+        fwd_f2_pair_kernel<0, 4, false, _Float16><<<grid, block, 0, stream>>>(x, n, table, stage, 2, 2 * n, lp, 0);
     else
-        fwd_f2_pair_kernel<1, 4, false, _Float16><<<grid, block, 0, stream>>>(x, n, table, stage, 2, 2 * n, lp);
+        fwd_f2_pair_kernel<1, 4, false, _Float16><<<grid, block, 0, stream>>>(x, n, table, stage, 2, 2 * n, lp, 0);
     return hipGetLastError();
 }
 

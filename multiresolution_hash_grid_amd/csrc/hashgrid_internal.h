@@ -40,7 +40,7 @@ struct LaunchParams {
 // Binned backward (binned_backward.hip): the table gradient routed to
 // per-partition owners instead of global atomics.
 constexpr int kBinTile = 512;
-constexpr int kRecordBytes = 12;   // one binned corner-pair record     // points per binning tile
+constexpr int kRecordBytes = 12;  // one binned corner-pair record
 constexpr int kMaxParts = 4096;   // partitions per level
 constexpr int kMaxSLog2 = 13;     // largest partition: 2^13 entries = 128 KB of 2 x int64 accumulators
 

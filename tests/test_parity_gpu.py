@@ -155,12 +155,18 @@ def test_forward_ragged_sizes(oracle, n, workspace):
     assert fwd_err(out, oracle.forward(oracle.grid_of(w), x, t), t) <= FWD_TOL
 
 
-def test_forward_staged_and_direct_are_identical():
-    # Both output paths compute every value with the same instructions.
-    w = I.resized(I.WORKLOADS["standard"], 7777)
+@pytest.mark.parametrize("name,log2T", [("standard", 19), ("standard", 20), ("large_f16", 21)])
+def test_forward_staged_and_direct_are_identical(oracle, name, log2T):
+    # Both output paths compute every value with the same instructions, also
+    # where a level's table exceeds 4 MiB (fp32 T = 2^20, binary16 T = 2^21) and
+    # is gathered one half per launch; those blends match the oracle too.
+    w = I.replace(I.resized(I.WORKLOADS[name], 7777), log2_table_size=log2T)
     cfg = hg.HashGridConfig.of(w)
     x, t = I.make_points(w), I.make_table(w)
-    assert np.array_equal(run_forward(cfg, x, t, workspace="auto"), run_forward(cfg, x, t, workspace=None))
+    staged = run_forward(cfg, x, t, workspace="auto")
+    assert np.array_equal(staged, run_forward(cfg, x, t, workspace=None))
+    assert np.array_equal(staged, run_forward(cfg, x, t, stride=cfg.out_features + 3)[:, :cfg.out_features])
+    assert fwd_err(staged, oracle.forward(oracle.grid_of(w), x, t), t) <= FWD_TOL
 
 
 # ----------------------------------------------------------------------------- backward
