@@ -156,8 +156,8 @@ int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *by
  *            results can differ from run to run in the last bits, and its
  *            rounding error grows with the additions an entry receives: within
  *            1e-5 of the level's largest gradient up to about 10^4 per entry,
- *            1.0-3.4e-5 measured at 1.2-9.5 * 10^4 (2- and 4-entry tables under
- *            4 * 10^3 to 2 * 10^4 points); the binned path sums exactly at any
+ *            1.0-3.4e-5 measured at 1.2-9.5 * 10^4 (tables of 2 to 8 entries
+ *            under 4 * 10^3 to 2 * 10^4 points); the binned path sums exactly at any
  *            count.  Both paths
  *            first sum, inside each wavefront, runs of consecutive points that
  *            share a voxel (ray samples at coarse levels) for the D = 3, F = 2
