@@ -167,6 +167,15 @@ def test_forward_staged_and_direct_are_identical(oracle, name, log2T):
     assert np.array_equal(staged, run_forward(cfg, x, t, workspace=None))
     assert np.array_equal(staged, run_forward(cfg, x, t, stride=cfg.out_features + 3)[:, :cfg.out_features])
     assert fwd_err(staged, oracle.forward(oracle.grid_of(w), x, t), t) <= FWD_TOL
+    # Non-temporal point and output traffic (the second half's read of the first
+    # half's partial blend included) does not change a bit.
+    old = hg.hashgrid_tune_get(B.HG_TUNE_FWD_NT)
+    try:
+        hg.hashgrid_tune(B.HG_TUNE_FWD_NT, 1)
+        assert np.array_equal(staged, run_forward(cfg, x, t, workspace="auto"))
+        assert np.array_equal(staged, run_forward(cfg, x, t, workspace=None))
+    finally:
+        hg.hashgrid_tune(B.HG_TUNE_FWD_NT, old)
 
 
 # ----------------------------------------------------------------------------- backward
