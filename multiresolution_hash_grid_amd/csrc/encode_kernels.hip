@@ -407,7 +407,9 @@ hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, 
 // A level's table above one XCD's L2 (4 MiB) is gathered in two launches,
 // one per half (fwd_f2_pair_kernel SPLIT): measured on the 8 MiB levels of a
 // binary16 T = 2^21 grid, 2.07 against 2.29 ms; quarters cost more in
-// instructions than they gain (3.8 ms).
+// instructions than they gain (3.8 ms).  The other shapes' kernels gather in
+// one pass: for F = 4 at 8 MiB a split gained 3 %, and F = 8 rows, written
+// directly, cost 2.9 times as much with the second half's read-modify-write.
 constexpr size_t kSplitTableBytes = (size_t)4 << 20;
 
 template <int DT>
