@@ -104,14 +104,16 @@ int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *byt
  *           stays in L2) and then transposed into the rows; without it every
  *           level writes its F values straight into the rows.  F = 8 grids
  *           always write the rows directly (32 bytes per level and row).
- *           Results are identical either way.  Concurrent calls must not share
+ *           Results are identical either way, except on the levels the
+ *           blend above gathers in two halves.  Concurrent calls must not share
  *           a workspace.
  *   The blend of level l is sum_k w_k * table[l][h(corner_k)][j] computed in
  *   fp32, with w_k the trilinear weight of corner k.  For the D = 3, F = 2
- *   grid a level whose table exceeds 4 MiB (fp32 T >= 2^20, binary16
- *   T >= 2^21) is gathered one table half per pass, so that the half fits one
- *   XCD's L2, and the two partial blends are added; staged and direct outputs
- *   still agree bit for bit.
+ *   grid with a workspace, a level whose table exceeds 4 MiB (fp32
+ *   T >= 2^20, binary16 T >= 2^21) is gathered one table half per pass, so
+ *   that the half fits one XCD's L2, and the two partial blends are added:
+ *   such levels round differently from the one-pass direct path, by a few
+ *   fp32 roundings of the blend (measured: 1.5e-7 of the largest table value).
  * Errors: HG_EINVAL (config, NULL, alignment, n < 0, stride), HG_EUNSUPPORTED,
  *         HG_EHIP. */
 int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void *table,
@@ -304,8 +306,10 @@ int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m
 /* Performance knobs (launch shapes).  Two change results within rounding:
  * HG_TUNE_FWD_LANES (the order in which the blend's eight terms are added) and
  * HG_TUNE_BWD_BINNED (fixed-point binned accumulation or fp32 atomics, whose
- * order is unspecified), as do the atomic path's HG_TUNE_BWD_LANES shapes.
- * The others give identical results.  Process-wide; not thread-safe against
+ * order is unspecified), as do the atomic path's HG_TUNE_BWD_LANES shapes,
+ * and HG_TUNE_FWD_STAGED on levels above 4 MiB (the staged forward gathers
+ * those in two halves).  The others give identical results.  Process-wide;
+ * not thread-safe against
  * concurrent launches.  Returns HG_EINVAL for an unknown key or an
  * out-of-range value. */
 #define HG_TUNE_FWD_LANES 0    /* lanes per (point, level) in the forward: 1 or 2        */

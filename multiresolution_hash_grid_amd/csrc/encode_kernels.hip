@@ -404,12 +404,14 @@ hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, 
     return hipGetLastError();
 }
 
-// A level's table above one XCD's L2 (4 MiB) is gathered in two launches,
-// one per half (fwd_f2_pair_kernel SPLIT): measured on the 8 MiB levels of a
-// binary16 T = 2^21 grid, 2.07 against 2.29 ms; quarters cost more in
-// instructions than they gain (3.8 ms).  The other shapes' kernels gather in
-// one pass: for F = 4 at 8 MiB a split gained 3 %, and F = 8 rows, written
-// directly, cost 2.9 times as much with the second half's read-modify-write.
+// On the staged path a level's table above one XCD's L2 (4 MiB) is gathered
+// in two launches, one per half (fwd_f2_pair_kernel SPLIT): measured on the
+// 8 MiB levels of a binary16 T = 2^21 grid, 2.07 against 2.29 ms; quarters
+// cost more in instructions than they gain (3.8 ms).  The direct path gathers
+// in one pass: there the second half's read-modify-write of 8 bytes per row
+// and level made the forward 1.6 times slower.  The other shapes' kernels
+// gather in one pass: for F = 4 at 8 MiB a split gained 3 %, and F = 8 rows,
+// written directly, cost 2.9 times as much.
 constexpr size_t kSplitTableBytes = (size_t)4 << 20;
 
 template <int DT>
@@ -419,7 +421,7 @@ hipError_t launch_gather_dt(const LaunchParams &lp, const float *x, int64_t n, c
     const size_t level_bytes = (DT == 0 ? sizeof(float2) : sizeof(uint32_t)) << lp.log2_table_size;
     if (lstride == 2 && ft.lanes == 1) {
         fwd_f2_kernel<DT><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lp);
-    } else if (level_bytes > kSplitTableBytes) {
+    } else if (lstride != 2 && level_bytes > kSplitTableBytes) {  // staged output only
         for (int half = 0; half < 2; ++half) {
             if (ft.nt) fwd_f2_pair_kernel<DT, 4, true, float, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, half);
             else fwd_f2_pair_kernel<DT, 4, false, float, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, half);

@@ -157,23 +157,31 @@ def test_forward_ragged_sizes(oracle, n, workspace):
 
 @pytest.mark.parametrize("name,log2T", [("standard", 19), ("standard", 20), ("large_f16", 21)])
 def test_forward_staged_and_direct_are_identical(oracle, name, log2T):
-    # Both output paths compute every value with the same instructions, also
-    # where a level's table exceeds 4 MiB (fp32 T = 2^20, binary16 T = 2^21) and
-    # is gathered one half per launch; those blends match the oracle too.
+    # Both output paths compute every value with the same instructions, except
+    # where a level's table exceeds 4 MiB (fp32 T = 2^20, binary16 T = 2^21):
+    # the staged path gathers those one table half per launch and adds the two
+    # partial blends, so the paths agree to fp32 rounding there, and both match
+    # the oracle.
     w = I.replace(I.resized(I.WORKLOADS[name], 7777), log2_table_size=log2T)
     cfg = hg.HashGridConfig.of(w)
     x, t = I.make_points(w), I.make_table(w)
     staged = run_forward(cfg, x, t, workspace="auto")
-    assert np.array_equal(staged, run_forward(cfg, x, t, workspace=None))
+    direct = run_forward(cfg, x, t, workspace=None)
+    split = cfg.table_size * (8 if cfg.table_dtype == "f32" else 4) > (4 << 20)
+    if split:
+        assert fwd_err(staged, direct, t) <= FWD_TOL
+    else:
+        assert np.array_equal(staged, direct)
     assert np.array_equal(staged, run_forward(cfg, x, t, stride=cfg.out_features + 3)[:, :cfg.out_features])
-    assert fwd_err(staged, oracle.forward(oracle.grid_of(w), x, t), t) <= FWD_TOL
+    ref = oracle.forward(oracle.grid_of(w), x, t)
+    assert fwd_err(staged, ref, t) <= FWD_TOL and fwd_err(direct, ref, t) <= FWD_TOL
     # Non-temporal point and output traffic (the second half's read of the first
     # half's partial blend included) does not change a bit.
     old = hg.hashgrid_tune_get(B.HG_TUNE_FWD_NT)
     try:
         hg.hashgrid_tune(B.HG_TUNE_FWD_NT, 1)
         assert np.array_equal(staged, run_forward(cfg, x, t, workspace="auto"))
-        assert np.array_equal(staged, run_forward(cfg, x, t, workspace=None))
+        assert np.array_equal(direct, run_forward(cfg, x, t, workspace=None))
     finally:
         hg.hashgrid_tune(B.HG_TUNE_FWD_NT, old)
 
