@@ -193,7 +193,7 @@ def measure_fused_mlp(dev, iters: int) -> dict:
     n = w.n_points
     x = torch.from_numpy(inputs.make_points(w)).to(dev)
     t = torch.from_numpy(inputs.make_table(w)).to(dev)
-    P = [torch.from_numpy(a).to(dev) for a in inputs.mlp_params(w.seed, bias_scale=0.1)]
+    P = [torch.from_numpy(a).to(dev) for a in inputs.mlp_params(w.seed)]
     dy = torch.from_numpy(inputs.dout_normal(w.seed + 7, n, 4)).to(dev)
     st_bytes, bw_bytes = hg.hashgrid_mlp_workspace_size(cfg, n)
     stage = torch.empty(st_bytes, dtype=torch.uint8, device=dev)

@@ -323,6 +323,9 @@ int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m
 #define HG_TUNE_BWD_PART_LOG2 8 /* log2 entries per binned-backward partition: 11..13, 0 = by T */
 #define HG_TUNE_BWD_GROUP_MIB 9 /* record MiB per binned level group (levels binned and
                                    accumulated together), 0 = all levels in one group   */
+#define HG_TUNE_BWD_DENSE 10    /* atomic backward: 1 sums levels of at most 16384 values
+                                   (T * F, or the vertex grid (N_l + 1)^D * F) in LDS per
+                                   workgroup first, 0 scatters every level directly     */
 int hashgrid_tune(int key, int value);
 int hashgrid_tune_get(int key);
 

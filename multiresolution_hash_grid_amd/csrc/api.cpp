@@ -43,6 +43,7 @@ struct Tuning {
     int fwd_staged = 1;
     int bwd_part_log2 = 0;  // 0: by table size
     int bwd_group_mib = 160;  // record bytes per binned level group, 0: all levels at once
+    int bwd_dense = 1;        // atomic backward: sum small levels in LDS first
 };
 Tuning g_tune;
 
@@ -100,6 +101,46 @@ int plan(const hg_config &c, int64_t n, hg::LaunchParams &lp) {
     for (int r = 0; r < hg::kNumXcd; ++r)
         for (int l = r; l < c.n_levels; l += hg::kNumXcd) lp.level_order[pos++] = (int8_t)l;
     return HG_OK;
+}
+
+// Keeps the work items of the levels flagged in keep[] (their order
+// unchanged); returns how many levels remain.
+int restrict_levels(hg::LaunchParams &lp, const bool *keep) {
+    int pos = 0;
+    for (int i = 0; i < lp.n_levels; ++i) {
+        const int l = lp.level_order[i];
+        if (keep[l]) lp.level_order[pos++] = (int8_t)l;
+    }
+    lp.items = lp.chunks * pos;
+    lp.per_xcd = (lp.items + hg::kNumXcd - 1) / hg::kNumXcd;
+    return pos;
+}
+
+// Levels of the atomic backward summed in LDS first: the table, or else the
+// level's whole vertex grid (N_l + 1)^D, holds at most kDenseVals values.
+void dense_levels(const hg_config &c, const hg::LaunchParams &lp, hg::DenseLevels &dl, bool *sparse) {
+    dl.count = 0;
+    dl.max_vals = 0;
+    for (int l = 0; l < c.n_levels; ++l) {
+        sparse[l] = true;
+        if (!g_tune.bwd_dense) continue;
+        const int64_t table_vals = ((int64_t)1 << c.log2_table_size) * c.n_features;
+        int64_t vertex_vals = c.n_features;
+        for (int d = 0; d < c.n_dims && vertex_vals <= hg::kDenseVals; ++d) vertex_vals *= (int64_t)lp.res[l] + 1;
+        int64_t vals;
+        if (table_vals <= hg::kDenseVals) {
+            dl.by_vertex[dl.count] = 0;
+            vals = table_vals;
+        } else if (vertex_vals <= hg::kDenseVals) {
+            dl.by_vertex[dl.count] = 1;
+            vals = vertex_vals;
+        } else {
+            continue;
+        }
+        sparse[l] = false;
+        dl.level[dl.count++] = (int8_t)l;
+        dl.max_vals = std::max<int32_t>(dl.max_vals, (int32_t)vals);
+    }
 }
 
 // Binned backward layout; returns false when the configuration has no binned
@@ -201,6 +242,18 @@ int table_backward(const hg_config *cfg, const float *x, int64_t n, const float 
     }
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
+    // Small tables and coarse vertex grids are summed per workgroup in LDS
+    // first; the other levels are scattered with fp32 atomics directly.
+    hg::DenseLevels dl;
+    bool sparse[hg::kMaxLevels];
+    dense_levels(*cfg, lp, dl, sparse);
+    if (dl.count) {
+        rc = launch_status(hg::launch_backward_dense(lp, dl, cfg->n_dims, cfg->n_features, x, n, dout,
+                                                     dout_row_stride, dtable, (hipStream_t)stream),
+                           "backward (LDS-summed levels)");
+        if (rc) return rc;
+    }
+    if (restrict_levels(lp, sparse) == 0) return ok();
     if (!standard_shape(*cfg))
         return launch_status(hg::launch_backward_generic(lp, cfg->n_dims, cfg->n_features, x, n, dout,
                                                          dout_row_stride, dtable, (hipStream_t)stream),
@@ -512,6 +565,10 @@ int hashgrid_tune(int key, int value) {
         if (value != 0 && (value < 11 || value > hg::kMaxSLog2)) break;
         g_tune.bwd_part_log2 = value;
         return ok();
+    case HG_TUNE_BWD_DENSE:
+        if (value != 0 && value != 1) break;
+        g_tune.bwd_dense = value;
+        return ok();
     default:
         return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
@@ -530,6 +587,7 @@ int hashgrid_tune_get(int key) {
     case HG_TUNE_FWD_STAGED: return g_tune.fwd_staged;
     case HG_TUNE_BWD_PART_LOG2: return g_tune.bwd_part_log2;
     case HG_TUNE_BWD_GROUP_MIB: return g_tune.bwd_group_mib;
+    case HG_TUNE_BWD_DENSE: return g_tune.bwd_dense;
     default: return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
 }

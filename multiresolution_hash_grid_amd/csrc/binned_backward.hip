@@ -113,8 +113,10 @@ struct Pairs {
 };
 
 // wbuf: this wave's 16 x 64 floats of LDS, free while the records are made.
+// glevel: level l's gradient [T][2], which takes the contributions that are
+// not binned (non-finite upstream values, non-finite run sums).
 __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1, int l, const BinParams &bp,
-                                           bool valid, float *wbuf, Pairs &out) {
+                                           bool valid, float *wbuf, float *__restrict__ glevel, Pairs &out) {
     const float N = (float)bp.res[l];
     int32_t v0, v1, v2;
     float a0, a1, a2;
@@ -124,8 +126,13 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
     const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hz0 = (uint32_t)v2 * kPrimeZ;
     const uint32_t cx0 = (uint32_t)v0, cx1 = cx0 + 1u;
     const uint32_t smask = (1u << bp.s_log2) - 1u;
-    out.dabs = fmaxf(fabsf(d0), fabsf(d1));
-    out.nrec = valid ? 4u : 0u;
+    // A point whose upstream values are not both finite (NaN, +-Inf) is not
+    // binned: its 16 contributions go to the gradient with fp32 atomics, so
+    // NaN and Inf reach the entries they touch as IEEE arithmetic has them,
+    // and the level's fixed-point scale comes from the finite values only.
+    const bool fin = isfinite(d0) && isfinite(d1);
+    out.dabs = fin ? fmaxf(fabsf(d0), fabsf(d1)) : 0.f;
+    out.nrec = valid && fin ? 4u : 0u;
     // trailing ones of v_x (bit 31 set keeps ctz defined for v_x = -1)
     const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 14u);
     // f_x * 2^23 (exact for positions >= 1; the first voxel's fraction rounds)
@@ -139,7 +146,15 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
         const float wyz = (dy ? a1 : 1.f - a1) * (dz ? a2 : 1.f - a2);
         const float A = wyz * d0, B = wyz * d1;
         out.part[c] = p0;
-        if ((i1 >> bp.s_log2) == p0) {
+        if (valid && !fin) {
+            unsafeAtomicAdd(glevel + 2 * i0, (1.f - a0) * A);
+            unsafeAtomicAdd(glevel + 2 * i0 + 1, (1.f - a0) * B);
+            unsafeAtomicAdd(glevel + 2 * i1, a0 * A);
+            unsafeAtomicAdd(glevel + 2 * i1 + 1, a0 * B);
+            out.rec[c] = Rec{0u, 0u, 0u};
+            out.split_idx[c] = ~0u;
+            out.split_val[c] = make_float2(0.f, 0.f);
+        } else if ((i1 >> bp.s_log2) == p0) {
             out.rec[c] = pack_record(i0 & smask, t, fx23, A, B);
             out.split_idx[c] = ~0u;
             out.split_val[c] = make_float2(0.f, 0.f);
@@ -155,7 +170,9 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
     const int lane = threadIdx.x & 63;
     // Every lane takes part in the shuffles (a short-circuited shuffle would read inactive lanes).
     const int32_t u0 = __shfl_up(v0, 1, 64), u1 = __shfl_up(v1, 1, 64), u2 = __shfl_up(v2, 1, 64);
-    const bool same = valid && lane > 0 && u0 == v0 && u1 == v1 && u2 == v2;
+    const int prev_fin = __shfl_up((int)fin, 1, 64);
+    // Points with non-finite upstream values stay runs of one (they are not binned).
+    const bool same = valid && fin && prev_fin && lane > 0 && u0 == v0 && u1 == v1 && u2 == v2;
     const uint64_t dup = __ballot(same);
     if (dup == 0) return;  // wave-uniform: no two neighbouring points share a voxel
     const uint64_t heads = ~dup, tails = (heads >> 1) | (1ull << 63);
@@ -198,7 +215,13 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
         const uint32_t K = (hy0 + dy * kPrimeY) ^ (hz0 + dz * kPrimeZ);
         const uint32_t i = ((first ? cx0 : cx1) ^ K) & bp.mask;
         out.part[c] = i >> bp.s_log2;
-        out.rec[c] = single_record(i & smask, sum[c][0], sum[c][1]);
+        if (isfinite(sum[c][0]) && isfinite(sum[c][1])) {
+            out.rec[c] = single_record(i & smask, sum[c][0], sum[c][1]);
+        } else {  // finite values whose sum overflows fp32: added as it is, the record adds zero
+            unsafeAtomicAdd(glevel + 2 * i, sum[c][0]);
+            unsafeAtomicAdd(glevel + 2 * i + 1, sum[c][1]);
+            out.rec[c] = single_record(i & smask, 0.f, 0.f);
+        }
     }
 }
 
@@ -277,7 +300,8 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
         float dm = 0.f;
 #pragma unroll
         for (int k = 0; k < kPtsPerThread; ++k) {
-            make_pairs(tp.xs[k], tp.dv[k][j][0], tp.dv[k][j][1], l, bp, tp.valid[k], wbuf, pr[k]);
+            make_pairs(tp.xs[k], tp.dv[k][j][0], tp.dv[k][j][1], l, bp, tp.valid[k], wbuf,
+                       grad + ((uint64_t)l << bp.log2_table_size) * 2, pr[k]);
             if (tp.valid[k]) dm = fmaxf(dm, pr[k].dabs);
 #pragma unroll
             for (int c = 0; c < 4; ++c) rank[k][c] = c < (int)pr[k].nrec ? atomicAdd(&cnt[pr[k].part[c]], 1u) : 0u;

@@ -106,12 +106,30 @@ __global__ __launch_bounds__(kGenThreads) void bin_generic_kernel(const float *_
         const uint32_t i0 = (cx0 ^ K) & bp.mask, i1 = ((cx0 + 1u) ^ K) & bp.mask;
         part[it] = i0 >> bp.s_log2;
         float gv[F];
+        bool fin = true;
 #pragma unroll
         for (int j = 0; j < F; ++j) {
             gv[j] = dout[q * dstride + (int64_t)l * F + j];
-            if (valid[it]) dm = fmaxf(dm, fabsf(gv[j]));
+            fin = fin && isfinite(gv[j]);
         }
-        if ((i1 >> bp.s_log2) == part[it]) {
+        // A pair whose upstream values are not all finite (NaN, +-Inf) is not
+        // binned: both corners go to the gradient with fp32 atomics, so NaN and
+        // Inf reach the entries they touch, and the level's fixed-point scale
+        // comes from the finite values only.
+        if (valid[it] && fin) {
+#pragma unroll
+            for (int j = 0; j < F; ++j) dm = fmaxf(dm, fabsf(gv[j]));
+        }
+        if (valid[it] && !fin) {
+            float *e0 = grad + (((uint64_t)l << bp.log2_table_size) + i0) * F;
+            float *e1 = grad + (((uint64_t)l << bp.log2_table_size) + i1) * F;
+#pragma unroll
+            for (int j = 0; j < F; ++j) {
+                unsafeAtomicAdd(e0 + j, (1.f - f0) * (w_rest * gv[j]));
+                unsafeAtomicAdd(e1 + j, f0 * (w_rest * gv[j]));
+            }
+            valid[it] = false;  // no record
+        } else if ((i1 >> bp.s_log2) == part[it]) {
             const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 15u);
             rec[it].head = (i0 & smask) | (t << 13);
             rec[it].fx = f0;

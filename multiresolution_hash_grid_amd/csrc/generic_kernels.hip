@@ -30,7 +30,7 @@
 // N_l (half(0) + half(1)), half(b) the corners with first-coordinate offset b.
 #include <type_traits>
 
-#include "device_common.h"
+#include "binned_common.h"
 
 namespace hg {
 namespace {
@@ -224,6 +224,120 @@ __global__ __launch_bounds__(kBlock) void bwd_generic_kernel(const float *__rest
 #pragma unroll
             for (int j = 0; j < F; ++j) unsafeAtomicAdd(e + j, w * g[j]);
         }
+    }
+}
+
+// Atomic backward of the levels with few distinct accumulators (small
+// tables, or coarse levels whose whole vertex grid fits): one workgroup per
+// (chunk of kDensePts points, level) first sums its points' contributions in
+// LDS, then adds each non-zero sum to the gradient with one fp32 atomic.  An
+// entry that receives 10^4 or more additions (a 2-entry table under a few
+// thousand points) would otherwise collect that many fp32 roundings in an
+// arbitrary order; the LDS sums are 64-bit fixed point, exact and
+// order-independent: contributions are rounded to 2^-k with k = 30 - e from
+// the chunk's largest finite |dL/dout| < 2^e, so each fits 31 bits and a
+// chunk's sum of at most 2^16 of them fits 47.  This is also the LDS
+// pre-reduction of duplicate coarse-level corners: a vertex-indexed level
+// makes one global atomic per touched vertex and chunk instead of one per
+// point and corner.  Points with a non-finite upstream value, and points whose
+// voxel leaves the vertex grid (outside [0,1)^D), add their contributions
+// straight to the gradient with fp32 atomics.
+constexpr int kDensePts = 4096;
+
+template <int D, int F>
+__global__ __launch_bounds__(kBlock) void bwd_dense_kernel(const float *__restrict__ x, int64_t n,
+                                                           const float *__restrict__ dout, int64_t dstride,
+                                                           float *__restrict__ grad, LaunchParams lp,
+                                                           DenseLevels dl) {
+    extern __shared__ unsigned long long acc[];  // [values]: entry- or vertex-indexed, F per index
+    __shared__ float wmax[kBlock / 64];
+    const int l = dl.level[blockIdx.y];
+    const bool by_vertex = dl.by_vertex[blockIdx.y] != 0;
+    const int res = lp.res[l];
+    const float N = (float)res;
+    const int V1 = res + 1;  // vertices per axis (by_vertex only)
+    int size = 1 << lp.log2_table_size;
+    if (by_vertex) {
+        size = 1;
+#pragma unroll
+        for (int d = 0; d < D; ++d) size *= V1;
+    }
+    const int vals = size * F;
+    float *__restrict__ g = grad + ((uint64_t)l << lp.log2_table_size) * F;
+    const int64_t p0 = (int64_t)blockIdx.x * kDensePts;
+    const int64_t end = min(p0 + (int64_t)kDensePts, n);
+    for (int i = threadIdx.x; i < vals; i += kBlock) acc[i] = 0ull;
+    // The chunk's largest finite |dL/dout| at this level sets the fixed-point step.
+    float m = 0.f;
+    for (int64_t p = p0 + threadIdx.x; p < end; p += kBlock) {
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            const float a = fabsf(dout[p * dstride + (int64_t)l * F + j]);
+            if (a <= 3.40282347e38f) m = fmaxf(m, a);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    for (int w = 0; w < kBlock / 64; ++w) m = fmaxf(m, wmax[w]);
+    const int k = binned::fixed_exponent(__float_as_uint(m));
+    for (int64_t p = p0 + threadIdx.x; p < end; p += kBlock) {
+        int32_t v[D];
+        float f[D];
+        bool inside = true;
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            locate1(x[p * D + d], N, v[d], f[d]);
+            inside = inside && v[d] >= 0 && v[d] < res;
+        }
+        float gv[F];
+        bool fin = true;
+#pragma unroll
+        for (int j = 0; j < F; ++j) {
+            gv[j] = dout[p * dstride + (int64_t)l * F + j];
+            fin = fin && isfinite(gv[j]);
+        }
+        const bool local = fin && (inside || !by_vertex);
+#pragma unroll
+        for (int c = 0; c < (1 << D); ++c) {
+            uint32_t h = 0, vid = 0, stride = 1;
+            float w = 1.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                const uint32_t b = (uint32_t)(c >> (D - 1 - d)) & 1u;
+                h ^= ((uint32_t)v[d] + b) * kPrimeList[d];
+                vid += ((uint32_t)v[d] + b) * stride;
+                stride *= (uint32_t)V1;
+                w *= b ? f[d] : 1.f - f[d];
+            }
+            h &= lp.mask;
+            if (local) {
+                const int base = (int)(by_vertex ? vid : h) * F;
+#pragma unroll
+                for (int j = 0; j < F; ++j) atomicAdd(acc + base + j, binned::to_fixed(w * gv[j], k));
+            } else {
+#pragma unroll
+                for (int j = 0; j < F; ++j) unsafeAtomicAdd(g + (uint64_t)h * F + j, w * gv[j]);
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < vals; i += kBlock) {
+        const long long s = (long long)acc[i];
+        if (s == 0) continue;
+        const int idx = i / F, j = i - idx * F;
+        uint32_t e = (uint32_t)idx;
+        if (by_vertex) {
+            uint32_t h = 0;
+            int r = idx;
+#pragma unroll
+            for (int d = 0; d < D; ++d) {
+                h ^= (uint32_t)(r % V1) * kPrimeList[d];
+                r /= V1;
+            }
+            e = h & lp.mask;
+        }
+        unsafeAtomicAdd(g + (uint64_t)e * F + j, (float)ldexp((double)s, -k));
     }
 }
 
@@ -647,6 +761,24 @@ hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const f
         bwd_generic_kernel<DD, FF><<<grid, block, 0, stream>>>(x, n, dout, dout_stride, dtable, lp);
     });
     return ok ? hipGetLastError() : hipErrorInvalidValue;
+}
+
+hipError_t launch_backward_dense(const LaunchParams &lp, const DenseLevels &dl, int D, int F, const float *x,
+                                 int64_t n, const float *dout, int64_t dout_stride, float *dtable,
+                                 hipStream_t stream) {
+    if (dl.count == 0) return hipSuccess;
+    if (dl.max_vals > kDenseVals) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((n + kDensePts - 1) / kDensePts), dl.count), block(kBlock);
+    const size_t lds = (size_t)dl.max_vals * sizeof(unsigned long long);
+    hipError_t e = hipSuccess;
+    const bool ok = dispatch_shape(D, F, [&]<int DD, int FF>() {
+        e = hipFuncSetAttribute((const void *)bwd_dense_kernel<DD, FF>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+        if (e == hipSuccess)
+            bwd_dense_kernel<DD, FF><<<grid, block, lds, stream>>>(x, n, dout, dout_stride, dtable, lp, dl);
+    });
+    if (!ok) return hipErrorInvalidValue;
+    return e != hipSuccess ? e : hipGetLastError();
 }
 
 hipError_t launch_debug_corners_generic(const LaunchParams &lp, int D, const float *x, int64_t n, uint32_t *idx,

@@ -109,6 +109,21 @@ hipError_t launch_transpose(int F, const float *stage, int64_t n, int L, float *
                             hipStream_t stream);
 hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,
                                    const float *dout, int64_t dout_stride, float *dtable, hipStream_t stream);
+
+// Levels of the atomic backward that are accumulated in LDS first
+// (generic_kernels.hip, bwd_dense_kernel): a level whose table holds at most
+// kDenseVals values (T F), indexed by table entry, or whose vertex grid
+// (N_l + 1)^D F does, indexed by vertex and hashed at the flush.
+constexpr int kDenseVals = 16384;  // 128 KB of 64-bit accumulators
+struct DenseLevels {
+    int32_t count;
+    int32_t max_vals;              // largest accumulator count among them
+    int8_t level[kMaxLevels];
+    int8_t by_vertex[kMaxLevels];
+};
+hipError_t launch_backward_dense(const LaunchParams &lp, const DenseLevels &dl, int D, int F, const float *x,
+                                 int64_t n, const float *dout, int64_t dout_stride, float *dtable,
+                                 hipStream_t stream);
 hipError_t launch_debug_corners_generic(const LaunchParams &lp, int D, const float *x, int64_t n, uint32_t *idx,
                                         float *w, hipStream_t stream);
 // dL/dx of every shape; stage ([L][n][D] fp32) selects the level-major path,

@@ -23,7 +23,12 @@
 // Backward: each wave recomputes z1, h1, z2, h2 from the stage, takes
 // dL/dy to dz2 = (W3^T g) * [z2 > 0], dz1 = (W2^T dz2) * [z1 > 0] and
 // dL/de = W1^T dz1 with the transposed weights in A, and writes dL/de as
-// the fp32 upstream rows of the encoder's table backward.  The weight
+// the fp32 upstream rows of the encoder's table backward.  dL/dy enters the
+// matrix cores scaled by one power of two s per call, chosen so that the
+// largest finite |dL/dy| lands in [1, 2): a loss averaged over millions of
+// points gives dL/dy ~ 1e-7, which unscaled would sit at binary16's
+// subnormal floor.  dz2 and dz1 carry the scale; dL/de and the weight and
+// bias gradients are multiplied by 1/s in fp32, which is exact.  The weight
 // gradients contract over points, so a tile's activations go through LDS
 // to put the 16 points on the k axis (dW2 = dz2 h1^T etc.); every wave keeps
 // its running dW and db in registers and writes them once, and two reduction
@@ -125,6 +130,29 @@ __device__ __forceinline__ void hidden_layers(const FwdWeights &w, const half4_t
     }
 }
 
+// Slices of dL/dy whose largest finite magnitude mlp_dy_max_kernel writes.
+constexpr int kDyMaxParts = 256;
+
+__device__ __forceinline__ float finite_abs_max(float m, float v) {
+    const float a = fabsf(v);
+    return a <= 3.40282347e38f ? fmaxf(m, a) : m;  // NaN and Inf fail the comparison
+}
+
+// parts[b]: bits of the largest finite |dy| over the float4 rows b, b + grid, ...
+__global__ __launch_bounds__(256) void mlp_dy_max_kernel(const float4 *__restrict__ dy, int64_t n,
+                                                         uint32_t *__restrict__ parts) {
+    __shared__ float wmax[4];
+    float m = 0.f;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)kDyMaxParts * 256) {
+        const float4 v = dy[i];
+        m = finite_abs_max(finite_abs_max(finite_abs_max(finite_abs_max(m, v.x), v.y), v.z), v.w);
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) parts[blockIdx.x] = __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
+}
+
 int mlp_grid(int64_t tiles) {
     const int64_t want = (tiles + kMlpWaves - 1) / kMlpWaves;
     return (int)std::min<int64_t>(want, 1024);  // persistent: 4 waves per CU-slot, 4096 waves at most
@@ -187,11 +215,23 @@ __device__ __forceinline__ half4_t get_cols(_Float16 (*src)[W], int m, int q, in
 
 __global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 *__restrict__ stage, int64_t n,
                                                                  MlpParams mp, const float *__restrict__ dy,
+                                                                 const uint32_t *__restrict__ dmax,
                                                                  float *__restrict__ de,
                                                                  float *__restrict__ partials, int64_t tiles) {
     __shared__ TileLds lds[kMlpWaves];
     const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15, wave = threadIdx.x >> 6;
     TileLds &tl = lds[wave];
+    // The call's scale s = 2^(1-e), max|dL/dy| in [2^(e-1), 2^e) (1 if dL/dy has no finite non-zero value).
+    uint32_t mbits = 0;
+    for (int i = lane; i < kDyMaxParts; i += 64) mbits = max(mbits, dmax[i]);
+    for (int off = 32; off > 0; off >>= 1) mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, off, 64));
+    float gscale = 1.f, ginv = 1.f;
+    if (__uint_as_float(mbits) > 0.f) {
+        int e;
+        frexpf(__uint_as_float(mbits), &e);
+        gscale = ldexpf(1.f, 1 - e);
+        ginv = ldexpf(1.f, e - 1);
+    }
     FwdWeights w;
     load_fwd_weights(mp, q, c, w);
     // Transposed weights as A operands: row = input unit of the layer, k = its output unit.
@@ -243,7 +283,8 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 
         if (t + nwaves < tiles) load_tile(t + nwaves, eb_next, g_next);
         uint32_t m1, m2;
         hidden_layers(w, eb, h1, h2, m1, m2);
-        g3 = half4_t{(_Float16)g.x, (_Float16)g.y, (_Float16)g.z, (_Float16)g.w};
+        g3 = half4_t{(_Float16)(g.x * gscale), (_Float16)(g.y * gscale), (_Float16)(g.z * gscale),
+                     (_Float16)(g.w * gscale)};
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             const float4_t acc = mfma(t3[mb], g3, float4_t{0.f, 0.f, 0.f, 0.f});
@@ -263,7 +304,9 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 
             float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) acc = mfma(t1[mb][kb], dz1[kb], acc);
-            if (ok) *reinterpret_cast<float4 *>(de + p * kIn + 16 * mb + 4 * q) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            if (ok)
+                *reinterpret_cast<float4 *>(de + p * kIn + 16 * mb + 4 * q) =
+                    make_float4(acc[0] * ginv, acc[1] * ginv, acc[2] * ginv, acc[3] * ginv);
         }
         // Bias gradients: this lane's units, summed over the points it sees.
 #pragma unroll
@@ -325,18 +368,18 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 
         for (int mb = 0; mb < 4; ++mb) {
             const int row = 16 * mb + 4 * q + r;
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) part[kOffW1 + row * kIn + 16 * nb + c] = gw1[mb][nb][r];
+            for (int nb = 0; nb < 2; ++nb) part[kOffW1 + row * kIn + 16 * nb + c] = gw1[mb][nb][r] * ginv;
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) part[kOffW2 + row * kHid + 16 * nb + c] = gw2[mb][nb][r];
+            for (int nb = 0; nb < 4; ++nb) part[kOffW2 + row * kHid + 16 * nb + c] = gw2[mb][nb][r] * ginv;
             if (c == 0) {
-                part[kOffB1 + row] = gb1[mb][r];
-                part[kOffB2 + row] = gb2[mb][r];
+                part[kOffB1 + row] = gb1[mb][r] * ginv;
+                part[kOffB2 + row] = gb2[mb][r] * ginv;
             }
         }
         if (q == 0) {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) part[kOffW3 + r * kHid + 16 * nb + c] = gw3[nb][r];
-            if (c == 0) part[kOffB3 + r] = gb3[r];
+            for (int nb = 0; nb < 4; ++nb) part[kOffW3 + r * kHid + 16 * nb + c] = gw3[nb][r] * ginv;
+            if (c == 0) part[kOffB3 + r] = gb3[r] * ginv;
         }
     }
 }
@@ -375,7 +418,7 @@ __global__ __launch_bounds__(256) void mlp_reduce2_kernel(const float *__restric
 
 size_t mlp_partials_bytes(int64_t n) {
     const int64_t tiles = (n + 15) / 16;
-    return ((size_t)mlp_grid(tiles) * kMlpWaves + kSplit) * kPartial * sizeof(float);
+    return ((size_t)mlp_grid(tiles) * kMlpWaves + kSplit) * kPartial * sizeof(float) + kDyMaxParts * sizeof(uint32_t);
 }
 
 hipError_t launch_mlp_forward(const _Float16 *stage, int64_t n, const MlpParams &mp, float *y, hipStream_t stream) {
@@ -388,11 +431,13 @@ hipError_t launch_mlp_backward(const _Float16 *stage, int64_t n, const MlpParams
                                float *partials, const MlpGrads &g, hipStream_t stream) {
     const int64_t tiles = (n + 15) / 16;
     const int grid = mlp_grid(tiles);
-    mlp_bwd_kernel<<<grid, 64 * kMlpWaves, 0, stream>>>(stage, n, mp, dy, de, partials, tiles);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int nparts = grid * kMlpWaves;
     float *rows = partials + (int64_t)nparts * kPartial;
+    uint32_t *dmax = reinterpret_cast<uint32_t *>(rows + (int64_t)kSplit * kPartial);
+    mlp_dy_max_kernel<<<kDyMaxParts, 256, 0, stream>>>(reinterpret_cast<const float4 *>(dy), n, dmax);
+    mlp_bwd_kernel<<<grid, 64 * kMlpWaves, 0, stream>>>(stage, n, mp, dy, dmax, de, partials, tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     mlp_reduce1_kernel<<<dim3((kPartial + 255) / 256, kSplit), 256, 0, stream>>>(partials, nparts, rows);
     mlp_reduce2_kernel<<<(kPartial + 255) / 256, 256, 0, stream>>>(rows, g);
     return hipGetLastError();

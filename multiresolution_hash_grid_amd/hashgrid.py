@@ -22,7 +22,7 @@ HG_OK, HG_EINVAL, HG_EUNSUPPORTED, HG_EHIP = 0, -1, -2, -3
 HG_F32, HG_F16 = 0, 1
 (HG_TUNE_FWD_LANES, HG_TUNE_BWD_LANES, HG_TUNE_CHUNK_POINTS, HG_TUNE_XCD_MAP, HG_TUNE_BWD_BINNED,
  HG_TUNE_FWD_UNROLL, HG_TUNE_FWD_NT, HG_TUNE_FWD_STAGED, HG_TUNE_BWD_PART_LOG2,
- HG_TUNE_BWD_GROUP_MIB) = range(10)
+ HG_TUNE_BWD_GROUP_MIB, HG_TUNE_BWD_DENSE) = range(11)
 _DTYPES = {"f32": HG_F32, "f16": HG_F16}
 _TORCH_DTYPES = {HG_F32: torch.float32, HG_F16: torch.float16}
 
@@ -154,6 +154,25 @@ def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _keep_for_stream(t: torch.Tensor, stream, *bufs) -> None:
+    """Buffers a wrapper allocated come from torch's caching allocator on the
+    current stream.  When the kernels run on another stream, mark them used
+    there so that the allocator does not hand them to a later allocation
+    before that stream's work is done."""
+    if stream is None:
+        return
+    cur = torch.cuda.current_stream(t.device)
+    if not isinstance(stream, torch.cuda.Stream):
+        if int(stream) == cur.cuda_stream:
+            return
+        stream = torch.cuda.ExternalStream(int(stream), device=t.device)
+    if stream.cuda_stream == cur.cuda_stream:
+        return
+    for b in bufs:
+        if isinstance(b, torch.Tensor):
+            b.record_stream(stream)
+
+
 def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
@@ -215,17 +234,20 @@ def hashgrid_forward(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tensor,
     if tuple(table.shape) != cfg.table_shape or not table.is_contiguous():
         raise ValueError(f"table must be a contiguous {cfg.table_shape} tensor")
     n = x.shape[0]
+    made = out is None
     if out is None:
         out = torch.empty((n, cfg.out_features), device=x.device, dtype=torch.float32)
     _dev(out, "out", torch.float32)
     if out.dim() != 2 or out.shape[0] != n or out.stride(1) != 1 or out.shape[1] < cfg.out_features:
         raise ValueError("out must be [n, >= L*F] with unit column stride")
+    auto = isinstance(workspace, str)
     ws_ptr, ws_bytes, _keep = _workspace(workspace, lambda: forward_workspace(cfg, n, x.device) if n else None,
                                          "workspace")
     c = cfg.c()
     _check(load_library().hashgrid_forward(ctypes.byref(c), x.data_ptr(), n, table.data_ptr(),
                                            out.data_ptr(), out.stride(0), ws_ptr, ws_bytes,
                                            _stream(x, stream)))
+    _keep_for_stream(x, stream, out if made else None, _keep if auto else None)
     return out
 
 
@@ -261,12 +283,14 @@ def hashgrid_backward(cfg: HashGridConfig, x: torch.Tensor, dout: torch.Tensor,
     _dev(dtable, "dtable", torch.float32)
     if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
         raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
+    auto = isinstance(workspace, str)
     ws_ptr, ws_bytes, _keep = _workspace(workspace, lambda: backward_workspace(cfg, n, x.device) if n else None,
                                          "workspace")
     c = cfg.c()
     _check(load_library().hashgrid_backward(ctypes.byref(c), x.data_ptr(), n, dout.data_ptr(),
                                             dout.stride(0), dtable.data_ptr(), ws_ptr, ws_bytes,
                                             _stream(x, stream)))
+    _keep_for_stream(x, stream, _keep if auto else None)
     return dtable
 
 
@@ -280,6 +304,7 @@ def hashgrid_debug_corners(cfg: HashGridConfig, x: torch.Tensor, stream=None):
     c = cfg.c()
     _check(load_library().hashgrid_debug_corners(ctypes.byref(c), x.data_ptr(), n, idx.data_ptr(),
                                                  w.data_ptr(), _stream(x, stream)))
+    _keep_for_stream(x, stream, idx, w)
     return idx, w
 
 
@@ -303,6 +328,7 @@ def hashgrid_input_grad(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tenso
     _dev(dout, "dout", torch.float32)
     if dout.dim() != 2 or dout.shape[0] != n or dout.stride(1) != 1 or dout.shape[1] < cfg.out_features:
         raise ValueError("dout must be [n, >= L*F] with unit column stride")
+    made = dx is None
     if dx is None:
         dx = torch.empty((n, cfg.n_dims), device=x.device, dtype=torch.float32)
     _dev(dx, "dx", torch.float32)
@@ -313,11 +339,13 @@ def hashgrid_input_grad(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tenso
         size = hashgrid_input_grad_workspace_size(cfg, n) if n else 0
         return torch.empty(size, dtype=torch.uint8, device=x.device) if size else None
 
+    auto = isinstance(workspace, str)
     ws_ptr, ws_bytes, _keep = _workspace(workspace, alloc, "workspace")
     c = cfg.c()
     _check(load_library().hashgrid_input_grad(ctypes.byref(c), x.data_ptr(), n, table.data_ptr(), dout.data_ptr(),
                                               dout.stride(0), dx.data_ptr(), ws_ptr, ws_bytes,
                                               _stream(x, stream)))
+    _keep_for_stream(x, stream, dx if made else None, _keep if auto else None)
     return dx
 
 
@@ -354,6 +382,7 @@ def hashgrid_mlp_forward(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tens
         raise ValueError(f"table must be a contiguous {cfg.table_shape} tensor")
     mp = _mlp_params(params)
     st_bytes, _ = hashgrid_mlp_workspace_size(cfg, n)
+    made = (stage is None, y is None)
     if stage is None:
         stage = torch.empty(max(st_bytes, 1), dtype=torch.uint8, device=x.device)
     _dev(stage, "stage", torch.uint8)
@@ -365,6 +394,7 @@ def hashgrid_mlp_forward(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tens
     c = cfg.c()
     _check(load_library().hashgrid_mlp_forward(ctypes.byref(c), x.data_ptr(), n, table.data_ptr(), ctypes.byref(mp),
                                                y.data_ptr(), stage.data_ptr(), stage.numel(), _stream(x, stream)))
+    _keep_for_stream(x, stream, stage if made[0] else None, y if made[1] else None)
     return y, stage
 
 
@@ -390,6 +420,7 @@ def hashgrid_mlp_backward(cfg: HashGridConfig, x: torch.Tensor, stage: torch.Ten
     _dev(dtable, "dtable", torch.float32)
     if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
         raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
+    auto = isinstance(workspace, str)
     ws_ptr, ws_bytes, _keep = _workspace(
         workspace, lambda: torch.empty(max(1, hashgrid_mlp_workspace_size(cfg, n)[1]), dtype=torch.uint8,
                                        device=x.device), "workspace")
@@ -397,6 +428,7 @@ def hashgrid_mlp_backward(cfg: HashGridConfig, x: torch.Tensor, stage: torch.Ten
     _check(load_library().hashgrid_mlp_backward(ctypes.byref(c), x.data_ptr(), n, stage.data_ptr(), ctypes.byref(mp),
                                                 dy.data_ptr(), ctypes.byref(g), dtable.data_ptr(), ws_ptr, ws_bytes,
                                                 _stream(x, stream)))
+    _keep_for_stream(x, stream, _keep if auto else None)
 
 
 def hashgrid_adam_step(param: torch.Tensor, m: torch.Tensor, v: torch.Tensor, grad: torch.Tensor, *,
@@ -465,46 +497,69 @@ def hashgrid_tune_get(key: int) -> int:
 class HashGridFunction(torch.autograd.Function):
     """Autograd wrapper: forward through hashgrid_forward; the table gradient
     through hashgrid_backward into a zeroed fp32 buffer and, when x requires
-    grad, dL/dx through hashgrid_input_grad."""
+    grad, dL/dx through hashgrid_input_grad.  ``kernel_table`` (optional) is
+    the table the kernels read -- e.g. a binary16 copy of an fp32 ``table``,
+    which then receives the fp32 gradient unrounded."""
 
     @staticmethod
-    def forward(ctx, x, table, cfg):
+    def forward(ctx, x, table, cfg, kernel_table=None):
         ctx.cfg = cfg
-        x, table = x.contiguous(), table.contiguous()
-        ctx.save_for_backward(x, table)
-        return hashgrid_forward(cfg, x, table)
+        kt = (table if kernel_table is None else kernel_table).contiguous()
+        x = x.contiguous()
+        ctx.save_for_backward(x, kt)
+        ctx.table_dtype = table.dtype
+        return hashgrid_forward(cfg, x, kt)
 
     @staticmethod
     def backward(ctx, dout):
-        x, table = ctx.saved_tensors
+        x, kt = ctx.saved_tensors
         cfg = ctx.cfg
         dout = dout.contiguous()
         dx = grad = None
         if ctx.needs_input_grad[0]:
-            dx = hashgrid_input_grad(cfg, x, table, dout)
+            dx = hashgrid_input_grad(cfg, x, kt, dout)
         if ctx.needs_input_grad[1]:
             grad = torch.zeros(cfg.table_shape, device=x.device, dtype=torch.float32)
             hashgrid_backward(cfg, x, dout, grad)
-            if cfg.table_dtype == "f16":
-                grad = grad.to(torch.float16)
-        return dx, grad, None
+            if ctx.table_dtype != torch.float32:
+                grad = grad.to(ctx.table_dtype)
+        return dx, grad, None, None
 
 
 class HashGridEncoder(torch.nn.Module):
     """Multiresolution hash-grid encoder with the pages' constructor arguments
     (ipipp.com HashGridEncoder): ``forward(x [N, D]) -> [N, L*F]`` (D = 3 by default).  The L
-    tables live in one [L, T, F] parameter initialised uniform(-1e-4, 1e-4)."""
+    tables live in one [L, T, F] parameter initialised uniform(-1e-4, 1e-4).
+
+    With ``table_dtype="f16"`` the kernels read binary16 tables (jsqmd.com's
+    half-precision storage tip).  By default (``fp32_master=True``) the
+    parameter itself stays fp32 and each forward reads a binary16 copy of it,
+    so the fp32 gradient reaches the parameter unrounded (gradients of ~1e-8,
+    common for tables, would underflow in binary16).  ``fp32_master=False``
+    keeps the parameter in binary16, and its gradient is rounded to binary16."""
 
     def __init__(self, n_levels=16, n_features_per_level=2, log2_hashmap_size=19,
-                 base_resolution=16, finest_resolution=512, table_dtype="f32", device="cuda", n_dims=3):
+                 base_resolution=16, finest_resolution=512, table_dtype="f32", device="cuda", n_dims=3,
+                 fp32_master=True):
         super().__init__()
         self.cfg = HashGridConfig(n_levels, n_features_per_level, log2_hashmap_size,
                                   base_resolution, finest_resolution, table_dtype, n_dims=n_dims)
         self.resolutions = hashgrid_resolutions(self.cfg)
         t = torch.empty(self.cfg.table_shape, dtype=torch.float32, device=device).uniform_(-1e-4, 1e-4)
-        self.embeddings = torch.nn.Parameter(t.to(self.cfg.torch_table_dtype))
+        self.fp32_master = bool(fp32_master) and table_dtype == "f16"
+        if self.fp32_master:
+            t = t.to(torch.float16).to(torch.float32)  # the values the kernels read, exactly
+        self.embeddings = torch.nn.Parameter(t if self.fp32_master else t.to(self.cfg.torch_table_dtype))
+
+    def kernel_table(self) -> torch.Tensor:
+        """The table in the dtype the kernels read."""
+        if self.fp32_master:
+            return self.embeddings.detach().to(torch.float16)
+        return self.embeddings
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if self.fp32_master:
+            return HashGridFunction.apply(x, self.embeddings, self.cfg, self.kernel_table())
         return HashGridFunction.apply(x, self.embeddings, self.cfg)
 
 
@@ -514,14 +569,16 @@ class HashGridMLPFunction(torch.autograd.Function):
     (fp32 master) weights and biases; no gradient flows to x."""
 
     @staticmethod
-    def forward(ctx, x, table, w1, b1, w2, b2, w3, b3, cfg):
-        x, table = x.contiguous(), table.contiguous()
+    def forward(ctx, x, table, w1, b1, w2, b2, w3, b3, cfg, kernel_table=None):
+        x = x.contiguous()
+        kt = (table if kernel_table is None else kernel_table).contiguous()
         params = [w1.to(torch.float16).contiguous(), b1.float().contiguous(), w2.to(torch.float16).contiguous(),
                   b2.float().contiguous(), w3.to(torch.float16).contiguous(), b3.float().contiguous()]
-        y, stage = hashgrid_mlp_forward(cfg, x, table, params)
+        y, stage = hashgrid_mlp_forward(cfg, x, kt, params)
         ctx.cfg = cfg
         ctx.save_for_backward(x, stage, *params)
         ctx.dtypes = [t.dtype for t in (w1, b1, w2, b2, w3, b3)]
+        ctx.table_dtype = table.dtype
         return y
 
     @staticmethod
@@ -531,17 +588,18 @@ class HashGridMLPFunction(torch.autograd.Function):
         grads = [torch.zeros(MLP_SHAPES[k], device=x.device) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
         dtable = torch.zeros(cfg.table_shape, device=x.device)
         hashgrid_mlp_backward(cfg, x, stage, params, dy.contiguous().float(), grads, dtable)
-        if cfg.table_dtype == "f16":
-            dtable = dtable.to(torch.float16)
-        return (None, dtable, *[g.to(dt) for g, dt in zip(grads, ctx.dtypes)], None)
+        if ctx.table_dtype != torch.float32:
+            dtable = dtable.to(ctx.table_dtype)
+        return (None, dtable, *[g.to(dt) for g, dt in zip(grads, ctx.dtypes)], None, None)
 
 
 class HashGridMLP(torch.nn.Module):
     """The encoder followed by the NeRFace head of ipipp.com section 3:
     Linear(32, 64), ReLU, Linear(64, 64), ReLU, Linear(64, 4) with biases;
     ``forward(x [N, 3]) -> [N, 4]`` (density and colour channels).  Weights
-    are fp32 masters initialised Xavier-uniform, biases zero; the matrix cores
-    read them as binary16."""
+    are fp32 masters initialised Xavier-uniform; biases are initialised as
+    torch.nn.Linear does, U(-1/sqrt(fan_in), 1/sqrt(fan_in)).  The matrix
+    cores read the weights as binary16."""
 
     def __init__(self, table_dtype="f16", device="cuda", **encoder_kw):
         super().__init__()
@@ -552,9 +610,12 @@ class HashGridMLP(torch.nn.Module):
         for fin, fout in ((32, 64), (64, 64), (64, 4)):
             w = torch.empty((fout, fin), device=device)
             torch.nn.init.xavier_uniform_(w)
-            layers += [torch.nn.Parameter(w), torch.nn.Parameter(torch.zeros(fout, device=device))]
+            b = torch.empty(fout, device=device).uniform_(-1.0 / fin ** 0.5, 1.0 / fin ** 0.5)
+            layers += [torch.nn.Parameter(w), torch.nn.Parameter(b)]
         self.w1, self.b1, self.w2, self.b2, self.w3, self.b3 = layers
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return HashGridMLPFunction.apply(x, self.encoder.embeddings, self.w1, self.b1, self.w2, self.b2, self.w3,
-                                         self.b3, self.encoder.cfg)
+        enc = self.encoder
+        kt = enc.kernel_table() if enc.fp32_master else None
+        return HashGridMLPFunction.apply(x, enc.embeddings, self.w1, self.b1, self.w2, self.b2, self.w3,
+                                         self.b3, enc.cfg, kt)

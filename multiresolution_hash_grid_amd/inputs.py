@@ -197,19 +197,21 @@ def xavier_uniform(seed: int, fan_in: int, fan_out: int, offset: int = 0) -> np.
     return ((2.0 * u - 1.0) * a).astype(np.float32).reshape(fan_out, fan_in)
 
 
-def mlp_params(seed: int, sizes=(32, 64, 64, 4), bias_scale: float = 0.0):
+def mlp_params(seed: int, sizes=(32, 64, 64, 4), bias_scale="linear"):
     """Weights and biases of the MLP head: per layer W [out, in] Xavier-uniform,
     rounded to binary16 (the dtype the matrix cores read), and fp32 biases
-    drawn U(-bias_scale, bias_scale) (0: the zero initialisation of a fresh
-    network).  Returns [W1, b1, W2, b2, ...] as numpy arrays."""
+    drawn U(-a, a) with a = bias_scale, or a = 1/sqrt(fan_in) for "linear"
+    (torch.nn.Linear's own bias initialisation, the layer the NeRFace head is
+    built from).  Returns [W1, b1, W2, b2, ...] as numpy arrays."""
     out, off = [], 0
     for fin, fout in zip(sizes[:-1], sizes[1:]):
         out.append(xavier_uniform(seed, fin, fout, offset=off).astype(np.float16))
         off += fin * fout
-    for fout in sizes[1:]:
+    for fin, fout in zip(sizes[:-1], sizes[1:]):
         u = uniform_f64(seed, STREAM_MLP, fout, offset=off)
         off += fout
-        out.append(((2.0 * u - 1.0) * bias_scale).astype(np.float32))
+        a = 1.0 / np.sqrt(fin) if isinstance(bias_scale, str) and bias_scale == "linear" else float(bias_scale)
+        out.append(((2.0 * u - 1.0) * a).astype(np.float32))
     n = len(sizes) - 1
     return [v for i in range(n) for v in (out[i], out[n + i])]
 

@@ -82,9 +82,18 @@ MUTANTS = {
     # MLP head
     "mlp_second_relu_dropped": (MLP, "h2 = _r(np.maximum(z2, 0.0), round_fp16)", "h2 = _r(z2, round_fp16)"),
     "mlp_output_bias_dropped": (MLP, "y = h2 @ W3.T + b3", "y = h2 @ W3.T"),
-    "mlp_dW2_wrong_activation": (MLP, "dW2=dz2.T @ cache[\"h1\"]", "dW2=dz2.T @ cache[\"h2\"]"),
+    "mlp_dW2_wrong_activation": (MLP, "dW2=(dz2.T @ cache[\"h1\"])", "dW2=(dz2.T @ cache[\"h2\"])"),
     "mlp_db1_from_layer_2": (MLP, "db1=dz1.sum(0)", "db1=dz2.sum(0)"),
-    "mlp_relu_mask_dropped": (MLP, "dz2 = _r((g3 @ W3) * (cache[\"z2\"] > 0), on)", "dz2 = _r(g3 @ W3, on)"),
+    "mlp_relu_mask_dropped": (MLP, "dz2 = _r(_sum(g3, W3, None, acc32) * (cache[\"z2\"] > 0), on)",
+                              "dz2 = _r(_sum(g3, W3, None, acc32), on)"),
+    # the backward's binary16 rounding points and its power-of-two scale
+    "mlp_dz1_not_rounded": (MLP, "dz1 = _r(_sum(dz2, W2, None, acc32) * (cache[\"z1\"] > 0), on)",
+                            "dz1 = _sum(dz2, W2, None, acc32) * (cache[\"z1\"] > 0)"),
+    "mlp_first_layer_sum_in_float64": (MLP, "z1 = _sum(e16, W1.T, b1, acc32)", "z1 = _sum(e16, W1.T, b1, False)"),
+    "mlp_dy_rounded_before_scaling": (MLP, "g3 = _r(np.asarray(dy, dtype=np.float64) * s, on)",
+                                      "g3 = _r(np.asarray(dy, dtype=np.float64), on) * s"),
+    "mlp_de_rounded_to_half": (MLP, "de = (dz1 @ W1) / s", "de = _r(dz1 @ W1, on) / s"),
+    "mlp_dW1_not_unscaled": (MLP, "dW1=(dz1.T @ cache[\"e\"]) / s", "dW1=dz1.T @ cache[\"e\"]"),
 }
 
 

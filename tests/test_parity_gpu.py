@@ -200,19 +200,25 @@ def test_backward_matches_oracle(oracle, name, n):
     bwd_check(grad, ref, w.n_levels)
 
 
-def test_backward_half_grid_full_size_properties():
-    # At full size (2^21 points, 32 levels): per-level gradient sums equal the
-    # upstream column sums (the weights of a point sum to one).
+def test_backward_half_grid_full_size(oracle):
+    # The large binary16 grid at its full size (2^21 points, 32 levels, 2^21
+    # entries per level), in the launch configuration the benchmark times:
+    # every entry of every level against the oracle, and the per-level sums
+    # against the upstream column sums (a point's weights sum to one).
     w = I.WORKLOADS["large_f16"]
-    print(f"backward properties large_f16 n={w.n_points}", flush=True)
+    print(f"backward parity large_f16 n={w.n_points} (every entry)", flush=True)
     cfg = hg.HashGridConfig.of(w)
-    x, d = dev(I.make_points(w)), dev(I.make_dout(w))
+    x_h, d_h = I.make_points(w), I.make_dout(w)
+    x, d = dev(x_h), dev(d_h)
     g = torch.zeros(cfg.table_shape, device=DEV)
-    hg.hashgrid_backward(cfg, x, d, g)
+    hg.hashgrid_backward(cfg, x, d, g, workspace=hg.backward_workspace(cfg, w.n_points, DEV))
     got = g.double().sum(dim=1)
     want = d.double().reshape(-1, w.n_levels, 2).sum(dim=0)
     scale = d.double().abs().reshape(-1, w.n_levels, 2).sum(dim=0)
     assert float(((got - want).abs() / scale).max()) < 1e-6
+    grad = g.cpu().numpy()
+    del g, x, d
+    bwd_check(grad, oracle.backward(oracle.grid_of(w), x_h, d_h), w.n_levels)
 
 
 def test_backward_exact_dyadic_case(oracle):
@@ -475,7 +481,7 @@ def test_head_input_grad_and_adam_captured_in_a_graph_replay_like_eager():
     cfg = hg.HashGridConfig.of(w)
     n = w.n_points
     x, t = dev(I.make_points(w)), dev(I.make_table(w))
-    P = [dev(a) for a in I.mlp_params(w.seed, bias_scale=0.1)]
+    P = [dev(a) for a in I.mlp_params(w.seed)]
     dy = dev(I.dout_normal(w.seed + 7, n, 4))
     st_bytes, bw_bytes = hg.hashgrid_mlp_workspace_size(cfg, n)
     stage = torch.empty(st_bytes, dtype=torch.uint8, device=DEV)
@@ -592,3 +598,25 @@ def test_encoder_module_autograd(oracle):
     g = oracle.grid_of(w)
     assert fwd_err(out.detach().cpu().numpy(), oracle.forward(g, x, t), t) <= FWD_TOL
     bwd_check(enc.embeddings.grad.cpu().numpy(), oracle.backward(g, x, d), w.n_levels)
+
+
+def test_half_table_module_keeps_fp32_gradients(oracle):
+    # A binary16-table encoder keeps an fp32 master parameter by default: the
+    # kernels read its binary16 copy, and gradients far below binary16's range
+    # (upstream values of 1e-6) reach the parameter unrounded.
+    w = I.resized(I.WORKLOADS["large_f16"], 3000, n_levels=4, log2_table_size=14)
+    enc = hg.HashGridEncoder(n_levels=4, log2_hashmap_size=14, finest_resolution=4096, table_dtype="f16",
+                             device=DEV)
+    assert enc.embeddings.dtype == torch.float32
+    t16 = I.make_table(w)  # binary16 values
+    with torch.no_grad():
+        enc.embeddings.copy_(dev(t16.astype(np.float32)))
+    x = I.make_points(w)
+    d = (I.make_dout(w) * np.float32(1e-6)).astype(np.float32)
+    out = enc(dev(x))
+    out.backward(dev(d))
+    g = oracle.grid_of(w)
+    assert fwd_err(out.detach().cpu().numpy(), oracle.forward(g, x, t16), t16) <= FWD_TOL
+    got = enc.embeddings.grad
+    assert got.dtype == torch.float32
+    bwd_check(got.cpu().numpy(), oracle.backward(g, x, d), w.n_levels)

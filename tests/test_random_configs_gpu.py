@@ -104,10 +104,8 @@ def test_random_configuration_matches_oracle(oracle, case):
     if coherent:
         w, spread = draw(1000 + case)
         rng = np.random.default_rng(95_000 + case)
-        # Tables of at least 2^10 entries: below that, 10^4 points put more than
-        # 10^4 fp32 additions on an entry of the atomic path, past its 1e-5 bar.
         w = I.replace(w, name=f"coherent{case}", n_dims=3, n_features=2, base_resolution=int(rng.integers(1, 9)),
-                      n_points=int(rng.integers(8000, 20001)), log2_table_size=max(10, w.log2_table_size))
+                      n_points=int(rng.integers(8000, 20001)))
     else:
         w, spread = draw(case) if case < CASES else edge_workload(case - CASES)
     print(f"[config {case}] D={w.n_dims} F={w.n_features} L={w.n_levels} log2T={w.log2_table_size} "

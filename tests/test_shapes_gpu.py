@@ -233,3 +233,36 @@ def test_input_grad_workspace_variants_agree(oracle, n):
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
     input_grad_check(outs[0], oracle.input_grad(oracle.grid_of(w), I.make_points(w), I.make_table(w),
                                                 I.make_dout(w)))
+
+
+@pytest.mark.parametrize("D,F", [(2, 2), (4, 2), (3, 1), (3, 4), (3, 8)])
+def test_benchmarked_shape_at_full_size(oracle, D, F):
+    # The shapes the benchmark times, at its size: the standard grid's L = 16,
+    # T = 2^19 and resolutions 16..512 over 2^18 uniform points, with the
+    # workspaces the benchmark passes (staged forward, binned backward in level
+    # groups, level-major dL/dx).  The binned backward walks every tile chunk
+    # and run-map window of the accumulate kernel; every output, gradient entry
+    # and dL/dx value is compared.
+    w = I.resized(I.WORKLOADS["standard"], 1 << 18, n_dims=D, n_features=F)
+    print(f"full-size shape D={D} F={F} n={w.n_points}", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    g = oracle.grid_of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    xd, td, dd = dev(x), dev(t), dev(d)
+    n = w.n_points
+    out = hg.hashgrid_forward(cfg, xd, td, workspace=hg.forward_workspace(cfg, n, DEV)).cpu().numpy()
+    tmax = float(np.max(np.abs(t.astype(np.float64))))
+    assert float(np.max(np.abs(out - oracle.forward(g, x, t)))) <= 1e-6 * tmax
+    del out
+    grad = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_backward(cfg, xd, dd, grad, workspace=hg.backward_workspace(cfg, n, DEV))
+    got = grad.cpu().numpy()
+    del grad
+    gref = oracle.backward(g, x, d)
+    for l in range(w.n_levels):
+        assert np.max(np.abs(got[l] - gref[l])) <= 1e-5 * np.max(np.abs(gref[l])), l
+    del got, gref
+    isz = hg.hashgrid_input_grad_workspace_size(cfg, n)
+    iws = torch.empty(isz, dtype=torch.uint8, device=DEV) if isz else None
+    dx = hg.hashgrid_input_grad(cfg, xd, td, dd, workspace=iws).cpu().numpy()
+    input_grad_check(dx, oracle.input_grad(g, x, t, d))
