@@ -177,6 +177,26 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
                       int64_t dout_row_stride, float *dtable, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/* Allocation-free variant of hashgrid_backward, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same table gradient, accumulated into
+ * dtable (arguments as hashgrid_backward), with the binned path's workspace
+ * taken from a fixed scratch array of HASHGRID_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds on each device it runs on until the process ends.
+ * Nothing is allocated or freed per call.  Levels are binned in groups that
+ * fit the scratch (4 levels at a time for n = 2^18 on the D = 3, F = 2 grid),
+ * so the result equals hashgrid_backward's binned result; grids without a
+ * binned path take the atomic scatter, as hashgrid_backward does without a
+ * workspace.  Every call on one device shares that device's scratch: calls
+ * that overlap on a device (other streams, other host threads) race, and the
+ * caller must order them.  Errors: as hashgrid_backward, and HG_EINVAL when
+ * one level's records of n points exceed the scratch (the message gives the
+ * largest n of the grid: about 1.37 * 10^6 points for D = 3, F = 2 at
+ * T = 2^19); HG_EHIP when the scratch's device address cannot be resolved. */
+#define HASHGRID_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int hashgrid_backward_noalloc(const hg_config *cfg, const float *x, int64_t n, const float *dout,
+                              int64_t dout_row_stride, float *dtable, void *stream);
+
 /* Debug export of the corner table indices and interpolation weights.
  *   idx : uint32 [n][L][2^D]  -- hashed index in [0, T) of corner k of level l,
  *   w   : float32 [n][L][2^D] -- its fp32 weight,

@@ -16,6 +16,7 @@ from .hashgrid import (  # noqa: F401
     backward_workspace,
     hashgrid_adam_step,
     hashgrid_backward,
+    hashgrid_backward_noalloc,
     hashgrid_backward_workspace_size,
     hashgrid_debug_corners,
     forward_workspace,

@@ -372,6 +372,37 @@ int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const flo
     return table_backward(cfg, x, n, dout, dout_row_stride, dtable, workspace, workspace_bytes, stream);
 }
 
+int hashgrid_backward_noalloc(const hg_config *cfg, const float *x, int64_t n, const float *dout,
+                              int64_t dout_row_stride, float *dtable, void *stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n == 0) return ok();
+    if ((rc = check_points(n, x))) return rc;
+    if (!dout || !aligned(dout, 4)) return fail(HG_EINVAL, "dout is NULL or not 4-byte aligned");
+    if (!dtable || !aligned(dtable, 4)) return fail(HG_EINVAL, "dtable is NULL or not 4-byte aligned");
+    if (dout_row_stride < (int64_t)cfg->n_levels * cfg->n_features)
+        return fail(HG_EINVAL, "dout_row_stride %lld < L*F", (long long)dout_row_stride);
+    // The scratch must hold one level's records (levels are binned in groups
+    // that fit it); a grid without a binned path uses no scratch.
+    hg::BinParams bp;
+    if (plan_binned(*cfg, n, bp)) {
+        const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
+        if (per_level > hg::kNoallocScratchBytes) {
+            const size_t per_tile = (size_t)bp.rec_per_tile * bp.rec_bytes + ((size_t)bp.parts + 2) * sizeof(uint32_t);
+            const long long max_n = (long long)((hg::kNoallocScratchBytes - 256) / per_tile) * bp.tile_pts;
+            return fail(HG_EINVAL,
+                        "n = %lld: one level's binned records take %zu bytes, more than the %zu-byte scratch of "
+                        "the allocation-free backward; it takes at most %lld points of this grid per call",
+                        (long long)n, per_level, hg::kNoallocScratchBytes, max_n);
+        }
+    }
+    void *scratch = nullptr;
+    const hipError_t e = hg::noalloc_scratch(&scratch);
+    if (e != hipSuccess)
+        return fail(HG_EHIP, "device scratch of the allocation-free backward: %s", hipGetErrorString(e));
+    return table_backward(cfg, x, n, dout, dout_row_stride, dtable, scratch, hg::kNoallocScratchBytes, stream);
+}
+
 int hashgrid_mlp_workspace_size(const hg_config *cfg, int64_t n, size_t *stage_bytes_out, size_t *bwd_bytes_out) {
     int rc = check_config(cfg);
     if (rc) return rc;

@@ -72,6 +72,12 @@ constexpr int generic_rec_per_tile(int D, int F) { return generic_tile(D, F) << 
 constexpr int generic_rec_bytes(int F) { return (2 + F) * 4; }
 constexpr int generic_s_log2(int F) { return F == 1 ? 13 : F == 2 ? 12 : F == 4 ? 11 : 10; }
 
+// The allocation-free backward's device scratch (noalloc.hip): one fixed
+// array per device; noalloc_scratch resolves the current device's address
+// (once per device) and returns it.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void **out);
+
 // Workspace bytes of one level (records, run starts, tile maxima).
 size_t binned_level_bytes(const BinParams &bp);
 hipError_t launch_binned_backward_generic(BinParams bp, int D, int F, int n_levels, int max_group, const float *x,

@@ -122,6 +122,7 @@ def load_library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
                 "hashgrid_forward_workspace_size": ([C, I64, P], ctypes.c_int),
                 "hashgrid_backward": ([C, P, I64, P, I64, P, P, ctypes.c_size_t, P], ctypes.c_int),
                 "hashgrid_backward_workspace_size": ([C, I64, P, P], ctypes.c_int),
+                "hashgrid_backward_noalloc": ([C, P, I64, P, I64, P, P], ctypes.c_int),
                 "hashgrid_debug_corners": ([C, P, I64, P, P, P], ctypes.c_int),
                 "hashgrid_input_grad": ([C, P, I64, P, P, I64, P, P, ctypes.c_size_t, P], ctypes.c_int),
                 "hashgrid_input_grad_workspace_size": ([C, I64, P], ctypes.c_int),
@@ -291,6 +292,25 @@ def hashgrid_backward(cfg: HashGridConfig, x: torch.Tensor, dout: torch.Tensor,
                                             dout.stride(0), dtable.data_ptr(), ws_ptr, ws_bytes,
                                             _stream(x, stream)))
     _keep_for_stream(x, stream, _keep if auto else None)
+    return dtable
+
+
+def hashgrid_backward_noalloc(cfg: HashGridConfig, x: torch.Tensor, dout: torch.Tensor,
+                              dtable: torch.Tensor, stream=None) -> torch.Tensor:
+    """hashgrid_backward without any workspace allocation: the library's own
+    fixed device scratch holds the binned records (calls that overlap on one
+    device race on it).  Accumulates into ``dtable``."""
+    _points(cfg, x)
+    n = x.shape[0]
+    _dev(dout, "dout", torch.float32)
+    if dout.dim() != 2 or dout.shape[0] != n or dout.stride(1) != 1 or dout.shape[1] < cfg.out_features:
+        raise ValueError("dout must be [n, >= L*F] with unit column stride")
+    _dev(dtable, "dtable", torch.float32)
+    if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
+        raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
+    c = cfg.c()
+    _check(load_library().hashgrid_backward_noalloc(ctypes.byref(c), x.data_ptr(), n, dout.data_ptr(),
+                                                    dout.stride(0), dtable.data_ptr(), _stream(x, stream)))
     return dtable
 
 

@@ -235,3 +235,23 @@ def test_other_shapes_are_accepted(lib, D, F):
     cfg = hg.HashGridConfig(n_dims=D, n_features=F)
     assert hg.hashgrid_resolutions(cfg)[0] == 16
     assert hg.hashgrid_input_grad_workspace_size(cfg, 64) == (16 * 64 * D * 4 if D >= 3 else 0)
+
+
+def test_noalloc_backward_rejects_batches_beyond_its_scratch(lib):
+    # The size check happens on the host before the scratch is looked up or
+    # anything is enqueued, so this needs no GPU (the pointers are never used).
+    cfg = hg.HashGridConfig()
+    c = cfg.c()
+    hdr = open(os.path.join(ROOT, "include", "hashgrid.h")).read()
+    assert "#define HASHGRID_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr
+    n = 1 << 21  # 2^21 points: one level's records alone need ~103 MB
+    rc = lib.hashgrid_backward_noalloc(ctypes.byref(c), 0x1000, n, 0x2000, 32, 0x3000, None)
+    assert rc == B.HG_EINVAL
+    msg = lib.hashgrid_last_error().decode()
+    assert "scratch" in msg and "at most" in msg
+    m = int(re.search(r"at most (\d+) points", msg).group(1))
+    assert 1_300_000 < m < 1_400_000
+    # argument errors as in hashgrid_backward
+    assert lib.hashgrid_backward_noalloc(ctypes.byref(c), 0x1000, -1, 0x2000, 32, 0x3000, None) == B.HG_EINVAL
+    assert lib.hashgrid_backward_noalloc(ctypes.byref(c), 0x1000, 16, 0x2000, 31, 0x3000, None) == B.HG_EINVAL
+    assert lib.hashgrid_backward_noalloc(ctypes.byref(c), 0x1000, 0, 0, 32, 0, None) == B.HG_OK
