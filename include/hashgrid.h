@@ -150,17 +150,24 @@ int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *by
  *   dtable : float32 [L][T][F], 4-byte aligned.  ACCUMULATED INTO:
  *            dtable[l][h(corner_k)][j] += w_k * dout[p][l*F + j] for every point,
  *            level and corner.  The caller zeroes the buffer when it wants the
- *            gradient of one batch alone.  On the binned path each contribution
- *            is rounded to 64-bit fixed point (a step below 2^-29 max|dout| of
- *            the level) and the integer sums do not depend on the order of the
- *            additions: for points in [0,1)^D the result is reproducible bit for
- *            bit.  The atomic path adds in fp32 in an unspecified order, so its
- *            results can differ from run to run in the last bits, and its
- *            rounding error grows with the additions an entry receives: within
- *            1e-5 of the level's largest gradient up to about 10^4 per entry,
- *            1.0-3.4e-5 measured at 1.2-9.5 * 10^4 (tables of 2 to 8 entries
- *            under 4 * 10^3 to 2 * 10^4 points); the binned path sums exactly at any
- *            count.  Both paths
+ *            gradient of one batch alone.  On the binned path the D = 3, F = 2
+ *            grid stores each corner pair's products w_y w_z dout with 20
+ *            significant bits (relative error <= 2^-21), each contribution is
+ *            rounded to 64-bit fixed point (a step below 2^-29 max|dout| of the
+ *            level, taken over its finite values) and the integer sums do not
+ *            depend on the order of the additions: for points in [0,1)^D the
+ *            result is reproducible bit for bit.  The atomic path (no
+ *            workspace) first sums, per workgroup of 4096 points, the levels
+ *            of at most 16384 values (T F, or the vertex grid (N_l + 1)^D F)
+ *            in the same 64-bit fixed point in LDS and adds each sum with one
+ *            fp32 atomic; other levels it scatters with fp32 atomics in an
+ *            unspecified order, so its results can differ from run to run in
+ *            the last bits.  Non-finite dout values (NaN, +-Inf) are never
+ *            summed in fixed point: their contributions are added with fp32
+ *            atomics, so they reach the entries they touch as IEEE arithmetic
+ *            has them (NaN stays NaN, Inf + finite = Inf, Inf - Inf = NaN) and
+ *            the other entries keep the precision of the finite values.  Both
+ *            paths
  *            first sum, inside each wavefront, runs of consecutive points that
  *            share a voxel (ray samples at coarse levels) for the D = 3, F = 2
  *            grid.
@@ -346,6 +353,9 @@ int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m
 #define HG_TUNE_BWD_DENSE 10    /* atomic backward: 1 sums levels of at most 16384 values
                                    (T * F, or the vertex grid (N_l + 1)^D * F) in LDS per
                                    workgroup first, 0 scatters every level directly     */
+#define HG_TUNE_FWD_SPLIT_KIB 11 /* staged D = 3, F = 2 forward: levels whose table exceeds
+                                   this many KiB are gathered one table half per pass
+                                   (64..2^20; 0 = never); 4096 by default              */
 int hashgrid_tune(int key, int value);
 int hashgrid_tune_get(int key);
 

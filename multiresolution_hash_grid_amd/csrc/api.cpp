@@ -44,6 +44,7 @@ struct Tuning {
     int bwd_part_log2 = 0;  // 0: by table size
     int bwd_group_mib = 160;  // record bytes per binned level group, 0: all levels at once
     int bwd_dense = 1;        // atomic backward: sum small levels in LDS first
+    int fwd_split_kib = 4096; // staged gather of levels above this table size: one half per pass
 };
 Tuning g_tune;
 
@@ -338,7 +339,7 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
                                                         cfg->table_dtype, out, out_row_stride, g_tune.fwd_lanes,
                                                         cfg->n_features <= 4 ? stage : nullptr, (hipStream_t)stream),
                              "forward");
-    const hg::FwdTune ft{g_tune.fwd_lanes, g_tune.fwd_unroll, g_tune.fwd_nt};
+    const hg::FwdTune ft{g_tune.fwd_lanes, g_tune.fwd_unroll, g_tune.fwd_nt, g_tune.fwd_split_kib};
     return launch_status(hg::launch_forward(lp, x, n, table, cfg->table_dtype, out, out_row_stride, ft, stage,
                                             (hipStream_t)stream),
                          "forward");
@@ -600,6 +601,10 @@ int hashgrid_tune(int key, int value) {
         if (value != 0 && value != 1) break;
         g_tune.bwd_dense = value;
         return ok();
+    case HG_TUNE_FWD_SPLIT_KIB:
+        if (value != 0 && (value < 64 || value > (1 << 20))) break;
+        g_tune.fwd_split_kib = value;
+        return ok();
     default:
         return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
@@ -619,6 +624,7 @@ int hashgrid_tune_get(int key) {
     case HG_TUNE_BWD_PART_LOG2: return g_tune.bwd_part_log2;
     case HG_TUNE_BWD_GROUP_MIB: return g_tune.bwd_group_mib;
     case HG_TUNE_BWD_DENSE: return g_tune.bwd_dense;
+    case HG_TUNE_FWD_SPLIT_KIB: return g_tune.fwd_split_kib;
     default: return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
 }

@@ -371,12 +371,6 @@ struct StdPolicy {
 
 }  // namespace
 
-size_t binned_level_bytes(const BinParams &bp) {
-    const size_t recs = (size_t)bp.level_records * bp.rec_bytes;
-    const size_t words = (size_t)bp.tiles * (bp.parts + 2);
-    return recs + words * sizeof(uint32_t);
-}
-
 hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, const float *x, int64_t n,
                                   const float *dout, int64_t dout_stride, float *dtable,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream) {

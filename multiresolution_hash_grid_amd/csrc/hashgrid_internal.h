@@ -79,7 +79,11 @@ constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
 hipError_t noalloc_scratch(void **out);
 
 // Workspace bytes of one level (records, run starts, tile maxima).
-size_t binned_level_bytes(const BinParams &bp);
+inline size_t binned_level_bytes(const BinParams &bp) {
+    const size_t recs = (size_t)bp.level_records * bp.rec_bytes;
+    const size_t words = (size_t)bp.tiles * (bp.parts + 2);
+    return recs + words * sizeof(uint32_t);
+}
 hipError_t launch_binned_backward_generic(BinParams bp, int D, int F, int n_levels, int max_group, const float *x,
                                           int64_t n, const float *dout, int64_t dout_stride, float *dtable,
                                           void *workspace, size_t workspace_bytes, hipStream_t stream);
@@ -95,6 +99,7 @@ struct FwdTune {
     int lanes;
     int unroll;
     int nt;
+    int split_kib;  // staged gather: levels whose table exceeds this many KiB go one half per pass (0: never)
 };
 
 // Kernel launchers (encode_kernels.hip).  They return the launch status.
