@@ -85,7 +85,9 @@ int hashgrid_resolutions(const hg_config *cfg, int32_t *res_out);
 
 /* Bytes of device workspace with which hashgrid_forward stages the encoding
  * level-major before writing the rows: L * n * F * 4 rounded up to 256
- * (32 MiB for L = 16, F = 2, n = 2^18).  *bytes_out is a HOST size_t.
+ * (32 MiB for L = 16, F = 2, n = 2^18), twice that for a D = 3, F = 2 grid
+ * whose levels are gathered one table half per pass (below), whose second
+ * half then writes its own stage.  *bytes_out is a HOST size_t.
  * Errors: HG_EINVAL, HG_EUNSUPPORTED. */
 int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *bytes_out);
 
@@ -111,9 +113,11 @@ int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *byt
  *   fp32, with w_k the trilinear weight of corner k.  For the D = 3, F = 2
  *   grid with a workspace, a level whose table exceeds 4 MiB (fp32
  *   T >= 2^20, binary16 T >= 2^21) is gathered one table half per pass, so
- *   that the half fits one XCD's L2, and the two partial blends are added:
- *   such levels round differently from the one-pass direct path, by a few
- *   fp32 roundings of the blend (measured: 1.5e-7 of the largest table value).
+ *   that the half fits one XCD's L2, and the two partial blends are added
+ *   (while transposing when the workspace holds two stages, in place when it
+ *   holds one; the sums are the same either way): such levels round
+ *   differently from the one-pass direct path, by a few fp32 roundings of the
+ *   blend (measured: 1.5e-7 of the largest table value).
  * Errors: HG_EINVAL (config, NULL, alignment, n < 0, stride), HG_EUNSUPPORTED,
  *         HG_EHIP. */
 int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void *table,

@@ -190,6 +190,13 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // generic ones.
 bool standard_shape(const hg_config &c) { return c.n_dims == 3 && c.n_features == 2; }
 
+// The staged forward of the D = 3, F = 2 grid gathers levels whose table
+// exceeds the split threshold one half per pass.
+bool split_forward(const hg_config &c) {
+    const size_t level_bytes = (size_t)(c.table_dtype == HG_F32 ? 8 : 4) << c.log2_table_size;
+    return standard_shape(c) && g_tune.fwd_split_kib > 0 && level_bytes > ((size_t)g_tune.fwd_split_kib << 10);
+}
+
 // Levels per binned group.  Where the budget (sized for the 256 MB last-level
 // cache of the MI355X) holds enough levels for at least 1024 accumulate
 // workgroups (two rounds of two per CU), groups take as many levels as keep
@@ -312,7 +319,9 @@ int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *byt
     if (rc) return rc;
     if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
     if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
-    *bytes_out = round_up((size_t)n * cfg->n_levels * cfg->n_features * sizeof(float), 256);
+    // One stage, or two where the gather splits levels (the second half's blends).
+    const size_t stage = round_up((size_t)n * cfg->n_levels * cfg->n_features * sizeof(float), 256);
+    *bytes_out = split_forward(*cfg) ? 2 * stage : stage;
     return ok();
 }
 
@@ -340,8 +349,12 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
                                                         cfg->n_features <= 4 ? stage : nullptr, (hipStream_t)stream),
                              "forward");
     const hg::FwdTune ft{g_tune.fwd_lanes, g_tune.fwd_unroll, g_tune.fwd_nt, g_tune.fwd_split_kib};
+    float *stage2 = nullptr;
+    const size_t stage_round = round_up(stage_bytes, 256);
+    if (stage && split_forward(*cfg) && workspace_bytes >= stage_round + stage_bytes)
+        stage2 = (float *)((char *)workspace + stage_round);
     return launch_status(hg::launch_forward(lp, x, n, table, cfg->table_dtype, out, out_row_stride, ft, stage,
-                                            (hipStream_t)stream),
+                                            (hipStream_t)stream, stage2),
                          "forward");
 }
 

@@ -115,14 +115,17 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_kernel(const float *__restrict_
 // level-major [L][n][F] staging array whose stores are fully coalesced.
 // SPLIT: one half of every level's table, the entries whose index has top bit
 // `half` (T = 2^s entries, so the bit is idx >> (s - 1)); the other half's
-// corners count as zero.  Half 0 writes its partial blend and half 1 adds its
-// own to it, so two launches give the blend while each XCD's L2 holds only
-// half of a level's table at a time.
+// corners count as zero.  Two launches give the blend while each XCD's L2
+// holds only half of a level's table at a time: half 0 writes its partial
+// blend, and half 1 either writes its own to a second stage, which the
+// transpose adds (add_prev = 0), or adds the first half's (add_prev = 1, when
+// the workspace holds one stage).
 template <int DT, int U, bool NT, typename OutT = float, bool SPLIT = false>
 __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__restrict__ x, int64_t n,
                                                              const void *__restrict__ table,
                                                              OutT *__restrict__ out, int64_t ostride,
-                                                             int64_t lstride, LaunchParams lp, int half) {
+                                                             int64_t lstride, LaunchParams lp, int half,
+                                                             int add_prev = 0) {
     Item it;
     if (!decode_item(lp, it)) return;
     constexpr int kPairs = kBlock / 2;
@@ -177,7 +180,8 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
             if (ok[u]) {
                 OutT *dst = out + (p0 + (int64_t)u * kPairs) * ostride + (int64_t)l * lstride + sub;
                 if constexpr (SPLIT) {
-                    if (half) v += NT ? __builtin_nontemporal_load(dst) : *dst;
+                    // (requesting this load with the gathers measured slower: 2.11 against 2.04 ms)
+                    if (add_prev) v += NT ? __builtin_nontemporal_load(dst) : *dst;
                 }
                 if constexpr (NT) __builtin_nontemporal_store((OutT)v, dst);
                 else *dst = (OutT)v;  // binary16 stage: round to nearest even
@@ -337,8 +341,11 @@ int grid_blocks(const LaunchParams &lp) {
 // points per workgroup through LDS so that both sides move whole lines.
 // VEC moves 16 bytes per access on both sides (F n and F L multiples of 4,
 // rows and output 16-byte aligned); otherwise 4 bytes.
+// stage2 (may be NULL): a second stage of partial blends, added element-wise
+// while transposing.
 template <int F, bool VEC>
-__global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restrict__ stage, int64_t n, int L,
+__global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restrict__ stage,
+                                                           const float *__restrict__ stage2, int64_t n, int L,
                                                            int pts, float *__restrict__ out, int64_t ostride) {
     extern __shared__ float tile[];  // [pts][F L + 4]: rows 16-byte aligned when F L is a multiple of 4
     const int row = F * L + 4;
@@ -350,7 +357,12 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restri
         for (int e = threadIdx.x; e < L * q_per_level; e += kBlock) {
             const int l = e / q_per_level, qd = e - l * q_per_level;
             if (4 * qd < F * np) {
-                const float4 v = *reinterpret_cast<const float4 *>(stage + ((int64_t)l * n + p0) * F + 4 * qd);
+                const int64_t off = ((int64_t)l * n + p0) * F + 4 * qd;
+                float4 v = *reinterpret_cast<const float4 *>(stage + off);
+                if (stage2) {
+                    const float4 w = *reinterpret_cast<const float4 *>(stage2 + off);
+                    v.x += w.x, v.y += w.y, v.z += w.z, v.w += w.w;
+                }
                 if constexpr (F == 1) {
                     tile[(4 * qd + 0) * row + l] = v.x;
                     tile[(4 * qd + 1) * row + l] = v.y;
@@ -380,7 +392,10 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restri
         for (int e = threadIdx.x; e < total; e += kBlock) {
             const int l = e / (F * pts), r = e - l * F * pts;
             const int i = r / F, j = r - i * F;
-            if (i < np) tile[i * row + F * l + j] = stage[((int64_t)l * n + p0 + i) * F + j];
+            if (i < np) {
+                const int64_t off = ((int64_t)l * n + p0 + i) * F + j;
+                tile[i * row + F * l + j] = stage2 ? stage[off] + stage2[off] : stage[off];
+            }
         }
         __syncthreads();
         for (int e = threadIdx.x; e < total; e += kBlock) {
@@ -392,22 +407,27 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restri
 
 template <int F>
 hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, int64_t ostride,
-                              hipStream_t stream) {
+                              hipStream_t stream, const float *stage2 = nullptr) {
     // Points per workgroup: 64, fewer for wide rows so that the tile stays near 32 KB.
     const int pts = std::max(4, std::min(64, 8192 / (F * L + 4)) / 4 * 4);
     const unsigned blocks = (unsigned)((n + pts - 1) / pts);
     const size_t lds = (size_t)pts * (F * L + 4) * sizeof(float);
-    const bool vec = (n * F) % 4 == 0 && (F * L) % 4 == 0 && ostride % 4 == 0 && ((uintptr_t)out & 15) == 0 &&
-                     ((uintptr_t)stage & 15) == 0;
-    if (vec) transpose_kernel<F, true><<<blocks, kBlock, lds, stream>>>(stage, n, L, pts, out, ostride);
-    else transpose_kernel<F, false><<<blocks, kBlock, lds, stream>>>(stage, n, L, pts, out, ostride);
+    bool vec = (n * F) % 4 == 0 && (F * L) % 4 == 0 && ostride % 4 == 0 && ((uintptr_t)out & 15) == 0 &&
+               ((uintptr_t)stage & 15) == 0;
+    if (vec && stage2 && ((uintptr_t)stage2 & 15)) vec = false;
+    if (vec) transpose_kernel<F, true><<<blocks, kBlock, lds, stream>>>(stage, stage2, n, L, pts, out, ostride);
+    else transpose_kernel<F, false><<<blocks, kBlock, lds, stream>>>(stage, stage2, n, L, pts, out, ostride);
     return hipGetLastError();
 }
 
 // On the staged path a level's table above one XCD's L2 (4 MiB) is gathered
 // in two launches, one per half (fwd_f2_pair_kernel SPLIT): measured on the
 // 8 MiB levels of a binary16 T = 2^21 grid, 2.07 against 2.29 ms; quarters
-// cost more in instructions than they gain (3.8 ms).  The direct path gathers
+// cost more in instructions than they gain (3.8 ms).  With room for a second
+// stage the second half writes its own partial blends and the transpose adds
+// the two (1.96 ms); adding into the first half's stage in place costs a
+// dependent read of it (2.04 ms).  Splitting the standard grid's 4 MiB levels
+// measured slower (110 against 98 us).  The direct path gathers
 // in one pass: there the second half's read-modify-write of 8 bytes per row
 // and level made the forward 1.6 times slower.  The other shapes' kernels
 // gather in one pass: for F = 4 at 8 MiB a split gained 3 %, and F = 8 rows,
@@ -415,15 +435,18 @@ hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, 
 
 template <int DT>
 hipError_t launch_gather_dt(const LaunchParams &lp, const float *x, int64_t n, const void *table, float *out,
-                            int64_t ostride, int64_t lstride, const FwdTune &ft, hipStream_t stream) {
+                            int64_t ostride, int64_t lstride, const FwdTune &ft, hipStream_t stream,
+                            float *out2 = nullptr) {
     dim3 grid(grid_blocks(lp)), block(kBlock);
     const size_t level_bytes = (DT == 0 ? sizeof(float2) : sizeof(uint32_t)) << lp.log2_table_size;
     if (lstride == 2 && ft.lanes == 1) {
         fwd_f2_kernel<DT><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lp);
     } else if (lstride != 2 && ft.split_kib > 0 && level_bytes > ((size_t)ft.split_kib << 10)) {  // staged output only
         for (int half = 0; half < 2; ++half) {
-            if (ft.nt) fwd_f2_pair_kernel<DT, 4, true, float, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, half);
-            else fwd_f2_pair_kernel<DT, 4, false, float, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, half);
+            float *dst = half && out2 ? out2 : out;
+            const int add = half && !out2;
+            if (ft.nt) fwd_f2_pair_kernel<DT, 4, true, float, true><<<grid, block, 0, stream>>>(x, n, table, dst, ostride, lstride, lp, half, add);
+            else fwd_f2_pair_kernel<DT, 4, false, float, true><<<grid, block, 0, stream>>>(x, n, table, dst, ostride, lstride, lp, half, add);
         }
     } else if (ft.nt) {
         if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, 0);
@@ -441,16 +464,16 @@ hipError_t launch_gather_dt(const LaunchParams &lp, const float *x, int64_t n, c
 
 hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, const void *table,
                           int table_dtype, float *out, int64_t out_stride, const FwdTune &ft,
-                          float *stage, hipStream_t stream) {
+                          float *stage, hipStream_t stream, float *stage2) {
     hipError_t e;
     if (!stage) {
         return table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, out, out_stride, 2, ft, stream)
                                 : launch_gather_dt<1>(lp, x, n, table, out, out_stride, 2, ft, stream);
     }
-    e = table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, stage, 2, 2 * n, ft, stream)
-                         : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream);
+    e = table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2)
+                         : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2);
     if (e != hipSuccess) return e;
-    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream);
+    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream, stage2);
 }
 
 hipError_t launch_transpose(int F, const float *stage, int64_t n, int L, float *out, int64_t ostride,

@@ -105,9 +105,13 @@ struct FwdTune {
 // Kernel launchers (encode_kernels.hip).  They return the launch status.
 // stage == NULL: write rows directly; otherwise stage is an fp32 [L][n][2]
 // scratch array and the rows are assembled by a transpose pass.
+// stage2 (NULL, or a second [L][n][2] stage): where the gather takes a level
+// one table half per pass (FwdTune::split_kib), the second half writes its
+// partial blends there and the transpose adds them; without it the second
+// half adds the first half's in place.
 hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, const void *table,
                           int table_dtype, float *out, int64_t out_stride, const FwdTune &ft,
-                          float *stage, hipStream_t stream);
+                          float *stage, hipStream_t stream, float *stage2 = nullptr);
 hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, const float *dout,
                            int64_t dout_stride, float *dtable, int lanes, hipStream_t stream);
 // Shapes other than D = 3, F = 2 (generic_kernels.hip): D in 1..4,

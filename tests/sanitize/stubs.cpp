@@ -25,7 +25,7 @@ hipError_t launch_binned_backward(BinParams, int, int, const float *, int64_t, c
     return reached("binned backward");
 }
 hipError_t launch_forward(const LaunchParams &, const float *, int64_t, const void *, int, float *, int64_t,
-                          const FwdTune &, float *, hipStream_t) {
+                          const FwdTune &, float *, hipStream_t, float *) {
     return reached("forward");
 }
 hipError_t launch_backward(const LaunchParams &, const float *, int64_t, const float *, int64_t, float *, int,

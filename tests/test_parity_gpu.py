@@ -175,6 +175,10 @@ def test_forward_staged_and_direct_are_identical(oracle, name, log2T):
     assert np.array_equal(staged, run_forward(cfg, x, t, stride=cfg.out_features + 3)[:, :cfg.out_features])
     ref = oracle.forward(oracle.grid_of(w), x, t)
     assert fwd_err(staged, ref, t) <= FWD_TOL and fwd_err(direct, ref, t) <= FWD_TOL
+    # A workspace of one stage: the second half adds into the first half's
+    # stage in place instead of writing a second one; the same sums.
+    one = torch.empty(cfg.table_shape[0] * x.shape[0] * 2 * 4, dtype=torch.uint8, device=DEV)
+    assert np.array_equal(staged, run_forward(cfg, x, t, workspace=one))
     # Non-temporal point and output traffic (the second half's read of the first
     # half's partial blend included) does not change a bit.
     old = hg.hashgrid_tune_get(B.HG_TUNE_FWD_NT)
