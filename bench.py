@@ -26,39 +26,41 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 # L2 request peak: 8 XCDs x 16 L2 channels, each serving one 128-byte request
 # per clock, at 2.4 GHz.
 L2_REQ_PEAK_PER_S = 8 * 16 * 2.4e9
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_standard.json")
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_standard_mlp.json")
+PROFILES = os.path.join(ROOT, "profiles")
 PASS_KERNELS = {"forward": "fwd_f2_pair_kernel + transpose_kernel",
                 "backward": "bin_kernel + accumulate_kernel per level group"}
 
 
-def load_counters():
-    """The committed rocprofv3 counter summary (L2 hit and request rates of the
-    standard workload's kernels, MFMA utilisation of the MLP head's), each part
-    None when it was taken on other kernel source."""
+def load_counters(name: str):
+    """The committed rocprofv3 counter summary of one configuration
+    (profiles/counters_<name>.json: per-pass HBM traffic, L2 hit and request
+    rates, MFMA utilisation), or None when it is missing or was taken on other
+    library sources."""
     from multiresolution_hash_grid_amd import profile_summary as ps
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(os.path.join(PROFILES, f"counters_{name}.json")) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None, None
-    l2 = rec.get("l2") if rec.get("source_sha256") == ps.source_digest() else None
-    mfma = rec.get("mfma") if rec.get("mlp_source_sha256") == ps.source_digest(ps.MLP_SOURCES) else None
-    return l2, mfma
+        return None
+    return rec if rec.get("source_sha256") == ps.source_digest() else None
 
 
-def cache_summary(l2) -> dict | None:
-    """L2 hit rate and request rate of the standard step's kernels, by pass."""
-    if not l2:
+def counter_summary(rec) -> dict | None:
+    """Per pass of a configuration: counter HBM bytes and their rate against
+    the HBM peak, L2 hit rate and request rate against the L2 request peak
+    (and MFMA utilisation of the kernels that use the matrix cores)."""
+    if not rec:
         return None
     out = {}
-    for name, k in l2.items():
-        if k.get("pass"):
-            rps = k["requests_per_s"]
-            out[name] = {"pass": k["pass"], "l2_hit_rate": k["hit_rate"],
-                         "l2_requests_per_dispatch": k["requests"], "l2_requests_per_s": rps,
-                         "l2_request_peak_per_s": L2_REQ_PEAK_PER_S,
-                         "l2_request_frac": None if rps is None else rps / L2_REQ_PEAK_PER_S}
+    for p, v in rec["passes"].items():
+        out[p] = {"hbm_bytes": v["hbm_bytes"], "hbm_GBps": v["hbm_GBps"], "hbm_frac": v["hbm_frac"],
+                  "traffic_over_algorithmic": v["traffic_over_algorithmic"], "l2_hit_rate": v["l2_hit_rate"],
+                  "l2_requests_per_s": v["l2_requests_per_s"], "l2_request_peak_per_s": L2_REQ_PEAK_PER_S,
+                  "l2_request_frac": v["l2_request_frac"], "profiled_time_us": v["time_us"]}
+        mf = {k: {"util_pct": kv["mfma_util_pct"], "tflops": kv.get("mfma_fp16_tflops"), "peak_tflops": 2500.0}
+              for k, kv in rec["kernels"].items() if kv["pass"] == p and kv.get("mfma_util_pct") is not None}
+        if mf:
+            out[p]["mfma"] = mf
     return out
 
 
@@ -72,19 +74,14 @@ def algorithmic_bytes_per_point(w, table_esize: int) -> dict:
             "bwd": 4 * D + 4 * L * F + corners * 4}
 
 
-def load_traffic(pass_name: str):
-    """HBM bytes per launch of a pass from the committed rocprofv3 counter
-    summary, or None when it is missing or was taken on other kernel source."""
-    from multiresolution_hash_grid_amd.profile_summary import source_digest
-    try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("source_sha256") != source_digest():
+def load_traffic(pass_name: str, name: str = "standard"):
+    """HBM bytes per call of a pass from the committed rocprofv3 counter
+    summary, or None when it is missing or was taken on other sources."""
+    rec = load_counters(name)
+    if rec is None:
         return None
     p = rec.get("passes", {}).get(pass_name)
-    return None if p is None else p.get("hbm_bytes_per_launch")
+    return None if p is None else p.get("hbm_bytes")
 
 
 def time_calls(fn, iters: int) -> float:
@@ -173,7 +170,8 @@ def measure_shapes(dev, n: int, iters: int) -> dict:
                              "input_grad_points_per_s": n / (ims * 1e-3),
                              "fwd_frac": fb * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             "input_grad_frac": ib * n / (ims * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                             "input_grad_frac": ib * n / (ims * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "counters": counter_summary(load_counters(f"D{D}F{F}"))}
         del x, t, d, o, g, ws, fws, iws, dx
     return out
 
@@ -206,16 +204,14 @@ def measure_fused_mlp(dev, iters: int) -> dict:
     L, F = cfg.n_levels, cfg.n_features
     fb = 12 + 8 * L * F * 2 + 16
     bb = 12 + 16 + 2 * L * F + 8 * L * F * 4
-    _, mfma = load_counters()
     return {"points": n, "fwd_points_per_s": n / (fms * 1e-3), "bwd_points_per_s": n / (bms * 1e-3),
             "step_points_per_s": n / ((fms + bms) * 1e-3), "fwd_us": fms * 1e3, "bwd_us": bms * 1e3,
             "algorithmic_bytes_per_point": {"fwd": fb, "bwd": bb},
             "fwd_frac": fb * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            # rocprofv3 MfmaUtil and fp16 MFMA throughput of the head kernels (committed summary)
-            "mfma": None if mfma is None else {
-                k: {"util_pct": v["mfma_util_pct"], "tflops": v["tflops"], "peak_tflops": 2500.0}
-                for k, v in mfma.items() if k.startswith("mlp_")}}
+            "step_frac": (fb + bb) * n / ((fms + bms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            # committed rocprofv3 summary: HBM traffic, L2 rates, MfmaUtil and fp16 MFMA throughput of the head
+            "counters": counter_summary(load_counters("fused_mlp"))}
 
 
 def measure_other_configs(dev, iters: int) -> dict:
@@ -243,7 +239,8 @@ def measure_other_configs(dev, iters: int) -> dict:
         out[name] = {"points": n, "fwd_us": fms * 1e3, "bwd_us": bms * 1e3,
                      "fwd_points_per_s": n / (fms * 1e-3), "bwd_points_per_s": n / (bms * 1e-3),
                      "fwd_frac": bpp["fwd"] * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "bwd_frac": bpp["bwd"] * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                     "bwd_frac": bpp["bwd"] * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "counters": counter_summary(load_counters(name))}
         del x, t, d, o, g, ws, fws
     return out
 
@@ -402,7 +399,7 @@ def main() -> int:
     dom_ms = bwd_ms if dom == "backward" else fwd_ms
     dom_bytes = bpp["bwd"] if dom == "backward" else bpp["fwd"]
     achieved = dom_bytes * w.n_points / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(dom)
+    traffic = load_traffic(dom, w.name)
 
     result = {
         "metric": "points/sec hash-grid encode fwd & fwd+bwd (L16,T2^19,F2); % HBM roofline",
@@ -442,8 +439,8 @@ def main() -> int:
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
         },
-        # L2 hit and request rates of the step's kernels (committed rocprofv3 counter summary)
-        "cache": cache_summary(load_counters()[0]),
+        # HBM traffic, L2 hit and request rates per pass (committed rocprofv3 counter summary)
+        "cache": counter_summary(load_counters(w.name)),
         "roofline_fwd_frac": bpp["fwd"] * w.n_points / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline_fwd_bwd_frac": (bpp["fwd"] + bpp["bwd"]) * w.n_points * K / elapsed / 1e9 / HBM_PEAK_GBS,
     }

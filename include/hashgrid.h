@@ -126,7 +126,7 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
 
 /* Bytes of device workspace that let hashgrid_backward route the whole
  * gradient of n points through its binned (atomic-free) path at full speed:
- * per level, 48 * ceil(n / 512) * 512 bytes of records plus small counters
+ * per level, 48 * ceil(n / 1024) * 1024 bytes of records plus small counters
  * (about 12.9 MB for n = 2^18) for the D = 3, F = 2 grid; for other shapes
  * (2 + F) * 4 bytes per corner pair, 2^(D-1) pairs per point -- times the
  * number of levels binned together.

@@ -9,11 +9,11 @@
 // ~4 requests per (point, level), which bounds an atomic scatter near 1 ms for
 // 2^18 points at L = 16.  Instead the work is routed to owners:
 //
-//   bin        : per (level, tile of 512 points), each corner pair (the two
+//   bin        : per (level, tile of 1024 points), each corner pair (the two
 //                x-corners of one (dy, dz), which share a table partition of
 //                2^s entries unless x+1 carries above bit s) becomes a 12-byte
 //                record {local index of the x corner, the x+1 corner's offset
-//                code, f_x, w_y w_z g_0, w_y w_z g_1}; the tile's 2048 records
+//                code, f_x, w_y w_z g_0, w_y w_z g_1}; the tile's 4096 records
 //                are counting-sorted by partition in LDS and written
 //                contiguously to the tile's own region together with the run
 //                offsets of every partition;
@@ -73,7 +73,7 @@ namespace {
 
 using namespace binned;
 
-constexpr int kBinThreads = 256;
+constexpr int kBinThreads = kBinTile / 2;  // 512
 constexpr int kPtsPerThread = kBinTile / kBinThreads;  // 2
 constexpr int kRecPerTile = kBinTile * 4;              // 4 corner pairs per point
 constexpr int kLevelsPerBlock = 4;                     // levels per bin workgroup
@@ -272,12 +272,12 @@ __device__ __forceinline__ void load_points(const float *__restrict__ x, int64_t
 __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restrict__ x, int64_t n,
                                                           const float *__restrict__ dout, int64_t dstride,
                                                           BinParams bp, StdSpace sp, float *__restrict__ grad) {
-    __shared__ Rec stage[kRecPerTile];
     __shared__ uint32_t wmax[kBinThreads / 64];
     __shared__ uint32_t wsum[kBinThreads / 64];
-    extern __shared__ uint32_t dyn[];  // cnt[parts], base[parts + 1]
-    uint32_t *cnt = dyn;
-    uint32_t *base = dyn + bp.parts;
+    extern __shared__ uint32_t dyn[];  // stage[kRecPerTile] records, cnt[parts], base[parts + 1]
+    Rec *stage = reinterpret_cast<Rec *>(dyn);
+    uint32_t *cnt = dyn + kRecPerTile * (sizeof(Rec) / sizeof(uint32_t));
+    uint32_t *base = cnt + bp.parts;
     const BinSlot slot = bin_slot((bp.group + kLevelsPerBlock - 1) / kLevelsPerBlock);
     if (slot.tile >= bp.tiles) return;
     const int tile = slot.tile;
@@ -380,7 +380,8 @@ hipError_t launch_binned_backward(BinParams bp, int n_levels, int max_group, con
     // Equal groups: 16 levels in groups of at most 6 run as 6 + 5 + 5.
     const int ngroups = (n_levels + group - 1) / group;
     group = (n_levels + ngroups - 1) / ngroups;
-    const size_t dyn = (2 * (size_t)bp.parts + 1) * sizeof(uint32_t);  // run counters: 32 KB at 4096 partitions
+    // the tile's record stage and the run counters (32 KB at 4096 partitions)
+    const size_t dyn = (size_t)kRecPerTile * sizeof(Rec) + (2 * (size_t)bp.parts + 1) * sizeof(uint32_t);
     hipError_t e = hipFuncSetAttribute((const void *)bin_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
     for (int l0 = 0; l0 < n_levels; l0 += group) {

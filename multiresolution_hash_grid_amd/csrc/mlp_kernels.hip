@@ -4,8 +4,10 @@
 // Linear(32, 64), ReLU, Linear(64, 64), ReLU, Linear(64, 4), biases on,
 //   y = W3 relu(W2 relu(W1 e + b1) + b2) + b3,
 // e being the 32 encoded features (L = 16 levels x F = 2) of a point.  It is
-// a dense contraction, so it runs on v_mfma_f32_16x16x16f16: binary16
-// operands, fp32 accumulation.
+// a dense contraction, so it runs on the matrix cores: binary16 operands,
+// fp32 accumulation.  The contractions over features and units (K = 32 and
+// 64) use gfx950's v_mfma_f32_16x16x32_f16, the weight gradients, which
+// contract over the 16 points of a tile, v_mfma_f32_16x16x16f16.
 //
 // Layout.  For D[i][j] = sum_k A[i][k] B[k][j] (16 x 16 x 16), lane l of the
 // wave holds A[l%16][4(l/16) + r], B[4(l/16) + r][l%16] and
@@ -13,7 +15,11 @@
 // output units) and 16 points in the columns of B and D; then the D of one
 // layer, rounded to binary16, is already the B operand of the next layer (the
 // four rows a lane holds are the four k a lane supplies), so activations go
-// from layer to layer in registers.
+// from layer to layer in registers.  The 16 x 16 x 32 shape takes eight k
+// per lane in A and B alike and the same D layout, and a contraction does not
+// depend on which k sits in which slot as long as A and B agree: a lane
+// supplies the k of two 16 x 16 x 16 operands, k-block 2h in slots 0..3 and
+// 2h + 1 in slots 4..7, and the weights are loaded in that order.
 //
 // Forward: the encoder's gather writes the encoding level-major as binary16
 // ([L][n][2], one 64-byte read per point here instead of a 128-byte fp32
@@ -35,6 +41,9 @@
 // kernels add the per-wave partials, in a fixed order, into the caller's fp32
 // gradients.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "device_common.h"
 
@@ -42,6 +51,7 @@ namespace hg {
 namespace {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kIn = 32, kHid = 64, kOut = 4;
@@ -52,6 +62,15 @@ constexpr int kOffW1 = 0, kOffB1 = kOffW1 + kHid * kIn, kOffW2 = kOffB1 + kHid, 
 
 __device__ __forceinline__ float4_t mfma(half4_t a, half4_t b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4_t mfma32(half8_t a, half8_t b, float4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Two 16 x 16 x 16 operands as one 16 x 16 x 32 operand: lo in slots 0..3, hi in 4..7.
+__device__ __forceinline__ half8_t join8(half4_t lo, half4_t hi) {
+    return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 __device__ __forceinline__ half4_t relu_half(float4_t v, uint32_t &mask, int shift) {
@@ -65,9 +84,10 @@ __device__ __forceinline__ half4_t relu_half(float4_t v, uint32_t &mask, int shi
     return h;
 }
 
-// The forward weights as A operands: row = output unit, k = input.
+// The forward weights as 16 x 16 x 32 A operands: row = output unit, slot
+// s of lane group q = input k-block 2h + s / 4, k = 16 (2h + s / 4) + 4 q + s % 4.
 struct FwdWeights {
-    half4_t a1[4][2], a2[4][4], a3[4];
+    half8_t a1[4], a2[4][2], a3[2];
     float4_t b1[4], b2[4], b3;
 };
 
@@ -75,20 +95,23 @@ __device__ __forceinline__ void load_fwd_weights(const MlpParams &mp, int q, int
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int kk = 16 * (s >> 2) + 4 * q + (s & 3);  // k within a 32-wide block
+            w.a1[mb][s] = mp.w1[(16 * mb + c) * kIn + kk];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) w.a2[mb][h][s] = mp.w2[(16 * mb + c) * kHid + 32 * h + kk];
+        }
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) w.a1[mb][kb][r] = mp.w1[(16 * mb + c) * kIn + 16 * kb + 4 * q + r];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) w.a2[mb][kb][r] = mp.w2[(16 * mb + c) * kHid + 16 * kb + 4 * q + r];
             w.b1[mb][r] = mp.b1[16 * mb + 4 * q + r];
             w.b2[mb][r] = mp.b2[16 * mb + 4 * q + r];
         }
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            w.a3[kb][r] = c < kOut ? mp.w3[c * kHid + 16 * kb + 4 * q + r] : (_Float16)0.f;
+        for (int s = 0; s < 8; ++s)
+            w.a3[h][s] = c < kOut ? mp.w3[c * kHid + 32 * h + 16 * (s >> 2) + 4 * q + (s & 3)] : (_Float16)0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) w.b3[r] = q == 0 ? mp.b3[r] : 0.f;
 }
@@ -114,24 +137,19 @@ __device__ __forceinline__ void load_encoding(const _Float16 *__restrict__ stage
 __device__ __forceinline__ void hidden_layers(const FwdWeights &w, const half4_t (&eb)[2], half4_t (&h1)[4],
                                               half4_t (&h2)[4], uint32_t &m1, uint32_t &m2) {
     m1 = m2 = 0;
+    const half8_t e8 = join8(eb[0], eb[1]);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) h1[mb] = relu_half(mfma32(w.a1[mb], e8, w.b1[mb]), m1, 4 * mb);
+    const half8_t h1lo = join8(h1[0], h1[1]), h1hi = join8(h1[2], h1[3]);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-        float4_t acc = w.b1[mb];
-        acc = mfma(w.a1[mb][0], eb[0], acc);
-        acc = mfma(w.a1[mb][1], eb[1], acc);
-        h1[mb] = relu_half(acc, m1, 4 * mb);
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        float4_t acc = w.b2[mb];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = mfma(w.a2[mb][kb], h1[kb], acc);
+        const float4_t acc = mfma32(w.a2[mb][1], h1hi, mfma32(w.a2[mb][0], h1lo, w.b2[mb]));
         h2[mb] = relu_half(acc, m2, 4 * mb);
     }
 }
 
 // Slices of dL/dy whose largest finite magnitude mlp_dy_max_kernel writes.
-constexpr int kDyMaxParts = 256;
+constexpr int kDyMaxParts = 1024;
 
 __device__ __forceinline__ float finite_abs_max(float m, float v) {
     const float a = fabsf(v);
@@ -153,9 +171,33 @@ __global__ __launch_bounds__(256) void mlp_dy_max_kernel(const float4 *__restric
     if (threadIdx.x == 0) parts[blockIdx.x] = __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])));
 }
 
-int mlp_grid(int64_t tiles) {
+// Persistent grids: as many workgroups as the chip holds at once (the
+// kernel's occupancy times the CU count, found once per device and kernel),
+// so that no round of workgroups runs alone at the end; never more than the
+// 16-point tiles need.  1024 workgroups when the occupancy query fails.
+int resident_workgroups(const void *kernel) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void *>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1024;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({dev, kernel});
+    if (it != cache.end()) return it->second;
+    int per_cu = 0, cus = 0;
+    int r = 1024;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kMlpWaves, 0) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 &&
+        cus > 0)
+        r = per_cu * cus;
+    cache[{dev, kernel}] = r;
+    return r;
+}
+
+constexpr int kMaxMlpGrid = 1024;  // the partials workspace is sized for this many workgroups
+
+int mlp_grid(int64_t tiles, const void *kernel) {
     const int64_t want = (tiles + kMlpWaves - 1) / kMlpWaves;
-    return (int)std::min<int64_t>(want, 1024);  // persistent: 4 waves per CU-slot, 4096 waves at most
+    return (int)std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)resident_workgroups(kernel), kMaxMlpGrid}));
 }
 
 // ---------------------------------------------------------------- forward
@@ -177,9 +219,7 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 
         if (t + nwaves < tiles) load_encoding(stage, n, min((t + nwaves) * 16 + c, n - 1), q, eb_next);
         uint32_t m1, m2;
         hidden_layers(w, eb, h1, h2, m1, m2);
-        float4_t o = w.b3;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) o = mfma(w.a3[kb], h2[kb], o);
+        const float4_t o = mfma32(w.a3[1], join8(h2[2], h2[3]), mfma32(w.a3[0], join8(h2[0], h2[1]), w.b3));
         if (q == 0 && ok) *reinterpret_cast<float4 *>(y + p * kOut) = make_float4(o[0], o[1], o[2], o[3]);
     }
 }
@@ -234,20 +274,23 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 
     }
     FwdWeights w;
     load_fwd_weights(mp, q, c, w);
-    // Transposed weights as A operands: row = input unit of the layer, k = its output unit.
-    half4_t t3[4], t2[4][4], t1[2][4];
+    // Transposed weights as A operands: row = input unit of the layer, k = its
+    // output unit (t2, t1: 16 x 16 x 32 slots as the forward's; t3: K = 4
+    // outputs padded to one 16 x 16 x 16 operand).
+    half4_t t3[4];
+    half8_t t2[4][2], t1[2][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            t3[mb][r] = q == 0 ? mp.w3[r * kHid + 16 * mb + c] : (_Float16)0.f;
+        for (int r = 0; r < 4; ++r) t3[mb][r] = q == 0 ? mp.w3[r * kHid + 16 * mb + c] : (_Float16)0.f;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) t2[mb][kb][r] = mp.w2[(16 * kb + 4 * q + r) * kHid + 16 * mb + c];
-        }
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) t1[mb][kb][r] = mp.w1[(16 * kb + 4 * q + r) * kIn + 16 * mb + c];
+            for (int s = 0; s < 8; ++s) {
+                const int k = 32 * h + 16 * (s >> 2) + 4 * q + (s & 3);
+                t2[mb][h][s] = mp.w2[k * kHid + 16 * mb + c];
+                if (mb < 2) t1[mb][h][s] = mp.w1[k * kIn + 16 * mb + c];
+            }
     }
     float4_t gw1[4][2], gw2[4][4], gw3[4];
     float4_t gb1[4], gb2[4], gb3;
@@ -291,19 +334,17 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 
 #pragma unroll
             for (int r = 0; r < 4; ++r) dz2[mb][r] = (_Float16)(((m2 >> (4 * mb + r)) & 1) ? acc[r] : 0.f);
         }
+        const half8_t dz2lo = join8(dz2[0], dz2[1]), dz2hi = join8(dz2[2], dz2[3]);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) acc = mfma(t2[mb][kb], dz2[kb], acc);
+            const float4_t acc = mfma32(t2[mb][1], dz2hi, mfma32(t2[mb][0], dz2lo, float4_t{0.f, 0.f, 0.f, 0.f}));
 #pragma unroll
             for (int r = 0; r < 4; ++r) dz1[mb][r] = (_Float16)(((m1 >> (4 * mb + r)) & 1) ? acc[r] : 0.f);
         }
+        const half8_t dz1lo = join8(dz1[0], dz1[1]), dz1hi = join8(dz1[2], dz1[3]);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) acc = mfma(t1[mb][kb], dz1[kb], acc);
+            const float4_t acc = mfma32(t1[mb][1], dz1hi, mfma32(t1[mb][0], dz1lo, float4_t{0.f, 0.f, 0.f, 0.f}));
             if (ok)
                 *reinterpret_cast<float4 *>(de + p * kIn + 16 * mb + 4 * q) =
                     make_float4(acc[0] * ginv, acc[1] * ginv, acc[2] * ginv, acc[3] * ginv);
@@ -418,19 +459,21 @@ __global__ __launch_bounds__(256) void mlp_reduce2_kernel(const float *__restric
 
 size_t mlp_partials_bytes(int64_t n) {
     const int64_t tiles = (n + 15) / 16;
-    return ((size_t)mlp_grid(tiles) * kMlpWaves + kSplit) * kPartial * sizeof(float) + kDyMaxParts * sizeof(uint32_t);
+    const size_t grid = (size_t)std::max<int64_t>(1, std::min<int64_t>((tiles + kMlpWaves - 1) / kMlpWaves, kMaxMlpGrid));
+    return (grid * kMlpWaves + kSplit) * kPartial * sizeof(float) + kDyMaxParts * sizeof(uint32_t);
 }
 
 hipError_t launch_mlp_forward(const _Float16 *stage, int64_t n, const MlpParams &mp, float *y, hipStream_t stream) {
     const int64_t tiles = (n + 15) / 16;
-    mlp_fwd_kernel<<<mlp_grid(tiles), 64 * kMlpWaves, 0, stream>>>(stage, n, mp, y, tiles);
+    mlp_fwd_kernel<<<mlp_grid(tiles, (const void *)mlp_fwd_kernel), 64 * kMlpWaves, 0, stream>>>(stage, n, mp, y,
+                                                                                                  tiles);
     return hipGetLastError();
 }
 
 hipError_t launch_mlp_backward(const _Float16 *stage, int64_t n, const MlpParams &mp, const float *dy, float *de,
                                float *partials, const MlpGrads &g, hipStream_t stream) {
     const int64_t tiles = (n + 15) / 16;
-    const int grid = mlp_grid(tiles);
+    const int grid = mlp_grid(tiles, (const void *)mlp_bwd_kernel);
     const int nparts = grid * kMlpWaves;
     float *rows = partials + (int64_t)nparts * kPartial;
     uint32_t *dmax = reinterpret_cast<uint32_t *>(rows + (int64_t)kSplit * kPartial);

@@ -1,27 +1,26 @@
 """Summaries of rocprofv3 output for the encoder's passes.
 
     # kernel durations of a --kernel-trace --stats -f csv run that made PASSES
-    # calls of each library entry point
+    # calls of each library entry point (e.g. the benchmark itself)
     python -m multiresolution_hash_grid_amd.profile_summary stats DIR --passes P --command "..." --out FILE.md
 
-    # HBM traffic per pass from --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of the
-    # benchmark and of a plain device copy (the calibration)
-    python -m multiresolution_hash_grid_amd.profile_summary traffic --fetch D1 --write D2 \\
-        --copy-fetch D3 --copy-write D4 --copy-bytes B --passes P --out FILE.json
-
-    # the calibration workload itself: a device-to-device copy of B bytes
-    python -m multiresolution_hash_grid_amd.profile_summary copy --bytes B
-
-    # L2 (TCC) hit rate and request rate per kernel from a --pmc TCC_HIT_sum
-    # TCC_MISS_sum TCC_REQ_sum run, MFMA utilisation from a --pmc MfmaUtil
-    # SQ_INSTS_VALU_MFMA_MOPS_F16 run; durations from kernel-trace --stats runs
-    python -m multiresolution_hash_grid_amd.profile_summary counters --l2 D1 --l2-stats S1 \
-        --mfma D2 --mfma-stats S2 --out FILE.json
+    # per-pass HBM traffic, L2 hit and request rates, MFMA utilisation and
+    # roofline fractions of one configuration, from three runs of
+    # ``python -m multiresolution_hash_grid_amd.profile_workloads NAME --calls K``:
+    #   --stats: rocprofv3 --kernel-trace --stats -f csv
+    #   --pmc1 : rocprofv3 --pmc FETCH_SIZE TCC_REQ_sum -f csv
+    #   --pmc2 : rocprofv3 --pmc WRITE_SIZE TCC_HIT_sum TCC_MISS_sum -f csv
+    #   --mfma : (optional) rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F16 -f csv
+    python -m multiresolution_hash_grid_amd.profile_summary workload NAME --stats D1 --pmc1 D2 --pmc2 D3 \
+        --calls K --command "..." --out profiles/counters_NAME.json
 
 A pass is the group of kernels one library call launches: the forward is the
-gather plus the level-major transpose, the backward the binned path's bin and
-accumulate kernels, once per level group (or the atomic scatter).  Per-pass
-figures weight each kernel by its launches per call.
+gather (plus the level-major transpose, or the MLP head), the backward the
+binned path's bin and accumulate kernels, once per level group (plus the MLP
+head's backward and its reductions).  Per-pass figures weight each kernel by
+its launches per call.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are
+scaled by the factors that make them read the known 256 MiB of the device
+copy each run starts with.
 """
 from __future__ import annotations
 
@@ -35,13 +34,23 @@ import re
 import sys
 
 PASSES = {
-    "forward": ("fwd_f2_kernel", "fwd_f2_pair_kernel", "transpose_kernel"),
-    "backward": ("bin_kernel", "accumulate_kernel", "bwd_f2_kernel"),
+    "forward": ("fwd_f2_kernel", "fwd_f2_pair_kernel", "transpose_kernel", "fwd_generic_kernel",
+                "fwd_generic_pair_kernel", "mlp_fwd_kernel"),
+    "backward": ("bin_kernel", "accumulate_kernel", "bwd_f2_kernel", "bwd_f2_quad_kernel", "bin_generic_kernel",
+                 "bwd_generic_kernel", "bwd_dense_kernel", "mlp_bwd_kernel", "mlp_dy_max_kernel",
+                 "mlp_reduce1_kernel", "mlp_reduce2_kernel"),
 }
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCES = ("device_common.h", "hashgrid_internal.h", "encode_kernels.hip", "binned_common.h",
-           "binned_backward.hip")
-MLP_SOURCES = SOURCES + ("mlp_kernels.hip",)
+CSRC = os.path.join(ROOT, "multiresolution_hash_grid_amd", "csrc")
+HBM_PEAK_BPS = 8000e9                 # MI355X HBM3E, AMD published peak
+L2_REQ_PEAK_PER_S = 8 * 16 * 2.4e9    # 8 XCDs x 16 L2 channels x one request per clock at 2.4 GHz
+COPY_BYTES = 256 << 20
+
+
+def all_sources() -> tuple:
+    """Every file of the library's sources: kernels, their headers and the host
+    code that sizes and launches them."""
+    return tuple(sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp"))))
 
 
 def _code_only(text: str) -> str:
@@ -52,11 +61,12 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def source_digest(files=SOURCES) -> str:
-    """sha256 over the code of the kernel sources (counter figures are only valid for it)."""
+def source_digest(files=None) -> str:
+    """sha256 over the code of the library sources (counter figures are only valid for it)."""
     h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "multiresolution_hash_grid_amd", "csrc", f), encoding="utf-8") as fh:
+    for f in files if files is not None else all_sources():
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(f.encode())
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
@@ -150,100 +160,126 @@ def _avg(vals):
     return sum(vals) / len(vals)
 
 
-def traffic(args) -> None:
-    fetch = _counter_per_dispatch(args.fetch, "FETCH_SIZE")
-    write = _counter_per_dispatch(args.write, "WRITE_SIZE")
-    cf = _counter_per_dispatch(args.copy_fetch, "FETCH_SIZE")
-    cw = _counter_per_dispatch(args.copy_write, "WRITE_SIZE")
-    # The copy moves copy_bytes in and copy_bytes out; counters are in KiB.
-    copy_read_kib = max(max(v) for v in cf.values())
-    copy_write_kib = max(max(v) for v in cw.values())
-    f_scale = args.copy_bytes / (copy_read_kib * 1024.0)
-    w_scale = args.copy_bytes / (copy_write_kib * 1024.0)
-    kernels = {}
-    passes = collections.defaultdict(lambda: {"fetch_bytes": 0.0, "write_bytes": 0.0})
-    for name in set(fetch) | set(write):
-        p = pass_of(name)
-        fv, wv = fetch.get(name, [0.0]), write.get(name, [0.0])
-        fb = _avg(fv) * 1024.0 * f_scale
-        wb = _avg(wv) * 1024.0 * w_scale
-        per_call = len(fv) / args.passes  # launches of this kernel per library call
-        kernels[short_name(name)] = {"pass": p, "fetch_bytes": fb, "write_bytes": wb,
-                                     "launches_per_call": per_call}
-        if p:
-            passes[p]["fetch_bytes"] += fb * per_call
-            passes[p]["write_bytes"] += wb * per_call
-    for p in passes.values():
-        p["hbm_bytes_per_launch"] = p["fetch_bytes"] + p["write_bytes"]
-    rec = {
-        "about": "HBM bytes per call of each entry point from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB "
-                 "per dispatch, times dispatches per call), each scaled by the factor that makes the same "
-                 "counter read the known size of a plain device copy.",
-        "calls_per_run": args.passes,
-        "command_fetch": args.command_fetch, "command_write": args.command_write,
-        "copy_bytes": args.copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
-        "source_sha256": source_digest(), "passes": dict(passes), "kernels": kernels,
-    }
-    with open(args.out, "w") as f:
-        json.dump(rec, f, indent=1)
-    print(json.dumps(rec, indent=1))
-
-
 def _durations_us(d: str) -> dict:
     """{kernel short name: average duration in us} of a --kernel-trace --stats run."""
     return {short_name(r["Name"]): float(r["AverageNs"]) / 1e3
             for r in csv.DictReader(open(_find(d, "kernel_stats.csv")))}
 
 
-def counters(args) -> None:
-    hit = _counter_per_dispatch(args.l2, "TCC_HIT_sum")
-    miss = _counter_per_dispatch(args.l2, "TCC_MISS_sum")
-    req = _counter_per_dispatch(args.l2, "TCC_REQ_sum")
-    dur = _durations_us(args.l2_stats)
-    l2 = {}
-    for name in hit:
-        sn = short_name(name)
-        h, m, r = _avg(hit[name]), _avg(miss.get(name, [0.0])), _avg(req.get(name, [0.0]))
-        us = dur.get(sn)
-        l2[sn] = {"pass": pass_of(name), "hit_rate": h / (h + m) if h + m else None, "requests": r,
-                  "hits": h, "misses": m, "duration_us": us,
-                  "requests_per_s": r / (us * 1e-6) if us else None}
-    util = _counter_per_dispatch(args.mfma, "MfmaUtil")
-    mops = _counter_per_dispatch(args.mfma, "SQ_INSTS_VALU_MFMA_MOPS_F16")
-    mdur = _durations_us(args.mfma_stats)
-    mfma = {}
-    for name in mops:
-        sn = short_name(name)
-        ops = _avg(mops[name])
-        if ops <= 0:
+def _find_copy(per: dict) -> tuple:
+    """(name, KiB per dispatch) of the calibration copy: the largest dispatch
+    of a kernel that is not one of the library's."""
+    best = None
+    for name, vals in per.items():
+        if pass_of(name) is None and not short_name(name).startswith(("fwd_", "bin", "acc", "mlp", "bwd")):
+            v = max(vals)
+            if best is None or v > best[1]:
+                best = (name, v)
+    if best is None:
+        raise ValueError("no calibration copy in the counter run")
+    return best
+
+
+def workload(args) -> None:
+    from multiresolution_hash_grid_amd import profile_workloads as pw
+    w = pw.workload(args.name)
+    alg = pw.algorithmic_bytes(w)
+    dur = _durations_us(args.stats)
+    calls = {short_name(r["Name"]): int(r["Calls"])
+             for r in csv.DictReader(open(_find(args.stats, "kernel_stats.csv")))}
+    fetch = _counter_per_dispatch(args.pmc1, "FETCH_SIZE")
+    req = _counter_per_dispatch(args.pmc1, "TCC_REQ_sum")
+    write = _counter_per_dispatch(args.pmc2, "WRITE_SIZE")
+    hit = _counter_per_dispatch(args.pmc2, "TCC_HIT_sum")
+    miss = _counter_per_dispatch(args.pmc2, "TCC_MISS_sum")
+    mdir = getattr(args, "mfma", None) or args.pmc2
+    util = _counter_per_dispatch(mdir, "MfmaUtil")
+    mops = _counter_per_dispatch(mdir, "SQ_INSTS_VALU_MFMA_MOPS_F16")
+    copy_name, copy_fetch_kib = _find_copy(fetch)
+    if copy_name not in write:
+        raise ValueError(f"the calibration copy {copy_name} is missing from the WRITE_SIZE run")
+    copy_write_kib = max(write[copy_name])
+    f_scale = COPY_BYTES / (copy_fetch_kib * 1024.0)
+    w_scale = COPY_BYTES / (copy_write_kib * 1024.0)
+    kernels = {}
+    passes = {p: collections.defaultdict(float) for p in PASSES}
+    for name in set(fetch) | set(write):
+        p = pass_of(name)
+        if p is None:
             continue
-        us = mdur.get(sn)
-        flops = ops * 512.0  # the counter counts fp16 MFMA work in units of 512 flops
-        mfma[sn] = {"mfma_util_pct": _avg(util[name]) if name in util else None, "fp16_flops": flops,
-                    "duration_us": us, "tflops": flops / (us * 1e-6) / 1e12 if us else None}
+        sn = short_name(name)
+        per_call = calls.get(sn, len(fetch.get(name, write.get(name)))) / args.calls
+        k = {"pass": p, "launches_per_call": per_call, "duration_us": dur.get(sn),
+             "fetch_bytes": _avg(fetch[name]) * 1024.0 * f_scale if name in fetch else None,
+             "write_bytes": _avg(write[name]) * 1024.0 * w_scale if name in write else None,
+             "l2_requests": _avg(req[name]) if name in req else None}
+        if name in hit and name in miss:
+            h, m = _avg(hit[name]), _avg(miss[name])
+            k["l2_hit_rate"] = h / (h + m) if h + m else None
+        if name in mops and _avg(mops[name]) > 0:
+            flops = _avg(mops[name]) * 512.0  # the counter counts fp16 MFMA work in units of 512 flops
+            k["mfma_util_pct"] = _avg(util[name]) if name in util else None
+            k["mfma_fp16_tflops"] = flops / (k["duration_us"] * 1e-6) / 1e12 if k["duration_us"] else None
+        kernels[sn] = k
+        acc = passes[p]
+        acc["time_us"] += per_call * (k["duration_us"] or 0.0)
+        acc["hbm_bytes"] += per_call * ((k["fetch_bytes"] or 0.0) + (k["write_bytes"] or 0.0))
+        acc["fetch_bytes"] += per_call * (k["fetch_bytes"] or 0.0)
+        acc["write_bytes"] += per_call * (k["write_bytes"] or 0.0)
+        acc["l2_requests"] += per_call * (k["l2_requests"] or 0.0)
+        if "l2_hit_rate" in k and k["l2_hit_rate"] is not None:
+            acc["_hits"] += per_call * k["l2_hit_rate"] * (k["l2_requests"] or 0.0)
+    out_passes = {}
+    for p, acc in passes.items():
+        if not acc["time_us"]:
+            continue
+        t = acc["time_us"] * 1e-6
+        a = alg[p] * w.n_points
+        out_passes[p] = {
+            "time_us": acc["time_us"], "points_per_s": w.n_points / t,
+            "algorithmic_bytes_per_point": alg[p], "algorithmic_GBps": a / t / 1e9, "frac": a / t / HBM_PEAK_BPS,
+            "hbm_bytes": acc["hbm_bytes"], "fetch_bytes": acc["fetch_bytes"], "write_bytes": acc["write_bytes"],
+            "hbm_GBps": acc["hbm_bytes"] / t / 1e9, "hbm_frac": acc["hbm_bytes"] / t / HBM_PEAK_BPS,
+            "traffic_over_algorithmic": acc["hbm_bytes"] / a,
+            "l2_requests": acc["l2_requests"], "l2_requests_per_s": acc["l2_requests"] / t,
+            "l2_request_frac": acc["l2_requests"] / t / L2_REQ_PEAK_PER_S,
+            "l2_hit_rate": acc["_hits"] / acc["l2_requests"] if acc["l2_requests"] else None}
     rec = {
-        "about": "Per-kernel L2 (TCC) hit rate, requests per dispatch and request rate of the standard "
-                 "workload's kernels; MFMA utilisation (busy cycles over SIMD cycles) and fp16 MFMA "
-                 "throughput of the MLP head's kernels. Durations are the kernel-trace averages of "
-                 "runs without counters.",
-        "command_l2": args.command_l2, "command_mfma": args.command_mfma,
-        "source_sha256": source_digest(), "mlp_source_sha256": source_digest(MLP_SOURCES),
-        "l2": l2, "mfma": mfma,
+        "about": "Per-pass figures of one configuration from rocprofv3: kernel-trace durations, FETCH_SIZE and "
+                 "WRITE_SIZE (scaled by a 256 MiB device copy in the same run), L2 (TCC) requests and hit rate, "
+                 "MFMA utilisation; algorithmic bytes as the benchmark counts them; peaks: HBM 8 TB/s, L2 "
+                 "307 G requests/s.",
+        "workload": args.name, "points": w.n_points, "calls": args.calls, "command": args.command,
+        "source_sha256": source_digest(),
+        "calibration": {"kernel": short_name(copy_name), "copy_bytes": COPY_BYTES, "fetch_scale": f_scale,
+                        "write_scale": w_scale},
+        "passes": out_passes, "kernels": kernels,
     }
     with open(args.out, "w") as f:
         json.dump(rec, f, indent=1)
-    print(json.dumps(rec, indent=1))
-
-
-def copy(args) -> None:
-    import torch
-    n = args.bytes // 4
-    a = torch.ones(n, device="cuda:0")
-    b = torch.empty_like(a)
-    for _ in range(5):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    print("copied", args.bytes, "bytes x5", flush=True)
+    lines = [f"# Counters: {args.name} ({w.n_points} points, {args.calls} calls of each pass)", "",
+             "Commands:", "", "```", args.command, "```", "",
+             "| pass | time (us) | points/s | algorithmic GB/s | frac of 8 TB/s | HBM bytes | HBM / algorithmic "
+             "| L2 hit | L2 requests/s | frac of L2 request peak |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for p, v in out_passes.items():
+        hr = "-" if v["l2_hit_rate"] is None else f"{v['l2_hit_rate']:.2f}"
+        lines.append(f"| {p} | {v['time_us']:.1f} | {v['points_per_s']:.3g} | {v['algorithmic_GBps']:.0f} | "
+                     f"{v['frac']:.3f} | {v['hbm_bytes'] / 1e6:.1f} MB | {v['traffic_over_algorithmic']:.2f} | {hr} | "
+                     f"{v['l2_requests_per_s'] / 1e9:.0f} G | {v['l2_request_frac']:.2f} |")
+    lines += ["", "| kernel | pass | launches per call | us | fetch MB | write MB | L2 hit | MFMA busy % |",
+              "|---|---|---|---|---|---|---|---|"]
+    for sn, k in sorted(kernels.items(), key=lambda kv: (kv[1]["pass"], kv[0])):
+        f = "-" if k["fetch_bytes"] is None else f"{k['fetch_bytes'] / 1e6:.1f}"
+        wr = "-" if k["write_bytes"] is None else f"{k['write_bytes'] / 1e6:.1f}"
+        hr = "-" if k.get("l2_hit_rate") is None else f"{k['l2_hit_rate']:.2f}"
+        mu = "-" if k.get("mfma_util_pct") is None else f"{k['mfma_util_pct']:.1f}"
+        d = "-" if k["duration_us"] is None else f"{k['duration_us']:.1f}"
+        lines.append(f"| `{sn}` | {k['pass']} | {k['launches_per_call']:.2f} | {d} | {f} | {wr} | {hr} | {mu} |")
+    lines.append("")
+    with open(os.path.splitext(args.out)[0] + ".md", "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def main() -> int:
@@ -256,22 +292,14 @@ def main() -> int:
     s.add_argument("--title", default="rocprofv3 --kernel-trace --stats")
     s.add_argument("--passes", type=int, required=True,
                    help="calls of each entry point in the run (0: list the kernels only)")
-    t = sub.add_parser("traffic")
-    for k in ("fetch", "write", "copy_fetch", "copy_write", "out"):
-        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
-    t.add_argument("--copy-bytes", type=int, required=True)
-    t.add_argument("--passes", type=int, required=True, help="calls of each entry point in the run")
-    t.add_argument("--command-fetch", default="")
-    t.add_argument("--command-write", default="")
-    k = sub.add_parser("counters")
-    for a in ("l2", "l2_stats", "mfma", "mfma_stats", "out"):
-        k.add_argument("--" + a.replace("_", "-"), dest=a, required=True)
-    k.add_argument("--command-l2", default="")
-    k.add_argument("--command-mfma", default="")
-    c = sub.add_parser("copy")
-    c.add_argument("--bytes", type=int, default=256 << 20)
+    k = sub.add_parser("workload")
+    k.add_argument("name")
+    for a in ("stats", "pmc1", "pmc2", "out", "command"):
+        k.add_argument("--" + a, dest=a, required=True)
+    k.add_argument("--calls", type=int, required=True)
+    k.add_argument("--mfma", default=None, help="run with --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F16")
     args = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "counters": counters, "copy": copy}[args.cmd](args)
+    {"stats": stats, "workload": workload}[args.cmd](args)
     return 0
 
 

@@ -35,18 +35,28 @@ def test_l2_request_peak_is_the_chip_derivation():
 
 
 def test_counter_summaries_missing_or_stale(tmp_path, monkeypatch):
-    monkeypatch.setattr(bench, "COUNTERS_FILE", str(tmp_path / "absent.json"))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
-    assert bench.load_counters() == (None, None)
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.load_counters("standard") is None
     assert bench.load_traffic("backward") is None
-    assert bench.cache_summary(None) is None
-    stale = tmp_path / "stale.json"
-    stale.write_text('{"source_sha256": "0", "mlp_source_sha256": "0", "l2": {"k": {}}, "mfma": {"m": {}},'
-                     ' "passes": {"backward": {"hbm_bytes_per_launch": 1.0}}}')
-    monkeypatch.setattr(bench, "COUNTERS_FILE", str(stale))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stale))
-    assert bench.load_counters() == (None, None)       # taken on other kernel sources
+    assert bench.counter_summary(None) is None
+    (tmp_path / "counters_standard.json").write_text(
+        '{"source_sha256": "0", "passes": {"backward": {"hbm_bytes": 1.0}}, "kernels": {}}')
+    assert bench.load_counters("standard") is None       # taken on other library sources
     assert bench.load_traffic("backward") is None
+
+
+def test_counter_summary_fields(tmp_path, monkeypatch):
+    from multiresolution_hash_grid_amd import profile_summary as ps
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    p = {"hbm_bytes": 7.0, "hbm_GBps": 1.0, "hbm_frac": 0.1, "traffic_over_algorithmic": 2.0, "l2_hit_rate": 0.5,
+         "l2_requests_per_s": 3.0, "l2_request_frac": 0.2, "time_us": 10.0}
+    rec = {"source_sha256": ps.source_digest(), "passes": {"backward": p},
+           "kernels": {"mlp_bwd_kernel": {"pass": "backward", "mfma_util_pct": 24.0, "mfma_fp16_tflops": 300.0}}}
+    import json
+    (tmp_path / "counters_standard.json").write_text(json.dumps(rec))
+    assert bench.load_traffic("backward") == 7.0
+    cs = bench.counter_summary(bench.load_counters("standard"))
+    assert cs["backward"]["l2_hit_rate"] == 0.5 and cs["backward"]["mfma"]["mlp_bwd_kernel"]["util_pct"] == 24.0
 
 
 def test_cpu_model_is_reported():

@@ -19,6 +19,8 @@ def test_kernel_names_and_passes():
     assert ps.pass_of("hg::(anonymous namespace)::transpose_kernel<2, true>(float const*)") == "forward"
     assert ps.short_name("_ZN2hg12_GLOBAL__N_114mlp_bwd_kernelEPKDF16_lNS_9MlpParamsEP") == "mlp_bwd_kernel"
     assert ps.pass_of("void at::native::vectorized_elementwise_kernel<4>(int)") is None
+    assert ps.pass_of("hg::(anonymous namespace)::mlp_dy_max_kernel(float4 const*)") == "backward"
+    assert ps.pass_of("hg::(anonymous namespace)::fwd_generic_pair_kernel<3, 4, 0>(float const*)") == "forward"
 
 
 def _write(path, rows, fields):
@@ -30,43 +32,58 @@ def _write(path, rows, fields):
         w.writerows(rows)
 
 
-def test_counters_summary(tmp_path):
-    k = "hg::(anonymous namespace)::bin_kernel(float const*, long)"
-    m = "_ZN2hg12_GLOBAL__N_114mlp_fwd_kernelEPKDF16_lNS_9MlpParamsEP"
-    cfields = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
-    rows = []
-    for did in range(1, 7):   # six dispatches; the summary drops the first two as cold
-        hit = 900.0 if did > 2 else 0.0
-        rows += [{"Dispatch_Id": did, "Kernel_Name": k, "Counter_Name": "TCC_HIT_sum", "Counter_Value": hit},
-                 {"Dispatch_Id": did, "Kernel_Name": k, "Counter_Name": "TCC_MISS_sum", "Counter_Value": 100.0},
-                 {"Dispatch_Id": did, "Kernel_Name": k, "Counter_Name": "TCC_REQ_sum", "Counter_Value": 1000.0}]
-    _write(str(tmp_path / "l2"), rows, cfields)
-    mrows = [{"Dispatch_Id": d, "Kernel_Name": m, "Counter_Name": c, "Counter_Value": v}
-             for d in range(1, 4) for c, v in (("MfmaUtil", 40.0), ("SQ_INSTS_VALU_MFMA_MOPS_F16", 1e6))]
-    _write(str(tmp_path / "mfma"), mrows, cfields)
-    sfields = ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"]
-    _write(str(tmp_path / "s1"), [{"Name": k, "Calls": 6, "AverageNs": 1000.0, "MinNs": 1, "MaxNs": 1}], sfields)
-    _write(str(tmp_path / "s2"), [{"Name": m, "Calls": 3, "AverageNs": 2000.0, "MinNs": 1, "MaxNs": 1}], sfields)
-    out = str(tmp_path / "c.json")
-    ps.counters(types.SimpleNamespace(l2=str(tmp_path / "l2"), l2_stats=str(tmp_path / "s1"),
-                                      mfma=str(tmp_path / "mfma"), mfma_stats=str(tmp_path / "s2"), out=out,
-                                      command_l2="", command_mfma=""))
+def test_workload_summary(tmp_path):
+    # A synthetic run of the standard workload with K = 2 calls of each pass:
+    # the calibration copy (256 MiB read and written; the counters read half of
+    # it for FETCH_SIZE, all of it for WRITE_SIZE), one gather and one
+    # transpose per forward, two bin and two accumulate launches per backward.
+    K = 2
+    copy = "void at::native::copy_kernel(float*)"
+    ks = {"hg::(anonymous namespace)::fwd_f2_pair_kernel<0, 4, false, float, false>(float const*)": (1, 100e3),
+          "hg::(anonymous namespace)::transpose_kernel<2, true>(float const*)": (1, 10e3),
+          "hg::(anonymous namespace)::bin_kernel(float const*, long)": (2, 30e3),
+          "void hg::binned::accumulate_kernel<1024, hg::(anonymous namespace)::StdPolicy>(hg::BinParams)": (2, 50e3)}
+    cf = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    r1, r2, did = [], [], 0
+    did += 1
+    r1 += [{"Dispatch_Id": did, "Kernel_Name": copy, "Counter_Name": "FETCH_SIZE", "Counter_Value": 131072.0}]
+    r2 += [{"Dispatch_Id": did, "Kernel_Name": copy, "Counter_Name": "WRITE_SIZE", "Counter_Value": 262144.0}]
+    for name, (per, _) in ks.items():
+        for _ in range(per * K):
+            did += 1
+            r1 += [{"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": "FETCH_SIZE", "Counter_Value": 1024.0},
+                   {"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": "TCC_REQ_sum", "Counter_Value": 1e6}]
+            r2 += [{"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": "WRITE_SIZE", "Counter_Value": 2048.0},
+                   {"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": "TCC_HIT_sum", "Counter_Value": 9e5},
+                   {"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": "TCC_MISS_sum", "Counter_Value": 1e5}]
+    _write(str(tmp_path / "p1"), r1, cf)
+    _write(str(tmp_path / "p2"), r2, cf)
+    sf = ["Name", "Calls", "AverageNs", "MinNs", "MaxNs"]
+    _write(str(tmp_path / "st"), [{"Name": n, "Calls": per * K, "AverageNs": ns, "MinNs": 1, "MaxNs": 1}
+                                  for n, (per, ns) in ks.items()], sf)
+    out = str(tmp_path / "counters_standard.json")
+    ps.workload(types.SimpleNamespace(name="standard", stats=str(tmp_path / "st"), pmc1=str(tmp_path / "p1"),
+                                      pmc2=str(tmp_path / "p2"), calls=K, command="cmd", out=out))
     rec = json.load(open(out))
-    b = rec["l2"]["bin_kernel"]
-    assert b["pass"] == "backward" and abs(b["hit_rate"] - 0.9) < 1e-12
-    assert b["requests"] == 1000.0 and abs(b["requests_per_s"] - 1e9) < 1e-3   # 1000 in 1 us
-    f = rec["mfma"]["mlp_fwd_kernel"]
-    assert f["mfma_util_pct"] == 40.0 and f["fp16_flops"] == 512e6
-    assert abs(f["tflops"] - 512e6 / 2e-6 / 1e12) < 1e-9
+    assert rec["calibration"]["fetch_scale"] == 2.0 and rec["calibration"]["write_scale"] == 1.0
+    f, b = rec["passes"]["forward"], rec["passes"]["backward"]
+    assert f["time_us"] == 110.0 and b["time_us"] == 160.0
+    # per launch 1024 KiB fetched (x2 calibration) and 2048 KiB written: 4 MiB per launch
+    assert f["hbm_bytes"] == 2 * (4 << 20) and b["hbm_bytes"] == 4 * (4 << 20)
+    n = 1 << 18
+    assert abs(f["frac"] - 1164 * n / 110e-6 / 8e12) < 1e-12
+    assert abs(b["l2_hit_rate"] - 0.9) < 1e-12 and b["l2_requests"] == 4e6
+    assert os.path.exists(str(tmp_path / "counters_standard.md"))
 
 
 def test_committed_summaries_parse():
-    t = json.load(open(os.path.join(ROOT, "profiles", "traffic_standard.json")))
-    assert {"forward", "backward"} <= set(t["passes"])
-    c = json.load(open(os.path.join(ROOT, "profiles", "counters_standard_mlp.json")))
-    gather = [k for k in c["l2"] if k.startswith("fwd_f2_pair_kernel<0, 4, false, float")]
-    assert len(gather) == 1 and 0.0 <= c["l2"][gather[0]]["hit_rate"] <= 1.0
-    assert set(c["mfma"]) >= {"mlp_fwd_kernel", "mlp_bwd_kernel"}
+    names = [f for f in os.listdir(os.path.join(ROOT, "profiles")) if f.startswith("counters_") and
+             f.endswith(".json")]
+    for fn in names:
+        rec = json.load(open(os.path.join(ROOT, "profiles", fn)))
+        assert set(rec["passes"]) <= {"forward", "backward"} and rec["passes"]
+        for p in rec["passes"].values():
+            assert p["time_us"] > 0 and p["hbm_bytes"] > 0 and 0 < p["frac"] < 1.5
 
 
 def test_source_digest_ignores_comments_and_layout():
