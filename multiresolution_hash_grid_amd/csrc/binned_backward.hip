@@ -76,7 +76,7 @@ using namespace binned;
 constexpr int kBinThreads = kBinTile / 2;  // 512
 constexpr int kPtsPerThread = kBinTile / kBinThreads;  // 2
 constexpr int kRecPerTile = kBinTile * 4;              // 4 corner pairs per point
-constexpr int kLevelsPerBlock = 4;                     // levels per bin workgroup
+constexpr int kLevelsPerBlock = 4;                     // levels per bin workgroup (even)
 
 // One corner-pair or single-corner record (see the packing above); 4-byte aligned, 12 bytes.
 struct Rec12 {
@@ -106,9 +106,7 @@ __device__ __forceinline__ Rec single_record(uint32_t lo, float A, float B) {
 struct Pairs {
     uint32_t part[4];
     Rec rec[4];
-    uint32_t nrec;          // 4, or 0 / 4 inside a pre-reduced run of lanes
-    uint32_t split_idx[4];  // table entry of an x+1 corner outside the pair's partition, or ~0u
-    float2 split_val[4];
+    uint32_t nrec;          // 4 or 0 (0: not binned, or inside a pre-reduced run of lanes)
     float dabs;             // max(|g_0|, |g_1|)
 };
 
@@ -137,6 +135,8 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
     const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 14u);
     // f_x * 2^23 (exact for positions >= 1; the first voxel's fraction rounds)
     const uint32_t fx23 = min(__float2uint_rn(a0 * 8388608.f), 8388607u);
+    const float wx0 = 1.f - a0;
+    uint32_t splits = 0;  // bit c: pair c's x+1 corner lies outside its partition
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const uint32_t dy = (uint32_t)(c >> 1), dz = (uint32_t)(c & 1);
@@ -146,35 +146,61 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
         const float wyz = (dy ? a1 : 1.f - a1) * (dz ? a2 : 1.f - a2);
         const float A = wyz * d0, B = wyz * d1;
         out.part[c] = p0;
-        if (valid && !fin) {
-            unsafeAtomicAdd(glevel + 2 * i0, (1.f - a0) * A);
-            unsafeAtomicAdd(glevel + 2 * i0 + 1, (1.f - a0) * B);
+        // Branch-free: a pair whose x+1 corner lies in another partition keeps
+        // only its x corner, with f_x = 0 and the weight 1 - f_x folded in
+        // (times 1 is exact, so the pair values are A and B themselves).
+        const bool split = (i1 >> bp.s_log2) != p0;
+        const float s = split ? wx0 : 1.f;
+        out.rec[c] = pack_record(i0 & smask, split ? 0u : t, split ? 0u : fx23, s * A, s * B);
+        splits |= split ? 1u << c : 0u;
+    }
+    if (!(valid && fin)) splits = 0;
+    if (valid && !fin) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t dy = (uint32_t)(c >> 1), dz = (uint32_t)(c & 1);
+            const uint32_t K = (hy0 + dy * kPrimeY) ^ (hz0 + dz * kPrimeZ);
+            const uint32_t i0 = (cx0 ^ K) & bp.mask, i1 = (cx1 ^ K) & bp.mask;
+            const float wyz = (dy ? a1 : 1.f - a1) * (dz ? a2 : 1.f - a2);
+            const float A = wyz * d0, B = wyz * d1;
+            unsafeAtomicAdd(glevel + 2 * i0, wx0 * A);
+            unsafeAtomicAdd(glevel + 2 * i0 + 1, wx0 * B);
             unsafeAtomicAdd(glevel + 2 * i1, a0 * A);
             unsafeAtomicAdd(glevel + 2 * i1 + 1, a0 * B);
-            out.rec[c] = Rec{0u, 0u, 0u};
-            out.split_idx[c] = ~0u;
-            out.split_val[c] = make_float2(0.f, 0.f);
-        } else if ((i1 >> bp.s_log2) == p0) {
-            out.rec[c] = pack_record(i0 & smask, t, fx23, A, B);
-            out.split_idx[c] = ~0u;
-            out.split_val[c] = make_float2(0.f, 0.f);
-        } else {
-            // f_x = 0 in the record: only the x corner, with its weight folded in.
-            const float w0 = 1.f - a0;
-            out.rec[c] = pack_record(i0 & smask, 0u, 0u, w0 * A, w0 * B);
-            out.split_idx[c] = i1;
-            out.split_val[c] = make_float2(a0 * A, a0 * B);
         }
     }
+    // The x+1 corners outside their pair's partition, added with atomics by a
+    // lane that keeps its pair records (recomputed here rather than held in
+    // registers across the wave pre-reduction).
+    auto add_splits = [&]() {
+        if (!splits) return;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (!((splits >> c) & 1u)) continue;
+            const uint32_t dy = (uint32_t)(c >> 1), dz = (uint32_t)(c & 1);
+            const uint32_t K = (hy0 + dy * kPrimeY) ^ (hz0 + dz * kPrimeZ);
+            const uint32_t i1 = (cx1 ^ K) & bp.mask;
+            const float wyz = (dy ? a1 : 1.f - a1) * (dz ? a2 : 1.f - a2);
+            const float A = wyz * d0, B = wyz * d1;
+            unsafeAtomicAdd(glevel + 2 * i1, a0 * A);
+            unsafeAtomicAdd(glevel + 2 * i1 + 1, a0 * B);
+        }
+    };
     // Wave pre-reduction of runs of consecutive lanes in one voxel.
     const int lane = threadIdx.x & 63;
-    // Every lane takes part in the shuffles (a short-circuited shuffle would read inactive lanes).
-    const int32_t u0 = __shfl_up(v0, 1, 64), u1 = __shfl_up(v1, 1, 64), u2 = __shfl_up(v2, 1, 64);
-    const int prev_fin = __shfl_up((int)fin, 1, 64);
+    // Every lane takes part in the shifts (a short-circuited shift would read
+    // inactive lanes).  DPP wave_shr:1: lane i reads lane i - 1's value, lane 0
+    // keeps its own (it never continues a run).
+    auto up1 = [](int32_t v) { return __builtin_amdgcn_update_dpp(v, v, 0x138, 0xF, 0xF, false); };
+    const int32_t u0 = up1(v0), u1 = up1(v1), u2 = up1(v2);
+    const int prev_fin = up1((int)fin);
     // Points with non-finite upstream values stay runs of one (they are not binned).
     const bool same = valid && fin && prev_fin && lane > 0 && u0 == v0 && u1 == v1 && u2 == v2;
     const uint64_t dup = __ballot(same);
-    if (dup == 0) return;  // wave-uniform: no two neighbouring points share a voxel
+    if (dup == 0) {  // wave-uniform: no two neighbouring points share a voxel
+        add_splits();
+        return;
+    }
     const uint64_t heads = ~dup, tails = (heads >> 1) | (1ull << 63);
     const int start = 63 - __builtin_clzll(heads & ((2ull << lane) - 1ull));  // first lane of this lane's run
     const int end = __builtin_ctzll(tails & (~0ull << lane));                // last lane of this lane's run
@@ -192,11 +218,13 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
         wbuf[(8 + 2 * c + 1) * 64 + lane] = w1 * d1;
     }
     wave_lds_fence();
-    if (start == end) return;  // a run of one lane keeps its pair records
+    if (start == end) {  // a run of one lane keeps its pair records
+        add_splits();
+        return;
+    }
     // A run of m >= 2 lanes emits 8 single-corner records in place of 4 m pair
-    // records: 4 from its first lane, 4 from its last.
-#pragma unroll
-    for (int c = 0; c < 4; ++c) out.split_idx[c] = ~0u;
+    // records: 4 from its first lane, 4 from its last (the run sums hold the
+    // x+1 corners, so no lane of the run adds them separately).
     const bool first = lane == start;
     out.nrec = first || lane == end ? 4u : 0u;
     if (!out.nrec) return;
@@ -252,10 +280,14 @@ __device__ __forceinline__ void load_points(const float *__restrict__ x, int64_t
         if (!kDout) continue;
         const float *drow = dout + q * dstride + 2 * lfirst;
         if (vec) {
-            const float4 a = *reinterpret_cast<const float4 *>(drow);
-            const float4 b = *reinterpret_cast<const float4 *>(drow + 4);
-            tp.dv[k][0][0] = a.x; tp.dv[k][0][1] = a.y; tp.dv[k][1][0] = a.z; tp.dv[k][1][1] = a.w;
-            tp.dv[k][2][0] = b.x; tp.dv[k][2][1] = b.y; tp.dv[k][3][0] = b.z; tp.dv[k][3][1] = b.w;
+#pragma unroll
+            for (int h = 0; h < kLevelsPerBlock / 2; ++h) {
+                const float4 a = *reinterpret_cast<const float4 *>(drow + 4 * h);
+                tp.dv[k][2 * h][0] = a.x;
+                tp.dv[k][2 * h][1] = a.y;
+                tp.dv[k][2 * h + 1][0] = a.z;
+                tp.dv[k][2 * h + 1][1] = a.w;
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < kLevelsPerBlock; ++j) {
@@ -283,18 +315,24 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
     const int tile = slot.tile;
     const int gb = slot.block * kLevelsPerBlock;
     const int nlev = min(bp.group - gb, kLevelsPerBlock);
-    // The wave pre-reduction borrows the stage before the records are sorted into it.
-    static_assert(kBinThreads / 64 * 16 * 64 * sizeof(float) <= sizeof(Rec) * kRecPerTile, "stage too small");
-    float *wbuf = reinterpret_cast<float *>(stage) + (threadIdx.x >> 6) * (16 * 64);
+    // Each wave copies its own slice of the sorted stage out to the records,
+    // and its wave pre-reduction parks its values in that same slice: a wave
+    // starts the next level while the others still copy theirs, with no
+    // barrier between the levels (the next level's sorted writes into the
+    // stage come after the barrier that follows every wave's counting).
+    constexpr int kWaveRecs = kRecPerTile / (kBinThreads / 64);
+    static_assert(16 * 64 * sizeof(float) <= kWaveRecs * sizeof(Rec), "wave slice too small");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float *wbuf = reinterpret_cast<float *>(stage + wave * kWaveRecs);
     TilePoints tp;
     load_points<true>(x, n, dout, dstride, tile, bp.level0 + gb, nlev, tp);
+    for (int i = threadIdx.x; i < bp.parts; i += kBinThreads) cnt[i] = 0;
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < kLevelsPerBlock; ++j) {
         if (j >= nlev) break;
         const int g = gb + j;
         const int l = bp.level0 + g;
-        for (int i = threadIdx.x; i < bp.parts; i += kBinThreads) cnt[i] = 0;
-        __syncthreads();
         Pairs pr[kPtsPerThread];
         uint32_t rank[kPtsPerThread][4];
         float dm = 0.f;
@@ -304,14 +342,10 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
                        grad + ((uint64_t)l << bp.log2_table_size) * 2, pr[k]);
             if (tp.valid[k]) dm = fmaxf(dm, pr[k].dabs);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) rank[k][c] = c < (int)pr[k].nrec ? atomicAdd(&cnt[pr[k].part[c]], 1u) : 0u;
+            for (int c = 0; c < 4; ++c) rank[k][c] = 0u;
+            if (pr[k].nrec) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (tp.valid[k] && pr[k].split_idx[c] != ~0u) {
-                    float *e = grad + (((uint64_t)l << bp.log2_table_size) + pr[k].split_idx[c]) * 2;
-                    unsafeAtomicAdd(e, pr[k].split_val[c].x);
-                    unsafeAtomicAdd(e + 1, pr[k].split_val[c].y);
-                }
+                for (int c = 0; c < 4; ++c) rank[k][c] = atomicAdd(&cnt[pr[k].part[c]], 1u);
             }
         }
         for (int off = 32; off > 0; off >>= 1) dm = fmaxf(dm, __shfl_xor(dm, off, 64));
@@ -329,15 +363,31 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
         for (int i = threadIdx.x; i <= bp.parts; i += kBinThreads) runs[i] = base[i];
 #pragma unroll
         for (int k = 0; k < kPtsPerThread; ++k) {
+            if (pr[k].nrec) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (c < (int)pr[k].nrec) stage[base[pr[k].part[c]] + rank[k][c]] = pr[k].rec[c];
+                for (int c = 0; c < 4; ++c) stage[base[pr[k].part[c]] + rank[k][c]] = pr[k].rec[c];
+            }
         }
+        // The scan has consumed the counts: clear them for the next level.
+        for (int i = threadIdx.x; i < bp.parts; i += kBinThreads) cnt[i] = 0;
         __syncthreads();
         const uint32_t total = base[bp.parts];
         Rec *trec = sp.records + (int64_t)g * bp.level_records + (int64_t)tile * kRecPerTile;
-        for (uint32_t i = threadIdx.x; i < total; i += kBinThreads) trec[i] = stage[i];
-        __syncthreads();
+        const uint32_t w0 = (uint32_t)(wave * kWaveRecs), w1 = min(total, w0 + (uint32_t)kWaveRecs);
+        if (w1 > w0) {
+            // The slice as 16-byte words (slices start at multiples of 16 bytes;
+            // a record region is 16-byte aligned when the workspace is).
+            const uint32_t words = (w1 - w0) * 3;  // dwords
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(stage + w0);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(trec + w0);
+            uint32_t i = 0;
+            if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                for (uint32_t q = lane; q < words / 4; q += 64)
+                    reinterpret_cast<uint4 *>(dst)[q] = reinterpret_cast<const uint4 *>(src)[q];
+                i = words & ~3u;
+            }
+            for (uint32_t q = i + lane; q < words; q += 64) dst[q] = src[q];
+        }
     }
 }
 
