@@ -191,6 +191,17 @@ __device__ __forceinline__ void build_run_map(typename MapVec<PPL>::T *map, uint
     wave_lds_fence();
 }
 
+// An empty use of a value's registers: the compiler waits here for the load
+// that writes them.
+template <class T>
+__device__ __forceinline__ void hold_registers(const T &v) {
+    static_assert(sizeof(T) % 4 == 0, "whole dwords");
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"v"(w[i]));
+}
+
 template <int THREADS, class P>
 __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space<typename P::Rec> sp,
                                                             float *__restrict__ grad) {
@@ -253,7 +264,8 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
         if (chunk + THREADS < bp.tiles) load_run(chunk + THREADS, s_next, len_next);
         const uint32_t incl = wave_inclusive_scan(len);
         const uint32_t pre = incl - len;
-        const uint32_t total = __shfl(incl, 63, 64);
+        // wave-uniform, and known to be: the record loop below is then scalar
+        const uint32_t total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
         // Records of the chunk's tiles, relative to the first of them.
         const Rec *trec = grec + (int64_t)chunk * kRecPerTile;
         offs[wave][lane] = tl * kRecPerTile + (int32_t)s - (int32_t)pre;
@@ -270,28 +282,47 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
             carry = (uint32_t)__popcll(__ballot(pre <= w0)) - 1u;
             build_run_map<PPL>(map, w0, pre, len);
         };
-        if (total) open_window(0);
-        Rec cur[kAccBatch], nxt[kAccBatch];
+        // Batches alternate between two register sets, so a batch's loads
+        // stay in flight while the previous batch is added (copying the
+        // next batch into the current one would wait for its loads).
+        constexpr uint32_t kStep = 64 * kAccBatch;
+        Rec ra[kAccBatch], rb[kAccBatch];
+        auto request = [&](Rec(&r)[kAccBatch], uint32_t b) {
+            // The batches in flight already have their addresses: the map may move on.
+            if (b > 0 && b < total && b % kMapWindow == 0) open_window(b);
+            // Every lane loads, also past the end (the last record again, to be
+            // ignored), so the number of loads in flight is fixed and the adds
+            // wait only for their own batch.
 #pragma unroll
-        for (int u = 0; u < kAccBatch; ++u) {
-            const uint32_t i = u * 64 + lane;
-            if (i < total) cur[u] = fetch(i);
-        }
-        for (uint32_t b0 = 0; b0 < total; b0 += 64 * kAccBatch) {
-            const uint32_t b1 = b0 + 64 * kAccBatch;
-            // The batch in flight already has its addresses: the map may move on.
-            if (b1 < total && b1 % kMapWindow == 0) open_window(b1);
+            for (int u = 0; u < kAccBatch; ++u) r[u] = fetch(min(b + u * 64 + lane, total - 1));
+        };
+        // Each record is marked as used before the lanes past the end are
+        // masked off: a wait for its load inside a block the wave may skip
+        // would leave the compiler unsure what is in flight, and it would
+        // then wait for every load.
+        auto add = [&](const Rec(&r)[kAccBatch], uint32_t b) {
 #pragma unroll
             for (int u = 0; u < kAccBatch; ++u) {
-                const uint32_t i = b1 + u * 64 + lane;
-                if (i < total) nxt[u] = fetch(i);
+                hold_registers(r[u]);
+                if (b + u * 64 + lane < total) P::apply(slice, r[u], k, smask);
             }
-#pragma unroll
-            for (int u = 0; u < kAccBatch; ++u)
-                if (b0 + u * 64 + lane < total) P::apply(slice, cur[u], k, smask);
-#pragma unroll
-            for (int u = 0; u < kAccBatch; ++u) cur[u] = nxt[u];
+        };
+        if (total) {
+            open_window(0);
+            request(ra, 0);
+            request(rb, kStep);
+            for (uint32_t b0 = 0;; b0 += 2 * kStep) {
+                add(ra, b0);
+                if (b0 + kStep >= total) break;
+                request(ra, b0 + 2 * kStep);
+                add(rb, b0 + kStep);
+                if (b0 + 2 * kStep >= total) break;
+                request(rb, b0 + 3 * kStep);
+            }
         }
+        // The last batch requested is never added: wait for it here, so that
+        // the next chunk's loop does not inherit loads in flight.
+        __builtin_amdgcn_s_waitcnt(0);
         wave_lds_fence();
     }
     __syncthreads();
