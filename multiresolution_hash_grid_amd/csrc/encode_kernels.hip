@@ -165,6 +165,10 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
             e[u][2] = corner((cx ^ hy1 ^ hz0) & mask);
             e[u][3] = corner((cx ^ hy1 ^ hz1) & mask);
         }
+        // All U points' gathers are issued before the first blend waits for
+        // its loads (left to itself the scheduler interleaves them, which
+        // keeps only one point's four loads in flight per lane).
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float wy0 = 1.f - a1[u], wz0 = 1.f - a2[u];
