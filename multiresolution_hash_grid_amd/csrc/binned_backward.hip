@@ -39,21 +39,25 @@
 // low s bits of the x coordinate are all ones, e.g. x = -1) keeps the x
 // corner in its record and adds the x+1 corner with a global fp32 atomic.
 //
-// Record packing (96 bits; the records are three quarters of the backward's
-// memory traffic, written once and read once):
-//   bits  0..12  lo0, the x corner's index inside the partition (s <= 13);
-//   bits 13..16  t = min(trailing ones of v_x, 14): the x+1 corner's index is
+// Record packing (three 32-bit words; the records are three quarters of the
+// backward's memory traffic, written once and read once):
+//   words 0, 1   w_y w_z g_0 and w_y w_z g_1, each an fp32 value rounded to
+//                nearest on its 4 lowest mantissa bits (relative error
+//                <= 2^-21, far inside the gradient's 1e-5 bound); the freed
+//                low 4 bits hold bits 0..3 (word 0) and 4..7 (word 1) of f_x;
+//   word 2       bits 0..14 bits 8..22 of f_x * 2^23, bits 15..27 lo0, bits
+//                28..31 t, where
+//     f_x * 2^23 is exact, as f_x is a multiple of the ulp of the fp32
+//                position, >= 2^-23 once the position is >= 1 (below 1, i.e.
+//                in the first voxel, it is rounded to 2^-24);
+//     lo0        is the x corner's index inside the partition (s <= 13);
+//     t          = min(trailing ones of v_x, 14): the x+1 corner's index is
 //                lo0 XOR (2^(t+1) - 1) within the partition, because
 //                v_x XOR (v_x + 1) = 2^(t+1) - 1 and the x prime is 1 (the
-//                cap is exact as partitions have at most 2^13 entries);
-//   bits 17..39  f_x * 2^23: exact, as f_x is a multiple of the ulp of the
-//                fp32 position, >= 2^-23 once the position is >= 1 (below 1,
-//                i.e. in the first voxel, it is rounded to 2^-24);
-//   bits 40..67  w_y w_z g_0 and bits 68..95 w_y w_z g_1, each an fp32 value
-//                rounded to nearest on its 4 lowest mantissa bits (relative
-//                error <= 2^-21, far inside the gradient's 1e-5 bound).
-// t = 15 marks a single-corner record instead: bits 0..12 the corner's index
-// in the partition, words 1 and 2 its two fp32 sums.
+//                cap is exact as partitions have at most 2^13 entries).
+// t = 15 marks a single-corner record instead: words 0 and 1 are its two
+// fp32 sums, unrounded, and word 2 holds only lo0 and t.  Each field is one
+// or two instructions to pack and to unpack.
 //
 // Wave pre-reduction: the 64 lanes of a wave hold 64 consecutive points.
 // Where consecutive points fall in the same voxel of a level (coarse levels
@@ -86,19 +90,18 @@ static_assert(sizeof(Rec12) == kRecordBytes, "records are 12 bytes");
 using Rec = Rec12;
 using StdSpace = binned::Space<Rec>;
 
-// fp32 bits rounded to nearest on the 4 lowest mantissa bits, as 28 bits.
-__device__ __forceinline__ uint32_t pack28(float v) { return (__float_as_uint(v) + 8u) >> 4; }
-__device__ __forceinline__ float unpack28(uint32_t v) { return __uint_as_float(v << 4); }
+// fp32 bits rounded to nearest on the 4 lowest mantissa bits, which then hold n.
+__device__ __forceinline__ uint32_t round28(float v, uint32_t n) { return ((__float_as_uint(v) + 8u) & ~0xFu) | n; }
 
-__device__ __forceinline__ Rec pack_record(uint32_t lo0, uint32_t t, uint32_t fx23, float A, float B) {
-    const uint32_t a28 = pack28(A), b28 = pack28(B);
-    return Rec{lo0 | (t << 13) | (fx23 << 17), (fx23 >> 15) | (a28 << 8), (a28 >> 24) | (b28 << 4)};
+// A pair record; head = t << 28 | (f_x 2^23) >> 8, n0 / n1 = bits 0..3 / 4..7 of f_x 2^23.
+__device__ __forceinline__ Rec pack_record(uint32_t lo0, uint32_t head, uint32_t n0, uint32_t n1, float A, float B) {
+    return Rec{round28(A, n0), round28(B, n1), (lo0 << 15) | head};
 }
 
 constexpr uint32_t kSingle = 15u;  // t of a single-corner record
 
 __device__ __forceinline__ Rec single_record(uint32_t lo, float A, float B) {
-    return Rec{lo | (kSingle << 13), __float_as_uint(A), __float_as_uint(B)};
+    return Rec{__float_as_uint(A), __float_as_uint(B), (kSingle << 28) | (lo << 15)};
 }
 
 // The records of one point at one level: the four corner pairs (dy, dz), or
@@ -135,6 +138,7 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
     const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 14u);
     // f_x * 2^23 (exact for positions >= 1; the first voxel's fraction rounds)
     const uint32_t fx23 = min(__float2uint_rn(a0 * 8388608.f), 8388607u);
+    const uint32_t head = (t << 28) | (fx23 >> 8), n0 = fx23 & 0xFu, n1 = (fx23 >> 4) & 0xFu;
     const float wx0 = 1.f - a0;
     uint32_t splits = 0;  // bit c: pair c's x+1 corner lies outside its partition
 #pragma unroll
@@ -151,7 +155,7 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
         // (times 1 is exact, so the pair values are A and B themselves).
         const bool split = (i1 >> bp.s_log2) != p0;
         const float s = split ? wx0 : 1.f;
-        out.rec[c] = pack_record(i0 & smask, split ? 0u : t, split ? 0u : fx23, s * A, s * B);
+        out.rec[c] = pack_record(i0 & smask, split ? 0u : head, split ? 0u : n0, split ? 0u : n1, s * A, s * B);
         splits |= split ? 1u << c : 0u;
     }
     if (!(valid && fin)) splits = 0;
@@ -399,16 +403,16 @@ struct StdPolicy {
     static constexpr int F = 2;
     static constexpr int kRecPerTile = kBinTile * 4;
     static __device__ __forceinline__ void apply(unsigned long long *slice, const Rec r, int k, uint32_t smask) {
-        const uint32_t lo0 = r.a & 0x1FFFu, t = (r.a >> 13) & 0xFu;
+        const uint32_t t = r.c >> 28, lo0 = (r.c >> 15) & 0x1FFFu;
         if (t == kSingle) {  // a pre-reduced run's corner: its sums may exceed max|dL/dout|
-            atomicAdd(slice + 2 * lo0, to_fixed_wide(__uint_as_float(r.b), k));
-            atomicAdd(slice + 2 * lo0 + 1, to_fixed_wide(__uint_as_float(r.c), k));
+            atomicAdd(slice + 2 * lo0, to_fixed_wide(__uint_as_float(r.a), k));
+            atomicAdd(slice + 2 * lo0 + 1, to_fixed_wide(__uint_as_float(r.b), k));
             return;
         }
         const uint32_t lo1 = lo0 ^ (((2u << t) - 1u) & smask);
-        const uint32_t fx23 = (r.a >> 17) | ((r.b & 0xFFu) << 15);
+        const uint32_t fx23 = ((r.c & 0x7FFFu) << 8) | ((r.b & 0xFu) << 4) | (r.a & 0xFu);
         const float fx = (float)fx23 * 0x1p-23f;  // exact: fx23 < 2^23
-        const float A = unpack28((r.b >> 8) | ((r.c & 0xFu) << 24)), B = unpack28(r.c >> 4);
+        const float A = __uint_as_float(r.a & ~0xFu), B = __uint_as_float(r.b & ~0xFu);
         const float w0 = 1.f - fx;
         atomicAdd(slice + 2 * lo0, to_fixed(w0 * A, k));
         atomicAdd(slice + 2 * lo0 + 1, to_fixed(w0 * B, k));
