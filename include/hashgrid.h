@@ -360,6 +360,11 @@ int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m
 #define HG_TUNE_FWD_SPLIT_KIB 11 /* staged D = 3, F = 2 forward: levels whose table exceeds
                                    this many KiB are gathered one table half per pass
                                    (64..2^20; 0 = never); 4096 by default              */
+#define HG_TUNE_FWD_DENSE 12    /* staged D = 3, F = 2 forward and the MLP head's stage:
+                                   blend the coarsest levels whose vertex grids or tables
+                                   fit 128 KiB of LDS together from LDS (same bits as the
+                                   gather): 1 (default) from 2^21 points, 2 always,
+                                   0 never                                             */
 int hashgrid_tune(int key, int value);
 int hashgrid_tune_get(int key);
 

@@ -45,6 +45,7 @@ struct Tuning {
     int bwd_group_mib = 160;  // record bytes per binned level group, 0: all levels at once
     int bwd_dense = 1;        // atomic backward: sum small levels in LDS first
     int fwd_split_kib = 4096; // staged gather of levels above this table size: one half per pass
+    int fwd_dense = 1;        // staged forward: blend levels that fit LDS from LDS (1: from kFwdDenseMinPoints)
 };
 Tuning g_tune;
 
@@ -141,6 +142,36 @@ void dense_levels(const hg_config &c, const hg::LaunchParams &lp, hg::DenseLevel
         sparse[l] = false;
         dl.level[dl.count++] = (int8_t)l;
         dl.max_vals = std::max<int32_t>(dl.max_vals, (int32_t)vals);
+    }
+}
+
+// Levels of the staged D = 3, F = 2 forward blended from LDS: from the
+// coarsest up, each level's vertex grid (N_l + 1)^3, or else its table, as
+// long as their entries fit kFwdDenseBytes together.  keep[l] is left true
+// for the levels the gather takes.  The copies cost a fixed ~8 us a call,
+// recovered from about 2^20 uniform points (measured at 2^18: +3 %, 2^20:
+// -3 %, 2^22: -4 % fp32 and -11 % with the binary16 stage of the MLP head);
+// ray-ordered points, whose coarse gathers already share lines, lose 2 % at
+// 2^20.  So the default takes them from kFwdDenseMinPoints points.
+constexpr int64_t kFwdDenseMinPoints = (int64_t)1 << 21;
+void fwd_dense_levels(const hg_config &c, int64_t n, const hg::LaunchParams &lp, hg::DenseLevels &dl, bool *keep) {
+    dl.count = 0;
+    dl.max_vals = 0;
+    const int64_t esize = c.table_dtype == HG_F32 ? 8 : 4;
+    const bool on = g_tune.fwd_dense == 2 || (g_tune.fwd_dense == 1 && n >= kFwdDenseMinPoints);
+    int64_t room = on ? hg::kFwdDenseBytes / esize : 0;
+    for (int l = 0; l < c.n_levels; ++l) {
+        keep[l] = true;
+        const int64_t table_entries = (int64_t)1 << c.log2_table_size;
+        const int64_t r = (int64_t)lp.res[l] + 1;
+        const int64_t vertex_entries = r <= 4096 ? r * r * r : INT64_MAX;
+        const int64_t entries = std::min(table_entries, vertex_entries);
+        if (entries > room) continue;
+        room -= entries;
+        keep[l] = false;
+        dl.by_vertex[dl.count] = vertex_entries < table_entries ? 1 : 0;
+        dl.level[dl.count++] = (int8_t)l;
+        dl.max_vals += (int32_t)entries;
     }
 }
 
@@ -353,6 +384,18 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
     const size_t stage_round = round_up(stage_bytes, 256);
     if (stage && split_forward(*cfg) && workspace_bytes >= stage_round + stage_bytes)
         stage2 = (float *)((char *)workspace + stage_round);
+    if (stage) {  // coarse levels from LDS, the others gathered
+        hg::DenseLevels dl;
+        bool keep[hg::kMaxLevels];
+        fwd_dense_levels(*cfg, n, lp, dl, keep);
+        if (dl.count) {
+            rc = launch_status(hg::launch_forward_dense(lp, dl, x, n, table, cfg->table_dtype, stage, false,
+                                                        (hipStream_t)stream),
+                               "forward (LDS levels)");
+            if (rc) return rc;
+            restrict_levels(lp, keep);
+        }
+    }
     return launch_status(hg::launch_forward(lp, x, n, table, cfg->table_dtype, out, out_row_stride, ft, stage,
                                             (hipStream_t)stream, stage2),
                          "forward");
@@ -445,6 +488,16 @@ int hashgrid_mlp_forward(const hg_config *cfg, const float *x, int64_t n, const 
         return fail(HG_EINVAL, "stage must be 256-byte aligned and hold n * 64 bytes");
     hg::LaunchParams lp;
     if ((rc = plan(*cfg, n, lp))) return rc;
+    hg::DenseLevels dl;
+    bool keep[hg::kMaxLevels];
+    fwd_dense_levels(*cfg, n, lp, dl, keep);
+    if (dl.count) {
+        rc = launch_status(hg::launch_forward_dense(lp, dl, x, n, table, cfg->table_dtype, stage, true,
+                                                    (hipStream_t)stream),
+                           "encode stage (LDS levels)");
+        if (rc) return rc;
+        restrict_levels(lp, keep);
+    }
     hipError_t e = hg::launch_encode_stage_f16(lp, x, n, table, cfg->table_dtype, (_Float16 *)stage,
                                                (hipStream_t)stream);
     if (e != hipSuccess) return launch_status(e, "encode stage");
@@ -618,6 +671,10 @@ int hashgrid_tune(int key, int value) {
         if (value != 0 && (value < 64 || value > (1 << 20))) break;
         g_tune.fwd_split_kib = value;
         return ok();
+    case HG_TUNE_FWD_DENSE:
+        if (value < 0 || value > 2) break;
+        g_tune.fwd_dense = value;
+        return ok();
     default:
         return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
@@ -638,6 +695,7 @@ int hashgrid_tune_get(int key) {
     case HG_TUNE_BWD_GROUP_MIB: return g_tune.bwd_group_mib;
     case HG_TUNE_BWD_DENSE: return g_tune.bwd_dense;
     case HG_TUNE_FWD_SPLIT_KIB: return g_tune.fwd_split_kib;
+    case HG_TUNE_FWD_DENSE: return g_tune.fwd_dense;
     default: return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
 }

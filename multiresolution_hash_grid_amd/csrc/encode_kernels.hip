@@ -35,22 +35,42 @@ namespace {
 template <int DT>
 struct Table2;
 
+// Raw is an entry as stored (both features), widen() its fp32 values.
 template <>
 struct Table2<0> {
-    static __device__ __forceinline__ float2 load(const void *base, uint64_t e) {
+    using Raw = float2;
+    static __device__ __forceinline__ Raw raw(const void *base, uint64_t e) {
         return reinterpret_cast<const float2 *>(base)[e];
     }
+    static __device__ __forceinline__ float2 widen(Raw r) { return r; }
+    static __device__ __forceinline__ float2 load(const void *base, uint64_t e) { return raw(base, e); }
 };
 
 template <>
 struct Table2<1> {
-    static __device__ __forceinline__ float2 load(const void *base, uint64_t e) {
-        uint32_t r = reinterpret_cast<const uint32_t *>(base)[e];
+    using Raw = uint32_t;
+    static __device__ __forceinline__ Raw raw(const void *base, uint64_t e) {
+        return reinterpret_cast<const uint32_t *>(base)[e];
+    }
+    static __device__ __forceinline__ float2 widen(Raw r) {
         _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(r & 0xFFFFu));
         _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(r >> 16));
         return make_float2((float)lo, (float)hi);
     }
+    static __device__ __forceinline__ float2 load(const void *base, uint64_t e) { return widen(raw(base, e)); }
 };
+
+// One x-half of a point's blend at a level: the four corners with x offset
+// sub, e[c] = corner (v_x + sub, v_y + dy, v_z + dz), c = 2 dy + dz, both
+// features.  The point's features are the sum of its two halves.  Explicit
+// fused multiply-adds: the rounding does not depend on how the compiler
+// contracts, so every kernel that blends through here gives the same bits.
+__device__ __forceinline__ float2 half_blend(float a0, float a1, float a2, uint32_t sub, const float2 (&e)[4]) {
+    const float wy0 = 1.f - a1, wz0 = 1.f - a2;
+    const float wx = sub ? a0 : 1.f - a0;
+    return make_float2(wx * fmaf(a1, fmaf(a2, e[3].x, wz0 * e[2].x), wy0 * fmaf(a2, e[1].x, wz0 * e[0].x)),
+                       wx * fmaf(a1, fmaf(a2, e[3].y, wz0 * e[2].y), wy0 * fmaf(a2, e[1].y, wz0 * e[0].y)));
+}
 
 __device__ __forceinline__ void fadd(float *p, float v) { unsafeAtomicAdd(p, v); }
 
@@ -171,14 +191,8 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float wy0 = 1.f - a1[u], wz0 = 1.f - a2[u];
-            const float wx = sub ? a0[u] : 1.f - a0[u];
-            // Explicit fused multiply-adds: the rounding does not depend on
-            // how the compiler contracts each unroll depth.
-            const float rx = wx * fmaf(a1[u], fmaf(a2[u], e[u][3].x, wz0 * e[u][2].x),
-                                       wy0 * fmaf(a2[u], e[u][1].x, wz0 * e[u][0].x));
-            const float ry = wx * fmaf(a1[u], fmaf(a2[u], e[u][3].y, wz0 * e[u][2].y),
-                                       wy0 * fmaf(a2[u], e[u][1].y, wz0 * e[u][0].y));
+            const float2 r = half_blend(a0[u], a1[u], a2[u], sub, e[u]);
+            const float rx = r.x, ry = r.y;
             // lane 0 keeps feature 0 and needs lane 1's x-half; lane 1 the reverse.
             float v = (sub ? ry : rx) + swap_pair(sub ? rx : ry);
             if (ok[u]) {
@@ -190,6 +204,127 @@ __global__ __launch_bounds__(kBlock) void fwd_f2_pair_kernel(const float *__rest
                 if constexpr (NT) __builtin_nontemporal_store((OutT)v, dst);
                 else *dst = (OutT)v;  // binary16 stage: round to nearest even
             }
+        }
+    }
+}
+
+// Coarse levels whose whole vertex grid (N_l + 1)^3 -- or whole table, if
+// smaller -- fit in LDS together (kFwdDenseBytes): each workgroup copies them
+// from the table once, then blends its chunk of points at every one of these
+// levels from LDS (a point is read once for all of them), so the corners cost
+// LDS reads instead of the L2 line requests that bound the gather.  A row of
+// x-vertices maps to one or two table lines (the x prime is 1), so a copy
+// costs a few hundred requests against four per point and level.  One thread
+// per point adds the two x-halves that a lane pair of the gather adds, through
+// the same half_blend, so the two kernels agree bit for bit.  Corners outside
+// the grid (points at x = 1, or outside [0, 1)) are read from the table.
+// Output: out[p * ostride + l * lstride + j] (a level-major stage).
+constexpr int kDenseFwdThreads = 1024;
+
+template <int DT, class OutT>
+__global__ __launch_bounds__(kDenseFwdThreads) void fwd_dense_kernel(const float *__restrict__ x, int64_t n,
+                                                                     const void *__restrict__ table,
+                                                                     OutT *__restrict__ out, int64_t ostride,
+                                                                     int64_t lstride, LaunchParams lp,
+                                                                     DenseLevels dl, int64_t chunk_pts) {
+    // The gather adds a point's two halves across a lane pair; here both are
+    // in one thread, and a contracted (fused) final add would round differently.
+#pragma clang fp contract(off)
+    using T2 = Table2<DT>;
+    using Raw = typename T2::Raw;
+    extern __shared__ __align__(16) unsigned char dense_lds[];
+    Raw *grids = reinterpret_cast<Raw *>(dense_lds);
+    const uint32_t mask = lp.mask;
+    // The levels' copies, one after the other.
+    int base = 0;
+    for (int li = 0; li < dl.count; ++li) {
+        const int l = dl.level[li];
+        const int R = lp.res[l] + 1;  // vertices per axis
+        const bool by_vertex = dl.by_vertex[li] != 0;
+        const int V = by_vertex ? R * R * R : (int)(mask + 1u);
+        const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+        // v = cx + R (cy + R cz); q / R as the high word of q * ceil(2^32 / R),
+        // exact for q < 2^20 (integer division is a long instruction sequence).
+        const uint32_t M = 0xFFFFFFFFu / (uint32_t)R + 1u;
+        // kCopyBatch loads in flight per thread before their LDS stores.
+        constexpr int kCopyBatch = 8;
+        for (int v0 = threadIdx.x; v0 < V; v0 += kCopyBatch * kDenseFwdThreads) {
+            Raw r[kCopyBatch];
+#pragma unroll
+            for (int k = 0; k < kCopyBatch; ++k) {
+                const int v = min(v0 + k * kDenseFwdThreads, V - 1);
+                uint32_t e = (uint32_t)v;
+                if (by_vertex) {
+                    const uint32_t q = __umulhi((uint32_t)v, M), cz = __umulhi(q, M);
+                    const uint32_t cx = (uint32_t)v - q * (uint32_t)R, cy = q - cz * (uint32_t)R;
+                    e = (cx ^ cy * kPrimeY ^ cz * kPrimeZ) & mask;
+                }
+                r[k] = T2::raw(table, lbase + e);
+            }
+#pragma unroll
+            for (int k = 0; k < kCopyBatch; ++k)
+                if (v0 + k * kDenseFwdThreads < V) grids[base + v0 + k * kDenseFwdThreads] = r[k];
+        }
+        base += V;
+    }
+    __syncthreads();
+    const int64_t p_begin = (int64_t)blockIdx.x * chunk_pts, p_end = min(p_begin + chunk_pts, n);
+    // kDenseUnroll points per thread and pass: their coordinates are loaded
+    // together, so that the loads overlap.
+    constexpr int kDenseUnroll = 4;
+    for (int64_t pq = p_begin + threadIdx.x; pq < p_end; pq += kDenseUnroll * kDenseFwdThreads) {
+        float xs[kDenseUnroll][3];
+#pragma unroll
+        for (int u = 0; u < kDenseUnroll; ++u) {
+            const int64_t q = min(pq + (int64_t)u * kDenseFwdThreads, p_end - 1);
+            xs[u][0] = x[3 * q + 0];
+            xs[u][1] = x[3 * q + 1];
+            xs[u][2] = x[3 * q + 2];
+        }
+#pragma unroll
+        for (int u = 0; u < kDenseUnroll; ++u) {
+        const int64_t p = pq + (int64_t)u * kDenseFwdThreads;
+        if (p >= p_end) break;
+        const float x0 = xs[u][0], x1 = xs[u][1], x2 = xs[u][2];
+        int gbase = 0;
+        for (int li = 0; li < dl.count; ++li) {
+            const int l = dl.level[li];
+            const int R = lp.res[l] + 1;
+            const bool by_vertex = dl.by_vertex[li] != 0;
+            const Raw *grid = grids + gbase;
+            gbase += by_vertex ? R * R * R : (int)(mask + 1u);
+            const uint64_t lbase = (uint64_t)l << lp.log2_table_size;
+            const float N = (float)lp.res[l];
+            int32_t v0, v1, v2;
+            float a0, a1, a2;
+            locate1(x0, N, v0, a0);
+            locate1(x1, N, v1, a1);
+            locate1(x2, N, v2, a2);
+            // the voxel's 8 corners are vertices of the grid
+            const bool inside = (uint32_t)v0 < (uint32_t)(R - 1) && (uint32_t)v1 < (uint32_t)(R - 1) &&
+                                (uint32_t)v2 < (uint32_t)(R - 1);
+            const uint32_t hy0 = (uint32_t)v1 * kPrimeY, hz0 = (uint32_t)v2 * kPrimeZ;
+            float2 h[2];
+#pragma unroll
+            for (uint32_t sub = 0; sub < 2; ++sub) {
+                float2 e[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t dy = (uint32_t)(c >> 1), dz = (uint32_t)(c & 1);
+                    if (by_vertex && inside) {
+                        e[c] = T2::widen(grid[(v0 + (int)sub) + R * ((v1 + (int)dy) + R * (v2 + (int)dz))]);
+                    } else {
+                        const uint32_t idx =
+                            (((uint32_t)v0 + sub) ^ (hy0 + dy * kPrimeY) ^ (hz0 + dz * kPrimeZ)) & mask;
+                        e[c] = by_vertex ? T2::load(table, lbase + idx) : T2::widen(grid[idx]);
+                    }
+                }
+                h[sub] = half_blend(a0, a1, a2, sub, e);
+            }
+            OutT *dst = out + p * ostride + (int64_t)l * lstride;
+            dst[0] = (OutT)(h[0].x + h[1].x);
+            dst[1] = (OutT)(h[1].y + h[0].y);
+        }
         }
     }
 }
@@ -346,11 +481,12 @@ int grid_blocks(const LaunchParams &lp) {
 // VEC moves 16 bytes per access on both sides (F n and F L multiples of 4,
 // rows and output 16-byte aligned); otherwise 4 bytes.
 // stage2 (may be NULL): a second stage of partial blends, added element-wise
-// while transposing.
+// while transposing at the levels whose bit is set in second.
 template <int F, bool VEC>
 __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restrict__ stage,
-                                                           const float *__restrict__ stage2, int64_t n, int L,
-                                                           int pts, float *__restrict__ out, int64_t ostride) {
+                                                           const float *__restrict__ stage2, uint64_t second,
+                                                           int64_t n, int L, int pts, float *__restrict__ out,
+                                                           int64_t ostride) {
     extern __shared__ float tile[];  // [pts][F L + 4]: rows 16-byte aligned when F L is a multiple of 4
     const int row = F * L + 4;
     const int64_t p0 = (int64_t)blockIdx.x * pts;
@@ -363,7 +499,7 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restri
             if (4 * qd < F * np) {
                 const int64_t off = ((int64_t)l * n + p0) * F + 4 * qd;
                 float4 v = *reinterpret_cast<const float4 *>(stage + off);
-                if (stage2) {
+                if (stage2 && ((second >> l) & 1u)) {
                     const float4 w = *reinterpret_cast<const float4 *>(stage2 + off);
                     v.x += w.x, v.y += w.y, v.z += w.z, v.w += w.w;
                 }
@@ -398,7 +534,7 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restri
             const int i = r / F, j = r - i * F;
             if (i < np) {
                 const int64_t off = ((int64_t)l * n + p0 + i) * F + j;
-                tile[i * row + F * l + j] = stage2 ? stage[off] + stage2[off] : stage[off];
+                tile[i * row + F * l + j] = stage2 && ((second >> l) & 1u) ? stage[off] + stage2[off] : stage[off];
             }
         }
         __syncthreads();
@@ -411,7 +547,7 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restri
 
 template <int F>
 hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, int64_t ostride,
-                              hipStream_t stream, const float *stage2 = nullptr) {
+                              hipStream_t stream, const float *stage2 = nullptr, uint64_t second = ~0ull) {
     // Points per workgroup: 64, fewer for wide rows so that the tile stays near 32 KB.
     const int pts = std::max(4, std::min(64, 8192 / (F * L + 4)) / 4 * 4);
     const unsigned blocks = (unsigned)((n + pts - 1) / pts);
@@ -419,8 +555,8 @@ hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, 
     bool vec = (n * F) % 4 == 0 && (F * L) % 4 == 0 && ostride % 4 == 0 && ((uintptr_t)out & 15) == 0 &&
                ((uintptr_t)stage & 15) == 0;
     if (vec && stage2 && ((uintptr_t)stage2 & 15)) vec = false;
-    if (vec) transpose_kernel<F, true><<<blocks, kBlock, lds, stream>>>(stage, stage2, n, L, pts, out, ostride);
-    else transpose_kernel<F, false><<<blocks, kBlock, lds, stream>>>(stage, stage2, n, L, pts, out, ostride);
+    if (vec) transpose_kernel<F, true><<<blocks, kBlock, lds, stream>>>(stage, stage2, second, n, L, pts, out, ostride);
+    else transpose_kernel<F, false><<<blocks, kBlock, lds, stream>>>(stage, stage2, second, n, L, pts, out, ostride);
     return hipGetLastError();
 }
 
@@ -474,10 +610,32 @@ hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, con
         return table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, out, out_stride, 2, ft, stream)
                                 : launch_gather_dt<1>(lp, x, n, table, out, out_stride, 2, ft, stream);
     }
-    e = table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2)
-                         : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2);
+    // Levels of this gather (lp.level_order; the others came from launch_forward_dense).
+    uint64_t gathered = 0;
+    const int levels = lp.chunks ? lp.items / lp.chunks : 0;
+    for (int i = 0; i < levels; ++i) gathered |= 1ull << lp.level_order[i];
+    if (lp.items > 0) {
+        e = table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2)
+                             : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2);
+        if (e != hipSuccess) return e;
+    }
+    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream, stage2, gathered);
+}
+
+template <int DT, class OutT>
+hipError_t launch_dense_dt(const LaunchParams &lp, const DenseLevels &dl, const float *x, int64_t n,
+                           const void *table, OutT *out, int64_t ostride, int64_t lstride, hipStream_t stream) {
+    // dl.max_vals: the entries of all the levels' copies together.
+    const size_t lds = (size_t)dl.max_vals * sizeof(typename Table2<DT>::Raw);
+    hipError_t e = hipFuncSetAttribute((const void *)fwd_dense_kernel<DT, OutT>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream, stage2);
+    // About 256 workgroups (one per CU), of at least 1024 points.
+    const int64_t chunk = std::max<int64_t>(1024, (n + 255) / 256 + 1023) / 1024 * 1024;
+    const int64_t blocks = (n + chunk - 1) / chunk;
+    fwd_dense_kernel<DT, OutT><<<(unsigned)blocks, kDenseFwdThreads, lds, stream>>>(x, n, table, out, ostride,
+                                                                                   lstride, lp, dl, chunk);
+    return hipGetLastError();
 }
 
 hipError_t launch_transpose(int F, const float *stage, int64_t n, int L, float *out, int64_t ostride,
@@ -491,8 +649,20 @@ hipError_t launch_transpose(int F, const float *stage, int64_t n, int L, float *
     }
 }
 
+hipError_t launch_forward_dense(const LaunchParams &lp, const DenseLevels &dl, const float *x, int64_t n,
+                                const void *table, int table_dtype, void *stage, bool half_stage,
+                                hipStream_t stream) {
+    if (!dl.count || n == 0) return hipSuccess;
+    if (half_stage)
+        return table_dtype == 0 ? launch_dense_dt<0>(lp, dl, x, n, table, (_Float16 *)stage, 2, 2 * n, stream)
+                                : launch_dense_dt<1>(lp, dl, x, n, table, (_Float16 *)stage, 2, 2 * n, stream);
+    return table_dtype == 0 ? launch_dense_dt<0>(lp, dl, x, n, table, (float *)stage, 2, 2 * n, stream)
+                            : launch_dense_dt<1>(lp, dl, x, n, table, (float *)stage, 2, 2 * n, stream);
+}
+
 hipError_t launch_encode_stage_f16(const LaunchParams &lp, const float *x, int64_t n, const void *table,
                                    int table_dtype, _Float16 *stage, hipStream_t stream) {
+    if (lp.items == 0) return hipSuccess;
     dim3 grid(grid_blocks(lp)), block(kBlock);
     if (table_dtype == 0)
         fwd_f2_pair_kernel<0, 4, false, _Float16><<<grid, block, 0, stream>>>(x, n, table, stage, 2, 2 * n, lp, 0);

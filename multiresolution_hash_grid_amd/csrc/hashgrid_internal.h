@@ -137,10 +137,20 @@ hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const f
 constexpr int kDenseVals = 16384;  // 128 KB of 64-bit accumulators
 struct DenseLevels {
     int32_t count;
-    int32_t max_vals;              // largest accumulator count among them
+    int32_t max_vals;              // largest accumulator (or, forward, entry) count among them
     int8_t level[kMaxLevels];
     int8_t by_vertex[kMaxLevels];
 };
+// Forward of the D = 3, F = 2 grid (encode_kernels.hip, fwd_dense_kernel):
+// the coarsest levels whose vertex grids (N_l + 1)^3, or tables, fit
+// kFwdDenseBytes of LDS together as stored entries (max_vals: their entries
+// in all) are blended from LDS into a level-major stage ([L][n][2], fp32 or,
+// half_stage, binary16); the gather then takes the other levels
+// (launch_forward, launch_encode_stage_f16 with those levels).
+constexpr int kFwdDenseBytes = 128 << 10;
+hipError_t launch_forward_dense(const LaunchParams &lp, const DenseLevels &dl, const float *x, int64_t n,
+                                const void *table, int table_dtype, void *stage, bool half_stage,
+                                hipStream_t stream);
 hipError_t launch_backward_dense(const LaunchParams &lp, const DenseLevels &dl, int D, int F, const float *x,
                                  int64_t n, const float *dout, int64_t dout_stride, float *dtable,
                                  hipStream_t stream);

@@ -28,6 +28,10 @@ hipError_t launch_forward(const LaunchParams &, const float *, int64_t, const vo
                           const FwdTune &, float *, hipStream_t, float *) {
     return reached("forward");
 }
+hipError_t launch_forward_dense(const LaunchParams &, const DenseLevels &, const float *, int64_t, const void *,
+                                int, void *, bool, hipStream_t) {
+    return reached("forward_dense");
+}
 hipError_t launch_backward(const LaunchParams &, const float *, int64_t, const float *, int64_t, float *, int,
                            hipStream_t) {
     return reached("backward");

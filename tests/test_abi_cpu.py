@@ -172,7 +172,8 @@ def test_tuning_knobs(lib):
                            (B.HG_TUNE_CHUNK_POINTS, 512, 100), (B.HG_TUNE_XCD_MAP, 0, 2),
                            (B.HG_TUNE_BWD_BINNED, 0, 3), (B.HG_TUNE_FWD_UNROLL, 2, 3),
                            (B.HG_TUNE_FWD_NT, 1, 2), (B.HG_TUNE_FWD_STAGED, 0, 2),
-                           (B.HG_TUNE_BWD_PART_LOG2, 12, 14), (B.HG_TUNE_BWD_GROUP_MIB, 64, -1)):
+                           (B.HG_TUNE_BWD_PART_LOG2, 12, 14), (B.HG_TUNE_BWD_GROUP_MIB, 64, -1),
+                           (B.HG_TUNE_FWD_DENSE, 2, 3)):
         old = hg.hashgrid_tune_get(key)
         hg.hashgrid_tune(key, good)
         assert hg.hashgrid_tune_get(key) == good
