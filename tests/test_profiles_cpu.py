@@ -21,6 +21,7 @@ def test_kernel_names_and_passes():
     assert ps.pass_of("void at::native::vectorized_elementwise_kernel<4>(int)") is None
     assert ps.pass_of("hg::(anonymous namespace)::mlp_dy_max_kernel(float4 const*)") == "backward"
     assert ps.pass_of("hg::(anonymous namespace)::fwd_generic_pair_kernel<3, 4, 0>(float const*)") == "forward"
+    assert ps.pass_of("void hg::(anonymous namespace)::fwd_dense_kernel<1, _Float16>(float const*, long)") == "forward"
 
 
 def _write(path, rows, fields):
