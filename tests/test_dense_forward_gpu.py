@@ -133,3 +133,49 @@ def test_mlp_stage_lds_levels_match_the_gather(n):
         hg.hashgrid_tune(B.HG_TUNE_FWD_DENSE, old)
     assert np.array_equal(res[0][1], res[1][1])
     assert np.array_equal(res[0][0], res[1][0])
+
+
+def test_lds_levels_captured_in_a_graph_replay_like_eager():
+    # The LDS path under HIP graph capture (its launcher sets the kernel's LDS
+    # size attribute on every call): the staged forward and the MLP head's
+    # stage, captured once and replayed with eager work in between, match the
+    # eager results bit for bit.
+    w = I.resized(I.WORKLOADS["fused_mlp"], 1 << 14)
+    cfg = hg.HashGridConfig.of(w)
+    n = w.n_points
+    x, t = dev(I.make_points(w)), dev(I.make_table(w))
+    P = [dev(a) for a in I.mlp_params(w.seed)]
+    st_bytes, _ = hg.hashgrid_mlp_workspace_size(cfg, n)
+    stage = torch.empty(st_bytes, dtype=torch.uint8, device=DEV)
+    y = torch.empty((n, 4), device=DEV)
+    out = torch.empty((n, cfg.out_features), device=DEV)
+    fws = hg.forward_workspace(cfg, n, DEV)
+    old = hg.hashgrid_tune_get(B.HG_TUNE_FWD_DENSE)
+    try:
+        hg.hashgrid_tune(B.HG_TUNE_FWD_DENSE, 2)
+
+        def step():
+            hg.hashgrid_forward(cfg, x, t, out=out, workspace=fws)
+            hg.hashgrid_mlp_forward(cfg, x, t, P, y=y, stage=stage)
+
+        step()
+        torch.cuda.synchronize()
+        ref_out, ref_y = out.clone(), y.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            out.fill_(-1.0)
+            y.fill_(-1.0)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_out) and torch.equal(y, ref_y)
+    finally:
+        hg.hashgrid_tune(B.HG_TUNE_FWD_DENSE, old)
