@@ -117,7 +117,10 @@ int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *byt
  *   (while transposing when the workspace holds two stages, in place when it
  *   holds one; the sums are the same either way): such levels round
  *   differently from the one-pass direct path, by a few fp32 roundings of the
- *   blend (measured: 1.5e-7 of the largest table value).
+ *   blend (measured: 1.5e-7 of the largest table value).  With a workspace
+ *   and from 2^21 points (HG_TUNE_FWD_DENSE), the coarsest levels whose
+ *   vertex grids fit 128 KiB of LDS together are blended from LDS copies of
+ *   them, with the same arithmetic as the one-pass gather (same bits).
  * Errors: HG_EINVAL (config, NULL, alignment, n < 0, stride), HG_EUNSUPPORTED,
  *         HG_EHIP. */
 int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void *table,
