@@ -125,6 +125,8 @@ __device__ __forceinline__ int fixed_exponent(uint32_t dmax_bits) {
 // batches of kAccBatch steps are in flight: the next batch is requested
 // before the current one is added.
 constexpr int kAccBatch = 2;
+// Consecutive (level, partition) slots an XCD takes at a time (accumulate_kernel).
+constexpr uint32_t kAccXcdRun = 4;
 // float4 gradient values per thread of a partition: S * F / 4 <= kFlushPer *
 // THREADS for the partition size each workgroup width serves (launch_accumulate
 // checks).
@@ -220,8 +222,20 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     __shared__ MapT maps[kWaves][64];                    // per wave: byte map of the current window
     __shared__ uint32_t touched;
     __shared__ uint32_t wmax[kWaves];
-    const int g = blockIdx.x / bp.parts;
-    const int part = blockIdx.x - g * bp.parts;
+    // Workgroups reach the XCDs round-robin.  A tile's runs of neighbouring
+    // partitions lie next to each other in the records and in the run table,
+    // sharing cache lines, so each XCD takes kAccXcdRun consecutive
+    // (level, partition) slots at a time: most shared lines are then fetched
+    // into one L2, not two.  Longer stretches (a contiguous range per XCD)
+    // leave the XCDs unevenly loaded, coarse levels having fewer records.
+    const uint32_t nblocks = gridDim.x;
+    const uint32_t kk = blockIdx.x / kNumXcd;
+    const uint32_t slot = nblocks % (kNumXcd * kAccXcdRun)
+                              ? blockIdx.x
+                              : (kk / kAccXcdRun) * (kNumXcd * kAccXcdRun) + (blockIdx.x % kNumXcd) * kAccXcdRun +
+                                    kk % kAccXcdRun;
+    const int g = (int)(slot / (uint32_t)bp.parts);
+    const int part = (int)slot - g * bp.parts;
     const int l = bp.level0 + g;
     const int S = 1 << bp.s_log2;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -82,29 +82,22 @@ __global__ __launch_bounds__(kGenThreads) void bin_generic_kernel(const float *_
     uint32_t part[kItems], rank[kItems];
     bool valid[kItems];
     float dm = 0.f;
+    // A thread locates a point once and makes kPer of its P pairs: all of
+    // them, for kPts points kGenThreads apart (kItems >= P), else kItems
+    // consecutive pairs of one point.
+    constexpr int kPts = kItems >= P ? kItems / P : 1, kPer = kItems >= P ? P : kItems;
+    static_assert(kPts * kPer == kItems && R == kItems * kGenThreads, "items per thread");
 #pragma unroll
-    for (int it = 0; it < kItems; ++it) {
-        const int item = threadIdx.x + it * kGenThreads;
-        const int pi = item / P, c = item % P;
+    for (int ps = 0; ps < kPts; ++ps) {
+        const int pi = kItems >= P ? ps * kGenThreads + (int)threadIdx.x : (int)threadIdx.x * kItems / P;
+        const int c0 = kItems >= P ? 0 : (int)threadIdx.x * kItems % P;
         const int64_t p = (int64_t)tile * TILE + pi;
-        valid[it] = item < R && p < n;
-        const int64_t q = valid[it] ? p : n - 1;  // in bounds; emits nothing
-        int32_t v0;
-        float f0, w_rest = 1.f;
-        uint32_t K = 0;
-        locate1(x[q * D], N, v0, f0);
+        const bool vp = p < n;
+        const int64_t q = vp ? p : n - 1;  // in bounds; emits nothing
+        int32_t vv[D];
+        float ff[D];
 #pragma unroll
-        for (int d = 1; d < D; ++d) {
-            int32_t v;
-            float f;
-            locate1(x[q * D + d], N, v, f);
-            const uint32_t up = (c >> (D - 1 - d)) & 1;
-            K ^= ((uint32_t)v + up) * kPrimeList[d];
-            w_rest *= up ? f : 1.f - f;
-        }
-        const uint32_t cx0 = (uint32_t)v0;
-        const uint32_t i0 = (cx0 ^ K) & bp.mask, i1 = ((cx0 + 1u) ^ K) & bp.mask;
-        part[it] = i0 >> bp.s_log2;
+        for (int d = 0; d < D; ++d) locate1(x[q * D + d], N, vv[d], ff[d]);
         float gv[F];
         bool fin = true;
 #pragma unroll
@@ -116,37 +109,55 @@ __global__ __launch_bounds__(kGenThreads) void bin_generic_kernel(const float *_
         // binned: both corners go to the gradient with fp32 atomics, so NaN and
         // Inf reach the entries they touch, and the level's fixed-point scale
         // comes from the finite values only.
-        if (valid[it] && fin) {
+        if (vp && fin) {
 #pragma unroll
             for (int j = 0; j < F; ++j) dm = fmaxf(dm, fabsf(gv[j]));
         }
-        if (valid[it] && !fin) {
-            float *e0 = grad + (((uint64_t)l << bp.log2_table_size) + i0) * F;
-            float *e1 = grad + (((uint64_t)l << bp.log2_table_size) + i1) * F;
+        const int32_t v0 = vv[0];
+        const float f0 = ff[0];
+        const uint32_t cx0 = (uint32_t)v0;
 #pragma unroll
-            for (int j = 0; j < F; ++j) {
-                unsafeAtomicAdd(e0 + j, (1.f - f0) * (w_rest * gv[j]));
-                unsafeAtomicAdd(e1 + j, f0 * (w_rest * gv[j]));
+        for (int cc = 0; cc < kPer; ++cc) {
+            const int it = ps * kPer + cc, c = c0 + cc;
+            float w_rest = 1.f;
+            uint32_t K = 0;
+#pragma unroll
+            for (int d = 1; d < D; ++d) {
+                const uint32_t up = (c >> (D - 1 - d)) & 1;
+                K ^= ((uint32_t)vv[d] + up) * kPrimeList[d];
+                w_rest *= up ? ff[d] : 1.f - ff[d];
             }
-            valid[it] = false;  // no record
-        } else if ((i1 >> bp.s_log2) == part[it]) {
-            const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 15u);
-            rec[it].head = (i0 & smask) | (t << 13);
-            rec[it].fx = f0;
+            const uint32_t i0 = (cx0 ^ K) & bp.mask, i1 = ((cx0 + 1u) ^ K) & bp.mask;
+            part[it] = i0 >> bp.s_log2;
+            valid[it] = vp;
+            if (vp && !fin) {
+                float *e0 = grad + (((uint64_t)l << bp.log2_table_size) + i0) * F;
+                float *e1 = grad + (((uint64_t)l << bp.log2_table_size) + i1) * F;
 #pragma unroll
-            for (int j = 0; j < F; ++j) rec[it].g[j] = w_rest * gv[j];
-        } else {
-            rec[it].head = i0 & smask;
-            rec[it].fx = 0.f;
+                for (int j = 0; j < F; ++j) {
+                    unsafeAtomicAdd(e0 + j, (1.f - f0) * (w_rest * gv[j]));
+                    unsafeAtomicAdd(e1 + j, f0 * (w_rest * gv[j]));
+                }
+                valid[it] = false;  // no record
+            } else if ((i1 >> bp.s_log2) == part[it]) {
+                const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 15u);
+                rec[it].head = (i0 & smask) | (t << 13);
+                rec[it].fx = f0;
 #pragma unroll
-            for (int j = 0; j < F; ++j) rec[it].g[j] = (1.f - f0) * (w_rest * gv[j]);
-            if (valid[it]) {
-                float *e = grad + (((uint64_t)l << bp.log2_table_size) + i1) * F;
+                for (int j = 0; j < F; ++j) rec[it].g[j] = w_rest * gv[j];
+            } else {
+                rec[it].head = i0 & smask;
+                rec[it].fx = 0.f;
 #pragma unroll
-                for (int j = 0; j < F; ++j) unsafeAtomicAdd(e + j, f0 * (w_rest * gv[j]));
+                for (int j = 0; j < F; ++j) rec[it].g[j] = (1.f - f0) * (w_rest * gv[j]);
+                if (vp) {
+                    float *e = grad + (((uint64_t)l << bp.log2_table_size) + i1) * F;
+#pragma unroll
+                    for (int j = 0; j < F; ++j) unsafeAtomicAdd(e + j, f0 * (w_rest * gv[j]));
+                }
             }
+            rank[it] = valid[it] ? atomicAdd(&cnt[part[it]], 1u) : 0u;
         }
-        rank[it] = valid[it] ? atomicAdd(&cnt[part[it]], 1u) : 0u;
     }
     for (int off = 32; off > 0; off >>= 1) dm = fmaxf(dm, __shfl_xor(dm, off, 64));
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = __float_as_uint(dm);
