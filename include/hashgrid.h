@@ -68,7 +68,7 @@ typedef struct hg_config {
     int32_t base_resolution;   /* N_min >= 1                                                    */
     int32_t finest_resolution; /* N_max, N_min <= N_max < 2^24                                  */
     int32_t table_dtype;       /* HG_F32 or HG_F16                                              */
-    int32_t grad_dtype;        /* HG_F32 (the gradient buffer is always accumulated in fp32)    */
+    int32_t grad_dtype;        /* HG_F32, or HG_F16 (binned backward only, see hashgrid_backward) */
 } hg_config;
 
 /* Version of this ABI (HASHGRID_ABI_VERSION of the built library). */
@@ -154,7 +154,8 @@ int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *by
  *   x      : float32 [n][D], the points of the forward call.
  *   dout   : float32, dL/dout with row stride dout_row_stride >= L*F elements;
  *            element (p, l*F + j) is read, other columns are ignored.
- *   dtable : float32 [L][T][F], 4-byte aligned.  ACCUMULATED INTO:
+ *   dtable : float32 [L][T][F] (binary16 with grad_dtype HG_F16, below),
+ *            4-byte aligned.  ACCUMULATED INTO:
  *            dtable[l][h(corner_k)][j] += w_k * dout[p][l*F + j] for every point,
  *            level and corner.  The caller zeroes the buffer when it wants the
  *            gradient of one batch alone.  On the binned path the D = 3, F = 2
@@ -186,6 +187,18 @@ int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *by
  *            workspace it is scattered with fp32 global atomics (correct, but
  *            an order of magnitude slower on MI355X).  Concurrent calls must
  *            not share a workspace.
+ * grad_dtype HG_F16 (a binary16 gradient buffer beside binary16 tables,
+ * jsqmd.com section 5's half-precision tip): the binned path sums each
+ * partition in fixed point as above and rounds every entry once, from the fp32
+ * sum of its old value and the partition's sum to binary16 (relative error
+ * <= 2^-11 of the entry; magnitudes past 65504 become +-Inf).  The few
+ * contributions it adds directly (non-finite dout values, corners whose pair
+ * straddles two partitions, run sums past fp32) use packed binary16 atomics,
+ * each addition rounded.  Summing with atomics alone would round at every
+ * addition, an error that grows with the additions an entry takes, so HG_F16 needs
+ * the binned path: without a workspace of at least the minimum, with a dtable
+ * that is not 16-byte aligned, or on a grid without a binned path the call
+ * returns HG_EUNSUPPORTED and changes nothing.
  * Errors: as hashgrid_forward. */
 int hashgrid_backward(const hg_config *cfg, const float *x, int64_t n, const float *dout,
                       int64_t dout_row_stride, float *dtable, void *workspace,
@@ -262,7 +275,8 @@ int hashgrid_mlp_forward(const hg_config *cfg, const float *x, int64_t n, const 
 
 /* Backward of encoder + MLP head for upstream dy = dL/dy [n][4] fp32
  * (16-byte aligned): adds the weight and bias gradients into *grads and the
- * table gradient into dtable ([L][T][F] fp32, as hashgrid_backward).
+ * table gradient into dtable ([L][T][F] fp32, or binary16 with grad_dtype
+ * HG_F16, as hashgrid_backward).
  *   stage     : the stage the forward of the same x, table and params wrote.
  *   workspace : hashgrid_mlp_workspace_size's bwd bytes (256-byte aligned);
  *               at least the dL/de rows and partials are required, and with

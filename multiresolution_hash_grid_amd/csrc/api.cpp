@@ -80,7 +80,6 @@ int check_config(const hg_config *c) {
     if (c->n_dims > 4) return fail(HG_EUNSUPPORTED, "n_dims %d: 1..4 are built", c->n_dims);
     if (c->n_features != 1 && c->n_features != 2 && c->n_features != 4 && c->n_features != 8)
         return fail(HG_EUNSUPPORTED, "n_features %d: 1, 2, 4 and 8 are built", c->n_features);
-    if (c->grad_dtype != HG_F32) return fail(HG_EUNSUPPORTED, "grad_dtype must be HG_F32");
     return HG_OK;
 }
 
@@ -210,6 +209,7 @@ bool plan_binned(const hg_config &c, int64_t n, hg::BinParams &bp) {
     bp.level_records = tiles * rec_per_tile;
     bp.rec_per_tile = rec_per_tile;
     bp.rec_bytes = rec_bytes;
+    bp.grad_f16 = c.grad_dtype == HG_F16;
     resolutions(c, bp.res);
     return true;
 }
@@ -263,7 +263,20 @@ int table_backward(const hg_config *cfg, const float *x, int64_t n, const float 
                    float *dtable, void *workspace, size_t workspace_bytes, void *stream) {
     int rc;
     hg::BinParams bp;
-    if (g_tune.bwd_binned && workspace && aligned(dtable, 16) && plan_binned(*cfg, n, bp)) {
+    const bool binned = g_tune.bwd_binned && workspace && aligned(dtable, 16) && plan_binned(*cfg, n, bp);
+    if (cfg->grad_dtype == HG_F16) {
+        // binary16 gradients are summed exactly in fixed point and rounded
+        // once; the atomic scatter would round at every addition.
+        if (!plan_binned(*cfg, n, bp))
+            return fail(HG_EUNSUPPORTED, "grad_dtype HG_F16 needs the binned backward, which this grid and n lack");
+        const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
+        if (!binned || workspace_bytes < per_level)
+            return fail(HG_EUNSUPPORTED,
+                        "grad_dtype HG_F16 needs the binned backward: a workspace of at least %zu bytes and a "
+                        "16-byte aligned dtable",
+                        per_level);
+    }
+    if (binned) {
         const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
         if (workspace_bytes >= per_level) {
             // Whole levels per group; the launcher splits the workspace itself.

@@ -114,10 +114,13 @@ struct Pairs {
 };
 
 // wbuf: this wave's 16 x 64 floats of LDS, free while the records are made.
-// glevel: level l's gradient [T][2], which takes the contributions that are
-// not binned (non-finite upstream values, non-finite run sums).
+// grad: the gradient [L][T][2] (fp32 or binary16, bp.grad_f16), which takes
+// the contributions that are not binned (non-finite upstream values, x+1
+// corners outside their pair's partition, non-finite run sums).
 __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1, int l, const BinParams &bp,
-                                           bool valid, float *wbuf, float *__restrict__ glevel, Pairs &out) {
+                                           bool valid, float *wbuf, float *__restrict__ grad, Pairs &out) {
+    const uint64_t lbase = (uint64_t)l << bp.log2_table_size;  // level l's first entry
+    const bool f16 = bp.grad_f16 != 0;
     const float N = (float)bp.res[l];
     int32_t v0, v1, v2;
     float a0, a1, a2;
@@ -167,10 +170,8 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
             const uint32_t i0 = (cx0 ^ K) & bp.mask, i1 = (cx1 ^ K) & bp.mask;
             const float wyz = (dy ? a1 : 1.f - a1) * (dz ? a2 : 1.f - a2);
             const float A = wyz * d0, B = wyz * d1;
-            unsafeAtomicAdd(glevel + 2 * i0, wx0 * A);
-            unsafeAtomicAdd(glevel + 2 * i0 + 1, wx0 * B);
-            unsafeAtomicAdd(glevel + 2 * i1, a0 * A);
-            unsafeAtomicAdd(glevel + 2 * i1 + 1, a0 * B);
+            grad_atomic_add2(grad, f16, (lbase + i0) * 2, wx0 * A, wx0 * B);
+            grad_atomic_add2(grad, f16, (lbase + i1) * 2, a0 * A, a0 * B);
         }
     }
     // The x+1 corners outside their pair's partition, added with atomics by a
@@ -186,8 +187,7 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
             const uint32_t i1 = (cx1 ^ K) & bp.mask;
             const float wyz = (dy ? a1 : 1.f - a1) * (dz ? a2 : 1.f - a2);
             const float A = wyz * d0, B = wyz * d1;
-            unsafeAtomicAdd(glevel + 2 * i1, a0 * A);
-            unsafeAtomicAdd(glevel + 2 * i1 + 1, a0 * B);
+            grad_atomic_add2(grad, f16, (lbase + i1) * 2, a0 * A, a0 * B);
         }
     };
     // Wave pre-reduction of runs of consecutive lanes in one voxel.
@@ -250,8 +250,7 @@ __device__ __forceinline__ void make_pairs(const float xp[3], float d0, float d1
         if (isfinite(sum[c][0]) && isfinite(sum[c][1])) {
             out.rec[c] = single_record(i & smask, sum[c][0], sum[c][1]);
         } else {  // finite values whose sum overflows fp32: added as it is, the record adds zero
-            unsafeAtomicAdd(glevel + 2 * i, sum[c][0]);
-            unsafeAtomicAdd(glevel + 2 * i + 1, sum[c][1]);
+            grad_atomic_add2(grad, f16, (lbase + i) * 2, sum[c][0], sum[c][1]);
             out.rec[c] = single_record(i & smask, 0.f, 0.f);
         }
     }
@@ -343,7 +342,7 @@ __global__ __launch_bounds__(kBinThreads) void bin_kernel(const float *__restric
 #pragma unroll
         for (int k = 0; k < kPtsPerThread; ++k) {
             make_pairs(tp.xs[k], tp.dv[k][j][0], tp.dv[k][j][1], l, bp, tp.valid[k], wbuf,
-                       grad + ((uint64_t)l << bp.log2_table_size) * 2, pr[k]);
+                       grad, pr[k]);
             if (tp.valid[k]) dm = fmaxf(dm, pr[k].dabs);
 #pragma unroll
             for (int c = 0; c < 4; ++c) rank[k][c] = 0u;

@@ -17,6 +17,46 @@
 namespace hg {
 namespace binned {
 
+// The gradient holds fp32 values, or binary16 values when bp.grad_f16 is set
+// (the same element indices: element e of [L][T][F]).  The binned path adds to
+// it directly only for the few contributions it does not bin (non-finite
+// upstream values, x+1 corners outside their pair's partition, run sums past
+// fp32); these helpers add them with atomics of the gradient's own type.  A
+// binary16 atomic is a packed add of an aligned pair of halves: where only one
+// half takes a value the other adds -0, which leaves every value as it is
+// (-0 + -0 = -0, +0 + -0 = +0).
+using Half2 = _Float16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void grad_atomic_half2(float *grad, uint64_t e_even, Half2 v) {
+    __builtin_amdgcn_flat_atomic_fadd_v2f16(reinterpret_cast<Half2 *>(reinterpret_cast<_Float16 *>(grad) + e_even), v);
+}
+__device__ __forceinline__ void grad_atomic_add(float *grad, bool f16, uint64_t e, float v) {
+    if (!f16) {
+        unsafeAtomicAdd(grad + e, v);
+        return;
+    }
+    const _Float16 h = (_Float16)v, z = (_Float16)-0.0f;
+    grad_atomic_half2(grad, e & ~1ull, (e & 1) ? Half2{z, h} : Half2{h, z});
+}
+// Elements e and e + 1, e even.
+__device__ __forceinline__ void grad_atomic_add2(float *grad, bool f16, uint64_t e, float a, float b) {
+    if (!f16) {
+        unsafeAtomicAdd(grad + e, a);
+        unsafeAtomicAdd(grad + e + 1, b);
+        return;
+    }
+    grad_atomic_half2(grad, e, Half2{(_Float16)a, (_Float16)b});
+}
+// The F values value(j) of the entry whose first element is e (e a multiple of F).
+template <int F, class Fn>
+__device__ __forceinline__ void grad_atomic_entry(float *grad, bool f16, uint64_t e, Fn value) {
+    if constexpr (F == 1) {
+        grad_atomic_add(grad, f16, e, value(0));
+    } else {
+#pragma unroll
+        for (int j = 0; j < F; j += 2) grad_atomic_add2(grad, f16, e + j, value(j), value(j + 1));
+    }
+}
+
 // Workspace of one launch group.
 template <class Rec>
 struct Space {
@@ -256,8 +296,7 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     // workgroup writes them.  They are read at the flush: holding them in
     // registers through the record loop (87 instead of 63 VGPRs) cost more
     // than the exposed read latency (standard backward 162 -> 158 us without).
-    float *gbase = grad + ((((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * F);
-    float4 *gl = reinterpret_cast<float4 *>(gbase);
+    const uint64_t e0 = (((uint64_t)l << bp.log2_table_size) + (uint64_t)part * S) * F;  // first element
     for (int i = threadIdx.x; i < S * F; i += THREADS) slice[i] = 0ull;
     if (threadIdx.x == 0) touched = 0;
     // The level's max |dL/dout| over the tiles' maxima.
@@ -342,19 +381,45 @@ __global__ __launch_bounds__(THREADS) void accumulate_kernel(BinParams bp, Space
     __syncthreads();
     if (!touched) return;  // no corner of this batch fell in the partition: nothing to add
     const long long *sl = reinterpret_cast<const long long *>(slice);
-    if (S * F < 4) {  // a 2-entry table with one feature: two floats, less than a float4
-        if (threadIdx.x < S * F) gbase[threadIdx.x] += (float)ldexp((double)sl[threadIdx.x], -k);
+    auto sum = [&](int i) { return (float)ldexp((double)sl[i], -k); };
+    if (bp.grad_f16) {
+        // binary16: each value rounded once, from the fp32 sum of the old value
+        // and the partition's sum.
+        _Float16 *hbase = reinterpret_cast<_Float16 *>(grad) + e0;
+        if (S * F < 4) {
+            if (threadIdx.x < S * F) hbase[threadIdx.x] = (_Float16)((float)hbase[threadIdx.x] + sum(threadIdx.x));
+            return;
+        }
+        using Half4 = _Float16 __attribute__((ext_vector_type(4)));
+        Half4 *hl = reinterpret_cast<Half4 *>(hbase);
+#pragma unroll
+        for (int u = 0; u < kFlushPer; ++u) {
+            const int j = threadIdx.x + u * THREADS;
+            if (j >= S * F / 4) break;
+            Half4 a = hl[j];
+            a.x = (_Float16)((float)a.x + sum(4 * j + 0));
+            a.y = (_Float16)((float)a.y + sum(4 * j + 1));
+            a.z = (_Float16)((float)a.z + sum(4 * j + 2));
+            a.w = (_Float16)((float)a.w + sum(4 * j + 3));
+            hl[j] = a;
+        }
         return;
     }
+    float *gbase = grad + e0;
+    if (S * F < 4) {  // a 2-entry table with one feature: two floats, less than a float4
+        if (threadIdx.x < S * F) gbase[threadIdx.x] += sum(threadIdx.x);
+        return;
+    }
+    float4 *gl = reinterpret_cast<float4 *>(gbase);
 #pragma unroll
     for (int u = 0; u < kFlushPer; ++u) {
         const int j = threadIdx.x + u * THREADS;
         if (j >= S * F / 4) break;
         float4 a = gl[j];
-        a.x += (float)ldexp((double)sl[4 * j + 0], -k);
-        a.y += (float)ldexp((double)sl[4 * j + 1], -k);
-        a.z += (float)ldexp((double)sl[4 * j + 2], -k);
-        a.w += (float)ldexp((double)sl[4 * j + 3], -k);
+        a.x += sum(4 * j + 0);
+        a.y += sum(4 * j + 1);
+        a.z += sum(4 * j + 2);
+        a.w += sum(4 * j + 3);
         gl[j] = a;
     }
 }

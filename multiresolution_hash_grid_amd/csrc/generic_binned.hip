@@ -130,14 +130,12 @@ __global__ __launch_bounds__(kGenThreads) void bin_generic_kernel(const float *_
             const uint32_t i0 = (cx0 ^ K) & bp.mask, i1 = ((cx0 + 1u) ^ K) & bp.mask;
             part[it] = i0 >> bp.s_log2;
             valid[it] = vp;
+            const uint64_t lbase = (uint64_t)l << bp.log2_table_size;  // level l's first entry
             if (vp && !fin) {
-                float *e0 = grad + (((uint64_t)l << bp.log2_table_size) + i0) * F;
-                float *e1 = grad + (((uint64_t)l << bp.log2_table_size) + i1) * F;
-#pragma unroll
-                for (int j = 0; j < F; ++j) {
-                    unsafeAtomicAdd(e0 + j, (1.f - f0) * (w_rest * gv[j]));
-                    unsafeAtomicAdd(e1 + j, f0 * (w_rest * gv[j]));
-                }
+                grad_atomic_entry<F>(grad, bp.grad_f16, (lbase + i0) * F,
+                                     [&](int j) { return (1.f - f0) * (w_rest * gv[j]); });
+                grad_atomic_entry<F>(grad, bp.grad_f16, (lbase + i1) * F,
+                                     [&](int j) { return f0 * (w_rest * gv[j]); });
                 valid[it] = false;  // no record
             } else if ((i1 >> bp.s_log2) == part[it]) {
                 const uint32_t t = min((uint32_t)__builtin_ctz(~cx0 | 0x80000000u), 15u);
@@ -150,11 +148,9 @@ __global__ __launch_bounds__(kGenThreads) void bin_generic_kernel(const float *_
                 rec[it].fx = 0.f;
 #pragma unroll
                 for (int j = 0; j < F; ++j) rec[it].g[j] = (1.f - f0) * (w_rest * gv[j]);
-                if (vp) {
-                    float *e = grad + (((uint64_t)l << bp.log2_table_size) + i1) * F;
-#pragma unroll
-                    for (int j = 0; j < F; ++j) unsafeAtomicAdd(e + j, f0 * (w_rest * gv[j]));
-                }
+                if (vp)
+                    grad_atomic_entry<F>(grad, bp.grad_f16, (lbase + i1) * F,
+                                         [&](int j) { return f0 * (w_rest * gv[j]); });
             }
             rank[it] = valid[it] ? atomicAdd(&cnt[part[it]], 1u) : 0u;
         }

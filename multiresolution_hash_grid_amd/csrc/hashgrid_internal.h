@@ -62,6 +62,7 @@ struct BinParams {
     int64_t level_records;   // record slots per level = tiles * rec_per_tile
     int32_t rec_per_tile;    // record slots of one tile (points x corner pairs)
     int32_t rec_bytes;       // bytes of one record
+    int32_t grad_f16;        // the gradient holds binary16 values (else fp32)
     int32_t res[kMaxLevels];
 };
 

@@ -87,6 +87,12 @@ class HashGridConfig:
     def torch_table_dtype(self) -> torch.dtype:
         return _TORCH_DTYPES[_DTYPES[self.table_dtype]]
 
+    @property
+    def torch_grad_dtype(self) -> torch.dtype:
+        """Element type of the table gradient buffer (binary16 only on the
+        binned backward, which then rounds each entry once)."""
+        return _TORCH_DTYPES[_DTYPES[self.grad_dtype]]
+
     def c(self) -> _Config:
         return _Config(self.n_dims, self.n_levels, self.n_features, self.log2_table_size,
                        self.base_resolution, self.finest_resolution,
@@ -273,15 +279,17 @@ def backward_workspace(cfg: HashGridConfig, n: int, device) -> torch.Tensor | No
 def hashgrid_backward(cfg: HashGridConfig, x: torch.Tensor, dout: torch.Tensor,
                       dtable: torch.Tensor, workspace="auto", stream=None) -> torch.Tensor:
     """Accumulate the table gradient of ``dout`` [n, >= L*F] into ``dtable``
-    (float32, table shape).  ``workspace``: a uint8 GPU tensor, "auto" (sized
-    by hashgrid_backward_workspace_size and allocated here) or None (the
-    atomic scatter)."""
+    (table shape, ``cfg.torch_grad_dtype``: float32, or float16 with
+    grad_dtype "f16", which needs the binned path's workspace).
+    ``workspace``: a uint8 GPU tensor, "auto" (sized by
+    hashgrid_backward_workspace_size and allocated here) or None (the atomic
+    scatter)."""
     _points(cfg, x)
     n = x.shape[0]
     _dev(dout, "dout", torch.float32)
     if dout.dim() != 2 or dout.shape[0] != n or dout.stride(1) != 1 or dout.shape[1] < cfg.out_features:
         raise ValueError("dout must be [n, >= L*F] with unit column stride")
-    _dev(dtable, "dtable", torch.float32)
+    _dev(dtable, "dtable", cfg.torch_grad_dtype)
     if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
         raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
     auto = isinstance(workspace, str)
@@ -305,7 +313,7 @@ def hashgrid_backward_noalloc(cfg: HashGridConfig, x: torch.Tensor, dout: torch.
     _dev(dout, "dout", torch.float32)
     if dout.dim() != 2 or dout.shape[0] != n or dout.stride(1) != 1 or dout.shape[1] < cfg.out_features:
         raise ValueError("dout must be [n, >= L*F] with unit column stride")
-    _dev(dtable, "dtable", torch.float32)
+    _dev(dtable, "dtable", cfg.torch_grad_dtype)
     if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
         raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
     c = cfg.c()
@@ -437,7 +445,7 @@ def hashgrid_mlp_backward(cfg: HashGridConfig, x: torch.Tensor, stage: torch.Ten
         if tuple(t.shape) != MLP_SHAPES[name[1:]] or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous {MLP_SHAPES[name[1:]]} tensor")
     g = _MlpGrads(*[t.data_ptr() for t in grads])
-    _dev(dtable, "dtable", torch.float32)
+    _dev(dtable, "dtable", cfg.torch_grad_dtype)
     if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
         raise ValueError(f"dtable must be a contiguous {cfg.table_shape} tensor")
     auto = isinstance(workspace, str)

@@ -81,7 +81,7 @@ def _call_backward(lib, cfg, x=0x1000, n=16, dout=0x2000, stride=None, dtable=0x
     (dict(table_dtype="bf16"), B.HG_EINVAL),
     (dict(n_features=3), B.HG_EUNSUPPORTED),
     (dict(n_dims=5), B.HG_EUNSUPPORTED),
-    (dict(grad_dtype="f16"), B.HG_EUNSUPPORTED),
+    (dict(grad_dtype="bf16"), B.HG_EINVAL),
 ])
 def test_bad_config_is_rejected(lib, bad, code):
     cfg = hg.HashGridConfig(**bad)
@@ -109,6 +109,34 @@ def test_bad_arguments_are_rejected(lib):
                                  None) == B.HG_EINVAL                 # workspace not 256-aligned
     big = hg.HashGridConfig(n_levels=64)
     assert _call_forward(lib, big, n=1 << 40) == B.HG_EINVAL
+
+
+def test_half_gradients_need_the_binned_path(lib):
+    # A binary16 gradient is rounded once per entry after an exact fixed-point
+    # sum; the atomic scatter would round at every addition, so every way to
+    # the atomic path is refused before anything is launched.
+    cfg = hg.HashGridConfig(grad_dtype="f16", table_dtype="f16")
+    c = cfg.c()
+    assert _call_backward(lib, cfg) == B.HG_EUNSUPPORTED  # no workspace
+    assert "binned" in lib.hashgrid_last_error().decode()
+    assert lib.hashgrid_backward(ctypes.byref(c), 0x1000, 16, 0x2000, 32, 0x3000, 0x4000, 256,
+                                 None) == B.HG_EUNSUPPORTED  # less than one level's workspace
+    assert lib.hashgrid_backward(ctypes.byref(c), 0x1000, 16, 0x2000, 32, 0x3004, 0x4000, 1 << 30,
+                                 None) == B.HG_EUNSUPPORTED  # dtable not 16-byte aligned
+    huge = hg.HashGridConfig(grad_dtype="f16", log2_table_size=28)  # 2^15 partitions: no binned path
+    ch = huge.c()
+    assert lib.hashgrid_backward(ctypes.byref(ch), 0x1000, 16, 0x2000, 32, 0x3000, 0x4000, 1 << 30,
+                                 None) == B.HG_EUNSUPPORTED
+    old = lib.hashgrid_tune_get(B.HG_TUNE_BWD_BINNED)
+    try:
+        assert lib.hashgrid_tune(B.HG_TUNE_BWD_BINNED, 0) == B.HG_OK
+        assert lib.hashgrid_backward(ctypes.byref(c), 0x1000, 16, 0x2000, 32, 0x3000, 0x4000, 1 << 30,
+                                     None) == B.HG_EUNSUPPORTED  # binning switched off
+    finally:
+        lib.hashgrid_tune(B.HG_TUNE_BWD_BINNED, old)
+    # The other entry points take the config as it is.
+    res = (ctypes.c_int32 * cfg.n_levels)()
+    assert lib.hashgrid_resolutions(ctypes.byref(c), res) == B.HG_OK
 
 
 def test_half_table_alignment_is_four_bytes(lib):
