@@ -138,6 +138,28 @@ def measure_input_grad(cfg, x, t, d, iters: int) -> dict:
             "algorithmic_bytes_per_point": bpp, "achieved_GBps": gbs, "frac": gbs / HBM_PEAK_GBS}
 
 
+def measure_half_grad(cfg, x, d, iters: int) -> dict:
+    """The standard workload's backward into a binary16 gradient buffer
+    (grad_dtype "f16", binned path: each entry rounded once), with the fp32
+    buffer's time beside it.  Algorithmic bytes as the fp32 backward's, the
+    gradient additions priced at 2 bytes."""
+    import dataclasses
+    import torch
+    import multiresolution_hash_grid_amd as hg
+    n = x.shape[0]
+    D, L, F = cfg.n_dims, cfg.n_levels, cfg.n_features
+    ws = hg.backward_workspace(cfg, n, x.device)
+    res = {}
+    for name, c in (("f32", cfg), ("f16", dataclasses.replace(cfg, grad_dtype="f16"))):
+        g = torch.zeros(cfg.table_shape, device=x.device, dtype=c.torch_grad_dtype)
+        res[name] = time_calls(lambda: hg.hashgrid_backward(c, x, d, g, workspace=ws), iters)
+    bpp = 4 * D + 4 * L * F + (1 << D) * L * F * 2
+    gbs = bpp * n / (res["f16"] * 1e-3) / 1e9
+    return {"points": n, "us_per_call": res["f16"] * 1e3, "f32_grad_us_per_call": res["f32"] * 1e3,
+            "points_per_s": n / (res["f16"] * 1e-3), "algorithmic_bytes_per_point": bpp,
+            "achieved_GBps": gbs, "frac": gbs / HBM_PEAK_GBS}
+
+
 def measure_shapes(dev, n: int, iters: int) -> dict:
     """Forward (lane-pair kernel, staged for F <= 4), backward (generic binned
     path) and dL/dx (lane pairs level-major for D >= 3) of other grid shapes at
@@ -361,6 +383,7 @@ def main() -> int:
     if args.section == "next":
         print(json.dumps({"next": {"adam": measure_adam(cfg, dev, 50),
                                    "input_grad": measure_input_grad(cfg, x, t, d, 20),
+                                   "half_grad": measure_half_grad(cfg, x, d, 20),
                                    "shapes": measure_shapes(dev, w.n_points, 10),
                                    "fused_mlp": measure_fused_mlp(dev, 5),
                                    "other_configs": measure_other_configs(dev, 5)}}), flush=True)
@@ -445,11 +468,12 @@ def main() -> int:
         "roofline_fwd_bwd_frac": (bpp["fwd"] + bpp["bwd"]) * w.n_points * K / elapsed / 1e9 / HBM_PEAK_GBS,
     }
     # The paths after the encoder's own step: Adam over the tables, dL/dx,
-    # other grid shapes, the MLP head.
+    # the binary16 gradient buffer, other grid shapes, the MLP head.
     if args.section in ("all", "next"):
         print("[bench] optimizer, input gradient, shapes, MLP head", file=sys.stderr, flush=True)
         result["next"] = {"adam": measure_adam(cfg, dev, 50),
                           "input_grad": measure_input_grad(cfg, x, t, d, 20),
+                          "half_grad": measure_half_grad(cfg, x, d, 20),
                           "shapes": measure_shapes(dev, w.n_points, 10),
                           "fused_mlp": measure_fused_mlp(dev, 5),
                           "other_configs": measure_other_configs(dev, 5)}
