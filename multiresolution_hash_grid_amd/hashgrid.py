@@ -9,6 +9,7 @@ library is not built, loading it fails loudly.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 import os
 import threading
 from dataclasses import dataclass
@@ -522,6 +523,16 @@ def hashgrid_tune_get(key: int) -> int:
     return v
 
 
+def _grad_config(cfg: HashGridConfig, param_dtype, n: int) -> HashGridConfig:
+    """Config for the autograd table gradient: a binary16 parameter gets a
+    binary16 gradient buffer where the binned path exists (each entry rounded
+    once, the same bits as rounding the fp32 gradient, half the memory), fp32
+    otherwise."""
+    if param_dtype == torch.float16 and n > 0 and hashgrid_backward_workspace_size(cfg, n)[0] > 0:
+        return dataclasses.replace(cfg, grad_dtype="f16")
+    return dataclasses.replace(cfg, grad_dtype="f32")
+
+
 class HashGridFunction(torch.autograd.Function):
     """Autograd wrapper: forward through hashgrid_forward; the table gradient
     through hashgrid_backward into a zeroed fp32 buffer and, when x requires
@@ -547,9 +558,10 @@ class HashGridFunction(torch.autograd.Function):
         if ctx.needs_input_grad[0]:
             dx = hashgrid_input_grad(cfg, x, kt, dout)
         if ctx.needs_input_grad[1]:
-            grad = torch.zeros(cfg.table_shape, device=x.device, dtype=torch.float32)
-            hashgrid_backward(cfg, x, dout, grad)
-            if ctx.table_dtype != torch.float32:
+            gcfg = _grad_config(cfg, ctx.table_dtype, x.shape[0])
+            grad = torch.zeros(cfg.table_shape, device=x.device, dtype=gcfg.torch_grad_dtype)
+            hashgrid_backward(gcfg, x, dout, grad)
+            if grad.dtype != ctx.table_dtype:
                 grad = grad.to(ctx.table_dtype)
         return dx, grad, None, None
 
@@ -614,9 +626,10 @@ class HashGridMLPFunction(torch.autograd.Function):
         x, stage, *params = ctx.saved_tensors
         cfg = ctx.cfg
         grads = [torch.zeros(MLP_SHAPES[k], device=x.device) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
-        dtable = torch.zeros(cfg.table_shape, device=x.device)
-        hashgrid_mlp_backward(cfg, x, stage, params, dy.contiguous().float(), grads, dtable)
-        if ctx.table_dtype != torch.float32:
+        gcfg = _grad_config(cfg, ctx.table_dtype, x.shape[0])
+        dtable = torch.zeros(cfg.table_shape, device=x.device, dtype=gcfg.torch_grad_dtype)
+        hashgrid_mlp_backward(gcfg, x, stage, params, dy.contiguous().float(), grads, dtable)
+        if dtable.dtype != ctx.table_dtype:
             dtable = dtable.to(ctx.table_dtype)
         return (None, dtable, *[g.to(dt) for g, dt in zip(grads, ctx.dtypes)], None, None)
 

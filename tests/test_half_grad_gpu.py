@@ -15,10 +15,10 @@ Covered: the standard grid (in one group and in the smallest level groups),
 binary16 tables, the large binary16 grid, the other shapes (D = 1, 2, 4;
 F = 1, 4, 8), a 2-entry F = 1 table (a partition flush of fewer than four
 values), starting values that are -0, subnormal or large, the
-allocation-free entry point, the MLP head's backward, and non-finite
-upstream values, which reach the entries through packed binary16 atomics as
-IEEE arithmetic has them.  A binary16 gradient without the binned path is
-refused.
+allocation-free entry point, the MLP head's backward, the autograd
+functions of a binary16 table parameter, and non-finite upstream values,
+which reach the entries through packed binary16 atomics as IEEE arithmetic
+has them.  A binary16 gradient without the binned path is refused.
 """
 import dataclasses
 import os
@@ -176,3 +176,36 @@ def test_half_gradient_without_a_workspace_is_refused():
     with pytest.raises(hg.HashGridError, match="binned"):
         hg.hashgrid_backward(cfg, dev(I.make_points(w)), dev(I.make_dout(w)), g, workspace=None)
     assert not torch.any(g.view(torch.int16) != 0)
+
+
+def test_half_parameter_autograd_gradient():
+    # A binary16 table parameter (fp32_master=False) gets its gradient from a
+    # binary16 buffer on the binned path: the same bits as the fp32 gradient
+    # rounded to binary16, through the encoder and through the MLP head.
+    w = I.resized(I.WORKLOADS["fused_mlp"], 3000)
+    x, d = dev(I.make_points(w)), dev(I.make_dout(w))
+    enc = hg.HashGridEncoder(table_dtype="f16", device=DEV, fp32_master=False)
+    with torch.no_grad():
+        enc.embeddings.copy_(dev(I.make_table(w)))
+    enc(x).backward(d)
+    got = enc.embeddings.grad
+    assert got.dtype == torch.float16
+    cfg = enc.cfg
+    g32 = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_backward(cfg, x, d, g32)
+    assert torch.equal(got.view(torch.int16), g32.half().view(torch.int16))
+
+    model = hg.HashGridMLP(device=DEV, fp32_master=False)
+    with torch.no_grad():
+        model.encoder.embeddings.copy_(enc.embeddings)
+    dy = dev(I.dout_normal(w.seed + 7, w.n_points, 4))
+    model(x).backward(dy)
+    got = model.encoder.embeddings.grad
+    assert got.dtype == torch.float16
+    params = [model.w1.detach().half(), model.b1.detach(), model.w2.detach().half(), model.b2.detach(),
+              model.w3.detach().half(), model.b3.detach()]
+    y, stage = hg.hashgrid_mlp_forward(cfg, x, model.encoder.embeddings.detach(), params)
+    grads = [torch.zeros(hg.hashgrid.MLP_SHAPES[k], device=DEV) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+    dt32 = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_mlp_backward(cfg, x, stage, params, dy, grads, dt32)
+    assert torch.equal(got.view(torch.int16), dt32.half().view(torch.int16))
