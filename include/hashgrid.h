@@ -194,7 +194,11 @@ int hashgrid_backward_workspace_size(const hg_config *cfg, int64_t n, size_t *by
  * <= 2^-11 of the entry; magnitudes past 65504 become +-Inf).  The few
  * contributions it adds directly (non-finite dout values, corners whose pair
  * straddles two partitions, run sums past fp32) use packed binary16 atomics,
- * each addition rounded.  Summing with atomics alone would round at every
+ * each addition rounded.  For points in [0,1)^D such pairs are rare (v_x + 1
+ * a multiple of the partition size, which needs N_l >= 8192 / F, 4096 for the
+ * D = 3, F = 2 grid up to T = 2^20), so the bound above holds.  Outside the
+ * cube every point with v_x = -1 (x_0 in [-1/N_l, 0)) straddles, so at coarse
+ * levels many points can reach one entry, each addition rounded to binary16.  Summing with atomics alone would round at every
  * addition, an error that grows with the additions an entry takes, so HG_F16 needs
  * the binned path: without a workspace of at least the minimum, with a dtable
  * that is not 16-byte aligned, or on a grid without a binned path the call

@@ -10,12 +10,17 @@ bars of the other parity tests:
   - forward <= 1e-6 * max|table|;
   - backward, binned (sized workspace) and atomic (no workspace), <= 1e-5 *
     max|oracle gradient| per level, added into a non-zero buffer;
+  - for points inside the unit cube, the binned backward into a binary16
+    gradient (each entry rounded once; pairs straddling two partitions, whose
+    additions round one by one, are rare there) <= 1e-3 * max|result| per
+    level;
   - dL/dx <= 1e-5 * max|oracle dL/dx| per coordinate.
 Eight more draws use the D = 3, F = 2 grid with the points sorted by a coarse
 cell, so that the wave pre-reduction meets long runs on random grids.  The
 draws are fixed by the case number, so a failure names a reproducible
 configuration (printed before each case runs).
 """
+import dataclasses
 import os
 
 import numpy as np
@@ -143,6 +148,15 @@ def test_random_configuration_matches_oracle(oracle, case):
         for l in range(w.n_levels):
             bound = 1e-5 * float(np.max(np.abs(gref[l]))) + 4e-7  # + the rounding of the fp32 base
             assert np.max(np.abs(got[l] - gref[l])) <= bound, (workspace, l)
+
+    if not spread and hg.hashgrid_backward_workspace_size(cfg, w.n_points)[0] > 0:
+        b16 = base.astype(np.float16)
+        grad = dev(b16)
+        hg.hashgrid_backward(dataclasses.replace(cfg, grad_dtype="f16"), xd, dd, grad, workspace="auto")
+        got = grad.cpu().numpy().astype(np.float64)
+        want = gref + b16.astype(np.float64)
+        for l in range(w.n_levels):
+            assert np.max(np.abs(got[l] - want[l])) <= 1e-3 * float(np.max(np.abs(want[l]))), ("f16", l)
 
     dxref = oracle.input_grad(g, x, t, d)
     dx = hg.hashgrid_input_grad(cfg, xd, td, dd).cpu().numpy().astype(np.float64)
