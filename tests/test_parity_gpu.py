@@ -114,6 +114,27 @@ def test_forward_half_tables_full_size_sampled(oracle):
     assert fwd_err(out[rows], ref, t) <= FWD_TOL
 
 
+def test_standard_grid_past_the_benchmarked_batch(oracle):
+    # 2^24 + 77 points on the standard grid, 64 times the benchmarked batch:
+    # 16385 bin tiles (the accumulate walks 17 chunks of tiles), level-major
+    # stages past 2^31 bytes, a ragged last tile.  Sampled forward rows (the
+    # first and last included) and every gradient entry against the oracle.
+    w = I.resized(I.WORKLOADS["standard"], (1 << 24) + 77)
+    print(f"standard grid n={w.n_points}", flush=True)
+    cfg = hg.HashGridConfig.of(w)
+    x, t, d = I.make_points(w), I.make_table(w), I.make_dout(w)
+    g = oracle.grid_of(w)
+    xd = dev(x)
+    out = hg.hashgrid_forward(cfg, xd, dev(t), workspace="auto")
+    rows = np.random.default_rng(17).choice(w.n_points, size=20000, replace=False)
+    rows[:2] = [0, w.n_points - 1]
+    assert fwd_err(out[torch.from_numpy(rows).to(DEV)].cpu().numpy(), oracle.forward(g, x[rows], t), t) <= FWD_TOL
+    del out
+    grad = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_backward(cfg, xd, dev(d), grad, workspace="auto")
+    bwd_check(grad.cpu().numpy(), oracle.backward(g, x, d), w.n_levels)
+
+
 @pytest.mark.parametrize("workspace", ["auto", None])
 def test_forward_writes_only_its_columns_of_a_wider_row(oracle, workspace):
     w = I.resized(I.WORKLOADS["standard"], 1000)
