@@ -67,10 +67,13 @@ struct BinParams {
 };
 
 // Binned backward of the other shapes (generic_binned.hip): records of
-// 2 + F words (corner code, f_x, F upstream products), at most 32 KB of them
-// per tile, tiles of at most 1024 points, and partitions of S entries with
-// S * F * 8 = 64 KB of fixed-point accumulators.
-constexpr int generic_max_recs(int F) { return F <= 2 ? 2048 : (F == 4 ? 1024 : 512); }
+// 2 + F words (corner code, f_x, F upstream products), 2048 of them per tile
+// (1024 for F = 8: 32, 48 or 40 KB), tiles of at most 1024 points, and
+// partitions of S entries with S * F * 8 = 64 KB of fixed-point
+// accumulators.  With many partitions (S = 8192 / F entries) a tile's runs
+// are short, so F = 4 and 8 take larger tiles than 32 KB would allow: each
+// accumulate workgroup then walks half as many tiles.
+constexpr int generic_max_recs(int F) { return F <= 4 ? 2048 : 1024; }
 constexpr int generic_tile(int D, int F) {
     return (generic_max_recs(F) >> (D - 1)) > 1024 ? 1024 : (generic_max_recs(F) >> (D - 1));
 }
