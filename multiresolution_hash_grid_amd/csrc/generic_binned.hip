@@ -188,8 +188,8 @@ hipError_t launch_shape(BinParams bp, int n_levels, int max_group, const float *
     if (group < 1) return hipErrorInvalidValue;
     const int ngroups = (n_levels + group - 1) / group;
     group = (n_levels + ngroups - 1) / ngroups;
-    // The run counters of 4096 partitions (32 KB) and a 32 KB record stage pass
-    // the default 64 KB of LDS per workgroup.  One level per workgroup, in
+    // The run counters of up to 4096 partitions (32 KB) next to a record stage
+    // of up to 48 KB can pass the default 64 KB of LDS per workgroup.  One level per workgroup, in
     // tile order: the XCD-paired order of the standard bin kernel (bin_slot)
     // measured mixed here (D2F2, D3F4 faster; D4F2 17 % slower).
     const size_t dyn = (2 * (size_t)bp.parts + 1) * sizeof(uint32_t);

@@ -300,6 +300,12 @@ def test_backward_runs_of_points_in_one_voxel(oracle, name, n):
 @pytest.mark.parametrize("name,kw", [
     # the largest table the binned backward takes: 2^25 / 2^13 = 4096 partitions, resolution 2^20
     ("max_binned_table", dict(n_levels=1, log2_table_size=25, base_resolution=1 << 20, finest_resolution=1 << 20)),
+    # the same 4096 partitions for F = 4 and F = 8 (2^11- and 2^10-entry partitions), whose
+    # 48 and 40 KB record stages sit next to 32 KB of run counters
+    ("max_binned_table_f4", dict(n_levels=1, n_dims=2, n_features=4, log2_table_size=23, base_resolution=1 << 12,
+                                 finest_resolution=1 << 12)),
+    ("max_binned_table_f8", dict(n_levels=1, n_dims=4, n_features=8, log2_table_size=22, base_resolution=64,
+                                 finest_resolution=64)),
     # past it (8192 partitions): the atomic path only
     ("beyond_binned_table", dict(n_levels=1, log2_table_size=26, base_resolution=1 << 12, finest_resolution=1 << 12)),
     # the most levels, up to resolution 2^23
