@@ -13,8 +13,6 @@ import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
-import pytest
-
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 C, OPT, MLP = "hashgrid_oracle.c", "optim_oracle.py", "mlp_oracle.py"
 PINS = {C: "tests/test_oracle_pins.py", OPT: "tests/test_oracle_optim.py", MLP: "tests/test_oracle_mlp.py"}
