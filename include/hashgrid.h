@@ -286,6 +286,9 @@ int hashgrid_mlp_forward(const hg_config *cfg, const float *x, int64_t n, const 
  *               at least the dL/de rows and partials are required, and with
  *               less than the full size the table gradient takes the smaller
  *               binned groups or the atomic scatter, as in hashgrid_backward.
+ *               A binary16 dtable (grad_dtype HG_F16) needs the binned
+ *               backward's minimum beyond the head's part; without it the
+ *               call returns HG_EUNSUPPORTED before anything is enqueued.
  * The weight gradients are summed per wave in registers and the wave
  * partials added in a fixed order: results do not depend on scheduling.
  * Errors: as hashgrid_backward. */

@@ -258,25 +258,32 @@ int launch_status(hipError_t e, const char *what) {
     return ok();
 }
 
+// A binary16 gradient is summed exactly in fixed point and rounded once per
+// entry on the binned path; the atomic scatter would round at every addition.
+// So HG_F16 needs the binned path with this workspace and dtable: refused
+// before anything is enqueued otherwise.
+int check_half_grad(const hg_config *cfg, int64_t n, const void *dtable, const void *workspace,
+                    size_t workspace_bytes) {
+    if (cfg->grad_dtype != HG_F16) return HG_OK;
+    hg::BinParams bp;
+    if (!plan_binned(*cfg, n, bp))
+        return fail(HG_EUNSUPPORTED, "grad_dtype HG_F16 needs the binned backward, which this grid and n lack");
+    const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
+    if (!g_tune.bwd_binned || !workspace || !aligned(dtable, 16) || workspace_bytes < per_level)
+        return fail(HG_EUNSUPPORTED,
+                    "grad_dtype HG_F16 needs the binned backward: a workspace of at least %zu bytes and a "
+                    "16-byte aligned dtable",
+                    per_level);
+    return HG_OK;
+}
+
 // The table gradient of upstream rows dout (validated by the caller).
 int table_backward(const hg_config *cfg, const float *x, int64_t n, const float *dout, int64_t dout_row_stride,
                    float *dtable, void *workspace, size_t workspace_bytes, void *stream) {
     int rc;
     hg::BinParams bp;
-    const bool binned = g_tune.bwd_binned && workspace && aligned(dtable, 16) && plan_binned(*cfg, n, bp);
-    if (cfg->grad_dtype == HG_F16) {
-        // binary16 gradients are summed exactly in fixed point and rounded
-        // once; the atomic scatter would round at every addition.
-        if (!plan_binned(*cfg, n, bp))
-            return fail(HG_EUNSUPPORTED, "grad_dtype HG_F16 needs the binned backward, which this grid and n lack");
-        const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
-        if (!binned || workspace_bytes < per_level)
-            return fail(HG_EUNSUPPORTED,
-                        "grad_dtype HG_F16 needs the binned backward: a workspace of at least %zu bytes and a "
-                        "16-byte aligned dtable",
-                        per_level);
-    }
-    if (binned) {
+    if ((rc = check_half_grad(cfg, n, dtable, workspace, workspace_bytes))) return rc;
+    if (g_tune.bwd_binned && workspace && aligned(dtable, 16) && plan_binned(*cfg, n, bp)) {
         const size_t per_level = round_up(hg::binned_level_bytes(bp), 256);
         if (workspace_bytes >= per_level) {
             // Whole levels per group; the launcher splits the workspace itself.
@@ -538,16 +545,17 @@ int hashgrid_mlp_backward(const hg_config *cfg, const float *x, int64_t n, const
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < de_bytes + part_bytes)
         return fail(HG_EINVAL, "workspace must be 256-byte aligned and hold at least n * 128 bytes plus the "
                                "weight-gradient partials (hashgrid_mlp_workspace_size)");
+    // The encoder's table gradient takes dL/de as its upstream rows and the
+    // rest of the workspace for the binned backward.
+    const size_t used = de_bytes + part_bytes;
+    void *rest = workspace_bytes > used ? (char *)workspace + used : nullptr;
+    if ((rc = check_half_grad(cfg, n, dtable, rest, workspace_bytes - used))) return rc;
     float *de = (float *)workspace;
     float *partials = (float *)((char *)workspace + de_bytes);
     const hg::MlpGrads g{grads->dw1, grads->db1, grads->dw2, grads->db2, grads->dw3, grads->db3};
     hipError_t e = hg::launch_mlp_backward((const _Float16 *)stage, n, mlp_params(params), dy, de, partials, g,
                                            (hipStream_t)stream);
     if (e != hipSuccess) return launch_status(e, "mlp backward");
-    // The encoder's table gradient with dL/de as the upstream rows; the rest of
-    // the workspace goes to the binned backward.
-    const size_t used = de_bytes + part_bytes;
-    void *rest = workspace_bytes > used ? (char *)workspace + used : nullptr;
     return table_backward(cfg, x, n, de, 32, dtable, rest, workspace_bytes - used, stream);
 }
 

@@ -139,6 +139,27 @@ def test_half_gradients_need_the_binned_path(lib):
     assert lib.hashgrid_resolutions(ctypes.byref(c), res) == B.HG_OK
 
 
+def test_mlp_backward_refuses_half_gradients_before_launching(lib):
+    # With only the head's part of the workspace (dL/de rows and partials) the
+    # table gradient would have no binned path: a binary16 dtable is refused
+    # before the head's kernels run, so the weight gradients stay untouched.
+    cfg = hg.HashGridConfig(grad_dtype="f16", table_dtype="f16")
+    c = cfg.c()
+    n = 4096
+    stage_b, bwd_b = ctypes.c_size_t(), ctypes.c_size_t()
+    full, least = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.hashgrid_mlp_workspace_size(ctypes.byref(c), n, ctypes.byref(stage_b), ctypes.byref(bwd_b)) == B.HG_OK
+    assert lib.hashgrid_backward_workspace_size(ctypes.byref(c), n, ctypes.byref(full), ctypes.byref(least)) == B.HG_OK
+    head_only = bwd_b.value - full.value
+    assert head_only > 0 and least.value > 0
+    params = B._MlpParams(*[0x10000 + 0x1000 * i for i in range(6)])
+    grads = B._MlpGrads(*[0x20000 + 0x1000 * i for i in range(6)])
+    rc = lib.hashgrid_mlp_backward(ctypes.byref(c), 0x1000, n, 0x40000, ctypes.byref(params), 0x50000,
+                                   ctypes.byref(grads), 0x60000, 0x100000, head_only, None)
+    assert rc == B.HG_EUNSUPPORTED
+    assert "binned" in lib.hashgrid_last_error().decode()
+
+
 def test_half_table_alignment_is_four_bytes(lib):
     cfg = hg.HashGridConfig(table_dtype="f16")
     assert _call_forward(lib, cfg, table=0x2002) == B.HG_EINVAL
