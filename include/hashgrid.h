@@ -389,6 +389,14 @@ int hashgrid_adam_step(const hg_adam *opt, int64_t count, float *param, float *m
                                    fit 128 KiB of LDS together from LDS (same bits as the
                                    gather): 1 (default) from 2^21 points, 2 always,
                                    0 never                                             */
+#define HG_TUNE_FWD_ORDER 13    /* staged D = 3, F = 2 forward: encode the points in the
+                                   order of a coarse cell (16^3 cells, Morton order) and
+                                   write each row back to its point's position (same
+                                   bits; the forward workspace grows by about 16 bytes
+                                   per point): 0 (default) never, 1 from 2^18 points,
+                                   2 always.  Pays on uniform batches (7 % at 2^18
+                                   points, 17 % at 2^22); costs on batches already in a
+                                   coherent order, such as ray samples (7 % at 2^20) */
 int hashgrid_tune(int key, int value);
 int hashgrid_tune_get(int key);
 

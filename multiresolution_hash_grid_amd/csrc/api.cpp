@@ -46,6 +46,7 @@ struct Tuning {
     int bwd_dense = 1;        // atomic backward: sum small levels in LDS first
     int fwd_split_kib = 4096; // staged gather of levels above this table size: one half per pass
     int fwd_dense = 1;        // staged forward: blend levels that fit LDS from LDS (1: from kFwdDenseMinPoints)
+    int fwd_order = 0;        // staged forward: order the points by a coarse cell (1: from kFwdOrderMinPoints)
 };
 Tuning g_tune;
 
@@ -228,6 +229,22 @@ bool split_forward(const hg_config &c) {
     return standard_shape(c) && g_tune.fwd_split_kib > 0 && level_bytes > ((size_t)g_tune.fwd_split_kib << 10);
 }
 
+// The staged D = 3, F = 2 forward can order its points by a coarse cell first
+// (point_order.hip: three short launches and 16 bytes per point), so that
+// neighbouring lanes share the coarse and middle levels' table lines; the
+// rows go back to the points' own positions.  Uniform batches gain from
+// 2^18 points (98 -> 91 us there, 1394 -> 1161 us at 2^22); batches whose
+// order is already coherent, as ray-ordered samples are, only pay for the
+// sort (2^20 ray samples: 256 -> 273 us), and so do binary16 tables and
+// levels gathered one half per pass.  The caller knows its batches, so the
+// order is off unless asked for (HG_TUNE_FWD_ORDER: 1 from
+// kFwdOrderMinPoints, 2 always).
+constexpr int64_t kFwdOrderMinPoints = (int64_t)1 << 18;
+bool fwd_order(const hg_config &c, int64_t n) {
+    if (!standard_shape(c) || n <= 0 || n >= ((int64_t)1 << 31)) return false;
+    return g_tune.fwd_order == 2 || (g_tune.fwd_order == 1 && n >= kFwdOrderMinPoints);
+}
+
 // Levels per binned group.  Where the budget (sized for the 256 MB last-level
 // cache of the MI355X) holds enough levels for at least 1024 accumulate
 // workgroups (two rounds of two per CU), groups take as many levels as keep
@@ -370,9 +387,10 @@ int hashgrid_forward_workspace_size(const hg_config *cfg, int64_t n, size_t *byt
     if (rc) return rc;
     if (n < 0) return fail(HG_EINVAL, "n = %lld < 0", (long long)n);
     if (!bytes_out) return fail(HG_EINVAL, "bytes_out is NULL");
-    // One stage, or two where the gather splits levels (the second half's blends).
+    // One stage, or two where the gather splits levels (the second half's
+    // blends), then the ordered points.
     const size_t stage = round_up((size_t)n * cfg->n_levels * cfg->n_features * sizeof(float), 256);
-    *bytes_out = split_forward(*cfg) ? 2 * stage : stage;
+    *bytes_out = (split_forward(*cfg) ? 2 * stage : stage) + (fwd_order(*cfg, n) ? hg::order_workspace_bytes(n) : 0);
     return ok();
 }
 
@@ -404,20 +422,34 @@ int hashgrid_forward(const hg_config *cfg, const float *x, int64_t n, const void
     const size_t stage_round = round_up(stage_bytes, 256);
     if (stage && split_forward(*cfg) && workspace_bytes >= stage_round + stage_bytes)
         stage2 = (float *)((char *)workspace + stage_round);
+    const float *xg = x;            // the points in the order the kernels encode them
+    const uint32_t *perm = nullptr;  // their original indices (NULL: the caller's order)
+    if (stage && fwd_order(*cfg, n)) {
+        const size_t off = (split_forward(*cfg) ? 2 : 1) * stage_round;
+        if (workspace_bytes >= off + hg::order_workspace_bytes(n)) {
+            float *xs;
+            uint32_t *pm;
+            rc = launch_status(hg::launch_point_order(x, n, (char *)workspace + off, &xs, &pm, (hipStream_t)stream),
+                               "forward (point order)");
+            if (rc) return rc;
+            xg = xs;
+            perm = pm;
+        }
+    }
     if (stage) {  // coarse levels from LDS, the others gathered
         hg::DenseLevels dl;
         bool keep[hg::kMaxLevels];
         fwd_dense_levels(*cfg, n, lp, dl, keep);
         if (dl.count) {
-            rc = launch_status(hg::launch_forward_dense(lp, dl, x, n, table, cfg->table_dtype, stage, false,
+            rc = launch_status(hg::launch_forward_dense(lp, dl, xg, n, table, cfg->table_dtype, stage, false,
                                                         (hipStream_t)stream),
                                "forward (LDS levels)");
             if (rc) return rc;
             restrict_levels(lp, keep);
         }
     }
-    return launch_status(hg::launch_forward(lp, x, n, table, cfg->table_dtype, out, out_row_stride, ft, stage,
-                                            (hipStream_t)stream, stage2),
+    return launch_status(hg::launch_forward(lp, xg, n, table, cfg->table_dtype, out, out_row_stride, ft, stage,
+                                            (hipStream_t)stream, stage2, perm),
                          "forward");
 }
 
@@ -696,6 +728,10 @@ int hashgrid_tune(int key, int value) {
         if (value < 0 || value > 2) break;
         g_tune.fwd_dense = value;
         return ok();
+    case HG_TUNE_FWD_ORDER:
+        if (value < 0 || value > 2) break;
+        g_tune.fwd_order = value;
+        return ok();
     default:
         return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
@@ -717,6 +753,7 @@ int hashgrid_tune_get(int key) {
     case HG_TUNE_BWD_DENSE: return g_tune.bwd_dense;
     case HG_TUNE_FWD_SPLIT_KIB: return g_tune.fwd_split_kib;
     case HG_TUNE_FWD_DENSE: return g_tune.fwd_dense;
+    case HG_TUNE_FWD_ORDER: return g_tune.fwd_order;
     default: return fail(HG_EINVAL, "unknown tuning key %d", key);
     }
 }

@@ -486,7 +486,7 @@ template <int F, bool VEC>
 __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restrict__ stage,
                                                            const float *__restrict__ stage2, uint64_t second,
                                                            int64_t n, int L, int pts, float *__restrict__ out,
-                                                           int64_t ostride) {
+                                                           int64_t ostride, const uint32_t *__restrict__ perm) {
     extern __shared__ float tile[];  // [pts][F L + 4]: rows 16-byte aligned when F L is a multiple of 4
     const int row = F * L + 4;
     const int64_t p0 = (int64_t)blockIdx.x * pts;
@@ -523,9 +523,11 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restri
         const int q_per_row = F * L / 4;  // float4 per output row
         for (int e = threadIdx.x; e < pts * q_per_row; e += kBlock) {
             const int i = e / q_per_row, c = e - i * q_per_row;
-            if (i < np)
-                *reinterpret_cast<float4 *>(out + (p0 + i) * ostride + 4 * c) =
+            if (i < np) {
+                const int64_t r = perm ? (int64_t)perm[p0 + i] : p0 + i;  // the row's point
+                *reinterpret_cast<float4 *>(out + r * ostride + 4 * c) =
                     *reinterpret_cast<const float4 *>(&tile[i * row + 4 * c]);
+            }
         }
     } else {
         const int total = pts * F * L;
@@ -540,14 +542,15 @@ __global__ __launch_bounds__(kBlock) void transpose_kernel(const float *__restri
         __syncthreads();
         for (int e = threadIdx.x; e < total; e += kBlock) {
             const int i = e / (F * L), c = e - i * F * L;
-            if (i < np) out[(p0 + i) * ostride + c] = tile[i * row + c];
+            if (i < np) out[(perm ? (int64_t)perm[p0 + i] : p0 + i) * ostride + c] = tile[i * row + c];
         }
     }
 }
 
 template <int F>
 hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, int64_t ostride,
-                              hipStream_t stream, const float *stage2 = nullptr, uint64_t second = ~0ull) {
+                              hipStream_t stream, const float *stage2 = nullptr, uint64_t second = ~0ull,
+                              const uint32_t *perm = nullptr) {
     // Points per workgroup: 64, fewer for wide rows so that the tile stays near 32 KB.
     const int pts = std::max(4, std::min(64, 8192 / (F * L + 4)) / 4 * 4);
     const unsigned blocks = (unsigned)((n + pts - 1) / pts);
@@ -555,8 +558,12 @@ hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, 
     bool vec = (n * F) % 4 == 0 && (F * L) % 4 == 0 && ostride % 4 == 0 && ((uintptr_t)out & 15) == 0 &&
                ((uintptr_t)stage & 15) == 0;
     if (vec && stage2 && ((uintptr_t)stage2 & 15)) vec = false;
-    if (vec) transpose_kernel<F, true><<<blocks, kBlock, lds, stream>>>(stage, stage2, second, n, L, pts, out, ostride);
-    else transpose_kernel<F, false><<<blocks, kBlock, lds, stream>>>(stage, stage2, second, n, L, pts, out, ostride);
+    if (vec)
+        transpose_kernel<F, true><<<blocks, kBlock, lds, stream>>>(stage, stage2, second, n, L, pts, out, ostride,
+                                                                   perm);
+    else
+        transpose_kernel<F, false><<<blocks, kBlock, lds, stream>>>(stage, stage2, second, n, L, pts, out, ostride,
+                                                                    perm);
     return hipGetLastError();
 }
 
@@ -604,7 +611,7 @@ hipError_t launch_gather_dt(const LaunchParams &lp, const float *x, int64_t n, c
 
 hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, const void *table,
                           int table_dtype, float *out, int64_t out_stride, const FwdTune &ft,
-                          float *stage, hipStream_t stream, float *stage2) {
+                          float *stage, hipStream_t stream, float *stage2, const uint32_t *perm) {
     hipError_t e;
     if (!stage) {
         return table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, out, out_stride, 2, ft, stream)
@@ -619,7 +626,7 @@ hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, con
                              : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2);
         if (e != hipSuccess) return e;
     }
-    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream, stage2, gathered);
+    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream, stage2, gathered, perm);
 }
 
 template <int DT, class OutT>

@@ -118,9 +118,12 @@ struct FwdTune {
 // one table half per pass (FwdTune::split_kib), the second half writes its
 // partial blends there and the transpose adds them; without it the second
 // half adds the first half's in place.
+// perm (NULL, or with a stage): x is in a sorted order and perm[i] is the
+// original index of point i; the transpose writes row i to out row perm[i].
 hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, const void *table,
                           int table_dtype, float *out, int64_t out_stride, const FwdTune &ft,
-                          float *stage, hipStream_t stream, float *stage2 = nullptr);
+                          float *stage, hipStream_t stream, float *stage2 = nullptr,
+                          const uint32_t *perm = nullptr);
 hipError_t launch_backward(const LaunchParams &lp, const float *x, int64_t n, const float *dout,
                            int64_t dout_stride, float *dtable, int lanes, hipStream_t stream);
 // Shapes other than D = 3, F = 2 (generic_kernels.hip): D in 1..4,
@@ -129,6 +132,18 @@ hipError_t launch_forward_generic(const LaunchParams &lp, int D, int F, const fl
                                   const void *table, int table_dtype, float *out, int64_t out_stride, int lanes,
                                   float *stage, hipStream_t stream);
 // [L][n][F] level-major stage -> rows out[p * ostride + l * F + j].
+// Point order of the staged D = 3, F = 2 forward (point_order.hip): the
+// points sorted by a coarse cell into xs [n][3], and perm[i] the original
+// index of sorted point i.  The points are counted in at most
+// kOrderMaxGroups groups of at least kOrderGroup points.  The workspace holds
+// xs, perm and the count tables: order_workspace_bytes(n) bytes, 256-byte
+// aligned.  n < 2^31.
+constexpr int kOrderGroup = 1024;
+constexpr int kOrderMaxGroups = 256;
+size_t order_workspace_bytes(int64_t n);
+hipError_t launch_point_order(const float *x, int64_t n, void *workspace, float **xs_out, uint32_t **perm_out,
+                              hipStream_t stream);
+
 hipError_t launch_transpose(int F, const float *stage, int64_t n, int L, float *out, int64_t ostride,
                             hipStream_t stream);
 hipError_t launch_backward_generic(const LaunchParams &lp, int D, int F, const float *x, int64_t n,

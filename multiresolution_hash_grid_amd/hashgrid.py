@@ -23,7 +23,8 @@ HG_OK, HG_EINVAL, HG_EUNSUPPORTED, HG_EHIP = 0, -1, -2, -3
 HG_F32, HG_F16 = 0, 1
 (HG_TUNE_FWD_LANES, HG_TUNE_BWD_LANES, HG_TUNE_CHUNK_POINTS, HG_TUNE_XCD_MAP, HG_TUNE_BWD_BINNED,
  HG_TUNE_FWD_UNROLL, HG_TUNE_FWD_NT, HG_TUNE_FWD_STAGED, HG_TUNE_BWD_PART_LOG2,
- HG_TUNE_BWD_GROUP_MIB, HG_TUNE_BWD_DENSE, HG_TUNE_FWD_SPLIT_KIB, HG_TUNE_FWD_DENSE) = range(13)
+ HG_TUNE_BWD_GROUP_MIB, HG_TUNE_BWD_DENSE, HG_TUNE_FWD_SPLIT_KIB, HG_TUNE_FWD_DENSE,
+ HG_TUNE_FWD_ORDER) = range(14)
 _DTYPES = {"f32": HG_F32, "f16": HG_F16}
 _TORCH_DTYPES = {HG_F32: torch.float32, HG_F16: torch.float16}
 

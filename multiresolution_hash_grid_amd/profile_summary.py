@@ -35,7 +35,8 @@ import sys
 
 PASSES = {
     "forward": ("fwd_f2_kernel", "fwd_f2_pair_kernel", "fwd_dense_kernel", "transpose_kernel", "fwd_generic_kernel",
-                "fwd_generic_pair_kernel", "mlp_fwd_kernel"),
+                "fwd_generic_pair_kernel", "mlp_fwd_kernel", "order_count_kernel", "order_prefix_kernel",
+                "order_scatter_kernel"),
     "backward": ("bin_kernel", "accumulate_kernel", "bwd_f2_kernel", "bwd_f2_quad_kernel", "bin_generic_kernel",
                  "bwd_generic_kernel", "bwd_dense_kernel", "mlp_bwd_kernel", "mlp_dy_max_kernel",
                  "mlp_reduce1_kernel", "mlp_reduce2_kernel"),

@@ -25,8 +25,12 @@ hipError_t launch_binned_backward(BinParams, int, int, const float *, int64_t, c
     return reached("binned backward");
 }
 hipError_t launch_forward(const LaunchParams &, const float *, int64_t, const void *, int, float *, int64_t,
-                          const FwdTune &, float *, hipStream_t, float *) {
+                          const FwdTune &, float *, hipStream_t, float *, const uint32_t *) {
     return reached("forward");
+}
+size_t order_workspace_bytes(int64_t n) { return (size_t)n * 16 + (1 << 16); }
+hipError_t launch_point_order(const float *, int64_t, void *, float **, uint32_t **, hipStream_t) {
+    return reached("point order");
 }
 hipError_t launch_forward_dense(const LaunchParams &, const DenseLevels &, const float *, int64_t, const void *,
                                 int, void *, bool, hipStream_t) {

@@ -211,7 +211,18 @@ def test_backward_workspace_size():
 
 def test_forward_workspace_size():
     cfg = hg.HashGridConfig()
-    assert hg.hashgrid_forward_workspace_size(cfg, 1 << 18) == 32 << 20
+    n = 1 << 18
+    stage = 32 << 20
+    # the ordered points and their indices, the 256 groups' cell counts and the cell totals
+    order = n * 12 + n * 4 + 256 * 4096 * 4 + 4096 * 4
+    assert hg.hashgrid_forward_workspace_size(cfg, n) == stage  # the order is off by default
+    old = hg.hashgrid_tune_get(B.HG_TUNE_FWD_ORDER)
+    try:
+        hg.hashgrid_tune(B.HG_TUNE_FWD_ORDER, 1)
+        assert hg.hashgrid_forward_workspace_size(cfg, n) == stage + order
+        assert hg.hashgrid_forward_workspace_size(cfg, n - 1) == stage  # below 2^18 points
+    finally:
+        hg.hashgrid_tune(B.HG_TUNE_FWD_ORDER, old)
     assert hg.hashgrid_forward_workspace_size(cfg, 3) == 512      # 3 * 16 * 2 * 4 = 384, rounded to 256
     assert hg.hashgrid_forward_workspace_size(cfg, 0) == 0
 
@@ -222,7 +233,7 @@ def test_tuning_knobs(lib):
                            (B.HG_TUNE_BWD_BINNED, 0, 3), (B.HG_TUNE_FWD_UNROLL, 2, 3),
                            (B.HG_TUNE_FWD_NT, 1, 2), (B.HG_TUNE_FWD_STAGED, 0, 2),
                            (B.HG_TUNE_BWD_PART_LOG2, 12, 14), (B.HG_TUNE_BWD_GROUP_MIB, 64, -1),
-                           (B.HG_TUNE_FWD_DENSE, 2, 3)):
+                           (B.HG_TUNE_FWD_DENSE, 2, 3), (B.HG_TUNE_FWD_ORDER, 2, 3)):
         old = hg.hashgrid_tune_get(key)
         hg.hashgrid_tune(key, good)
         assert hg.hashgrid_tune_get(key) == good

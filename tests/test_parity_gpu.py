@@ -437,7 +437,8 @@ def test_launch_variants_match_oracle(oracle, key, value):
                                        (B.HG_TUNE_XCD_MAP, 0), (B.HG_TUNE_FWD_UNROLL, 1), (B.HG_TUNE_FWD_NT, 1),
                                        (B.HG_TUNE_FWD_STAGED, 0), (B.HG_TUNE_BWD_PART_LOG2, 11),
                                        (B.HG_TUNE_BWD_PART_LOG2, 13), (B.HG_TUNE_BWD_GROUP_MIB, 0),
-                                       (B.HG_TUNE_BWD_GROUP_MIB, 3), (B.HG_TUNE_FWD_DENSE, 2)])
+                                       (B.HG_TUNE_BWD_GROUP_MIB, 3), (B.HG_TUNE_FWD_DENSE, 2),
+                                       (B.HG_TUNE_FWD_ORDER, 2)])
 def test_result_neutral_knobs_give_identical_results(key, value):
     # The launch shapes that the header documents as result-neutral reproduce
     # the default's forward and binned backward bit for bit.

@@ -22,6 +22,7 @@ def test_kernel_names_and_passes():
     assert ps.pass_of("hg::(anonymous namespace)::mlp_dy_max_kernel(float4 const*)") == "backward"
     assert ps.pass_of("hg::(anonymous namespace)::fwd_generic_pair_kernel<3, 4, 0>(float const*)") == "forward"
     assert ps.pass_of("void hg::(anonymous namespace)::fwd_dense_kernel<1, _Float16>(float const*, long)") == "forward"
+    assert ps.pass_of("hg::(anonymous namespace)::order_scatter_kernel(hg::(anonymous namespace)::Point3 const*)") == "forward"
 
 
 def _write(path, rows, fields):
