@@ -579,21 +579,73 @@ hipError_t launch_transpose_f(const float *stage, int64_t n, int L, float *out, 
 // and level made the forward 1.6 times slower.  The other shapes' kernels
 // gather in one pass: for F = 4 at 8 MiB a split gained 3 %, and F = 8 rows,
 // written directly, cost 2.9 times as much.
+//
+// Only a level whose gathers can touch more table lines than that is split.
+// The x prime is 1, so a row of N_l + 1 x-vertices (fixed y and z) lies in
+// one aligned block of next_pow2(N_l + 1) entries, and a level has
+// (N_l + 1)^2 such rows: the coarse levels of a large table touch a small
+// part of it (the binary16 T = 2^21 grid's levels up to N_l = 79 touch at
+// most 3.3 MB of its 8 MiB) and are gathered in one pass.
+size_t level_footprint(const LaunchParams &lp, int l, size_t entry_bytes) {
+    const uint64_t R = (uint64_t)lp.res[l] + 1;
+    uint64_t block = 1;
+    while (block < R) block <<= 1;
+    const uint64_t per_line = 128 / entry_bytes;
+    const uint64_t table_lines = std::max<uint64_t>(1, ((uint64_t)1 << lp.log2_table_size) / per_line);
+    const uint64_t row_lines = (block + per_line - 1) / per_line;
+    const uint64_t rows = R * R;
+    // rows * row_lines, capped at the table (no overflow: R <= 2^20 + 1)
+    const uint64_t lines = rows > table_lines / row_lines ? table_lines : std::min(table_lines, rows * row_lines);
+    return (size_t)(lines * 128);
+}
 
+// The levels of lp (a staged gather) whose footprint exceeds ft.split_kib.
+uint64_t split_levels(const LaunchParams &lp, size_t entry_bytes, const FwdTune &ft) {
+    uint64_t split = 0;
+    if (ft.split_kib <= 0) return 0;
+    const int have = lp.chunks ? lp.items / lp.chunks : 0;
+    for (int i = 0; i < have; ++i) {
+        const int l = lp.level_order[i];
+        if (level_footprint(lp, l, entry_bytes) > ((size_t)ft.split_kib << 10)) split |= 1ull << l;
+    }
+    return split;
+}
+
+// lp restricted to the levels of the bit mask (their order kept).
+LaunchParams with_levels(const LaunchParams &lp, uint64_t levels) {
+    LaunchParams r = lp;
+    int pos = 0;
+    const int have = lp.chunks ? lp.items / lp.chunks : 0;
+    for (int i = 0; i < have; ++i) {
+        const int l = lp.level_order[i];
+        if ((levels >> l) & 1u) r.level_order[pos++] = (int8_t)l;
+    }
+    r.items = r.chunks * pos;
+    r.per_xcd = (r.items + kNumXcd - 1) / kNumXcd;
+    return r;
+}
+
+// split: the levels gathered one table half per pass (split_levels).
 template <int DT>
 hipError_t launch_gather_dt(const LaunchParams &lp, const float *x, int64_t n, const void *table, float *out,
                             int64_t ostride, int64_t lstride, const FwdTune &ft, hipStream_t stream,
-                            float *out2 = nullptr) {
+                            float *out2 = nullptr, uint64_t split = 0) {
     dim3 grid(grid_blocks(lp)), block(kBlock);
-    const size_t level_bytes = (DT == 0 ? sizeof(float2) : sizeof(uint32_t)) << lp.log2_table_size;
     if (lstride == 2 && ft.lanes == 1) {
         fwd_f2_kernel<DT><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lp);
-    } else if (lstride != 2 && ft.split_kib > 0 && level_bytes > ((size_t)ft.split_kib << 10)) {  // staged output only
-        for (int half = 0; half < 2; ++half) {
+    } else if (split && lstride != 2) {  // staged output only
+        // The levels of `split` one table half per pass, the others in one.
+        const LaunchParams lw = with_levels(lp, ~split), ls = with_levels(lp, split);
+        if (lw.items > 0) {
+            hipError_t e = launch_gather_dt<DT>(lw, x, n, table, out, ostride, lstride, ft, stream, nullptr, 0);
+            if (e != hipSuccess) return e;
+        }
+        const dim3 sgrid(grid_blocks(ls));
+        for (int half = 0; half < 2 && ls.items > 0; ++half) {
             float *dst = half && out2 ? out2 : out;
             const int add = half && !out2;
-            if (ft.nt) fwd_f2_pair_kernel<DT, 4, true, float, true><<<grid, block, 0, stream>>>(x, n, table, dst, ostride, lstride, lp, half, add);
-            else fwd_f2_pair_kernel<DT, 4, false, float, true><<<grid, block, 0, stream>>>(x, n, table, dst, ostride, lstride, lp, half, add);
+            if (ft.nt) fwd_f2_pair_kernel<DT, 4, true, float, true><<<sgrid, block, 0, stream>>>(x, n, table, dst, ostride, lstride, ls, half, add);
+            else fwd_f2_pair_kernel<DT, 4, false, float, true><<<sgrid, block, 0, stream>>>(x, n, table, dst, ostride, lstride, ls, half, add);
         }
     } else if (ft.nt) {
         if (ft.unroll == 1) fwd_f2_pair_kernel<DT, 1, true><<<grid, block, 0, stream>>>(x, n, table, out, ostride, lstride, lp, 0);
@@ -617,16 +669,15 @@ hipError_t launch_forward(const LaunchParams &lp, const float *x, int64_t n, con
         return table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, out, out_stride, 2, ft, stream)
                                 : launch_gather_dt<1>(lp, x, n, table, out, out_stride, 2, ft, stream);
     }
-    // Levels of this gather (lp.level_order; the others came from launch_forward_dense).
-    uint64_t gathered = 0;
-    const int levels = lp.chunks ? lp.items / lp.chunks : 0;
-    for (int i = 0; i < levels; ++i) gathered |= 1ull << lp.level_order[i];
+    // Levels of this gather (lp.level_order; the others came from launch_forward_dense)
+    // that go one table half per pass; stage2, if any, holds their second halves.
+    const uint64_t split = split_levels(lp, table_dtype == 0 ? sizeof(float2) : sizeof(uint32_t), ft);
     if (lp.items > 0) {
-        e = table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2)
-                             : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2);
+        e = table_dtype == 0 ? launch_gather_dt<0>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2, split)
+                             : launch_gather_dt<1>(lp, x, n, table, stage, 2, 2 * n, ft, stream, stage2, split);
         if (e != hipSuccess) return e;
     }
-    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream, stage2, gathered, perm);
+    return launch_transpose_f<2>(stage, n, lp.n_levels, out, out_stride, stream, stage2, split, perm);
 }
 
 template <int DT, class OutT>

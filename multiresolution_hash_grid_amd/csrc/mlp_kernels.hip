@@ -6,8 +6,9 @@
 // e being the 32 encoded features (L = 16 levels x F = 2) of a point.  It is
 // a dense contraction, so it runs on the matrix cores: binary16 operands,
 // fp32 accumulation.  The contractions over features and units (K = 32 and
-// 64) use gfx950's v_mfma_f32_16x16x32_f16, the weight gradients, which
-// contract over the 16 points of a tile, v_mfma_f32_16x16x16f16.
+// 64) use gfx950's v_mfma_f32_16x16x32_f16, and so do the weight gradients,
+// which contract over 32 points at a time; dz2 = W3^T dL/dy (K = 4 outputs)
+// takes one v_mfma_f32_16x16x16f16 per 16 units.
 //
 // Layout.  For D[i][j] = sum_k A[i][k] B[k][j] (16 x 16 x 16), lane l of the
 // wave holds A[l%16][4(l/16) + r], B[4(l/16) + r][l%16] and
@@ -35,10 +36,12 @@
 // points gives dL/dy ~ 1e-7, which unscaled would sit at binary16's
 // subnormal floor.  dz2 and dz1 carry the scale; dL/de and the weight and
 // bias gradients are multiplied by 1/s in fp32, which is exact.  The weight
-// gradients contract over points, so a tile's activations go through LDS
-// to put the 16 points on the k axis (dW2 = dz2 h1^T etc.); every wave keeps
-// its running dW and db in registers and writes them once, and two reduction
-// kernels add the per-wave partials, in a fixed order, into the caller's fp32
+// gradients contract over points (dW2 = dz2 h1^T etc.), so the activations of
+// a workgroup's 64 points go through LDS, transposed, to put the points on
+// the k axis, and the four waves split the weight gradients between them:
+// each keeps a quarter of the running dW and db in registers (two waves then
+// fit a SIMD) and writes it once per workgroup, and two reduction kernels
+// add the workgroups' partials, in a fixed order, into the caller's fp32
 // gradients.
 #include <algorithm>
 #include <map>
@@ -73,15 +76,41 @@ __device__ __forceinline__ half8_t join8(half4_t lo, half4_t hi) {
     return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-__device__ __forceinline__ half4_t relu_half(float4_t v, uint32_t &mask, int shift) {
-    half4_t h;
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef short short2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half4_t to_half4(float4_t v) {
+    const half2_t lo = __builtin_convertvector(float2_t{v[0], v[1]}, half2_t);
+    const half2_t hi = __builtin_convertvector(float2_t{v[2], v[3]}, half2_t);
+    return half4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// ReLU of fp32 pre-activations, rounded to binary16 (to nearest even).  A
+// unit whose input is not > 0 (NaN included) gets -0 rather than +0: the
+// same value in every product, while the sign bit keeps the ReLU's decision
+// for the backward (an input in (0, 2^-25) rounds to +0 and still passes the
+// gradient, as [z > 0] has it).
+__device__ __forceinline__ half4_t relu_half(float4_t v) {
+    float4_t r;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const bool pos = v[r] > 0.f;
-        mask |= (uint32_t)pos << (shift + r);
-        h[r] = (_Float16)(pos ? v[r] : 0.f);
-    }
-    return h;
+    for (int i = 0; i < 4; ++i) r[i] = v[i] > 0.f ? v[i] : -0.f;
+    return to_half4(r);
+}
+
+// dL/dz of four units: the fp32 sums v rounded to binary16 where the unit's
+// activation h has a clear sign bit (the ReLU passed), +0 elsewhere.
+__device__ __forceinline__ half4_t relu_grad(float4_t v, half4_t h) {
+    typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
+    const uint2_t g = __builtin_bit_cast(uint2_t, to_half4(v));
+    const uint2_t hb = __builtin_bit_cast(uint2_t, h);
+    // 0xFFFF in each half whose sign bit is set (the vector elements are
+    // copied to scalars first: clang bit-casts an element operand of
+    // __builtin_bit_cast from the wrong element)
+    const uint32_t h0 = hb[0], h1 = hb[1];
+    const uint32_t blo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(short2_t, h0) >> (short)15);
+    const uint32_t bhi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(short2_t, h1) >> (short)15);
+    return __builtin_bit_cast(half4_t, uint2_t{g[0] & ~blo, g[1] & ~bhi});
 }
 
 // The forward weights as 16 x 16 x 32 A operands: row = output unit, slot
@@ -132,20 +161,15 @@ __device__ __forceinline__ void load_encoding(const _Float16 *__restrict__ stage
     }
 }
 
-// Layers 1 and 2 of 16 points: binary16 activations and their ReLU masks
-// (bit 4 mb + r: unit 16 mb + 4 q + r had a positive input).
+// Layers 1 and 2 of 16 points: binary16 activations, -0 where the ReLU blocked.
 __device__ __forceinline__ void hidden_layers(const FwdWeights &w, const half4_t (&eb)[2], half4_t (&h1)[4],
-                                              half4_t (&h2)[4], uint32_t &m1, uint32_t &m2) {
-    m1 = m2 = 0;
+                                              half4_t (&h2)[4]) {
     const half8_t e8 = join8(eb[0], eb[1]);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) h1[mb] = relu_half(mfma32(w.a1[mb], e8, w.b1[mb]), m1, 4 * mb);
+    for (int mb = 0; mb < 4; ++mb) h1[mb] = relu_half(mfma32(w.a1[mb], e8, w.b1[mb]));
     const half8_t h1lo = join8(h1[0], h1[1]), h1hi = join8(h1[2], h1[3]);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const float4_t acc = mfma32(w.a2[mb][1], h1hi, mfma32(w.a2[mb][0], h1lo, w.b2[mb]));
-        h2[mb] = relu_half(acc, m2, 4 * mb);
-    }
+    for (int mb = 0; mb < 4; ++mb) h2[mb] = relu_half(mfma32(w.a2[mb][1], h1hi, mfma32(w.a2[mb][0], h1lo, w.b2[mb])));
 }
 
 // Slices of dL/dy whose largest finite magnitude mlp_dy_max_kernel writes.
@@ -175,7 +199,7 @@ __global__ __launch_bounds__(256) void mlp_dy_max_kernel(const float4 *__restric
 // kernel's occupancy times the CU count, found once per device and kernel),
 // so that no round of workgroups runs alone at the end; never more than the
 // 16-point tiles need.  1024 workgroups when the occupancy query fails.
-int resident_workgroups(const void *kernel) {
+int resident_workgroups(const void *kernel, size_t lds_bytes) {
     static std::mutex mu;
     static std::map<std::pair<int, const void *>, int> cache;
     int dev = 0;
@@ -185,7 +209,7 @@ int resident_workgroups(const void *kernel) {
     if (it != cache.end()) return it->second;
     int per_cu = 0, cus = 0;
     int r = 1024;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kMlpWaves, 0) == hipSuccess &&
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kMlpWaves, lds_bytes) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && per_cu > 0 &&
         cus > 0)
         r = per_cu * cus;
@@ -195,9 +219,9 @@ int resident_workgroups(const void *kernel) {
 
 constexpr int kMaxMlpGrid = 1024;  // the partials workspace is sized for this many workgroups
 
-int mlp_grid(int64_t tiles, const void *kernel) {
+int mlp_grid(int64_t tiles, const void *kernel, size_t lds_bytes = 0) {
     const int64_t want = (tiles + kMlpWaves - 1) / kMlpWaves;
-    return (int)std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)resident_workgroups(kernel), kMaxMlpGrid}));
+    return (int)std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)resident_workgroups(kernel, lds_bytes), kMaxMlpGrid}));
 }
 
 // ---------------------------------------------------------------- forward
@@ -217,8 +241,7 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 
         const bool ok = p < n;
         half4_t eb[2] = {eb_next[0], eb_next[1]}, h1[4], h2[4];
         if (t + nwaves < tiles) load_encoding(stage, n, min((t + nwaves) * 16 + c, n - 1), q, eb_next);
-        uint32_t m1, m2;
-        hidden_layers(w, eb, h1, h2, m1, m2);
+        hidden_layers(w, eb, h1, h2);
         const float4_t o = mfma32(w.a3[1], join8(h2[2], h2[3]), mfma32(w.a3[0], join8(h2[0], h2[1]), w.b3));
         if (q == 0 && ok) *reinterpret_cast<float4 *>(y + p * kOut) = make_float4(o[0], o[1], o[2], o[3]);
     }
@@ -226,41 +249,66 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 
 
 // ---------------------------------------------------------------- backward
 
-// LDS rows of one wave's tile, points as rows, binary16, padded against bank conflicts.
-struct TileLds {
-    _Float16 e[16][kIn + 8];
-    _Float16 h1[16][kHid + 8];
-    _Float16 h2[16][kHid + 8];
-    _Float16 dz1[16][kHid + 8];
-    _Float16 dz2[16][kHid + 8];
-    _Float16 g3[16][8];
+// One workgroup's block of kBlockPts points for the weight gradients: the
+// activations transposed, units as rows and the block's points as columns
+// (binary16), so that an operand with the points on the k axis is two
+// 8-byte LDS reads per lane.  Rows are padded to 136 bytes: the 16 rows a
+// read or write touches then start 34 banks apart, and a half-wave's 8-byte
+// accesses meet 64 distinct banks.
+constexpr int kBlockPts = 16 * kMlpWaves;  // 64
+constexpr int kRowH = kBlockPts + 4;       // halves per row
+struct BlockLds {
+    _Float16 e[kIn][kRowH];
+    _Float16 h1[kHid][kRowH];
+    _Float16 h2[kHid][kRowH];
+    _Float16 dz1[kHid][kRowH];
+    _Float16 dz2[kHid][kRowH];
+    _Float16 g3[kOut][kRowH];  // dL/dy, scaled
 };
+constexpr size_t kBwdLds = 2 * sizeof(BlockLds);  // two blocks: one barrier per block
 
-__device__ __forceinline__ void wave_lds_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
-
-// Lane (q, c) holds rows 16 m + 4 q + r of point c (the D / B layout): store them as row c.
-template <int W>
-__device__ __forceinline__ void put_rows(_Float16 (*dst)[W], int m, int q, int c, half4_t v) {
-    *reinterpret_cast<half4_t *>(&dst[c][16 * m + 4 * q]) = v;
+// A 16 x 16 block X that a wave holds in the D layout (lane (q, c) holds
+// X[4 q + r][c], r = 0..3), transposed on the matrix cores: with X's
+// registers as the A operand (A[i][k] = X[k][i]) and the identity as B, the
+// product is X^T, so lane (q, c) then holds X[c][4 q + r].  Each sum has one
+// non-zero term, so the binary16 values come back exactly.
+__device__ __forceinline__ half4_t transpose16(half4_t x, half4_t ident) {
+    return to_half4(mfma(x, ident, float4_t{0.f, 0.f, 0.f, 0.f}));
 }
 
-// Operand with the points on the k axis: points 4 q + r, column 16 m + c.
-template <int W>
-__device__ __forceinline__ half4_t get_cols(_Float16 (*src)[W], int m, int q, int c) {
-    half4_t v;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = src[4 * q + r][16 * m + c];
-    return v;
+// X (units u0 .. u0 + 15 of this wave's 16 points, D layout) into rows
+// u0 + c, columns col0 + 4 q .. + 3 of a block array.
+__device__ __forceinline__ void put_cols(_Float16 (*dst)[kRowH], int u0, int q, int c, int col0, half4_t x,
+                                         half4_t ident) {
+    *reinterpret_cast<half4_t *>(&dst[u0 + c][col0 + 4 * q]) = transpose16(x, ident);
 }
 
-__global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 *__restrict__ stage, int64_t n,
-                                                                 MlpParams mp, const float *__restrict__ dy,
-                                                                 const uint32_t *__restrict__ dmax,
-                                                                 float *__restrict__ de,
-                                                                 float *__restrict__ partials, int64_t tiles) {
-    __shared__ TileLds lds[kMlpWaves];
+// A 16 x 16 x 32 operand with the points of half h of the block on the k
+// axis (slots 0..3: points 32 h + 4 q + 0..3, slots 4..7: 16 further), row
+// `row` of src on this lane.
+__device__ __forceinline__ half8_t get_k(const _Float16 (*src)[kRowH], int row, int q, int h) {
+    const half4_t lo = *reinterpret_cast<const half4_t *>(&src[row][32 * h + 4 * q]);
+    const half4_t hi = *reinterpret_cast<const half4_t *>(&src[row][32 * h + 16 + 4 * q]);
+    return join8(lo, hi);
+}
+
+// Each workgroup walks blocks of 64 points.  Wave w takes points 16 w + c of
+// the block through the layers (recomputed forward, dz2, dz1, dL/de) and
+// stores its tile's activations, transposed, in the block's LDS; after one
+// barrier, wave w contracts the whole block over its points for its quarter
+// of the weight gradients: rows 16 w .. 16 w + 15 of dW1 and dW2 (and of db1,
+// db2), columns 16 w .. 16 w + 15 of dW3 (and db3 on wave 0).  The bias
+// gradients are the same contractions against a ones operand.  The running
+// sums of a wave are 40 registers instead of the whole head's 148, which
+// lets two waves share a SIMD.  Each workgroup writes one set of partials.
+__global__ __launch_bounds__(64 * kMlpWaves, 2) void mlp_bwd_kernel(const _Float16 *__restrict__ stage, int64_t n,
+                                                                    MlpParams mp, const float *__restrict__ dy,
+                                                                    const uint32_t *__restrict__ dmax,
+                                                                    float *__restrict__ de,
+                                                                    float *__restrict__ partials) {
+    extern __shared__ __align__(16) unsigned char mlp_lds[];
+    BlockLds *blk = reinterpret_cast<BlockLds *>(mlp_lds);
     const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15, wave = threadIdx.x >> 6;
-    TileLds &tl = lds[wave];
     // The call's scale s = 2^(1-e), max|dL/dy| in [2^(e-1), 2^e) (1 if dL/dy has no finite non-zero value).
     uint32_t mbits = 0;
     for (int i = lane; i < kDyMaxParts; i += 64) mbits = max(mbits, dmax[i]);
@@ -292,135 +340,102 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_bwd_kernel(const _Float16 
                 if (mb < 2) t1[mb][h][s] = mp.w1[k * kIn + 16 * mb + c];
             }
     }
-    float4_t gw1[4][2], gw2[4][4], gw3[4];
-    float4_t gb1[4], gb2[4], gb3;
+    // B operands: the identity (k = 4 q + r against column c) and all ones.
+    half4_t ident;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        gw3[i] = gb1[i] = gb2[i] = float4_t{0.f, 0.f, 0.f, 0.f};
-        gw1[i][0] = gw1[i][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 4; ++r) ident[r] = 4 * q + r == c ? (_Float16)1.f : (_Float16)0.f;
+    const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+    const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    float4_t gw1[2], gw2[4], gw3, gb1 = zero4, gb2 = zero4, gb3 = zero4;
+    gw1[0] = gw1[1] = gw3 = zero4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) gw2[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    gb3 = float4_t{0.f, 0.f, 0.f, 0.f};
-    const int64_t nwaves = (int64_t)gridDim.x * kMlpWaves;
-    // The next tile's encoding and dL/dy are requested before the current tile
-    // is worked on (one wave per SIMD at this register count: the loads must
-    // not stall it).
-    auto load_tile = [&](int64_t t, half4_t (&eb)[2], float4 &g) {
-        const int64_t p = t * 16 + c;
-        const bool ok = p < n;
-        load_encoding(stage, n, ok ? p : n - 1, q, eb);
-        // dL/dy of the point as the B operand (k = output 0..3 on lanes q = 0); points past n give 0.
-        g = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (q == 0 && ok) g = *reinterpret_cast<const float4 *>(dy + p * kOut);
+    for (int j = 0; j < 4; ++j) gw2[j] = zero4;
+    const int64_t nblocks = (n + kBlockPts - 1) / kBlockPts;
+    // The next block's encoding is requested before the current block is
+    // worked on; dL/dy, needed after the two hidden layers, at its start.
+    auto load_tile = [&](int64_t b, half4_t (&eb)[2]) {
+        const int64_t p = b * kBlockPts + 16 * wave + c;
+        load_encoding(stage, n, p < n ? p : n - 1, q, eb);
     };
     half4_t eb_next[2];
-    float4 g_next;
-    int64_t t = (int64_t)blockIdx.x * kMlpWaves + wave;
-    if (t < tiles) load_tile(t, eb_next, g_next);
-    for (; t < tiles; t += nwaves) {
-        const int64_t p = t * 16 + c;
+    int64_t b = blockIdx.x;
+    if (b < nblocks) load_tile(b, eb_next);
+    for (int buf = 0; b < nblocks; b += gridDim.x, buf ^= 1) {
+        BlockLds &bl = blk[buf];
+        const int64_t p = b * kBlockPts + 16 * wave + c;
         const bool ok = p < n;
         half4_t eb[2] = {eb_next[0], eb_next[1]}, h1[4], h2[4], dz1[4], dz2[4], g3;
-        const float4 g = g_next;
-        if (t + nwaves < tiles) load_tile(t + nwaves, eb_next, g_next);
-        uint32_t m1, m2;
-        hidden_layers(w, eb, h1, h2, m1, m2);
-        g3 = half4_t{(_Float16)(g.x * gscale), (_Float16)(g.y * gscale), (_Float16)(g.z * gscale),
-                     (_Float16)(g.w * gscale)};
+        // dL/dy of the point as the B operand (k = output 0..3 on lanes q = 0); points past n give 0.
+        float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q == 0 && ok) g = *reinterpret_cast<const float4 *>(dy + p * kOut);
+        if (b + gridDim.x < nblocks) load_tile(b + gridDim.x, eb_next);
+        hidden_layers(w, eb, h1, h2);
+        // The tile's activations into the block, transposed (each as soon as
+        // it is made, so that few of them are live at once).
+        const int col0 = 16 * wave;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) put_cols(bl.e, 16 * kb, q, c, col0, eb[kb], ident);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            const float4_t acc = mfma(t3[mb], g3, float4_t{0.f, 0.f, 0.f, 0.f});
+            put_cols(bl.h1, 16 * mb, q, c, col0, h1[mb], ident);
+            put_cols(bl.h2, 16 * mb, q, c, col0, h2[mb], ident);
+        }
+        g3 = to_half4(float4_t{g.x * gscale, g.y * gscale, g.z * gscale, g.w * gscale});
+        {
+            const half4_t g3t = transpose16(g3, ident);  // rows c >= 4 are zero
+            if (c < kOut) *reinterpret_cast<half4_t *>(&bl.g3[c][col0 + 4 * q]) = g3t;
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dz2[mb][r] = (_Float16)(((m2 >> (4 * mb + r)) & 1) ? acc[r] : 0.f);
+        for (int mb = 0; mb < 4; ++mb) {
+            dz2[mb] = relu_grad(mfma(t3[mb], g3, zero4), h2[mb]);
+            put_cols(bl.dz2, 16 * mb, q, c, col0, dz2[mb], ident);
         }
         const half8_t dz2lo = join8(dz2[0], dz2[1]), dz2hi = join8(dz2[2], dz2[3]);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            const float4_t acc = mfma32(t2[mb][1], dz2hi, mfma32(t2[mb][0], dz2lo, float4_t{0.f, 0.f, 0.f, 0.f}));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dz1[mb][r] = (_Float16)(((m1 >> (4 * mb + r)) & 1) ? acc[r] : 0.f);
+            dz1[mb] = relu_grad(mfma32(t2[mb][1], dz2hi, mfma32(t2[mb][0], dz2lo, zero4)), h1[mb]);
+            put_cols(bl.dz1, 16 * mb, q, c, col0, dz1[mb], ident);
         }
         const half8_t dz1lo = join8(dz1[0], dz1[1]), dz1hi = join8(dz1[2], dz1[3]);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const float4_t acc = mfma32(t1[mb][1], dz1hi, mfma32(t1[mb][0], dz1lo, float4_t{0.f, 0.f, 0.f, 0.f}));
+            const float4_t acc = mfma32(t1[mb][1], dz1hi, mfma32(t1[mb][0], dz1lo, zero4));
             if (ok)
                 *reinterpret_cast<float4 *>(de + p * kIn + 16 * mb + 4 * q) =
                     make_float4(acc[0] * ginv, acc[1] * ginv, acc[2] * ginv, acc[3] * ginv);
         }
-        // Bias gradients: this lane's units, summed over the points it sees.
+        __syncthreads();
+        // This wave's quarter of the weight gradients over the block's 64 points.
+        const int u = 16 * wave + c;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+        for (int h = 0; h < 2; ++h) {
+            const half8_t a2 = get_k(bl.dz2, u, q, h), a1 = get_k(bl.dz1, u, q, h);
+            const half8_t a3 = c < kOut ? get_k(bl.g3, c, q, h) : half8_t{};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                gb1[mb][r] += (float)dz1[mb][r];
-                gb2[mb][r] += (float)dz2[mb][r];
-            }
+            for (int nb = 0; nb < 4; ++nb) gw2[nb] = mfma32(a2, get_k(bl.h1, 16 * nb + c, q, h), gw2[nb]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) gb3[r] += (float)g3[r];
-        // Weight gradients: the tile through LDS with the points on the k axis.
-        wave_lds_fence();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) put_rows(tl.e, kb, q, c, eb[kb]);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            put_rows(tl.h1, mb, q, c, h1[mb]);
-            put_rows(tl.h2, mb, q, c, h2[mb]);
-            put_rows(tl.dz1, mb, q, c, dz1[mb]);
-            put_rows(tl.dz2, mb, q, c, dz2[mb]);
-        }
-        if (q < 2) *reinterpret_cast<half4_t *>(&tl.g3[c][4 * q]) = g3;  // q = 1 writes the zero padding
-        wave_lds_fence();
-        half4_t ga;  // A of dW3: row = output c (< 4), k = point
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ga[r] = c < kOut ? tl.g3[4 * q + r][c] : (_Float16)0.f;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const half4_t bh2 = get_cols(tl.h2, nb, q, c), bh1 = get_cols(tl.h1, nb, q, c);
-            gw3[nb] = mfma(ga, bh2, gw3[nb]);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) gw2[mb][nb] = mfma(get_cols(tl.dz2, mb, q, c), bh1, gw2[mb][nb]);
-        }
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            const half4_t be = get_cols(tl.e, nb, q, c);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) gw1[mb][nb] = mfma(get_cols(tl.dz1, mb, q, c), be, gw1[mb][nb]);
+            for (int nb = 0; nb < 2; ++nb) gw1[nb] = mfma32(a1, get_k(bl.e, 16 * nb + c, q, h), gw1[nb]);
+            gw3 = mfma32(a3, get_k(bl.h2, u, q, h), gw3);
+            gb2 = mfma32(a2, ones, gb2);
+            gb1 = mfma32(a1, ones, gb1);
+            if (wave == 0) gb3 = mfma32(a3, ones, gb3);
         }
     }
-    // Bias sums over the 16 point columns (lanes of equal q).
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                gb1[mb][r] += __shfl_xor(gb1[mb][r], off, 64);
-                gb2[mb][r] += __shfl_xor(gb2[mb][r], off, 64);
-            }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gb3[r] += __shfl_xor(gb3[r], off, 64);
-    }
-    float *part = partials + ((int64_t)blockIdx.x * kMlpWaves + wave) * kPartial;
+    // Lane (q, c) holds D[4 q + r][c]: rows 16 w + 4 q + r of dW1, dW2, db1,
+    // db2 (the bias sums are equal in every column c), outputs 4 q + r of dW3.
+    float *part = partials + (int64_t)blockIdx.x * kPartial;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+        const int row = 16 * wave + 4 * q + r;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int row = 16 * mb + 4 * q + r;
+        for (int nb = 0; nb < 2; ++nb) part[kOffW1 + row * kIn + 16 * nb + c] = gw1[nb][r] * ginv;
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) part[kOffW1 + row * kIn + 16 * nb + c] = gw1[mb][nb][r] * ginv;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) part[kOffW2 + row * kHid + 16 * nb + c] = gw2[mb][nb][r] * ginv;
-            if (c == 0) {
-                part[kOffB1 + row] = gb1[mb][r] * ginv;
-                part[kOffB2 + row] = gb2[mb][r] * ginv;
-            }
-        }
-        if (q == 0) {
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) part[kOffW3 + r * kHid + 16 * nb + c] = gw3[nb][r] * ginv;
-            if (c == 0) part[kOffB3 + r] = gb3[r] * ginv;
+        for (int nb = 0; nb < 4; ++nb) part[kOffW2 + row * kHid + 16 * nb + c] = gw2[nb][r] * ginv;
+        if (q == 0) part[kOffW3 + r * kHid + 16 * wave + c] = gw3[r] * ginv;
+        if (c == 0) {
+            part[kOffB1 + row] = gb1[r] * ginv;
+            part[kOffB2 + row] = gb2[r] * ginv;
+            if (wave == 0 && q == 0) part[kOffB3 + r] = gb3[r] * ginv;
         }
     }
 }
@@ -460,7 +475,7 @@ __global__ __launch_bounds__(256) void mlp_reduce2_kernel(const float *__restric
 size_t mlp_partials_bytes(int64_t n) {
     const int64_t tiles = (n + 15) / 16;
     const size_t grid = (size_t)std::max<int64_t>(1, std::min<int64_t>((tiles + kMlpWaves - 1) / kMlpWaves, kMaxMlpGrid));
-    return (grid * kMlpWaves + kSplit) * kPartial * sizeof(float) + kDyMaxParts * sizeof(uint32_t);
+    return (grid + kSplit) * kPartial * sizeof(float) + kDyMaxParts * sizeof(uint32_t);
 }
 
 hipError_t launch_mlp_forward(const _Float16 *stage, int64_t n, const MlpParams &mp, float *y, hipStream_t stream) {
@@ -473,13 +488,17 @@ hipError_t launch_mlp_forward(const _Float16 *stage, int64_t n, const MlpParams 
 hipError_t launch_mlp_backward(const _Float16 *stage, int64_t n, const MlpParams &mp, const float *dy, float *de,
                                float *partials, const MlpGrads &g, hipStream_t stream) {
     const int64_t tiles = (n + 15) / 16;
-    const int grid = mlp_grid(tiles, (const void *)mlp_bwd_kernel);
-    const int nparts = grid * kMlpWaves;
+    hipError_t e = hipFuncSetAttribute((const void *)mlp_bwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)kBwdLds);
+    if (e != hipSuccess) return e;
+    // One set of partials per workgroup (its four waves own a quarter each).
+    const int grid = mlp_grid(tiles, (const void *)mlp_bwd_kernel, kBwdLds);
+    const int nparts = grid;
     float *rows = partials + (int64_t)nparts * kPartial;
     uint32_t *dmax = reinterpret_cast<uint32_t *>(rows + (int64_t)kSplit * kPartial);
     mlp_dy_max_kernel<<<kDyMaxParts, 256, 0, stream>>>(reinterpret_cast<const float4 *>(dy), n, dmax);
-    mlp_bwd_kernel<<<grid, 64 * kMlpWaves, 0, stream>>>(stage, n, mp, dy, dmax, de, partials, tiles);
-    hipError_t e = hipGetLastError();
+    mlp_bwd_kernel<<<grid, 64 * kMlpWaves, kBwdLds, stream>>>(stage, n, mp, dy, dmax, de, partials);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     mlp_reduce1_kernel<<<dim3((kPartial + 255) / 256, kSplit), 256, 0, stream>>>(partials, nparts, rows);
     mlp_reduce2_kernel<<<(kPartial + 255) / 256, 256, 0, stream>>>(rows, g);
