@@ -226,6 +226,13 @@ int mlp_grid(int64_t tiles, const void *kernel, size_t lds_bytes = 0) {
 
 // ---------------------------------------------------------------- forward
 
+// Tiles whose encodings a forward wave has requested ahead of the one it
+// works on.  With one tile ahead a wave had 1 KB of loads in flight and the
+// kernel streamed the stage at about 3 TB/s, bound by load latency; the ring
+// is walked in an unrolled loop, so each slot stays a register set of its own
+// (copying a slot with a load in flight into another would wait for that load).
+constexpr int kFwdAhead = 3;
+
 __global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 *__restrict__ stage, int64_t n,
                                                                  MlpParams mp, float *__restrict__ y,
                                                                  int64_t tiles) {
@@ -233,17 +240,24 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 
     FwdWeights w;
     load_fwd_weights(mp, q, c, w);
     const int64_t nwaves = (int64_t)gridDim.x * kMlpWaves;
-    half4_t eb_next[2];
-    int64_t t = (int64_t)blockIdx.x * kMlpWaves + (threadIdx.x >> 6);
-    if (t < tiles) load_encoding(stage, n, min(t * 16 + c, n - 1), q, eb_next);
-    for (; t < tiles; t += nwaves) {
-        const int64_t p = t * 16 + c;
-        const bool ok = p < n;
-        half4_t eb[2] = {eb_next[0], eb_next[1]}, h1[4], h2[4];
-        if (t + nwaves < tiles) load_encoding(stage, n, min((t + nwaves) * 16 + c, n - 1), q, eb_next);
-        hidden_layers(w, eb, h1, h2);
-        const float4_t o = mfma32(w.a3[1], join8(h2[2], h2[3]), mfma32(w.a3[0], join8(h2[0], h2[1]), w.b3));
-        if (q == 0 && ok) *reinterpret_cast<float4 *>(y + p * kOut) = make_float4(o[0], o[1], o[2], o[3]);
+    const int64_t t0 = (int64_t)blockIdx.x * kMlpWaves + (threadIdx.x >> 6);
+    // Past the last tile a slot loads the last point again (its result is not used).
+    auto request = [&](int64_t t, half4_t (&eb)[2]) { load_encoding(stage, n, min(t * 16 + c, n - 1), q, eb); };
+    half4_t ring[kFwdAhead][2];
+#pragma unroll
+    for (int s = 0; s < kFwdAhead; ++s) request(t0 + s * nwaves, ring[s]);
+    for (int64_t t = t0; t < tiles; t += kFwdAhead * nwaves) {
+#pragma unroll
+        for (int s = 0; s < kFwdAhead; ++s) {
+            const int64_t ts = t + s * nwaves;
+            if (ts >= tiles) break;  // wave-uniform
+            const int64_t p = ts * 16 + c;
+            half4_t h1[4], h2[4];
+            hidden_layers(w, ring[s], h1, h2);
+            const float4_t o = mfma32(w.a3[1], join8(h2[2], h2[3]), mfma32(w.a3[0], join8(h2[0], h2[1]), w.b3));
+            request(ts + kFwdAhead * nwaves, ring[s]);
+            if (q == 0 && p < n) *reinterpret_cast<float4 *>(y + p * kOut) = make_float4(o[0], o[1], o[2], o[3]);
+        }
     }
 }
 
