@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define HASHGRID_ABI_VERSION 1
+#define HASHGRID_ABI_VERSION 2
 
 /* Return codes. */
 #define HG_OK 0
@@ -238,23 +238,31 @@ int hashgrid_debug_corners(const hg_config *cfg, const float *x, int64_t n, uint
 
 /* MLP head after the encoder: the NeRFace head of ipipp.com (section 3
  * listing), Linear(32, 64), ReLU, Linear(64, 64), ReLU, Linear(64, 4) with
- * biases,  y = W3 relu(W2 relu(W1 e + b1) + b2) + b3,  where e is the 32-wide
- * encoding of a point (grids with D = 3, F = 2, L = 16).  It runs on the
- * matrix cores: binary16 operands (the encoding, the hidden activations and,
- * in the backward, dL/dy and the pre-activation gradients are rounded to
- * binary16 where they enter a product), fp32 accumulation.  The encoding is
- * computed once, in the forward, into a binary16 stage the backward reuses.
- * Weights are binary16 [out][in] (nn.Linear layout), biases fp32. */
+ * biases,  y = W3 relu(W2 relu(W1 u + b1) + b2) + b3,  where u = e is the
+ * 32-wide encoding of a point (grids with D = 3, F = 2, L = 16).  With
+ * coord_inputs = 3 it is instead the TinyNeRF head of the jsqmd.com page
+ * (section 4: the network concatenates the raw point before its hash
+ * features, then Linear(35, 64) and the same two layers): u = [x, e], the
+ * point's 3 coordinates first, and W1 is [64][35].  It runs on the matrix
+ * cores: binary16 operands (u -- coordinates included --, the hidden
+ * activations and, in the backward, dL/dy and the pre-activation gradients
+ * are rounded to binary16 where they enter a product), fp32 accumulation.
+ * The encoding is computed once, in the forward, into a binary16 stage the
+ * backward reuses.  Weights are binary16 [out][in] (nn.Linear layout),
+ * biases fp32. */
 typedef struct {
-    const void *w1;  /* binary16 [64][32], 8-byte aligned  */
-    const float *b1; /* [64]                               */
-    const void *w2;  /* binary16 [64][64]                   */
-    const float *b2; /* [64]                               */
-    const void *w3;  /* binary16 [4][64]                    */
-    const float *b3; /* [4]                                */
+    const void *w1;       /* binary16 [64][32], or [64][35] with coord_inputs = 3; 8-byte aligned */
+    const float *b1;      /* [64]                                                                 */
+    const void *w2;       /* binary16 [64][64]                                                     */
+    const float *b2;      /* [64]                                                                 */
+    const void *w3;       /* binary16 [4][64]                                                      */
+    const float *b3;      /* [4]                                                                  */
+    int32_t coord_inputs; /* 0: u = e (NeRFace head); 3: u = [x, e] (TinyNeRF head); else HG_EINVAL */
 } hg_mlp_params;
 
-/* fp32 gradients of the weights and biases, same shapes; ACCUMULATED. */
+/* fp32 gradients of the weights and biases, same shapes (dw1 [64][32] or
+ * [64][35]); ACCUMULATED.  The points are inputs: the head gives no gradient
+ * to x (the table backward's rule; dL/dx is hashgrid_input_grad's). */
 typedef struct {
     float *dw1, *db1, *dw2, *db2, *dw3, *db3;
 } hg_mlp_grads;

@@ -358,12 +358,14 @@ int check_mlp_params(const hg_mlp_params *mp) {
     if (!aligned(mp->w1, 8) || !aligned(mp->w2, 8) || !aligned(mp->w3, 8) || !aligned(mp->b1, 4) ||
         !aligned(mp->b2, 4) || !aligned(mp->b3, 4))
         return fail(HG_EINVAL, "weights must be 8-byte and biases 4-byte aligned");
+    if (mp->coord_inputs != 0 && mp->coord_inputs != hg::kMlpCoords)
+        return fail(HG_EINVAL, "coord_inputs %d: 0 (u = e) or 3 (u = [x, e])", (int)mp->coord_inputs);
     return HG_OK;
 }
 
 hg::MlpParams mlp_params(const hg_mlp_params *mp) {
     return hg::MlpParams{(const _Float16 *)mp->w1, (const _Float16 *)mp->w2, (const _Float16 *)mp->w3,
-                         mp->b1, mp->b2, mp->b3};
+                         mp->b1, mp->b2, mp->b3, (int)mp->coord_inputs};
 }
 
 }  // namespace
@@ -553,7 +555,7 @@ int hashgrid_mlp_forward(const hg_config *cfg, const float *x, int64_t n, const 
     hipError_t e = hg::launch_encode_stage_f16(lp, x, n, table, cfg->table_dtype, (_Float16 *)stage,
                                                (hipStream_t)stream);
     if (e != hipSuccess) return launch_status(e, "encode stage");
-    return launch_status(hg::launch_mlp_forward((const _Float16 *)stage, n, mlp_params(params), y,
+    return launch_status(hg::launch_mlp_forward((const _Float16 *)stage, x, n, mlp_params(params), y,
                                                 (hipStream_t)stream),
                          "mlp forward");
 }
@@ -585,7 +587,7 @@ int hashgrid_mlp_backward(const hg_config *cfg, const float *x, int64_t n, const
     float *de = (float *)workspace;
     float *partials = (float *)((char *)workspace + de_bytes);
     const hg::MlpGrads g{grads->dw1, grads->db1, grads->dw2, grads->db2, grads->dw3, grads->db3};
-    hipError_t e = hg::launch_mlp_backward((const _Float16 *)stage, n, mlp_params(params), dy, de, partials, g,
+    hipError_t e = hg::launch_mlp_backward((const _Float16 *)stage, x, n, mlp_params(params), dy, de, partials, g,
                                            (hipStream_t)stream);
     if (e != hipSuccess) return launch_status(e, "mlp backward");
     return table_backward(cfg, x, n, de, 32, dtable, rest, workspace_bytes - used, stream);

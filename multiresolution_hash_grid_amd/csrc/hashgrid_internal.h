@@ -184,9 +184,12 @@ hipError_t launch_input_grad(const LaunchParams &lp, int D, int F, const float *
 
 // MLP head 32 -> 64 -> 64 -> 4 (mlp_kernels.hip).  Weights binary16 [out][in],
 // biases and gradients fp32.
+// Raw coordinates the TinyNeRF head puts before the encoding (u = [x, e]).
+constexpr int kMlpCoords = 3;
 struct MlpParams {
     const _Float16 *w1, *w2, *w3;
     const float *b1, *b2, *b3;
+    int coords;  // 0 or kMlpCoords: W1 is [64][32 + coords]
 };
 struct MlpGrads {
     float *dw1, *db1, *dw2, *db2, *dw3, *db3;
@@ -195,9 +198,10 @@ struct MlpGrads {
 hipError_t launch_encode_stage_f16(const LaunchParams &lp, const float *x, int64_t n, const void *table,
                                    int table_dtype, _Float16 *stage, hipStream_t stream);
 size_t mlp_partials_bytes(int64_t n);
-hipError_t launch_mlp_forward(const _Float16 *stage, int64_t n, const MlpParams &mp, float *y, hipStream_t stream);
-hipError_t launch_mlp_backward(const _Float16 *stage, int64_t n, const MlpParams &mp, const float *dy, float *de,
-                               float *partials, const MlpGrads &g, hipStream_t stream);
+hipError_t launch_mlp_forward(const _Float16 *stage, const float *x, int64_t n, const MlpParams &mp, float *y,
+                              hipStream_t stream);
+hipError_t launch_mlp_backward(const _Float16 *stage, const float *x, int64_t n, const MlpParams &mp, const float *dy,
+                               float *de, float *partials, const MlpGrads &g, hipStream_t stream);
 
 struct AdamParams {
     float lr, beta1, beta2, eps;

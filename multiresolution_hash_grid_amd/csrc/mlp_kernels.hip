@@ -57,11 +57,16 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kIn = 32, kHid = 64, kOut = 4;
+constexpr int kIn = 32, kHid = 64, kOut = 4;  // kIn: the encoding's features
 constexpr int kMlpWaves = 4;  // waves per workgroup
-// Per-wave partial sums: dW1 [64][32], db1 [64], dW2 [64][64], db2 [64], dW3 [4][64], db3 [4].
+// Per-workgroup partial sums: dW1's encoding columns [64][32], db1 [64], dW2
+// [64][64], db2 [64], dW3 [4][64], db3 [4], then (with coordinate inputs)
+// dW1's coordinate columns [64][3].
 constexpr int kOffW1 = 0, kOffB1 = kOffW1 + kHid * kIn, kOffW2 = kOffB1 + kHid, kOffB2 = kOffW2 + kHid * kHid,
-              kOffW3 = kOffB2 + kHid, kOffB3 = kOffW3 + kOut * kHid, kPartial = kOffB3 + kOut;
+              kOffW3 = kOffB2 + kHid, kOffB3 = kOffW3 + kOut * kHid, kOffW1x = kOffB3 + kOut,
+              kPartial = kOffW1x + kHid * kMlpCoords;
+// Partial entries a head writes: the coordinate columns only with coordinate inputs.
+constexpr int partial_count(int coords) { return coords ? kPartial : kOffW1x; }
 
 __device__ __forceinline__ float4_t mfma(half4_t a, half4_t b, float4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
@@ -115,18 +120,27 @@ __device__ __forceinline__ half4_t relu_grad(float4_t v, half4_t h) {
 
 // The forward weights as 16 x 16 x 32 A operands: row = output unit, slot
 // s of lane group q = input k-block 2h + s / 4, k = 16 (2h + s / 4) + 4 q + s % 4.
+// With XIN coordinate inputs, W1's coordinate columns form one more A
+// operand per 16 units, non-zero only in lane group q = 0's first XIN slots
+// (k = 0 .. XIN - 1).
 struct FwdWeights {
     half8_t a1[4], a2[4][2], a3[2];
+    half4_t a1x[4];
     float4_t b1[4], b2[4], b3;
 };
 
+template <int XIN>
 __device__ __forceinline__ void load_fwd_weights(const MlpParams &mp, int q, int c, FwdWeights &w) {
+    constexpr int ld = kIn + XIN;  // W1's row: XIN coordinates, then the encoding
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
+        for (int r = 0; r < 4; ++r)
+            w.a1x[mb][r] = XIN && 4 * q + r < XIN ? mp.w1[(16 * mb + c) * ld + 4 * q + r] : (_Float16)0.f;
+#pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int kk = 16 * (s >> 2) + 4 * q + (s & 3);  // k within a 32-wide block
-            w.a1[mb][s] = mp.w1[(16 * mb + c) * kIn + kk];
+            w.a1[mb][s] = mp.w1[(16 * mb + c) * ld + XIN + kk];
 #pragma unroll
             for (int h = 0; h < 2; ++h) w.a2[mb][h][s] = mp.w2[(16 * mb + c) * kHid + 32 * h + kk];
         }
@@ -161,12 +175,45 @@ __device__ __forceinline__ void load_encoding(const _Float16 *__restrict__ stage
     }
 }
 
-// Layers 1 and 2 of 16 points: binary16 activations, -0 where the ReLU blocked.
-__device__ __forceinline__ void hidden_layers(const FwdWeights &w, const half4_t (&eb)[2], half4_t (&h1)[4],
-                                              half4_t (&h2)[4]) {
-    const half8_t e8 = join8(eb[0], eb[1]);
+// The point's coordinates as the B operand of W1's coordinate columns:
+// lane (q, c) holds x[p][4 q + r] for 4 q + r < XIN, zero elsewhere (binary16).
+template <int XIN>
+__device__ __forceinline__ half4_t coord_operand(const float (&xc)[kMlpCoords], int q) {
+    half4_t b = {0, 0, 0, 0};
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) h1[mb] = relu_half(mfma32(w.a1[mb], e8, w.b1[mb]));
+    for (int r = 0; r < XIN; ++r) b[r] = q == 0 ? (_Float16)xc[r] : (_Float16)0.f;
+    return b;
+}
+
+// The coordinates of point p (XIN of them; lanes of group q = 0 only).
+template <int XIN>
+__device__ __forceinline__ void load_coords(const float *__restrict__ x, int64_t p, int q, float (&xc)[kMlpCoords]) {
+#pragma unroll
+    for (int r = 0; r < kMlpCoords; ++r) xc[r] = 0.f;
+    if (XIN && q == 0) {
+#pragma unroll
+        for (int r = 0; r < XIN; ++r) xc[r] = x[3 * p + r];
+    }
+}
+
+// Layers 1 and 2 of 16 points: binary16 activations, -0 where the ReLU blocked.
+template <int XIN>
+__device__ __forceinline__ void hidden_layers(const FwdWeights &w, const half4_t (&eb)[2], half4_t xb,
+                                              half4_t (&h1)[4], half4_t (&h2)[4]) {
+    const half8_t e8 = join8(eb[0], eb[1]);
+    // The coordinate term accumulates onto the encoding's with the same
+    // 16 x 16 x 32 shape: only lane group 0's first XIN k-slots are non-zero,
+    // and they are k = 0 .. XIN - 1 in either shape's layout.  (Chained onto a
+    // 16 x 16 x 32 result as a 16 x 16 x 16 MFMA, it read that result before
+    // it was complete where the compiler issued the two seven instructions
+    // apart.)
+    const half4_t zh = {0, 0, 0, 0};
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        float4_t z = mfma32(w.a1[mb], e8, w.b1[mb]);
+        if constexpr (XIN) z = mfma32(join8(w.a1x[mb], zh), join8(xb, zh), z);
+        h1[mb] = relu_half(z);
+    }
     const half8_t h1lo = join8(h1[0], h1[1]), h1hi = join8(h1[2], h1[3]);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) h2[mb] = relu_half(mfma32(w.a2[mb][1], h1hi, mfma32(w.a2[mb][0], h1lo, w.b2[mb])));
@@ -233,19 +280,26 @@ int mlp_grid(int64_t tiles, const void *kernel, size_t lds_bytes = 0) {
 // (copying a slot with a load in flight into another would wait for that load).
 constexpr int kFwdAhead = 3;
 
-__global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 *__restrict__ stage, int64_t n,
+template <int XIN>
+__global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 *__restrict__ stage,
+                                                                 const float *__restrict__ x, int64_t n,
                                                                  MlpParams mp, float *__restrict__ y,
                                                                  int64_t tiles) {
     const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
     FwdWeights w;
-    load_fwd_weights(mp, q, c, w);
+    load_fwd_weights<XIN>(mp, q, c, w);
     const int64_t nwaves = (int64_t)gridDim.x * kMlpWaves;
     const int64_t t0 = (int64_t)blockIdx.x * kMlpWaves + (threadIdx.x >> 6);
     // Past the last tile a slot loads the last point again (its result is not used).
-    auto request = [&](int64_t t, half4_t (&eb)[2]) { load_encoding(stage, n, min(t * 16 + c, n - 1), q, eb); };
     half4_t ring[kFwdAhead][2];
+    float ring_x[kFwdAhead][kMlpCoords];
+    auto request = [&](int64_t t, int s) {
+        const int64_t p = min(t * 16 + c, n - 1);
+        load_encoding(stage, n, p, q, ring[s]);
+        load_coords<XIN>(x, p, q, ring_x[s]);
+    };
 #pragma unroll
-    for (int s = 0; s < kFwdAhead; ++s) request(t0 + s * nwaves, ring[s]);
+    for (int s = 0; s < kFwdAhead; ++s) request(t0 + s * nwaves, s);
     for (int64_t t = t0; t < tiles; t += kFwdAhead * nwaves) {
 #pragma unroll
         for (int s = 0; s < kFwdAhead; ++s) {
@@ -253,9 +307,9 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 
             if (ts >= tiles) break;  // wave-uniform
             const int64_t p = ts * 16 + c;
             half4_t h1[4], h2[4];
-            hidden_layers(w, ring[s], h1, h2);
+            hidden_layers<XIN>(w, ring[s], coord_operand<XIN>(ring_x[s], q), h1, h2);
             const float4_t o = mfma32(w.a3[1], join8(h2[2], h2[3]), mfma32(w.a3[0], join8(h2[0], h2[1]), w.b3));
-            request(ts + kFwdAhead * nwaves, ring[s]);
+            request(ts + kFwdAhead * nwaves, s);
             if (q == 0 && p < n) *reinterpret_cast<float4 *>(y + p * kOut) = make_float4(o[0], o[1], o[2], o[3]);
         }
     }
@@ -271,15 +325,19 @@ __global__ __launch_bounds__(64 * kMlpWaves) void mlp_fwd_kernel(const _Float16 
 // accesses meet 64 distinct banks.
 constexpr int kBlockPts = 16 * kMlpWaves;  // 64
 constexpr int kRowH = kBlockPts + 4;       // halves per row
+template <int XIN>
 struct BlockLds {
     _Float16 e[kIn][kRowH];
     _Float16 h1[kHid][kRowH];
     _Float16 h2[kHid][kRowH];
     _Float16 dz1[kHid][kRowH];
     _Float16 dz2[kHid][kRowH];
-    _Float16 g3[kOut][kRowH];  // dL/dy, scaled
+    _Float16 g3[kOut][kRowH];               // dL/dy, scaled
+    _Float16 x[XIN ? XIN : 1][kRowH];       // the coordinate inputs (XIN > 0)
 };
-constexpr size_t kBwdLds = 2 * sizeof(BlockLds);  // two blocks: one barrier per block
+// Two blocks: one barrier per block.
+template <int XIN>
+constexpr size_t bwd_lds() { return 2 * sizeof(BlockLds<XIN>); }
 
 // A 16 x 16 block X that a wave holds in the D layout (lane (q, c) holds
 // X[4 q + r][c], r = 0..3), transposed on the matrix cores: with X's
@@ -315,13 +373,20 @@ __device__ __forceinline__ half8_t get_k(const _Float16 (*src)[kRowH], int row, 
 // gradients are the same contractions against a ones operand.  The running
 // sums of a wave are 40 registers instead of the whole head's 148, which
 // lets two waves share a SIMD.  Each workgroup writes one set of partials.
-__global__ __launch_bounds__(64 * kMlpWaves, 2) void mlp_bwd_kernel(const _Float16 *__restrict__ stage, int64_t n,
+// With XIN coordinate inputs the coordinates go through the first layer as
+// one more operand, through the block's LDS like the encoding, and into
+// dW1's coordinate columns (wave w's rows, XIN more sums); dL/de skips them.
+// (The coordinate operands and sums do not fit two waves per SIMD: the
+// TinyNeRF instantiation takes the whole register file of one.)
+template <int XIN>
+__global__ __launch_bounds__(64 * kMlpWaves, XIN ? 1 : 2) void mlp_bwd_kernel(const _Float16 *__restrict__ stage,
+                                                                    const float *__restrict__ x, int64_t n,
                                                                     MlpParams mp, const float *__restrict__ dy,
                                                                     const uint32_t *__restrict__ dmax,
                                                                     float *__restrict__ de,
                                                                     float *__restrict__ partials) {
     extern __shared__ __align__(16) unsigned char mlp_lds[];
-    BlockLds *blk = reinterpret_cast<BlockLds *>(mlp_lds);
+    BlockLds<XIN> *blk = reinterpret_cast<BlockLds<XIN> *>(mlp_lds);
     const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15, wave = threadIdx.x >> 6;
     // The call's scale s = 2^(1-e), max|dL/dy| in [2^(e-1), 2^e) (1 if dL/dy has no finite non-zero value).
     uint32_t mbits = 0;
@@ -335,7 +400,7 @@ __global__ __launch_bounds__(64 * kMlpWaves, 2) void mlp_bwd_kernel(const _Float
         ginv = ldexpf(1.f, e - 1);
     }
     FwdWeights w;
-    load_fwd_weights(mp, q, c, w);
+    load_fwd_weights<XIN>(mp, q, c, w);
     // Transposed weights as A operands: row = input unit of the layer, k = its
     // output unit (t2, t1: 16 x 16 x 32 slots as the forward's; t3: K = 4
     // outputs padded to one 16 x 16 x 16 operand).
@@ -351,7 +416,7 @@ __global__ __launch_bounds__(64 * kMlpWaves, 2) void mlp_bwd_kernel(const _Float
             for (int s = 0; s < 8; ++s) {
                 const int k = 32 * h + 16 * (s >> 2) + 4 * q + (s & 3);
                 t2[mb][h][s] = mp.w2[k * kHid + 16 * mb + c];
-                if (mb < 2) t1[mb][h][s] = mp.w1[k * kIn + 16 * mb + c];
+                if (mb < 2) t1[mb][h][s] = mp.w1[k * (kIn + XIN) + XIN + 16 * mb + c];
             }
     }
     // B operands: the identity (k = 4 q + r against column c) and all ones.
@@ -360,35 +425,45 @@ __global__ __launch_bounds__(64 * kMlpWaves, 2) void mlp_bwd_kernel(const _Float
     for (int r = 0; r < 4; ++r) ident[r] = 4 * q + r == c ? (_Float16)1.f : (_Float16)0.f;
     const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
     const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-    float4_t gw1[2], gw2[4], gw3, gb1 = zero4, gb2 = zero4, gb3 = zero4;
+    float4_t gw1[2], gw2[4], gw3, gb1 = zero4, gb2 = zero4, gb3 = zero4, gw1x = zero4;
     gw1[0] = gw1[1] = gw3 = zero4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) gw2[j] = zero4;
     const int64_t nblocks = (n + kBlockPts - 1) / kBlockPts;
     // The next block's encoding is requested before the current block is
     // worked on; dL/dy, needed after the two hidden layers, at its start.
-    auto load_tile = [&](int64_t b, half4_t (&eb)[2]) {
+    auto load_tile = [&](int64_t b, half4_t (&eb)[2], float (&xc)[kMlpCoords]) {
         const int64_t p = b * kBlockPts + 16 * wave + c;
         load_encoding(stage, n, p < n ? p : n - 1, q, eb);
+        load_coords<XIN>(x, p < n ? p : n - 1, q, xc);
     };
     half4_t eb_next[2];
+    float xc_next[kMlpCoords];
     int64_t b = blockIdx.x;
-    if (b < nblocks) load_tile(b, eb_next);
+    if (b < nblocks) load_tile(b, eb_next, xc_next);
     for (int buf = 0; b < nblocks; b += gridDim.x, buf ^= 1) {
-        BlockLds &bl = blk[buf];
+        BlockLds<XIN> &bl = blk[buf];
         const int64_t p = b * kBlockPts + 16 * wave + c;
         const bool ok = p < n;
         half4_t eb[2] = {eb_next[0], eb_next[1]}, h1[4], h2[4], dz1[4], dz2[4], g3;
+        // binary16 before the next block's coordinates are requested into the same registers
+        const half4_t xb = coord_operand<XIN>(xc_next, q);
         // dL/dy of the point as the B operand (k = output 0..3 on lanes q = 0); points past n give 0.
         float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
         if (q == 0 && ok) g = *reinterpret_cast<const float4 *>(dy + p * kOut);
-        if (b + gridDim.x < nblocks) load_tile(b + gridDim.x, eb_next);
-        hidden_layers(w, eb, h1, h2);
+        if (b + gridDim.x < nblocks) load_tile(b + gridDim.x, eb_next, xc_next);
+        hidden_layers<XIN>(w, eb, xb, h1, h2);
         // The tile's activations into the block, transposed (each as soon as
         // it is made, so that few of them are live at once).
         const int col0 = 16 * wave;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) put_cols(bl.e, 16 * kb, q, c, col0, eb[kb], ident);
+        if constexpr (XIN) {
+            if (q == 0) {
+#pragma unroll
+                for (int r = 0; r < XIN; ++r) bl.x[r][col0 + c] = xb[r];
+            }
+        }
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             put_cols(bl.h1, 16 * mb, q, c, col0, h1[mb], ident);
@@ -430,6 +505,7 @@ __global__ __launch_bounds__(64 * kMlpWaves, 2) void mlp_bwd_kernel(const _Float
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) gw1[nb] = mfma32(a1, get_k(bl.e, 16 * nb + c, q, h), gw1[nb]);
             gw3 = mfma32(a3, get_k(bl.h2, u, q, h), gw3);
+            if constexpr (XIN) gw1x = mfma32(a1, c < XIN ? get_k(bl.x, c, q, h) : half8_t{}, gw1x);
             gb2 = mfma32(a2, ones, gb2);
             gb1 = mfma32(a1, ones, gb1);
             if (wave == 0) gb3 = mfma32(a3, ones, gb3);
@@ -446,6 +522,7 @@ __global__ __launch_bounds__(64 * kMlpWaves, 2) void mlp_bwd_kernel(const _Float
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) part[kOffW2 + row * kHid + 16 * nb + c] = gw2[nb][r] * ginv;
         if (q == 0) part[kOffW3 + r * kHid + 16 * wave + c] = gw3[r] * ginv;
+        if (XIN && c < XIN) part[kOffW1x + row * kMlpCoords + c] = gw1x[r] * ginv;
         if (c == 0) {
             part[kOffB1 + row] = gb1[r] * ginv;
             part[kOffB2 + row] = gb2[r] * ginv;
@@ -459,29 +536,65 @@ __global__ __launch_bounds__(64 * kMlpWaves, 2) void mlp_bwd_kernel(const _Float
 // after the partials); pass 2 adds rows 0..kSplit-1 into the gradients.
 constexpr int kSplit = 64;
 
-__global__ __launch_bounds__(256) void mlp_reduce1_kernel(const float *__restrict__ partials, int nparts,
+// np: the partial entries the head wrote (partial_count).
+__global__ __launch_bounds__(256) void mlp_reduce1_kernel(const float *__restrict__ partials, int nparts, int np,
                                                           float *__restrict__ rows) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     const int sidx = blockIdx.y;
-    if (j >= kPartial) return;
+    if (j >= np) return;
     float acc = 0.f;
     for (int w = sidx; w < nparts; w += kSplit) acc += partials[(int64_t)w * kPartial + j];
     rows[(int64_t)sidx * kPartial + j] = acc;
 }
 
-__global__ __launch_bounds__(256) void mlp_reduce2_kernel(const float *__restrict__ rows, MlpGrads g) {
+// dW1 is [64][coords + 32]: its coordinate columns first, then the encoding's.
+__global__ __launch_bounds__(256) void mlp_reduce2_kernel(const float *__restrict__ rows, int coords, MlpGrads g) {
     const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= kPartial) return;
+    if (j >= partial_count(coords)) return;
     float acc = 0.f;
     for (int sidx = 0; sidx < kSplit; ++sidx) acc += rows[(int64_t)sidx * kPartial + j];
+    const int ld1 = kIn + coords;
     float *dst;
-    if (j < kOffB1) dst = g.dw1 + (j - kOffW1);
+    if (j < kOffB1) dst = g.dw1 + (j - kOffW1) / kIn * ld1 + coords + (j - kOffW1) % kIn;
     else if (j < kOffW2) dst = g.db1 + (j - kOffB1);
     else if (j < kOffB2) dst = g.dw2 + (j - kOffW2);
     else if (j < kOffW3) dst = g.db2 + (j - kOffB2);
     else if (j < kOffB3) dst = g.dw3 + (j - kOffW3);
-    else dst = g.db3 + (j - kOffB3);
+    else if (j < kOffW1x) dst = g.db3 + (j - kOffB3);
+    else dst = g.dw1 + (j - kOffW1x) / kMlpCoords * ld1 + (j - kOffW1x) % kMlpCoords;
     *dst += acc;
+}
+
+template <int XIN>
+hipError_t mlp_forward_xin(const _Float16 *stage, const float *x, int64_t n, const MlpParams &mp, float *y,
+                           hipStream_t stream) {
+    const int64_t tiles = (n + 15) / 16;
+    mlp_fwd_kernel<XIN><<<mlp_grid(tiles, (const void *)mlp_fwd_kernel<XIN>), 64 * kMlpWaves, 0, stream>>>(
+        stage, x, n, mp, y, tiles);
+    return hipGetLastError();
+}
+
+template <int XIN>
+hipError_t mlp_backward_xin(const _Float16 *stage, const float *x, int64_t n, const MlpParams &mp, const float *dy,
+                            float *de, float *partials, const MlpGrads &g, hipStream_t stream) {
+    const int64_t tiles = (n + 15) / 16;
+    constexpr size_t lds = bwd_lds<XIN>();
+    hipError_t e = hipFuncSetAttribute((const void *)mlp_bwd_kernel<XIN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    // One set of partials per workgroup (its four waves own a quarter each).
+    const int grid = mlp_grid(tiles, (const void *)mlp_bwd_kernel<XIN>, lds);
+    const int nparts = grid;
+    float *rows = partials + (int64_t)nparts * kPartial;
+    uint32_t *dmax = reinterpret_cast<uint32_t *>(rows + (int64_t)kSplit * kPartial);
+    mlp_dy_max_kernel<<<kDyMaxParts, 256, 0, stream>>>(reinterpret_cast<const float4 *>(dy), n, dmax);
+    mlp_bwd_kernel<XIN><<<grid, 64 * kMlpWaves, lds, stream>>>(stage, x, n, mp, dy, dmax, de, partials);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int np = partial_count(XIN);
+    mlp_reduce1_kernel<<<dim3((np + 255) / 256, kSplit), 256, 0, stream>>>(partials, nparts, np, rows);
+    mlp_reduce2_kernel<<<(np + 255) / 256, 256, 0, stream>>>(rows, XIN, g);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -492,31 +605,16 @@ size_t mlp_partials_bytes(int64_t n) {
     return (grid + kSplit) * kPartial * sizeof(float) + kDyMaxParts * sizeof(uint32_t);
 }
 
-hipError_t launch_mlp_forward(const _Float16 *stage, int64_t n, const MlpParams &mp, float *y, hipStream_t stream) {
-    const int64_t tiles = (n + 15) / 16;
-    mlp_fwd_kernel<<<mlp_grid(tiles, (const void *)mlp_fwd_kernel), 64 * kMlpWaves, 0, stream>>>(stage, n, mp, y,
-                                                                                                  tiles);
-    return hipGetLastError();
+hipError_t launch_mlp_forward(const _Float16 *stage, const float *x, int64_t n, const MlpParams &mp, float *y,
+                              hipStream_t stream) {
+    return mp.coords ? mlp_forward_xin<kMlpCoords>(stage, x, n, mp, y, stream)
+                     : mlp_forward_xin<0>(stage, x, n, mp, y, stream);
 }
 
-hipError_t launch_mlp_backward(const _Float16 *stage, int64_t n, const MlpParams &mp, const float *dy, float *de,
-                               float *partials, const MlpGrads &g, hipStream_t stream) {
-    const int64_t tiles = (n + 15) / 16;
-    hipError_t e = hipFuncSetAttribute((const void *)mlp_bwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)kBwdLds);
-    if (e != hipSuccess) return e;
-    // One set of partials per workgroup (its four waves own a quarter each).
-    const int grid = mlp_grid(tiles, (const void *)mlp_bwd_kernel, kBwdLds);
-    const int nparts = grid;
-    float *rows = partials + (int64_t)nparts * kPartial;
-    uint32_t *dmax = reinterpret_cast<uint32_t *>(rows + (int64_t)kSplit * kPartial);
-    mlp_dy_max_kernel<<<kDyMaxParts, 256, 0, stream>>>(reinterpret_cast<const float4 *>(dy), n, dmax);
-    mlp_bwd_kernel<<<grid, 64 * kMlpWaves, kBwdLds, stream>>>(stage, n, mp, dy, dmax, de, partials);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    mlp_reduce1_kernel<<<dim3((kPartial + 255) / 256, kSplit), 256, 0, stream>>>(partials, nparts, rows);
-    mlp_reduce2_kernel<<<(kPartial + 255) / 256, 256, 0, stream>>>(rows, g);
-    return hipGetLastError();
+hipError_t launch_mlp_backward(const _Float16 *stage, const float *x, int64_t n, const MlpParams &mp, const float *dy,
+                               float *de, float *partials, const MlpGrads &g, hipStream_t stream) {
+    return mp.coords ? mlp_backward_xin<kMlpCoords>(stage, x, n, mp, dy, de, partials, g, stream)
+                     : mlp_backward_xin<0>(stage, x, n, mp, dy, de, partials, g, stream);
 }
 
 }  // namespace hg

@@ -50,7 +50,7 @@ class _Adam(ctypes.Structure):
 
 
 class _MlpParams(ctypes.Structure):
-    _fields_ = [(k, ctypes.c_void_p) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+    _fields_ = [(k, ctypes.c_void_p) for k in ("w1", "b1", "w2", "b2", "w3", "b3")] + [("coord_inputs", ctypes.c_int32)]
 
 
 class _MlpGrads(ctypes.Structure):
@@ -58,6 +58,16 @@ class _MlpGrads(ctypes.Structure):
 
 
 MLP_SHAPES = {"w1": (64, 32), "b1": (64,), "w2": (64, 64), "b2": (64,), "w3": (4, 64), "b3": (4,)}
+MLP_COORDS = 3  # raw coordinates the TinyNeRF head puts before the encoding
+
+
+def mlp_shapes(coord_inputs: int = 0) -> dict:
+    """Parameter shapes of the MLP head: the NeRFace head (coord_inputs = 0,
+    W1 [64, 32]) or the TinyNeRF head (coord_inputs = 3, input [x, e], W1
+    [64, 35])."""
+    if coord_inputs not in (0, MLP_COORDS):
+        raise ValueError(f"coord_inputs must be 0 or {MLP_COORDS}")
+    return dict(MLP_SHAPES, w1=(64, 32 + coord_inputs))
 
 
 @dataclass(frozen=True)
@@ -387,18 +397,29 @@ def hashgrid_mlp_workspace_size(cfg: HashGridConfig, n: int) -> tuple:
     return st.value, bw.value
 
 
-def _mlp_params(params) -> _MlpParams:
-    """[w1, b1, w2, b2, w3, b3]: binary16 weights [out][in], fp32 biases, contiguous GPU tensors."""
-    names = ("w1", "b1", "w2", "b2", "w3", "b3")
+def _mlp_coords(params) -> int:
+    """The head's coordinate inputs, read from W1's width (32: 0, 35: 3)."""
     if len(params) != 6:
         raise ValueError("params must be [w1, b1, w2, b2, w3, b3]")
+    w1 = params[0]
+    if w1.dim() != 2 or w1.shape[1] not in (32, 32 + MLP_COORDS):
+        raise ValueError(f"w1 must be [64, 32] (NeRFace head) or [64, {32 + MLP_COORDS}] (TinyNeRF head)")
+    return int(w1.shape[1]) - 32
+
+
+def _mlp_params(params) -> _MlpParams:
+    """[w1, b1, w2, b2, w3, b3]: binary16 weights [out][in], fp32 biases,
+    contiguous GPU tensors; W1 [64, 32], or [64, 35] for the TinyNeRF head."""
+    names = ("w1", "b1", "w2", "b2", "w3", "b3")
+    coords = _mlp_coords(params)
+    shapes = mlp_shapes(coords)
     ptrs = []
     for name, t in zip(names, params):
         _dev(t, name, torch.float16 if name[0] == "w" else torch.float32)
-        if tuple(t.shape) != MLP_SHAPES[name] or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {MLP_SHAPES[name]} tensor")
+        if tuple(t.shape) != shapes[name] or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {shapes[name]} tensor")
         ptrs.append(t.data_ptr())
-    return _MlpParams(*ptrs)
+    return _MlpParams(*ptrs, coords)
 
 
 def hashgrid_mlp_forward(cfg: HashGridConfig, x: torch.Tensor, table: torch.Tensor, params,
@@ -442,10 +463,11 @@ def hashgrid_mlp_backward(cfg: HashGridConfig, x: torch.Tensor, stage: torch.Ten
     names = ("dw1", "db1", "dw2", "db2", "dw3", "db3")
     if len(grads) != 6:
         raise ValueError("grads must be [dw1, db1, dw2, db2, dw3, db3]")
+    shapes = mlp_shapes(mp.coord_inputs)
     for name, t in zip(names, grads):
         _dev(t, name, torch.float32)
-        if tuple(t.shape) != MLP_SHAPES[name[1:]] or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {MLP_SHAPES[name[1:]]} tensor")
+        if tuple(t.shape) != shapes[name[1:]] or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {shapes[name[1:]]} tensor")
     g = _MlpGrads(*[t.data_ptr() for t in grads])
     _dev(dtable, "dtable", cfg.torch_grad_dtype)
     if tuple(dtable.shape) != cfg.table_shape or not dtable.is_contiguous():
@@ -626,7 +648,7 @@ class HashGridMLPFunction(torch.autograd.Function):
     def backward(ctx, dy):
         x, stage, *params = ctx.saved_tensors
         cfg = ctx.cfg
-        grads = [torch.zeros(MLP_SHAPES[k], device=x.device) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+        grads = [torch.zeros(p.shape, device=x.device) for p in params]
         gcfg = _grad_config(cfg, ctx.table_dtype, x.shape[0])
         dtable = torch.zeros(cfg.table_shape, device=x.device, dtype=gcfg.torch_grad_dtype)
         hashgrid_mlp_backward(gcfg, x, stage, params, dy.contiguous().float(), grads, dtable)
@@ -638,18 +660,21 @@ class HashGridMLPFunction(torch.autograd.Function):
 class HashGridMLP(torch.nn.Module):
     """The encoder followed by the NeRFace head of ipipp.com section 3:
     Linear(32, 64), ReLU, Linear(64, 64), ReLU, Linear(64, 4) with biases;
-    ``forward(x [N, 3]) -> [N, 4]`` (density and colour channels).  Weights
-    are fp32 masters initialised Xavier-uniform; biases are initialised as
-    torch.nn.Linear does, U(-1/sqrt(fan_in), 1/sqrt(fan_in)).  The matrix
-    cores read the weights as binary16."""
+    ``forward(x [N, 3]) -> [N, 4]`` (density and colour channels).  With
+    ``coord_inputs=3`` the head is jsqmd.com's TinyNeRF (section 4): the point
+    is concatenated before its encoding, Linear(35, 64) then the same layers.
+    Weights are fp32 masters initialised Xavier-uniform; biases are
+    initialised as torch.nn.Linear does, U(-1/sqrt(fan_in), 1/sqrt(fan_in)).
+    The matrix cores read the weights (and the head's inputs) as binary16."""
 
-    def __init__(self, table_dtype="f16", device="cuda", **encoder_kw):
+    def __init__(self, table_dtype="f16", device="cuda", coord_inputs: int = 0, **encoder_kw):
         super().__init__()
         self.encoder = HashGridEncoder(table_dtype=table_dtype, device=device, **encoder_kw)
         if self.encoder.cfg.out_features != 32:
             raise ValueError("the MLP head takes 32 encoded features (L * F = 32)")
+        fin1 = mlp_shapes(coord_inputs)["w1"][1]
         layers = []
-        for fin, fout in ((32, 64), (64, 64), (64, 4)):
+        for fin, fout in ((fin1, 64), (64, 64), (64, 4)):
             w = torch.empty((fout, fin), device=device)
             torch.nn.init.xavier_uniform_(w)
             b = torch.empty(fout, device=device).uniform_(-1.0 / fin ** 0.5, 1.0 / fin ** 0.5)

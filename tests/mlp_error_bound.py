@@ -77,15 +77,17 @@ def _f32sum(a, W):
 def bounds(e_exact, e_err, params, cache, grads, dy):
     """Bounds for y, de, dW1, db1, dW2, db2, dW3, db3 (the oracle's output
     keys, plus 'y'), and the count of uncertain ReLU decisions.
-      e_exact : the oracle's float64 encoding before rounding [n, 32];
-      e_err   : bound on the GPU encoding's fp32 error before rounding;
+      e_exact : the head's input before rounding, float64 [n, k] (the oracle's
+                encoding, or for the TinyNeRF head the point and its encoding);
+      e_err   : bound on the GPU input's fp32 error before rounding (a scalar,
+                or one per input column);
       params  : [W1, b1, W2, b2, W3, b3];  cache, grads : the oracle's (fp32 sums).
     """
     W1, b1, W2, b2, W3, b3 = (np.asarray(p, dtype=np.float64) for p in params)
     A1, A2, A3 = np.abs(W1), np.abs(W2), np.abs(W3)
     n = e_exact.shape[0]
     e, z1, h1, z2, h2 = cache["e"], cache["z1"], cache["h1"], cache["z2"], cache["h2"]
-    g33, g65, g5 = gamma(32), gamma(64), gamma(4)
+    g33, g65, g5 = gamma(W1.shape[1]), gamma(64), gamma(4)
     # forward
     de_in = rounding_step(e_exact, e_err)
     dz1 = (de_in @ A1.T) * (1 + g33) + 2 * g33 * (np.abs(e) @ A1.T + np.abs(b1))

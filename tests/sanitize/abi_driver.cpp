@@ -97,6 +97,11 @@ int main() {
     EXPECT(hashgrid_mlp_forward(&std_cfg, x, 16, t, nullptr, o, o, 1 << 20, nullptr) == HG_EINVAL);
     hg_mlp_grads mg{};
     EXPECT(hashgrid_mlp_backward(&std_cfg, x, 16, o, &mp, d, &mg, t, o, 1 << 20, nullptr) == HG_EINVAL);
+    const void *w = reinterpret_cast<const void *>(0x7000);
+    const float *bias = reinterpret_cast<const float *>(0x7100);
+    hg_mlp_params tiny{w, bias, w, bias, w, bias, 7};  // coord_inputs is 0 or 3
+    EXPECT(hashgrid_mlp_forward(&std_cfg, x, 16, t, &tiny, o, o, 1 << 20, nullptr) == HG_EINVAL);
+    EXPECT(std::strstr(hashgrid_last_error(), "coord_inputs") != nullptr);
     // Adam: every hyperparameter check
     float *p = reinterpret_cast<float *>(0x6000);
     hg_adam ok_opt{1e-2f, 0.9f, 0.999f, 1e-8f, 1};

@@ -70,11 +70,11 @@ hipError_t launch_encode_stage_f16(const LaunchParams &, const float *, int64_t,
 // Host-side size of the MLP backward's partials (the kernels' file holds the
 // real one); only workspace-size queries reach it here.
 size_t mlp_partials_bytes(int64_t n) { return (size_t)(n + 15) / 16 * 4 + 4096; }
-hipError_t launch_mlp_forward(const _Float16 *, int64_t, const MlpParams &, float *, hipStream_t) {
+hipError_t launch_mlp_forward(const _Float16 *, const float *, int64_t, const MlpParams &, float *, hipStream_t) {
     return reached("mlp forward");
 }
-hipError_t launch_mlp_backward(const _Float16 *, int64_t, const MlpParams &, const float *, float *, float *,
-                               const MlpGrads &, hipStream_t) {
+hipError_t launch_mlp_backward(const _Float16 *, const float *, int64_t, const MlpParams &, const float *, float *,
+                               float *, const MlpGrads &, hipStream_t) {
     return reached("mlp backward");
 }
 hipError_t launch_adam(const AdamParams &, int64_t, float *, float *, float *, float *, void *, bool, hipStream_t) {

@@ -160,6 +160,30 @@ def test_mlp_backward_refuses_half_gradients_before_launching(lib):
     assert "binned" in lib.hashgrid_last_error().decode()
 
 
+@pytest.mark.parametrize("coords", [1, 2, 4, 35, -3])
+def test_mlp_head_takes_zero_or_three_coordinate_inputs(lib, coords):
+    # coord_inputs selects the NeRFace head (0) or the TinyNeRF head (3); any
+    # other value is refused before anything is enqueued.
+    cfg = hg.HashGridConfig(table_dtype="f16")
+    c = cfg.c()
+    params = B._MlpParams(*[0x10000 + 0x1000 * i for i in range(6)], coords)
+    rc = lib.hashgrid_mlp_forward(ctypes.byref(c), 0x1000, 64, 0x40000, ctypes.byref(params), 0x50000, 0x100000,
+                                  64 * 64, None)
+    assert rc == B.HG_EINVAL and "coord_inputs" in lib.hashgrid_last_error().decode()
+    grads = B._MlpGrads(*[0x20000 + 0x1000 * i for i in range(6)])
+    rc = lib.hashgrid_mlp_backward(ctypes.byref(c), 0x1000, 64, 0x40000, ctypes.byref(params), 0x50000,
+                                   ctypes.byref(grads), 0x60000, 0x100000, 1 << 24, None)
+    assert rc == B.HG_EINVAL and "coord_inputs" in lib.hashgrid_last_error().decode()
+
+
+def test_mlp_parameter_shapes_of_both_heads():
+    assert hg.hashgrid.mlp_shapes(0)["w1"] == (64, 32)
+    assert hg.hashgrid.mlp_shapes(3)["w1"] == (64, 35)
+    assert hg.hashgrid.mlp_shapes(3)["w2"] == (64, 64)
+    with pytest.raises(ValueError):
+        hg.hashgrid.mlp_shapes(2)
+
+
 def test_half_table_alignment_is_four_bytes(lib):
     cfg = hg.HashGridConfig(table_dtype="f16")
     assert _call_forward(lib, cfg, table=0x2002) == B.HG_EINVAL

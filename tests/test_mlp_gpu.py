@@ -49,21 +49,27 @@ def close(got, ref, what):
     assert err <= TOL * scale, f"{what}: err {err:.3g} > {TOL} * {scale:.3g}"
 
 
-def run(oracle, w, bias="linear", grad_init=0.0, dy_scale=1.0, want_e=False):
+def run(oracle, w, bias="linear", grad_init=0.0, dy_scale=1.0, want_e=False, coords=0):
+    """coords = 3: the TinyNeRF head, whose input is [x, e] (W1 [64, 35]); the
+    oracle then takes that concatenation, and the encoding's part of its
+    dL/du (columns 3..34) is the table backward's upstream."""
     cfg = hg.HashGridConfig.of(w)
     x, t = I.make_points(w), I.make_table(w)
-    params = I.mlp_params(w.seed, bias_scale=bias)
+    params = I.mlp_params(w.seed, sizes=(32 + coords, 64, 64, 4), bias_scale=bias)
     dy = (I.dout_normal(w.seed + 7, w.n_points, 4).astype(np.float64) * dy_scale).astype(np.float32)
     P = [dev(a) for a in params]
     y, stage = hg.hashgrid_mlp_forward(cfg, dev(x), dev(t), P)
-    grads = [torch.full(hg.hashgrid.MLP_SHAPES[k], grad_init, device=DEV) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+    grads = [torch.full(a.shape, grad_init, device=DEV) for a in params]
     dtable = torch.zeros(cfg.table_shape, device=DEV)
     hg.hashgrid_mlp_backward(cfg, dev(x), stage, P, dev(dy), grads, dtable)
     g = oracle.grid_of(w)
     e = oracle.forward(g, x, t)
+    u = np.concatenate([x.astype(np.float64), e], axis=1) if coords else e
     W1, b1, W2, b2, W3, b3 = params
-    yr, cache = M.forward(e, W1, b1, W2, b2, W3, b3, round_fp16=True)
+    yr, cache = M.forward(u, W1, b1, W2, b2, W3, b3, round_fp16=True)
     gr = M.backward(cache, dy, W1, W2, W3)
+    gr["du"] = gr["de"]  # dL/du; its encoding columns are the table backward's upstream
+    gr["de"] = gr["de"][:, coords:]
     out = (cfg, y.cpu().numpy(), [a.cpu().numpy() for a in grads], dtable.cpu().numpy(), yr, gr, (x, g))
     if want_e:
         return out + ((e, t, params, cache, dy),)
@@ -160,6 +166,67 @@ def test_mlp_zero_biases_within_derived_bound(oracle, n):
     assert np.all(diff <= tb), float(np.max(diff - tb))
 
 
+@pytest.mark.parametrize("n", [16, 1000 + 7, 5 * 4096 + 3, (1 << 18) + 5])
+def test_tinynerf_head_matches_oracle(oracle, n):
+    # jsqmd.com section 4's TinyNeRF head: [x, e] -> Linear(35, 64), ReLU,
+    # Linear(64, 64), ReLU, Linear(64, 4); the coordinates enter the matrix
+    # cores as binary16 like the encoding.  The raw coordinates make the
+    # first layer's pre-activations cross zero across the batch, so a few
+    # ReLU decisions lie within the two sides' fp32 summation-order
+    # difference: every output, weight and bias gradient (dW1's coordinate
+    # columns included) and table gradient entry is held to the element-wise
+    # bound derived from that rounding (exact to a few fp32 roundings where no
+    # decision can flip), and y additionally to the 1e-3 bar.
+    w = I.resized(I.WORKLOADS["fused_mlp"], n)
+    print(f"tinynerf head n={n}", flush=True)
+    cfg, y, grads, dtable, yr, gr, (x, g), (e, t, params, cache, dy) = run(oracle, w, coords=3, want_e=True)
+    assert grads[0].shape == (64, 35)
+    close(y, yr, "y")
+    u = np.concatenate([x.astype(np.float64), e], axis=1)
+    u_err = np.concatenate([np.zeros(3), np.full(32, 1e-6 * float(np.max(np.abs(t.astype(np.float64)))))])
+    bd = EB.bounds(u, u_err, params, cache, dict(gr, de=gr["du"]), dy)
+    print(f"  uncertain ReLU decisions: {bd['uncertain_relu']}", flush=True)
+    checks = [("y", y, yr)] + [(name, got, gr[name]) for name, got in zip(NAMES, grads)]
+    for name, got, ref in checks:
+        diff = np.abs(np.asarray(got, dtype=np.float64) - ref)
+        assert np.all(diff <= bd[name]), (name, float(np.max(diff - bd[name])))
+    ref_t = oracle.backward(g, x, gr["de"].astype(np.float32))
+    tb = EB.table_bound(oracle, g, x, gr["de"], bd["de"][:, 3:], ref_t)
+    diff = np.abs(dtable.astype(np.float64) - ref_t)
+    assert np.all(diff <= tb), float(np.max(diff - tb))
+
+
+def test_tinynerf_gradients_accumulate_and_leave_the_head_unchanged():
+    # The TinyNeRF head adds its gradients into the caller's buffers, in a
+    # fixed order (a second call adds the same values); the NeRFace head run on
+    # the same points afterwards gives the bits it gives alone.
+    w = I.resized(I.WORKLOADS["fused_mlp"], 3000)
+    cfg = hg.HashGridConfig.of(w)
+    x, t = dev(I.make_points(w)), dev(I.make_table(w))
+    dy = dev(I.dout_normal(5, w.n_points, 4))
+    P3 = [dev(a) for a in I.mlp_params(w.seed, sizes=(35, 64, 64, 4))]
+    P0 = [dev(a) for a in I.mlp_params(w.seed)]
+    y0, st0 = hg.hashgrid_mlp_forward(cfg, x, t, P0)
+    g0 = [torch.zeros(a.shape, device=DEV) for a in P0]
+    d0 = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_mlp_backward(cfg, x, st0, P0, dy, g0, d0)
+    _, st3 = hg.hashgrid_mlp_forward(cfg, x, t, P3)
+    once = [torch.zeros(a.shape, device=DEV) for a in P3]
+    twice = [torch.full(a.shape, 0.5, device=DEV) for a in P3]
+    d1, d2 = torch.zeros(cfg.table_shape, device=DEV), torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_mlp_backward(cfg, x, st3, P3, dy, once, d1)
+    hg.hashgrid_mlp_backward(cfg, x, st3, P3, dy, twice, d2)
+    hg.hashgrid_mlp_backward(cfg, x, st3, P3, dy, twice, d2)
+    for a, b in zip(once, twice):
+        assert torch.allclose(b - 0.5, 2 * a, rtol=1e-6, atol=1e-6)
+    y0b, st0b = hg.hashgrid_mlp_forward(cfg, x, t, P0)
+    g0b = [torch.zeros(a.shape, device=DEV) for a in P0]
+    d0b = torch.zeros(cfg.table_shape, device=DEV)
+    hg.hashgrid_mlp_backward(cfg, x, st0b, P0, dy, g0b, d0b)
+    assert torch.equal(y0, y0b) and torch.equal(d0, d0b)
+    assert all(torch.equal(a, b) for a, b in zip(g0, g0b))
+
+
 def test_module_trains_one_step():
     torch.manual_seed(0)
     net = hg.HashGridMLP(device=DEV)
@@ -171,3 +238,16 @@ def test_module_trains_one_step():
     y.square().mean().backward()
     for p in (net.w1, net.b1, net.w2, net.b2, net.w3, net.b3, net.encoder.embeddings):
         assert p.grad is not None and torch.isfinite(p.grad.float()).all()
+
+
+def test_tinynerf_module_trains_one_step():
+    torch.manual_seed(1)
+    net = hg.HashGridMLP(device=DEV, coord_inputs=3)
+    assert tuple(net.w1.shape) == (64, 35)
+    x = torch.rand((4096, 3), device=DEV)
+    y = net(x)
+    assert y.shape == (4096, 4)
+    y.square().mean().backward()
+    for p in (net.w1, net.b1, net.w2, net.b2, net.w3, net.b3, net.encoder.embeddings):
+        assert p.grad is not None and torch.isfinite(p.grad.float()).all()
+    assert bool((net.w1.grad[:, :3] != 0).any())

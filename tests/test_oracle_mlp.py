@@ -43,6 +43,37 @@ def test_float64_network_matches_torch_autograd():
         np.testing.assert_allclose(g[name], tw.grad.numpy(), rtol=0, atol=1e-11, err_msg=name)
 
 
+def test_tinynerf_input_is_the_point_then_its_encoding():
+    # jsqmd.com section 4: TinyNeRF concatenates the raw point before its hash
+    # features and feeds Linear(35, 64), ReLU, Linear(64, 64), ReLU,
+    # Linear(64, 4).  The oracle takes that concatenation as its input u, and
+    # its dL/du splits into the point's part (the first 3 columns) and the
+    # encoding's (the upstream of the table backward).  Reference: the model
+    # built from torch.nn layers as the page writes it, in float64.
+    W1, b1, W2, b2, W3, b3 = I.mlp_params(11, sizes=(35, 64, 64, 4), bias_scale=0.1)
+    rng = np.random.default_rng(4)
+    x = rng.uniform(0.0, 1.0, (120, 3))
+    h = rng.standard_normal((120, 32)) * 0.3
+    dy = rng.standard_normal((120, 4))
+    y, cache = M.forward(np.concatenate([x, h], axis=1), W1, b1, W2, b2, W3, b3, round_fp16=False)
+    g = M.backward(cache, dy, W1, W2, W3)
+    net = torch.nn.Sequential(torch.nn.Linear(35, 64), torch.nn.ReLU(), torch.nn.Linear(64, 64), torch.nn.ReLU(),
+                              torch.nn.Linear(64, 4)).double()
+    with torch.no_grad():
+        for layer, (W, b) in zip((net[0], net[2], net[4]), ((W1, b1), (W2, b2), (W3, b3))):
+            layer.weight.copy_(torch.tensor(np.asarray(W, dtype=np.float64)))
+            layer.bias.copy_(torch.tensor(np.asarray(b, dtype=np.float64)))
+    xt = torch.tensor(x, requires_grad=True)
+    ht = torch.tensor(h, requires_grad=True)
+    ty = net(torch.cat([xt, ht], dim=-1))
+    ty.backward(torch.tensor(dy))
+    np.testing.assert_allclose(y, ty.detach().numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(g["de"][:, 3:], ht.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["de"][:, :3], xt.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dW1"], net[0].weight.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(g["db1"], net[0].bias.grad.numpy(), rtol=0, atol=1e-11)
+
+
 def test_weight_gradient_equals_central_difference():
     # The network is piecewise linear in each weight, so a small central
     # difference is exact unless a ReLU flips inside it.
