@@ -200,7 +200,8 @@ def measure_shapes(dev, n: int, iters: int) -> dict:
 
 def measure_fused_mlp(dev, iters: int) -> dict:
     """Encoder + MLP head (2^22 uniform points, standard grid with binary16
-    tables, 32-64-64-4): forward = binary16 encoding stage + head, backward =
+    tables, 32-64-64-4, and beside it the TinyNeRF head [x, e] -> 64 -> 64 -> 4):
+    forward = binary16 encoding stage + head, backward =
     head backward + weight-gradient reduction + table backward.  Algorithmic
     bytes per point: forward 12 (x) + 8 L F 2 (binary16 corners) + 16 (y);
     backward 12 (x) + 16 (dL/dy) + 2 L F (the stage) + 8 L F 4 (table
@@ -223,6 +224,11 @@ def measure_fused_mlp(dev, iters: int) -> dict:
     dtable = torch.zeros(cfg.table_shape, device=dev)
     fms = time_calls(lambda: hg.hashgrid_mlp_forward(cfg, x, t, P, y=y, stage=stage), iters)
     bms = time_calls(lambda: hg.hashgrid_mlp_backward(cfg, x, stage, P, dy, grads, dtable, workspace=ws), iters)
+    # The TinyNeRF head ([x, e] -> Linear(35, 64), ...) on the same grid and points.
+    P3 = [torch.from_numpy(a).to(dev) for a in inputs.mlp_params(w.seed, sizes=(35, 64, 64, 4))]
+    grads3 = [torch.zeros(a.shape, device=dev) for a in P3]
+    tfms = time_calls(lambda: hg.hashgrid_mlp_forward(cfg, x, t, P3, y=y, stage=stage), iters)
+    tbms = time_calls(lambda: hg.hashgrid_mlp_backward(cfg, x, stage, P3, dy, grads3, dtable, workspace=ws), iters)
     L, F = cfg.n_levels, cfg.n_features
     fb = 12 + 8 * L * F * 2 + 16
     bb = 12 + 16 + 2 * L * F + 8 * L * F * 4
@@ -232,6 +238,8 @@ def measure_fused_mlp(dev, iters: int) -> dict:
             "fwd_frac": fb * n / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bwd_frac": bb * n / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "step_frac": (fb + bb) * n / ((fms + bms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "tinynerf": {"fwd_us": tfms * 1e3, "bwd_us": tbms * 1e3,
+                         "step_points_per_s": n / ((tfms + tbms) * 1e-3)},
             # committed rocprofv3 summary: HBM traffic, L2 rates, MfmaUtil and fp16 MFMA throughput of the head
             "counters": counter_summary(load_counters("fused_mlp"))}
 
