@@ -519,24 +519,26 @@ def test_step_captured_in_a_graph_replays_like_eager(workspace):
             assert float((grad - ref_grad).abs().max()) <= 1e-6 * scale
 
 
-def test_head_input_grad_and_adam_captured_in_a_graph_replay_like_eager():
+@pytest.mark.parametrize("coords", [0, 3])
+def test_head_input_grad_and_adam_captured_in_a_graph_replay_like_eager(coords):
     # The other entry points under graph capture: encoder + MLP head forward and
-    # backward, dL/dx and the Adam step, with every buffer (stages, workspaces)
-    # allocated before capture.  Each replay starts from the same state, set by
-    # eager copies between replays, and matches the eager step bit for bit: the
+    # backward (the NeRFace head, or with coords = 3 the TinyNeRF head), dL/dx
+    # and the Adam step, with every buffer (stages, workspaces) allocated
+    # before capture.  Each replay starts from the same state, set by eager
+    # copies between replays, and matches the eager step bit for bit: the
     # binned table sums are exact and the weight gradients are reduced in a
     # fixed order.
     w = I.resized(I.WORKLOADS["fused_mlp"], 1 << 14)
     cfg = hg.HashGridConfig.of(w)
     n = w.n_points
     x, t = dev(I.make_points(w)), dev(I.make_table(w))
-    P = [dev(a) for a in I.mlp_params(w.seed)]
+    P = [dev(a) for a in I.mlp_params(w.seed, sizes=(32 + coords, 64, 64, 4))]
     dy = dev(I.dout_normal(w.seed + 7, n, 4))
     st_bytes, bw_bytes = hg.hashgrid_mlp_workspace_size(cfg, n)
     stage = torch.empty(st_bytes, dtype=torch.uint8, device=DEV)
     mws = torch.empty(bw_bytes, dtype=torch.uint8, device=DEV)
     y = torch.empty((n, 4), device=DEV)
-    grads = [torch.zeros(hg.hashgrid.MLP_SHAPES[k], device=DEV) for k in ("w1", "b1", "w2", "b2", "w3", "b3")]
+    grads = [torch.zeros(a.shape, device=DEV) for a in P]
     dtable = torch.zeros(cfg.table_shape, device=DEV)
     ws = I.resized(I.WORKLOADS["standard"], n)
     scfg = hg.HashGridConfig.of(ws)
